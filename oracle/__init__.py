@@ -1,0 +1,254 @@
+"""Plain CPU reference (oracle) of the routed-expert MoE layer.
+
+TEST INFRASTRUCTURE ONLY. The tests, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg are the only users; the product path
+(``expert_dispatch_amd``) never imports this package. It shares no code with
+the HIP library: the arithmetic lives in ``oracle.c`` (plain C, fp64 except
+for the single-precision router definition), this file only marshals numpy
+arrays.
+
+Sources followed (page title, section):
+  * "Three axes of Parallelism", Expert Parallel (EP) -> Producing assignments:
+    router scores [T,E], top-K ids and router weights, the token-major
+    assignment buffer, per-expert counts, offsets and the expert-major pack.
+  * same page, Dispatch, expert computation and combine: the receive-side
+    count matrix, the source-major -> expert-major reorder, E_local independent
+    MLPs, and the weighted sum of the K expert outputs per token.
+  * same page, Mapping experts to EP ranks: W_gate, W_val [E,d,f], W_out [E,f,d].
+  * "feat(parallelism): expert parallelism for the Nemotron-3 Nano MoE layers",
+    Design: the device-built permutation indices for the received buffer.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+
+# The one build line of the oracle (also used by __graft_entry__.build()).
+GCC_CMD = [
+    "gcc", "-O3", "-march=x86-64-v3", "-ffp-contract=off", "-fno-fast-math",
+    "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
+    os.path.join(_HERE, "oracle.c"), "-o", _SO, "-lm",
+]
+
+_lib = None
+
+
+def build():
+    subprocess.run(GCC_CMD, check=True)
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        L = ctypes.CDLL(_SO)
+        vp, i32p, i64p, f32p, f64p = (ctypes.c_void_p,) * 5
+        L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_route.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int64, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+        L.oracle_permute.argtypes = [vp, ctypes.c_int64, ctypes.c_int, vp, vp, vp, vp]
+        L.oracle_permute_recv.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                          vp, vp, vp, vp]
+        L.oracle_gather.argtypes = [vp, ctypes.c_int, ctypes.c_int64, vp, ctypes.c_int64,
+                                    ctypes.c_int, vp]
+        L.oracle_expert_ffn_rows.argtypes = [vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp,
+                                             ctypes.c_int64, vp]
+        L.oracle_combine.argtypes = [vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, vp, vp,
+                                     vp, vp, vp, vp]
+        for name in ("oracle_route", "oracle_permute", "oracle_permute_recv", "oracle_gather",
+                     "oracle_expert_ffn_rows", "oracle_combine"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _xtype(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return 0
+    if a.dtype == np.uint16:  # bf16 bit patterns
+        return 1
+    raise TypeError(f"oracle takes fp32 or bf16-as-uint16 arrays, got {a.dtype}")
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise OracleError(f"{what} failed with code {rc}")
+
+
+def _c(a, dtype=None):
+    a = np.asarray(a)
+    if dtype is not None:
+        a = a.astype(dtype, copy=False)
+    return np.ascontiguousarray(a)
+
+
+def route(x, w, bias, k: int, renorm: bool = True):
+    """Router scores, top-k ids and router weights. Returns (logits fp32 [T,E],
+    idx int32 [T,k], gates float64 [T,k])."""
+    x, w = _c(x), _c(w)
+    xt = _xtype(x)
+    if _xtype(w) != xt:
+        raise TypeError("x and w_router must have the same element type")
+    T, d = x.shape
+    d2, E = w.shape
+    assert d == d2
+    b = None if bias is None else _c(bias, np.float32)
+    logits = np.empty((T, E), np.float32)
+    idx = np.empty((T, k), np.int32)
+    gates = np.empty((T, k), np.float64)
+    _check(lib().oracle_route(_p(x), _p(w), xt, _p(b), T, d, E, k, int(bool(renorm)),
+                              _p(logits), _p(idx), _p(gates)), "oracle_route")
+    return logits, idx, gates
+
+
+def permute(idx, E: int):
+    """Expert-major packing of the flat assignments. Returns
+    (counts [E], offsets [E+1], perm_src [TK], dest [TK]), all int32."""
+    flat = _c(np.asarray(idx).reshape(-1), np.int32)
+    TK = flat.shape[0]
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    perm_src = np.empty(TK, np.int32)
+    dest = np.empty(TK, np.int32)
+    _check(lib().oracle_permute(_p(flat), TK, E, _p(counts), _p(offsets), _p(perm_src),
+                                _p(dest)), "oracle_permute")
+    return counts, offsets, perm_src, dest
+
+
+def permute_recv(recv_counts, N: int):
+    """Sender-major -> expert-major reorder of a received buffer of N rows."""
+    recv = _c(recv_counts, np.int32)
+    S, E_loc = recv.shape
+    counts = np.empty(E_loc, np.int32)
+    offsets = np.empty(E_loc + 1, np.int32)
+    perm_src = np.empty(N, np.int32)
+    dest = np.empty(N, np.int32)
+    _check(lib().oracle_permute_recv(_p(recv), S, E_loc, N, _p(counts), _p(offsets),
+                                     _p(perm_src), _p(dest)), "oracle_permute_recv")
+    return counts, offsets, perm_src, dest
+
+
+def gather(x, perm_src, k: int):
+    """x_perm[j] = x[perm_src[j] // k] (bitwise row copy)."""
+    x = _c(x)
+    ps = _c(perm_src, np.int32)
+    rows = ps.shape[0]
+    out = np.empty((rows,) + x.shape[1:], x.dtype)
+    d = int(np.prod(x.shape[1:]))
+    _check(lib().oracle_gather(_p(x), x.dtype.itemsize, d, _p(ps), rows, k, _p(out)),
+           "oracle_gather")
+    return out
+
+
+def expert_ffn_rows(x_perm, offsets, wg, wv, wo, rows=None):
+    """SwiGLU expert MLPs evaluated in double on the listed packed rows
+    (all rows if None). Returns float64 [len(rows), d]."""
+    x_perm, wg, wv, wo = _c(x_perm), _c(wg), _c(wv), _c(wo)
+    xt = _xtype(x_perm)
+    for w in (wg, wv, wo):
+        if _xtype(w) != xt:
+            raise TypeError("activations and expert weights must share an element type")
+    N, d = x_perm.shape
+    E, d2, f = wg.shape
+    assert d2 == d and wv.shape == wg.shape and wo.shape == (E, f, d)
+    off = _c(offsets, np.int32)
+    assert off.shape == (E + 1,)
+    rows = np.arange(N, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    y = np.empty((rows.shape[0], d), np.float64)
+    _check(lib().oracle_expert_ffn_rows(_p(x_perm), xt, N, d, f, E, _p(off), _p(wg), _p(wv),
+                                        _p(wo), _p(rows), rows.shape[0], _p(y)),
+           "oracle_expert_ffn_rows")
+    return y
+
+
+def combine(tokens, k: int, dest, gates, y, yrow=None, shared=None):
+    """out[r] = sum_s gates[t,s] * y[dest[t*k+s]] (+ shared[r]), t = tokens[r],
+    in double. gates None = weight 1; yrow maps packed rows to rows of y."""
+    tokens = _c(tokens, np.int32)
+    dest = _c(np.asarray(dest).reshape(-1), np.int32)
+    g = None if gates is None else _c(np.asarray(gates).reshape(-1), np.float64)
+    y = _c(y, np.float64)
+    yr = None if yrow is None else _c(yrow, np.int64)
+    sh = None if shared is None else _c(shared, np.float64)
+    d = y.shape[1]
+    out = np.empty((tokens.shape[0], d), np.float64)
+    _check(lib().oracle_combine(_p(tokens), tokens.shape[0], k, d, _p(dest), _p(g), _p(y),
+                                _p(yr), _p(sh), _p(out)), "oracle_combine")
+    return out
+
+
+def swiglu_shared(x, wg, wv, wo, rows=None):
+    """Sum of always-on shared experts on token rows: sum_q SwiGLU_q(x[t]),
+    in double, q ascending. wg/wv [Q,d,f], wo [Q,f,d]."""
+    x = _c(x)
+    T = x.shape[0]
+    rows = np.arange(T, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    total = None
+    for q in range(wg.shape[0]):
+        part = expert_ffn_rows(x, np.array([0, T], np.int32), wg[q:q + 1], wv[q:q + 1],
+                               wo[q:q + 1], rows)
+        total = part if total is None else total + part
+    return total
+
+
+def moe_layer(inp: dict, tokens=None):
+    """The whole layer on a token-routed workload dict (see
+    expert_dispatch_amd.workloads). Returns a dict of every intermediate.
+    With ``tokens`` given, the FFN and combine are evaluated only for the
+    packed rows those tokens need and for those tokens."""
+    k = inp["k"]
+    logits, idx, gates = route(inp["x"], inp["w_router"], inp.get("bias"), k,
+                               inp.get("renorm", True))
+    E = inp["w_gate"].shape[0]
+    counts, offsets, perm_src, dest = permute(idx, E)
+    x_perm = gather(inp["x"], perm_src, k)
+    T = inp["x"].shape[0]
+    tok = np.arange(T, dtype=np.int32) if tokens is None else _c(tokens, np.int32)
+    need = np.unique(dest.reshape(T, k)[tok].reshape(-1)).astype(np.int64)
+    y_rows = expert_ffn_rows(x_perm, offsets, inp["w_gate"], inp["w_val"], inp["w_out"], need)
+    yrow = np.full(T * k, -1, np.int64)
+    yrow[need] = np.arange(need.shape[0])
+    shared = None
+    if inp.get("shared_w_gate") is not None:
+        shared = swiglu_shared(inp["x"], inp["shared_w_gate"], inp["shared_w_val"],
+                               inp["shared_w_out"], tok.astype(np.int64))
+    out = combine(tok, k, dest, gates, y_rows, yrow, shared)
+    return dict(logits=logits, idx=idx, gates=gates, counts=counts, offsets=offsets,
+                perm_src=perm_src, dest=dest, x_perm=x_perm, y_rows=need, y=y_rows,
+                shared=shared, tokens=tok, out=out)
+
+
+def moe_recv_layer(inp: dict, rows=None):
+    """One EP rank's receive side: reorder, expert MLPs, unweighted un-permute
+    back to sender-major order. ``rows`` restricts the evaluated received rows."""
+    N = inp["x_recv"].shape[0]
+    counts, offsets, perm_src, dest = permute_recv(inp["recv_counts"], N)
+    x_perm = gather(inp["x_recv"], perm_src, 1)
+    r = np.arange(N, dtype=np.int32) if rows is None else _c(rows, np.int32)
+    need = np.unique(dest[r]).astype(np.int64)
+    y_rows = expert_ffn_rows(x_perm, offsets, inp["w_gate"], inp["w_val"], inp["w_out"], need)
+    yrow = np.full(N, -1, np.int64)
+    yrow[need] = np.arange(need.shape[0])
+    out = combine(r, 1, dest, None, y_rows, yrow, None)
+    return dict(counts=counts, offsets=offsets, perm_src=perm_src, dest=dest, x_perm=x_perm,
+                y_rows=need, y=y_rows, rows=r, out=out)

@@ -1,0 +1,106 @@
+/*
+ * oracle.h -- plain, slow CPU reference of the routed-expert MoE layer.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link,
+ * load or call this library: only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg do. It shares no source with the HIP library.
+ *
+ * Every floating-point result is computed in double from exactly widened
+ * inputs, except the router logits, whose definition is single precision
+ * (see oracle_route). Element type codes: 0 = fp32, 1 = bf16 (raw 16-bit
+ * patterns, the upper half of an IEEE binary32).
+ *
+ * Return value of every call: 0 on success, a negative number on a bad
+ * argument or an input that breaks the stated preconditions.
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Number of OpenMP threads the oracle's parallel loops use. */
+int oracle_num_threads(void);
+
+/*
+ * Router [Three axes of Parallelism, section "Expert Parallel (EP)" ->
+ * "Producing assignments"]: every token is scored against all E experts and
+ * the top k are kept together with their router weights.
+ *   logits[t,e] = fl32( sum_i x[t,i] * w[i,e] ) (+ bias[e])
+ * where the sum is taken in single precision, i ascending, one fused
+ * multiply-add per term starting from +0, and the bias is one fp32 add.
+ * Selection orders experts by (logit descending, index ascending); slot 0
+ * holds the largest. gates[t,s] = exp(l_s - l_0) / sum over the k selected
+ * (renorm != 0) or over all E experts (renorm == 0), in double.
+ *   x [T,d], w [d,E] (type xtype), bias [E] fp32 or NULL,
+ *   logits [T,E] fp32 out, idx [T,k] out, gates [T,k] double out.
+ */
+int oracle_route(const void* x, const void* w, int xtype, const float* bias,
+                 int64_t T, int d, int E, int k, int renorm,
+                 float* logits, int32_t* idx, double* gates);
+
+/*
+ * Expert-major packing [Three axes of Parallelism, "Producing assignments"]:
+ * counts[e] = number of flat assignments a = t*k+s with idx[a] == e;
+ * offsets[0] = 0, offsets[e+1] = offsets[e] + counts[e];
+ * expert e's region [offsets[e], offsets[e+1]) holds its assignments in
+ * ascending a. perm_src[j] = a of packed row j, dest[a] = its packed row.
+ * Fails (-2) if an id lies outside [0,E).
+ */
+int oracle_permute(const int32_t* idx, int64_t TK, int E,
+                   int32_t* counts, int32_t* offsets,
+                   int32_t* perm_src, int32_t* dest);
+
+/*
+ * Receive-side reorder [Three axes of Parallelism, "Dispatch, expert
+ * computation and combine"; Modalities PR "expert parallelism for the
+ * Nemotron-3 Nano MoE layers", section "Design"]: recv[i,j] rows came from
+ * sender i for local expert j; the N rows are sender-major and, inside a
+ * sender, grouped by local expert ascending. The reorder is the same stable
+ * expert-major packing as oracle_permute with one assignment per row.
+ * Fails (-2) if any count is negative or the counts do not sum to N.
+ */
+int oracle_permute_recv(const int32_t* recv, int S, int E_loc, int64_t N,
+                        int32_t* counts, int32_t* offsets,
+                        int32_t* perm_src, int32_t* dest);
+
+/* x_perm[j,:] = x[perm_src[j] / k, :], a bitwise row copy. */
+int oracle_gather(const void* x, int elem_bytes, int64_t d,
+                  const int32_t* perm_src, int64_t rows, int k, void* x_perm);
+
+/*
+ * Expert SwiGLU MLPs on the packed rows [Three axes of Parallelism,
+ * "Mapping experts to EP ranks" (W_gate, W_val, W_out) and "Dispatch, expert
+ * computation and combine" (E_local independent MLPs on contiguous rows)]:
+ * for packed row j in expert e's region,
+ *   g_c = sum_i x[j,i] Wg[e,i,c],  v_c = sum_i x[j,i] Wv[e,i,c],
+ *   h_c = g_c / (1 + exp(-g_c)) * v_c,  y[j,o] = sum_c h_c Wo[e,c,o],
+ * all in double with no intermediate rounding. Only the listed rows are
+ * evaluated: y is [nrows, d], row r holding packed row rows[r].
+ *   x [N,d], Wg/Wv [E,d,f], Wo [E,f,d] (type xtype), offsets [E+1].
+ */
+int oracle_expert_ffn_rows(const void* x, int xtype, int64_t N, int d, int f, int E,
+                           const int32_t* offsets,
+                           const void* wg, const void* wv, const void* wo,
+                           const int64_t* rows, int64_t nrows, double* y);
+
+/*
+ * Weighted combine [Three axes of Parallelism, "Dispatch, expert computation
+ * and combine": undo the packing, weight each expert output by its router
+ * weight, sum the k outputs of each token]:
+ *   out[r,:] = sum_{s ascending} g[t,s] * y[dest[t*k+s],:] (+ shared[r,:])
+ * for t = tokens[r]. gates NULL means weight 1. yrow maps a packed row to its
+ * row in y (NULL: y is indexed by the packed row itself; -1: missing -> -3).
+ */
+int oracle_combine(const int32_t* tokens, int64_t ntok, int k, int64_t d,
+                   const int32_t* dest, const double* gates,
+                   const double* y, const int64_t* yrow,
+                   const double* shared, double* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

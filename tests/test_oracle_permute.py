@@ -1,0 +1,110 @@
+"""Pins of the oracle's expert-major packing and receive-side reorder.
+
+"Three axes of Parallelism", Expert Parallel (EP) -> Producing assignments:
+count the assignments per expert, offsets from the cumulative counts, write
+each assignment into its expert's region. The Modalities EP page's tests check
+the same three things held here: the result is a permutation, it groups by
+expert, and it matches a loop reference; on top of that the packing is held
+to numpy's stable argsort and bincount, and the receive-side reorder to a
+closed form built block by block from the count matrix.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from expert_dispatch_amd import workloads as W
+
+
+def _check_invariants(key, E, counts, offsets, perm_src, dest):
+    n = key.shape[0]
+    assert counts.sum() == n and offsets[-1] == n and offsets[0] == 0
+    assert (np.diff(offsets) == counts).all()
+    # bijection between assignments and packed rows
+    assert sorted(perm_src.tolist()) == list(range(n))
+    np.testing.assert_array_equal(dest[perm_src], np.arange(n))
+    for e in range(E):
+        seg = perm_src[offsets[e]:offsets[e + 1]]
+        assert (key[seg] == e).all()          # groups by expert
+        assert (np.diff(seg) > 0).all()       # stable: ascending flat order
+
+
+def _loop_reference(flat, E):
+    # for every expert, its assignments in row-major (token, slot) order
+    parts = [np.argwhere(flat == e)[:, 0] for e in range(E)]
+    return np.concatenate(parts) if parts else np.zeros(0, np.int64)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "qwen3_small", "dsv2_small_empty4", "stress_small"])
+def test_pack_matches_libraries_and_loop(name):
+    inp = W.generate(W.get(name))
+    _, idx, _ = oracle.route(inp["x"], inp["w_router"], inp["bias"], inp["k"])
+    E = inp["w_gate"].shape[0]
+    counts, offsets, perm_src, dest = oracle.permute(idx, E)
+    flat = idx.reshape(-1)
+    np.testing.assert_array_equal(counts, np.bincount(flat, minlength=E))
+    np.testing.assert_array_equal(offsets[1:], np.cumsum(np.bincount(flat, minlength=E)))
+    np.testing.assert_array_equal(perm_src, np.argsort(flat, kind="stable"))
+    np.testing.assert_array_equal(perm_src, _loop_reference(flat, E))
+    _check_invariants(flat, E, counts, offsets, perm_src, dest)
+
+
+def test_pack_empty_and_single_expert_cases():
+    counts, offsets, perm_src, dest = oracle.permute(np.zeros(0, np.int32), 5)
+    assert counts.tolist() == [0] * 5 and offsets.tolist() == [0] * 6
+    flat = np.full(37, 3, np.int32)               # every assignment to one expert
+    counts, offsets, perm_src, dest = oracle.permute(flat, 5)
+    assert counts.tolist() == [0, 0, 0, 37, 0]
+    np.testing.assert_array_equal(perm_src, np.arange(37))
+    with pytest.raises(oracle.OracleError):
+        oracle.permute(np.array([0, 5], np.int32), 5)
+
+
+def _recv_closed_form(recv):
+    """dest(r) = offsets[j] + sum_{i'<i} recv[i',j] + (r - start of block (i,j))."""
+    S, E = recv.shape
+    offsets = np.concatenate([[0], np.cumsum(recv.sum(axis=0))])
+    dest = []
+    for i in range(S):
+        for j in range(E):
+            base = offsets[j] + recv[:i, j].sum()
+            dest.extend(range(base, base + recv[i, j]))
+    return np.array(dest, np.int64)
+
+
+@pytest.mark.parametrize("name", ["ep_share_small", "ep_rank_share"])
+def test_recv_reorder_closed_form_and_stable_sort(name):
+    cfg = W.get(name)
+    rng = np.random.default_rng(cfg.seed)
+    p = rng.dirichlet(np.full(cfg.S * cfg.E, cfg.alpha))
+    recv = rng.multinomial(cfg.N, p).astype(np.int32).reshape(cfg.S, cfg.E)
+    counts, offsets, perm_src, dest = oracle.permute_recv(recv, cfg.N)
+    np.testing.assert_array_equal(dest, _recv_closed_form(recv))
+    keys = np.repeat(np.tile(np.arange(cfg.E), cfg.S), recv.reshape(-1))
+    np.testing.assert_array_equal(perm_src, np.argsort(keys, kind="stable"))
+    np.testing.assert_array_equal(counts, recv.sum(axis=0))
+    _check_invariants(keys, cfg.E, counts, offsets, perm_src, dest)
+
+
+def test_recv_reorder_round_trip_and_errors():
+    inp = W.generate(W.get("ep_share_small"))
+    inp = W.zero_expert_column(inp, 2)
+    N = inp["x_recv"].shape[0]
+    counts, offsets, perm_src, dest = oracle.permute_recv(inp["recv_counts"], N)
+    assert counts[2] == 0
+    xp = oracle.gather(inp["x_recv"], perm_src, 1)
+    np.testing.assert_array_equal(xp[dest], inp["x_recv"])      # un-permute restores it
+    bad = inp["recv_counts"].copy()
+    bad[0, 0] += 1
+    with pytest.raises(oracle.OracleError):
+        oracle.permute_recv(bad, N)
+
+
+def test_gather_reads_each_token_for_each_slot():
+    inp = W.generate(W.get("qwen3_small"))
+    k = inp["k"]
+    _, idx, _ = oracle.route(inp["x"], inp["w_router"], inp["bias"], k)
+    _, _, perm_src, dest = oracle.permute(idx, inp["w_gate"].shape[0])
+    xp = oracle.gather(inp["x"], perm_src, k)
+    T = inp["x"].shape[0]
+    for a in range(0, T * k, 5):
+        np.testing.assert_array_equal(xp[dest[a]], inp["x"][a // k])
