@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Throughput of the routed-expert MoE layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+
+One step = one pass of the whole hot path over one batch: router (scores,
+top-k, weights) -> expert-major packing -> grouped SwiGLU gate/up -> down ->
+weighted combine (plus the shared experts where the workload has them; the
+receive-side workload runs the device reorder instead of router + packing and
+un-permutes back to sender-major order). Inputs are seeded synthetic tensors
+already resident in HBM; every buffer is allocated before timing, so the timed
+region is kernel launches only. Per-stage times come from HIP events recorded
+on the stream the kernels are launched on. Prints one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec at 1 GPU; % bf16 MFMA peak (GEMM), % HBM BW (permute)"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_MFMA_BF16_TFS = 2500.0    # dense bf16 matrix peak
+PEAK_MFMA_F32_TFS = 157.3      # used for the fp32 path (vector fp32 peak)
+PEAK_VALU_F32_TFS = 157.3      # fp32 vector peak: 256 CUs x 2.4 GHz x 256 flop/clk
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="qwen3_30b_a3b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU work of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def to_dev(a, torch):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def stage_work(cfg, counts, es):
+    """Algorithmic flops and bytes of one launch of each stage."""
+    T, k, d, f, E = cfg.T, cfg.k, cfg.d, cfg.f, cfg.E
+    rows = cfg.rows
+    active = int((counts > 0).sum())
+    w = {}
+    if cfg.kind == "routed":
+        w["route"] = dict(flops=2.0 * T * d * E,
+                          bytes=T * d * es + d * E * es + E * 4 + T * E * 4 + 2 * T * k * 4,
+                          bound="alu")
+        w["permute"] = dict(flops=0.0, bytes=(T + rows) * d * es + 4 * rows * 4, bound="hbm")
+    else:
+        w["permute_recv"] = dict(flops=0.0, bytes=2 * rows * d * es + 2 * rows * 4, bound="hbm")
+    w["gate_up"] = dict(flops=4.0 * rows * d * f,
+                        bytes=rows * d * es + active * 2 * d * f * es + rows * f * es)
+    w["down"] = dict(flops=2.0 * rows * f * d,
+                     bytes=rows * f * es + active * f * d * es + rows * d * 4)
+    if cfg.shared:
+        fs = cfg.shared * f
+        w["shared_gate_up"] = dict(flops=4.0 * T * d * fs,
+                                   bytes=T * d * es + 2 * d * fs * es + T * fs * es)
+        w["shared_down"] = dict(flops=2.0 * T * fs * d, bytes=T * fs * es + fs * d * es + T * d * 4)
+    units = T if cfg.kind == "routed" else rows
+    w["combine"] = dict(flops=2.0 * rows * d,
+                        bytes=rows * d * 4 + units * d * 4 + rows * 8
+                        + (units * d * 4 if cfg.shared else 0), bound="hbm")
+    mfma_peak = PEAK_MFMA_BF16_TFS if es == 2 else PEAK_MFMA_F32_TFS
+    for name, v in w.items():
+        if "bound" not in v:
+            ai = v["flops"] / max(v["bytes"], 1)
+            v["bound"] = "mfma" if ai * PEAK_HBM_GBS * 1e9 > mfma_peak * 1e12 else "hbm"
+    return w
+
+
+def roofline_entry(v, us, es):
+    if v["bound"] == "hbm":
+        ach = v["bytes"] / (us * 1e-6) / 1e9
+        return dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=ach / PEAK_HBM_GBS)
+    if v["bound"] == "alu":
+        ach = v["flops"] / (us * 1e-6) / 1e12
+        return dict(bound="alu", achieved=ach, peak=PEAK_VALU_F32_TFS, unit="TFLOP/s",
+                    frac=ach / PEAK_VALU_F32_TFS)
+    peak = PEAK_MFMA_BF16_TFS if es == 2 else PEAK_MFMA_F32_TFS
+    ach = v["flops"] / (us * 1e-6) / 1e12
+    return dict(bound="mfma", achieved=ach, peak=peak, unit="TFLOP/s", frac=ach / peak)
+
+
+def traffic_for(kernel: str, workload: str, per_launch_alg: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current source of the kernel; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        ent = rec.get(workload, {}).get(kernel)
+        if not ent:
+            return None
+        src = os.path.join(ROOT, ent["source"])
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if sha != ent["source_sha256"]:
+            return None
+        return float(ent["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(cfg, inp, target_s: float):
+    import oracle
+    if cfg.kind == "routed":
+        def run(n):
+            sub = dict(inp, x=inp["x"][:n])
+            t = time.perf_counter()
+            oracle.moe_layer(sub)
+            return time.perf_counter() - t
+        total = cfg.T
+    else:
+        def run(n):
+            t = time.perf_counter()
+            oracle.moe_recv_layer(inp, rows=np.arange(n, dtype=np.int32))
+            return time.perf_counter() - t
+        total = cfg.N
+    n0 = min(total, 16)
+    t0 = run(n0)
+    n = int(min(total, max(n0, n0 * target_s / max(t0, 1e-3))))
+    t = run(n)
+    unit_name = "tokens" if cfg.kind == "routed" else "rows"
+    return dict(value=n / t, unit=f"{unit_name}/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"first {n} of {total} {unit_name} of the same workload (same weights), "
+                       f"whole layer in the oracle, {t:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer runs on one GPU's share; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from expert_dispatch_amd import ops
+    from expert_dispatch_amd import workloads as W
+
+    cfg = W.get(args.config)
+    es = 2 if cfg.dtype == "bf16" else 4
+    log(f"[bench] generating {cfg.name}")
+    inp = W.generate(cfg)
+    torch.cuda.set_device(0)
+    dev = {k: to_dev(inp.get(k), torch) for k in
+           ("x", "w_router", "bias", "w_gate", "w_val", "w_out", "x_recv", "recv_counts")}
+    E, d, f = cfg.E, cfg.d, cfg.f
+    rows = cfg.rows
+    xdt = torch.bfloat16 if es == 2 else torch.float32
+    cuda = torch.device("cuda")
+    # every buffer of the step, allocated once
+    bufs = dict(
+        counts=torch.empty(E, dtype=torch.int32, device=cuda),
+        offsets=torch.empty(E + 1, dtype=torch.int32, device=cuda),
+        perm_src=torch.empty(rows, dtype=torch.int32, device=cuda),
+        dest=torch.empty(rows, dtype=torch.int32, device=cuda),
+        x_perm=torch.empty((rows, d), dtype=xdt, device=cuda),
+    )
+    h = torch.empty((rows, f), dtype=xdt, device=cuda)
+    y = torch.empty((rows, d), dtype=torch.float32, device=cuda)
+    units = cfg.units
+    out = torch.empty((units, d), dtype=torch.float32, device=cuda)
+    shared = None
+    if cfg.kind == "routed":
+        logits = torch.empty((cfg.T, E), dtype=torch.float32, device=cuda)
+        idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=cuda)
+        gates = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=cuda)
+        ws = torch.empty(max(1, ops.permute_workspace(cfg.T, cfg.k, E)), dtype=torch.uint8,
+                         device=cuda)
+        if cfg.shared:
+            shared = dict(
+                wg=to_dev(np.concatenate(list(inp["shared_w_gate"]), axis=1)[None], torch),
+                wv=to_dev(np.concatenate(list(inp["shared_w_val"]), axis=1)[None], torch),
+                wo=to_dev(np.concatenate(list(inp["shared_w_out"]), axis=0)[None], torch),
+                off=torch.tensor([0, cfg.T], dtype=torch.int32, device=cuda),
+                h=torch.empty((cfg.T, cfg.shared * f), dtype=xdt, device=cuda),
+                y=torch.empty((cfg.T, d), dtype=torch.float32, device=cuda))
+
+    stages = (["route", "permute"] if cfg.kind == "routed" else ["permute_recv"]) + \
+        ["gate_up", "down"] + (["shared_gate_up", "shared_down"] if shared else []) + ["combine"]
+
+    def step(ev=None):
+        i = 0
+        if ev is not None:
+            ev[0].record()
+        if cfg.kind == "routed":
+            ops.route(dev["x"], dev["w_router"], dev["bias"], cfg.k, out=(logits, idx, gates))
+            if ev is not None: ev[1].record()
+            ops.permute(idx, dev["x"], E, out=bufs, workspace=ws)
+            i = 2
+        else:
+            ops.permute_recv(dev["recv_counts"], dev["x_recv"], out=bufs)
+            i = 1
+        if ev is not None: ev[i].record()
+        ops.ffn_gate_up(bufs["x_perm"], bufs["offsets"], dev["w_gate"], dev["w_val"], h=h)
+        if ev is not None: ev[i + 1].record()
+        ops.ffn_down(h, bufs["offsets"], dev["w_out"], y=y)
+        if ev is not None: ev[i + 2].record()
+        i += 3
+        y_sh = None
+        if shared:
+            ops.ffn_gate_up(dev["x"], shared["off"], shared["wg"], shared["wv"], h=shared["h"])
+            if ev is not None: ev[i].record()
+            ops.ffn_down(shared["h"], shared["off"], shared["wo"], y=shared["y"])
+            if ev is not None: ev[i + 1].record()
+            i += 2
+            y_sh = shared["y"]
+        if cfg.kind == "routed":
+            ops.combine(y, bufs["dest"], gates, cfg.k, y_shared=y_sh, out=out)
+        else:
+            ops.combine(y, bufs["dest"], None, 1, out=out)
+        if ev is not None: ev[i].record()
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    n_ev = len(stages) + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start.record()
+    for s in range(args.steps):
+        step(evs[s])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+    stage_us = {}
+    for j, name in enumerate(stages):
+        stage_us[name] = float(np.mean([evs[s][j].elapsed_time(evs[s][j + 1])
+                                        for s in range(args.steps)]) * 1e3)
+
+    counts = bufs["counts"].cpu().numpy()
+    work = stage_work(cfg, counts, es)
+    stage_rep = {}
+    for name in stages:
+        r = roofline_entry(work[name], stage_us[name], es)
+        stage_rep[name] = dict(us=round(stage_us[name], 2), bound=r["bound"],
+                               achieved=round(r["achieved"], 1), unit=r["unit"],
+                               frac=round(r["frac"], 4), alg_flops=work[name]["flops"],
+                               alg_bytes=work[name]["bytes"])
+    gemm = [n for n in stages if n in ("gate_up", "down", "shared_gate_up", "shared_down")]
+    dominant = max(stages, key=lambda n: stage_us[n])
+    dom = roofline_entry(work[dominant], stage_us[dominant], es)
+    traffic = traffic_for(dominant, cfg.name, work[dominant]["bytes"])
+    gemm_flops = sum(work[n]["flops"] for n in gemm)
+    gemm_us = sum(stage_us[n] for n in gemm)
+    value = units / (ms * 1e-3)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s" if cfg.kind == "routed" else "received rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if es == 2 else "f32",
+        "data": "synthetic (seeded Gaussian inputs and weights of the stated shapes)",
+        "config": {"workload": cfg.name, "description": cfg.description, "T": cfg.T,
+                   "k": cfg.k, "N": cfg.N, "d": d, "f": f, "E": E, "shared": cfg.shared,
+                   "rows": rows, "load_max_over_mean": round(float(counts.max() / max(counts.mean(), 1e-9)), 3),
+                   "empty_experts": int((counts == 0).sum())},
+        "roofline": {"kernel": dominant, "bound": dom["bound"], "achieved": round(dom["achieved"], 1),
+                     "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4),
+                     "traffic": traffic},
+        "gemm_mfma_frac": round(gemm_flops / (gemm_us * 1e-6) / 1e12 / (PEAK_MFMA_BF16_TFS if es == 2 else PEAK_MFMA_F32_TFS), 4),
+        "stages": stage_rep,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] oracle CPU baseline")
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+// Weighted combine / un-permute.
+//
+// "Three axes of Parallelism", Dispatch, expert computation and combine: undo
+// the original packing, multiply each expert output by its router weight and
+// sum the K outputs of each token, restoring [T,D]. Written as a gather per
+// token (the deterministic form of the scatter-add, no atomics): one
+// wavefront per token reads its k packed rows (indices and weights held in
+// lanes 0..k-1 and broadcast by shuffles), sums them in fp32 in slot order,
+// adds the always-on shared-expert row if given, and writes the token once.
+#include "common.hpp"
+
+namespace moe {
+
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+    static __device__ __forceinline__ void load(const float* p, float (&v)[4]) {
+        const f32x4 u = *reinterpret_cast<const f32x4*>(p);
+        v[0] = u[0]; v[1] = u[1]; v[2] = u[2]; v[3] = u[3];
+    }
+    static __device__ __forceinline__ void store(float* p, const float (&v)[4]) {
+        f32x4 u = {v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(p) = u;
+    }
+};
+template <> struct Vec4<uint16_t> {
+    static __device__ __forceinline__ void load(const uint16_t* p, float (&v)[4]) {
+        const u32x2 u = *reinterpret_cast<const u32x2*>(p);
+        v[0] = __uint_as_float(u[0] << 16);
+        v[1] = __uint_as_float(u[0] & 0xffff0000u);
+        v[2] = __uint_as_float(u[1] << 16);
+        v[3] = __uint_as_float(u[1] & 0xffff0000u);
+    }
+    static __device__ __forceinline__ void store(uint16_t* p, const float (&v)[4]) {
+        u32x2 u;
+        u[0] = (unsigned)f32_to_bf16(v[0]) | ((unsigned)f32_to_bf16(v[1]) << 16);
+        u[1] = (unsigned)f32_to_bf16(v[2]) | ((unsigned)f32_to_bf16(v[3]) << 16);
+        *reinterpret_cast<u32x2*>(p) = u;
+    }
+};
+
+template <typename YT, typename ST, typename OT, bool VEC>
+__global__ __launch_bounds__(256) void combine_kernel(
+    const YT* __restrict__ y, const int32_t* __restrict__ dest, const float* __restrict__ gates,
+    int T, int k, int d, const ST* __restrict__ shared, OT* __restrict__ out)
+{
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T) return;
+    const int lane = lane_id();
+    const long long rows = (long long)T * k;
+    int my_j = -1;
+    float my_g = 0.0f;
+    if (lane < k) {
+        my_j = dest[(size_t)t * k + lane];
+        if (my_j < 0 || my_j >= rows) my_j = -1;
+        my_g = gates ? gates[(size_t)t * k + lane] : 1.0f;
+    }
+    OT* o = out + (size_t)t * d;
+    if constexpr (VEC) {
+        constexpr int U = 2;
+        for (int c0 = lane * 4; c0 < d; c0 += kWave * 4 * U) {
+            float acc[U][4];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[u][q] = 0.0f;
+            for (int s = 0; s < k; ++s) {
+                const int j = __shfl(my_j, s, kWave);
+                const float g = __shfl(my_g, s, kWave);
+                if (j < 0) continue;
+                const YT* yr = y + (size_t)j * d;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + u * kWave * 4;
+                    if (c < d) {
+                        float v[4];
+                        Vec4<YT>::load(yr + c, v);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[u][q] = __builtin_fmaf(g, v[q], acc[u][q]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * kWave * 4;
+                if (c < d) {
+                    if (shared) {
+                        float v[4];
+                        Vec4<ST>::load(shared + (size_t)t * d + c, v);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[u][q] += v[q];
+                    }
+                    Vec4<OT>::store(o + c, acc[u]);
+                }
+            }
+        }
+    } else {
+        for (int c = lane; c < d; c += kWave) {
+            float acc = 0.0f;
+            for (int s = 0; s < k; ++s) {
+                const int j = __shfl(my_j, s, kWave);
+                const float g = __shfl(my_g, s, kWave);
+                if (j < 0) continue;
+                acc = __builtin_fmaf(g, Elem<YT>::load(y, (size_t)j * d + c), acc);
+            }
+            if (shared) acc += Elem<ST>::load(shared, (size_t)t * d + c);
+            Elem<OT>::store(out, (size_t)t * d + c, acc);
+        }
+    }
+}
+
+template <typename YT, typename ST, typename OT>
+static hipError_t launch_combine_t(const void* y, const int32_t* dest, const float* gates, int T,
+                                   int k, int d, const void* sh, void* out, hipStream_t st)
+{
+    const dim3 grid((T + 3) / 4);
+    auto al = [](const void* p, size_t a) { return p == nullptr || (uintptr_t)p % a == 0; };
+    const bool vec = d % 4 == 0 && al(y, 4 * sizeof(YT)) && al(sh, 4 * sizeof(ST)) &&
+                     al(out, 4 * sizeof(OT));
+    if (vec)
+        combine_kernel<YT, ST, OT, true><<<grid, 256, 0, st>>>(
+            (const YT*)y, dest, gates, T, k, d, (const ST*)sh, (OT*)out);
+    else
+        combine_kernel<YT, ST, OT, false><<<grid, 256, 0, st>>>(
+            (const YT*)y, dest, gates, T, k, d, (const ST*)sh, (OT*)out);
+    return hipGetLastError();
+}
+
+template <typename YT, typename ST>
+static hipError_t launch_combine_o(moe_dtype out_dt, const void* y, const int32_t* dest,
+                                   const float* gates, int T, int k, int d, const void* sh,
+                                   void* out, hipStream_t st)
+{
+    if (out_dt == MOE_BF16) return launch_combine_t<YT, ST, uint16_t>(y, dest, gates, T, k, d, sh, out, st);
+    return launch_combine_t<YT, ST, float>(y, dest, gates, T, k, d, sh, out, st);
+}
+
+template <typename YT>
+static hipError_t launch_combine_s(moe_dtype sh_dt, moe_dtype out_dt, const void* y,
+                                   const int32_t* dest, const float* gates, int T, int k, int d,
+                                   const void* sh, void* out, hipStream_t st)
+{
+    if (sh_dt == MOE_BF16) return launch_combine_o<YT, uint16_t>(out_dt, y, dest, gates, T, k, d, sh, out, st);
+    return launch_combine_o<YT, float>(out_dt, y, dest, gates, T, k, d, sh, out, st);
+}
+
+hipError_t launch_combine(const void* y, moe_dtype y_dt, const int32_t* dest, const float* gates,
+                          int T, int k, int d, const void* sh, moe_dtype sh_dt, void* out,
+                          moe_dtype out_dt, hipStream_t st)
+{
+    if (y_dt == MOE_BF16)
+        return launch_combine_s<uint16_t>(sh_dt, out_dt, y, dest, gates, T, k, d, sh, out, st);
+    return launch_combine_s<float>(sh_dt, out_dt, y, dest, gates, T, k, d, sh, out, st);
+}
+
+}  // namespace moe

@@ -1,0 +1,111 @@
+// Shared device helpers of libmoe (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// bf16 <-> fp32. Widening is exact; narrowing rounds to nearest, ties to even.
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<unsigned>(h) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    unsigned u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN stays NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float load(const float* p, size_t i) { return p[i]; }
+    static __device__ __forceinline__ void store(float* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+    static __device__ __forceinline__ float load(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+    static __device__ __forceinline__ void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ unsigned long long ballot(bool p) { return __ballot(p); }
+
+// Mask of the lanes below the calling lane.
+__device__ __forceinline__ unsigned long long lanes_below() {
+    const int l = lane_id();
+    return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    const int l = lane_id();
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        int n = __shfl_up(v, off, kWave);
+        if (l >= off) v += n;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// Exclusive scan of s[0..n) in LDS in place, n <= 4096, whole block takes
+// part (blockDim.x a multiple of 64, at most 1024). Returns the total.
+// `scratch` must hold blockDim.x/64 + 1 ints.
+__device__ inline int block_exclusive_scan_lds(int* s, int n, int* scratch) {
+    const int tid = threadIdx.x;
+    const int nt = blockDim.x;
+    const int per = (n + nt - 1) / nt;
+    const int beg = min(n, tid * per);
+    const int end = min(n, beg + per);
+    int local = 0;
+    for (int i = beg; i < end; ++i) local += s[i];
+    const int incl = wave_inclusive_scan(local);
+    const int w = tid / kWave;
+    if (lane_id() == kWave - 1) scratch[w] = incl;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int i = 0; i < nt / kWave; ++i) {
+            int t = scratch[i];
+            scratch[i] = run;
+            run += t;
+        }
+        scratch[nt / kWave] = run;
+    }
+    __syncthreads();
+    int run = scratch[w] + incl - local;
+    for (int i = beg; i < end; ++i) {
+        int t = s[i];
+        s[i] = run;
+        run += t;
+    }
+    const int total = scratch[nt / kWave];
+    __syncthreads();
+    return total;
+}
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace moe

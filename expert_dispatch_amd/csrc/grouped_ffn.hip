@@ -1,0 +1,427 @@
+// Grouped SwiGLU expert MLPs over expert-contiguous rows.
+//
+// "Three axes of Parallelism", Mapping experts to EP ranks: each rank holds
+// W_gate, W_val [E_local,d,f] and W_out [E_local,f,d], experts contiguous;
+// Dispatch, expert computation and combine: once the rows of every local
+// expert are contiguous the work is E_local independent MLPs.
+//
+// Two launches: gate_up (h = silu(x.W_gate) * (x.W_val), stored bf16) and
+// down (y = h.W_out, stored fp32). Both use one kernel shape:
+//  * a device-side tile scheduler: every block reads offsets[0..E], turns the
+//    per-expert row counts into a prefix of tiles and finds its own
+//    (expert, column tile, row tile) by binary search. Nothing is read back
+//    to the host, empty experts own no tile, the grid is an upper bound and
+//    surplus blocks leave at once;
+//  * XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs,
+//    so block b works on tile (b % 8) * ceil(tiles / 8) + b / 8. Each XCD
+//    then walks a contiguous run of the tile list, in which the row tiles of
+//    one (expert, column tile) are adjacent and share that weight panel
+//    through the XCD's L2;
+//  * block tile 128 rows x 256 B-columns (gate_up: 128 gate + 128 val columns
+//    of the same hidden units), BK = 64, 4 wavefronts of 64 x 128, each a
+//    2 x 4 grid of v_mfma_f32_32x32x16_bf16 accumulators (128 fp32 / lane);
+//  * LDS double buffer (108 KB): A rows K-contiguous; the weight panel, which
+//    is N-contiguous in memory, is transposed 8x8 in registers on its way in
+//    so that both MFMA operands are read with 16-byte LDS loads. Rows are
+//    padded by 16 bytes, which keeps the 16-byte reads and writes free of
+//    bank conflicts;
+//  * the fused epilogue applies SwiGLU on the two accumulator sets of a lane
+//    (gate and val of the same element sit in the same lane and register).
+// A plain fp32-FMA kernel covers fp32 data and shapes the matrix-core path
+// does not tile.
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int kMaxE = 4096;
+
+// ----------------------------------------------------------- tile scheduler
+
+struct Tile {
+    int e, m0, seg_end, n_tile;
+};
+
+// All threads of the block must call it. s_off needs E+1 ints, s_pre E ints.
+__device__ bool schedule_tile(const int32_t* __restrict__ offsets, int N, int E, int bm,
+                              int n_tiles, int* s_off, int* s_pre, int* scratch, Tile& tile)
+{
+    const int tid = threadIdx.x;
+    for (int e = tid; e <= E; e += blockDim.x) s_off[e] = min(max(offsets[e], 0), N);
+    __syncthreads();
+    for (int e = tid; e < E; e += blockDim.x) {
+        const int lo = s_off[e];
+        const int hi = max(lo, s_off[e + 1]);
+        s_pre[e] = (hi - lo + bm - 1) / bm * n_tiles;
+    }
+    __syncthreads();
+    const int total = block_exclusive_scan_lds(s_pre, E, scratch);
+    const int per_xcd = (total + 7) / 8;
+    const int b = blockIdx.x;
+    const int slot = b / 8;
+    if (slot >= per_xcd) return false;
+    const int t = (b % 8) * per_xcd + slot;
+    if (t >= total) return false;
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pre[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int e = lo;
+    const int rows_lo = s_off[e];
+    const int rows_hi = max(rows_lo, s_off[e + 1]);
+    const int mt = (rows_hi - rows_lo + bm - 1) / bm;
+    const int local = t - s_pre[e];
+    tile.e = e;
+    tile.n_tile = local / mt;
+    tile.m0 = rows_lo + (local % mt) * bm;
+    tile.seg_end = rows_hi;
+    return true;
+}
+
+static long long max_row_tiles(int N, int E, int bm) {
+    // sum_e ceil(n_e / bm) <= (N + E * (bm - 1)) / bm
+    return ((long long)N + (long long)E * (bm - 1)) / bm;
+}
+
+// ------------------------------------------------------ matrix-core kernel
+
+constexpr int BM = 128;
+constexpr int BK = 64;
+constexpr int LDK = BK + 8;   // LDS row stride in bf16 (144 bytes)
+constexpr int BNB = 256;      // B-panel rows (output columns of the block)
+constexpr int kMfmaThreads = 256;
+
+__device__ __forceinline__ unsigned pack_lo(unsigned a, unsigned b) {  // low halves
+    return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ unsigned pack_hi(unsigned a, unsigned b) {  // high halves
+    return (a >> 16) | (b & 0xffff0000u);
+}
+
+template <bool GATE_UP, bool Y_BF16>
+__global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int N, int K, int NC,
+    int E, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
+    void* __restrict__ C)
+{
+    constexpr int BNT = GATE_UP ? 128 : 256;   // output columns per tile
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BNB * LDK];
+    __shared__ int scratch[kMfmaThreads / kWave + 1];
+
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid / kWave;
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+
+    Tile tile;
+    {
+        int* s_off = reinterpret_cast<int*>(&sB[0][0]);
+        int* s_pre = s_off + kMaxE + 1;
+        const bool ok = schedule_tile(offsets, N, E, BM, NC / BNT, s_off, s_pre, scratch, tile);
+        if (!ok) return;  // uniform over the block
+        __syncthreads();  // scheduler LDS is reused below
+    }
+    const int m0 = tile.m0;
+    const int seg_last = tile.seg_end - 1;
+    const size_t wbase = (size_t)tile.e * (size_t)K * (size_t)NC;
+    const int n0 = tile.n_tile * BNT;
+
+    // global -> register staging
+    // A: 128 rows x 64 k: chunk c = tid + 256 q -> row c/8, 8 k at (c%8)*8
+    const uint16_t* a_src[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int c = tid + kMfmaThreads * q;
+        const int row = min(m0 + (c >> 3), seg_last);
+        a_src[q] = A + (size_t)row * K + (c & 7) * 8;
+    }
+    // B: an 8x8 block per thread: k rows 8*kb.., columns 8*nb..
+    const int kb = tid & 7;
+    const int nb = tid >> 3;
+    const uint16_t* b_src;
+    if (GATE_UP)
+        b_src = (nb < 16 ? B0 : B1) + wbase + (size_t)(kb * 8) * NC + n0 + (nb & 15) * 8;
+    else
+        b_src = B0 + wbase + (size_t)(kb * 8) * NC + n0 + nb * 8;
+
+    u32x4 ra[4];
+    u32x4 rb[8];
+    auto load_stage = [&](int kt) {
+        const size_t ko = (size_t)kt * BK;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ra[q] = *reinterpret_cast<const u32x4*>(a_src[q] + ko);
+        const uint16_t* bs = b_src + ko * NC;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) rb[r] = *reinterpret_cast<const u32x4*>(bs + (size_t)r * NC);
+    };
+    auto store_stage = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = tid + kMfmaThreads * q;
+            *reinterpret_cast<u32x4*>(&sA[buf][(c >> 3) * LDK + (c & 7) * 8]) = ra[q];
+        }
+        // transpose the 8 (k) x 8 (n) block: column n becomes 8 consecutive k
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const unsigned lo = rb[2 * q][n >> 1];
+                const unsigned hi = rb[2 * q + 1][n >> 1];
+                o[q] = (n & 1) ? pack_hi(lo, hi) : pack_lo(lo, hi);
+            }
+            *reinterpret_cast<u32x4*>(&sB[buf][(nb * 8 + n) * LDK + kb * 8]) = o;
+        }
+    };
+
+    int nbase[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (GATE_UP) nbase[q] = (q < 2) ? (64 * wn + 32 * q) : (128 + 64 * wn + 32 * (q - 2));
+        else nbase[q] = 128 * wn + 32 * q;
+    }
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mi][q][r] = 0.0f;
+
+    const int KT = K / BK;
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+
+    const int frow = lane & 31;
+    const int fk = (lane >> 5) * 8;
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < KT) load_stage(kt + 1);
+        const uint16_t* sa = sA[cur];
+        const uint16_t* sb = sB[cur];
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            bf16x8 af[2], bfr[4];
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+                af[mi] = *reinterpret_cast<const bf16x8*>(&sa[(64 * wm + 32 * mi + frow) * LDK + ks * 16 + fk]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                bfr[q] = *reinterpret_cast<const bf16x8*>(&sb[(nbase[q] + frow) * LDK + ks * 16 + fk]);
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[mi][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[q], acc[mi][q], 0, 0, 0);
+        }
+        if (kt + 1 < KT) store_stage(cur ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: lane holds column (lane % 32) of each 32x32 accumulator and
+    // rows 8*(r/4) + 4*(lane/32) + r%4 for register r
+    const int col_l = lane & 31;
+    const int row_l = 4 * (lane >> 5);
+    if (GATE_UP) {
+        uint16_t* H = static_cast<uint16_t*>(C);
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int col = n0 + 64 * wn + 32 * q + col_l;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + 64 * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
+                    if (row <= seg_last) {
+                        const float g = acc[mi][q][r];
+                        const float v = acc[mi][q + 2][r];
+                        const float h = g / (1.0f + __expf(-g)) * v;
+                        H[(size_t)row * NC + col] = f32_to_bf16(h);
+                    }
+                }
+            }
+    } else {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = n0 + 128 * wn + 32 * q + col_l;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + 64 * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
+                    if (row <= seg_last) {
+                        if (Y_BF16)
+                            static_cast<uint16_t*>(C)[(size_t)row * NC + col] = f32_to_bf16(acc[mi][q][r]);
+                        else
+                            static_cast<float*>(C)[(size_t)row * NC + col] = acc[mi][q][r];
+                    }
+                }
+            }
+    }
+}
+
+// ------------------------------------------------------------ generic kernel
+
+constexpr int GBM = 64, GBN = 64, GBK = 16;
+
+template <typename XT, typename OT, bool GATE_UP>
+__global__ __launch_bounds__(256) void ffn_generic_kernel(
+    const XT* __restrict__ A, const int32_t* __restrict__ offsets, int N, int K, int NC, int E,
+    const XT* __restrict__ B0, const XT* __restrict__ B1, OT* __restrict__ C)
+{
+    __shared__ float sAg[GBM][GBK + 1];
+    __shared__ float sB0[GBK][GBN];
+    __shared__ float sB1[GBK][GBN];
+    __shared__ int s_sched[2 * kMaxE + 1];
+    __shared__ int scratch[256 / kWave + 1];
+
+    Tile tile;
+    if (!schedule_tile(offsets, N, E, GBM, (NC + GBN - 1) / GBN, s_sched, s_sched + kMaxE + 1,
+                       scratch, tile))
+        return;
+    const int tid = threadIdx.x;
+    const int tx = tid % 16, ty = tid / 16;
+    const int m0 = tile.m0, seg_last = tile.seg_end - 1;
+    const int n0 = tile.n_tile * GBN;
+    const size_t wbase = (size_t)tile.e * (size_t)K * (size_t)NC;
+
+    float acc0[4][4], acc1[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { acc0[i][j] = 0.f; acc1[i][j] = 0.f; }
+
+    for (int k0 = 0; k0 < K; k0 += GBK) {
+        for (int q = tid; q < GBM * GBK; q += 256) {
+            const int r = q / GBK, kk = q % GBK;
+            const int row = min(m0 + r, seg_last);
+            const int kx = k0 + kk;
+            sAg[r][kk] = kx < K ? Elem<XT>::load(A, (size_t)row * K + kx) : 0.f;
+        }
+        for (int q = tid; q < GBK * GBN; q += 256) {
+            const int kk = q / GBN, c = q % GBN;
+            const int kx = k0 + kk, col = n0 + c;
+            const bool in = kx < K && col < NC;
+            const size_t o = wbase + (size_t)kx * NC + col;
+            sB0[kk][c] = in ? Elem<XT>::load(B0, o) : 0.f;
+            if (GATE_UP) sB1[kk][c] = in ? Elem<XT>::load(B1, o) : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < GBK; ++kk) {
+            float a[4], b0[4], b1[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = sAg[ty * 4 + i][kk];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                b0[j] = sB0[kk][tx * 4 + j];
+                if (GATE_UP) b1[j] = sB1[kk][tx * 4 + j];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc0[i][j] = __builtin_fmaf(a[i], b0[j], acc0[i][j]);
+                    if (GATE_UP) acc1[i][j] = __builtin_fmaf(a[i], b1[j], acc1[i][j]);
+                }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = m0 + ty * 4 + i;
+        if (row > seg_last) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = n0 + tx * 4 + j;
+            if (col >= NC) continue;
+            float v = acc0[i][j];
+            if (GATE_UP) v = v / (1.0f + __expf(-v)) * acc1[i][j];
+            Elem<OT>::store(C, (size_t)row * NC + col, v);
+        }
+    }
+}
+
+// ----------------------------------------------------------------- launches
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+bool ffn_gate_up_uses_mfma(moe_dtype dt, int d, int f, const void* x, const void* wg,
+                           const void* wv, const void* h) {
+    return dt == MOE_BF16 && d % BK == 0 && f % 128 == 0 && aligned16(x) && aligned16(wg) &&
+           aligned16(wv) && aligned16(h);
+}
+bool ffn_down_uses_mfma(moe_dtype dt, int f, int d, const void* h, const void* wo) {
+    return dt == MOE_BF16 && f % BK == 0 && d % 256 == 0 && aligned16(h) && aligned16(wo);
+}
+
+static unsigned grid_for(long long tiles) {
+    long long g = (tiles + 7) / 8 * 8;
+    return (unsigned)std::max(8LL, g);
+}
+
+hipError_t launch_gate_up(const void* x, moe_dtype dt, int N, int d, int f, int E,
+                          const int32_t* offsets, const void* wg, const void* wv, void* h,
+                          hipStream_t st)
+{
+    if (ffn_gate_up_uses_mfma(dt, d, f, x, wg, wv, h)) {
+        const long long tiles = max_row_tiles(N, E, BM) * (f / 128);
+        ffn_mfma_kernel<true, false><<<grid_for(tiles), kMfmaThreads, 0, st>>>(
+            (const uint16_t*)x, offsets, N, d, f, E, (const uint16_t*)wg, (const uint16_t*)wv, h);
+    } else {
+        const long long tiles = max_row_tiles(N, E, GBM) * ((f + GBN - 1) / GBN);
+        if (dt == MOE_BF16)
+            ffn_generic_kernel<uint16_t, uint16_t, true><<<grid_for(tiles), 256, 0, st>>>(
+                (const uint16_t*)x, offsets, N, d, f, E, (const uint16_t*)wg,
+                (const uint16_t*)wv, (uint16_t*)h);
+        else
+            ffn_generic_kernel<float, float, true><<<grid_for(tiles), 256, 0, st>>>(
+                (const float*)x, offsets, N, d, f, E, (const float*)wg, (const float*)wv,
+                (float*)h);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_down(const void* h, moe_dtype dt, int N, int f, int d, int E,
+                       const int32_t* offsets, const void* wo, void* y, moe_dtype y_dt,
+                       hipStream_t st)
+{
+    if (ffn_down_uses_mfma(dt, f, d, h, wo) && aligned16(y)) {
+        const long long tiles = max_row_tiles(N, E, BM) * (d / 256);
+        if (y_dt == MOE_BF16)
+            ffn_mfma_kernel<false, true><<<grid_for(tiles), kMfmaThreads, 0, st>>>(
+                (const uint16_t*)h, offsets, N, f, d, E, (const uint16_t*)wo, nullptr, y);
+        else
+            ffn_mfma_kernel<false, false><<<grid_for(tiles), kMfmaThreads, 0, st>>>(
+                (const uint16_t*)h, offsets, N, f, d, E, (const uint16_t*)wo, nullptr, y);
+    } else {
+        const long long tiles = max_row_tiles(N, E, GBM) * ((d + GBN - 1) / GBN);
+        const unsigned g = grid_for(tiles);
+        if (dt == MOE_BF16) {
+            if (y_dt == MOE_BF16)
+                ffn_generic_kernel<uint16_t, uint16_t, false><<<g, 256, 0, st>>>(
+                    (const uint16_t*)h, offsets, N, f, d, E, (const uint16_t*)wo, nullptr,
+                    (uint16_t*)y);
+            else
+                ffn_generic_kernel<uint16_t, float, false><<<g, 256, 0, st>>>(
+                    (const uint16_t*)h, offsets, N, f, d, E, (const uint16_t*)wo, nullptr,
+                    (float*)y);
+        } else {
+            if (y_dt == MOE_BF16)
+                ffn_generic_kernel<float, uint16_t, false><<<g, 256, 0, st>>>(
+                    (const float*)h, offsets, N, f, d, E, (const float*)wo, nullptr, (uint16_t*)y);
+            else
+                ffn_generic_kernel<float, float, false><<<g, 256, 0, st>>>(
+                    (const float*)h, offsets, N, f, d, E, (const float*)wo, nullptr, (float*)y);
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,303 @@
+// Expert-major packing and the receive-side reorder.
+//
+// "Three axes of Parallelism", Expert Parallel (EP) -> Producing assignments:
+// count the assignments routed to each expert, take offsets from the
+// cumulative counts, and write every assignment into its expert's region of
+// the packed buffer. Same page, Dispatch, expert computation and combine: a
+// received buffer is source-major and is permuted expert-major with counts
+// recv_matrix.sum(0) and their cumulative sums as offsets. The Modalities EP
+// page (Design) builds those indices on the device with no readback.
+//
+// Token-routed packing, three launches and no host synchronisation:
+//  1. perm_hist:  per-chunk expert histogram in LDS (4096 assignments/block);
+//  2. perm_rank:  every block re-derives the global offsets and its own base
+//                 per expert from the chunk histograms, then ranks its
+//                 assignments stably with wave ballots (a bit-sliced match of
+//                 equal expert ids, popcount of the lanes below) -> dest and
+//                 perm_src; no atomics decide a position, so the result is the
+//                 unique stable order;
+//  3. perm_gather: one wavefront per token reads its row once with 16-byte
+//                 loads and writes it to its k packed rows.
+// The receive-side reorder is one launch: each block rebuilds the (sender,
+// expert) block starts from the count matrix in LDS, then each wavefront maps
+// its rows and copies them.
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int kPermThreads = 256;
+constexpr int kPermChunk = 4096;                       // assignments per block
+constexpr int kPermIters = kPermChunk / kPermThreads;  // 16 per lane
+constexpr int kPermMaxE = 1024;
+
+__global__ __launch_bounds__(kPermThreads) void perm_hist_kernel(
+    const int32_t* __restrict__ idx, int TK, int E, int32_t* __restrict__ bc)
+{
+    __shared__ int h[kPermMaxE];
+    for (int e = threadIdx.x; e < E; e += kPermThreads) h[e] = 0;
+    __syncthreads();
+    const int base = blockIdx.x * kPermChunk;
+#pragma unroll 4
+    for (int q = 0; q < kPermIters; ++q) {
+        const int a = base + threadIdx.x + q * kPermThreads;
+        if (a < TK) {
+            const int e = idx[a];
+            if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kPermThreads) bc[(size_t)blockIdx.x * E + e] = h[e];
+}
+
+__global__ __launch_bounds__(kPermThreads) void perm_rank_kernel(
+    const int32_t* __restrict__ idx, int TK, int E, int nbits,
+    const int32_t* __restrict__ bc, int nb,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm_src, int32_t* __restrict__ dest)
+{
+    __shared__ int s_off[kPermMaxE];       // global offsets
+    __shared__ int s_base[kPermMaxE];      // offsets + assignments of earlier blocks
+    __shared__ int s_wcnt[4][kPermMaxE];   // per-wave running counts, then wave bases
+    __shared__ int scratch[kPermThreads / kWave + 1];
+
+    const int tid = threadIdx.x;
+    const int w = tid / kWave;
+    const int lane = lane_id();
+
+    for (int e = tid; e < E; e += kPermThreads) {
+        int tot = 0, pre = 0;
+        for (int b = 0; b < nb; ++b) {
+            const int c = bc[(size_t)b * E + e];
+            tot += c;
+            if (b < (int)blockIdx.x) pre += c;
+        }
+        s_off[e] = tot;
+        s_base[e] = pre;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s_wcnt[q][e] = 0;
+    }
+    __syncthreads();
+    const int total = block_exclusive_scan_lds(s_off, E, scratch);
+    for (int e = tid; e < E; e += kPermThreads) {
+        s_base[e] += s_off[e];
+        if (blockIdx.x == 0) {
+            const int next = (e + 1 < E) ? s_off[e + 1] : total;
+            counts[e] = next - s_off[e];
+            offsets[e] = s_off[e];
+        }
+    }
+    if (blockIdx.x == 0 && tid == 0) offsets[E] = total;
+    __syncthreads();
+
+    // stable ranks inside this wave's 1024 consecutive assignments
+    volatile int* wc = s_wcnt[w];
+    const int a0 = blockIdx.x * kPermChunk + w * (kPermChunk / 4);
+    int loc[kPermIters];
+    int key[kPermIters];
+#pragma unroll
+    for (int it = 0; it < kPermIters; ++it) {
+        const int a = a0 + it * kWave + lane;
+        int e = (a < TK) ? idx[a] : -1;
+        const bool valid = (unsigned)e < (unsigned)E;
+        if (!valid) e = -1;
+        unsigned long long m = ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = valid && ((e >> b) & 1);
+            const unsigned long long bb = ballot(bit);
+            m &= bit ? bb : ~bb;
+        }
+        const unsigned long long below = m & lanes_below();
+        int prior = 0;
+        if (valid) prior = wc[e];
+        __builtin_amdgcn_wave_barrier();
+        if (valid && below == 0) wc[e] = prior + __popcll(m);
+        __builtin_amdgcn_wave_barrier();
+        loc[it] = prior + __popcll(below);
+        key[it] = e;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kPermThreads) {
+        int run = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int t = s_wcnt[q][e];
+            s_wcnt[q][e] = run;
+            run += t;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < kPermIters; ++it) {
+        const int a = a0 + it * kWave + lane;
+        if (a >= TK) continue;
+        const int e = key[it];
+        int j = -1;
+        if (e >= 0) {
+            j = s_base[e] + s_wcnt[w][e] + loc[it];
+            if (j >= TK) j = -1;
+        }
+        dest[a] = j;
+        if (j >= 0) perm_src[j] = a;
+    }
+}
+
+// x_perm[dest[t*k+s]] = x[t]: one wavefront per token, V-byte vectors.
+template <typename V>
+__global__ __launch_bounds__(256) void perm_gather_kernel(
+    const V* __restrict__ x, int vecs_per_row, int T, int k, const int32_t* __restrict__ dest,
+    int rows_out, V* __restrict__ x_perm)
+{
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T) return;
+    const int lane = lane_id();
+    const int my_dest = lane < k ? dest[(size_t)t * k + lane] : -1;
+    const V* src = x + (size_t)t * vecs_per_row;
+    constexpr int U = 4;
+    for (int c0 = 0; c0 < vecs_per_row; c0 += kWave * U) {
+        V v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u * kWave + lane;
+            if (c < vecs_per_row) v[u] = src[c];
+        }
+        for (int s = 0; s < k; ++s) {
+            const int j = __shfl(my_dest, s, kWave);
+            if ((unsigned)j >= (unsigned)rows_out) continue;
+            V* dst = x_perm + (size_t)j * vecs_per_row;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * kWave + lane;
+                if (c < vecs_per_row) dst[c] = v[u];
+            }
+        }
+    }
+}
+
+constexpr int kRecvMaxCells = 4096;
+constexpr int kRecvRowsPerBlock = 16;
+
+template <typename V>
+__global__ __launch_bounds__(256) void perm_recv_kernel(
+    const int32_t* __restrict__ recv, int S, int E, int N,
+    const V* __restrict__ x, int vecs_per_row,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm_src, int32_t* __restrict__ dest, V* __restrict__ x_perm)
+{
+    __shared__ int s_start[kRecvMaxCells];   // first received row of cell (i,j)
+    __shared__ int s_dbase[kRecvMaxCells];   // first packed row of cell (i,j)
+    __shared__ int s_off[kPermMaxE + 1];
+    __shared__ int scratch[256 / kWave + 1];
+    const int tid = threadIdx.x;
+    const int C = S * E;
+    for (int c = tid; c < C; c += blockDim.x) {
+        const int v = max(recv[c], 0);
+        s_start[c] = v;
+        s_dbase[c] = v;
+    }
+    __syncthreads();
+    // per local expert: rows from earlier senders, and the expert's total
+    for (int j = tid; j < E; j += blockDim.x) {
+        int run = 0;
+        for (int i = 0; i < S; ++i) {
+            const int t = s_dbase[i * E + j];
+            s_dbase[i * E + j] = run;
+            run += t;
+        }
+        s_off[j] = run;
+    }
+    __syncthreads();
+    const int total_rows = block_exclusive_scan_lds(s_start, C, scratch);
+    const int total_e = block_exclusive_scan_lds(s_off, E, scratch);
+    for (int c = tid; c < C; c += blockDim.x) s_dbase[c] += s_off[c % E];
+    if (blockIdx.x == 0) {
+        for (int j = tid; j < E; j += blockDim.x) {
+            const int next = (j + 1 < E) ? s_off[j + 1] : total_e;
+            counts[j] = next - s_off[j];
+            offsets[j] = s_off[j];
+        }
+        if (tid == 0) offsets[E] = total_e;
+    }
+    __syncthreads();
+
+    const int lane = lane_id();
+    const int w = tid / kWave;
+    for (int q = w; q < kRecvRowsPerBlock; q += blockDim.x / kWave) {
+        const int r = blockIdx.x * kRecvRowsPerBlock + q;
+        if (r >= N) break;
+        int j = -1;
+        if (r < total_rows) {
+            // last cell whose first row is <= r (a non-empty cell)
+            int lo = 0, hi = C - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_start[mid] <= r) lo = mid; else hi = mid - 1;
+            }
+            j = s_dbase[lo] + (r - s_start[lo]);
+            if (j >= N) j = -1;
+        }
+        if (lane == 0) {
+            dest[r] = j;
+            if (j >= 0) perm_src[j] = r;
+        }
+        if (j < 0) continue;
+        const V* src = x + (size_t)r * vecs_per_row;
+        V* dst = x_perm + (size_t)j * vecs_per_row;
+        for (int c = lane; c < vecs_per_row; c += kWave) dst[c] = src[c];
+    }
+}
+
+static int ceil_log2(int v) {
+    int b = 0;
+    while ((1 << b) < v) ++b;
+    return b;
+}
+
+size_t permute_ws_bytes(int T, int k, int E) {
+    const long long TK = (long long)T * k;
+    const long long nb = std::max(1LL, (TK + kPermChunk - 1) / kPermChunk);
+    return align_up((size_t)(nb * E) * sizeof(int32_t), 256);
+}
+
+hipError_t launch_permute(const int32_t* idx, int T, int k, int E, const void* x, int es, int d,
+                          int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* dest,
+                          void* x_perm, void* ws, hipStream_t st)
+{
+    const int TK = T * k;
+    const int nb = std::max(1, (TK + kPermChunk - 1) / kPermChunk);
+    int32_t* bc = static_cast<int32_t*>(ws);
+    perm_hist_kernel<<<nb, kPermThreads, 0, st>>>(idx, TK, E, bc);
+    perm_rank_kernel<<<nb, kPermThreads, 0, st>>>(idx, TK, E, ceil_log2(E), bc, nb, counts,
+                                                  offsets, perm_src, dest);
+    if (T > 0) {
+        const size_t row_bytes = (size_t)d * es;
+        const dim3 grid((T + 3) / 4);
+        if (row_bytes % 16 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)x_perm % 16 == 0)
+            perm_gather_kernel<u32x4><<<grid, 256, 0, st>>>(
+                (const u32x4*)x, (int)(row_bytes / 16), T, k, dest, TK, (u32x4*)x_perm);
+        else
+            perm_gather_kernel<uint16_t><<<grid, 256, 0, st>>>(
+                (const uint16_t*)x, (int)(row_bytes / 2), T, k, dest, TK, (uint16_t*)x_perm);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_permute_recv(const int32_t* recv, int S, int E, int N, const void* x, int es,
+                               int d, int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                               int32_t* dest, void* x_perm, hipStream_t st)
+{
+    const int nblk = std::max(1, (N + kRecvRowsPerBlock - 1) / kRecvRowsPerBlock);
+    const size_t row_bytes = (size_t)d * es;
+    if (row_bytes % 16 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)x_perm % 16 == 0)
+        perm_recv_kernel<u32x4><<<nblk, 256, 0, st>>>(recv, S, E, N, (const u32x4*)x,
+                                                      (int)(row_bytes / 16), counts, offsets,
+                                                      perm_src, dest, (u32x4*)x_perm);
+    else
+        perm_recv_kernel<uint16_t><<<nblk, 256, 0, st>>>(recv, S, E, N, (const uint16_t*)x,
+                                                         (int)(row_bytes / 2), counts, offsets,
+                                                         perm_src, dest, (uint16_t*)x_perm);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -3,14 +3,16 @@
 This module only draws inputs; it holds none of the layer's arithmetic, so
 both the HIP path's tests and the CPU oracle can take their inputs from it.
 
-Recipe (numpy ``default_rng(seed)``, PCG64):
-  * draw order: x, router weight W_r, router bias, then for each expert e in
-    ascending order W_gate[e], W_val[e], W_out[e], then the shared experts in
-    the same way, then the structure that is particular to a config (experts
-    forced empty, Zipf popularity ranks, Dirichlet count shares);
-  * values are drawn in fp32 (``standard_normal`` times the std) and, for
-    bf16 configs, rounded to bf16 with round-to-nearest-even; the rounded
-    values are the inputs of both sides;
+Recipe:
+  * Gaussian values come from ``torch.Generator().manual_seed(seed)`` on the
+    CPU (``torch.randn`` in fp32, times the std) in this order: x, router
+    weight W_r, router bias, then for each expert e in ascending order
+    W_gate[e], W_val[e], W_out[e], then the shared experts in the same way;
+  * the structure that is particular to a config (experts forced empty, Zipf
+    popularity ranks, Dirichlet count shares) comes from numpy's
+    ``default_rng(seed)``;
+  * for bf16 configs the fp32 draws are rounded to bf16 (round to nearest,
+    ties to even); the rounded values are the inputs of both sides;
   * x ~ N(0, 1); W_r ~ N(0, 0.02); expert weights ~ N(0, 1/sqrt(fan_in)) with
     fan_in = d for W_gate and W_val and f for W_out (the second parameter of
     N is the standard deviation);
@@ -29,6 +31,7 @@ import dataclasses
 import math
 
 import numpy as np
+import torch
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -124,23 +127,34 @@ def get(name: str, **overrides) -> Config:
     return dataclasses.replace(c, **overrides) if overrides else c
 
 
-def _normal(rng, shape, std, dtype):
-    a = rng.standard_normal(size=shape, dtype=np.float32)
+def _draw(gen, shape, std, dtype) -> torch.Tensor:
+    a = torch.randn(shape, generator=gen, dtype=torch.float32)
     if std != 1.0:
-        a *= np.float32(std)
-    return f32_to_bf16_bits(a) if dtype == "bf16" else a
+        a.mul_(float(np.float32(std)))
+    return a.to(torch.bfloat16).view(torch.int16) if dtype == "bf16" else a
 
 
-def _experts(rng, n, d, f, dtype):
-    npdt = np.uint16 if dtype == "bf16" else np.float32
-    wg = np.empty((n, d, f), npdt)
-    wv = np.empty((n, d, f), npdt)
-    wo = np.empty((n, f, d), npdt)
+def _as_numpy(t: torch.Tensor) -> np.ndarray:
+    a = t.numpy()
+    return a.view(np.uint16) if a.dtype == np.int16 else a
+
+
+def _normal(gen, shape, std, dtype):
+    return _as_numpy(_draw(gen, shape, std, dtype))
+
+
+def _experts(gen, n, d, f, dtype):
+    # large host buffers are allocated by torch, whose parallel copies also
+    # spread the first touch of the pages over the host threads
+    tdt = torch.int16 if dtype == "bf16" else torch.float32
+    wg = torch.empty((n, d, f), dtype=tdt)
+    wv = torch.empty((n, d, f), dtype=tdt)
+    wo = torch.empty((n, f, d), dtype=tdt)
     for e in range(n):
-        wg[e] = _normal(rng, (d, f), 1.0 / math.sqrt(d), dtype)
-        wv[e] = _normal(rng, (d, f), 1.0 / math.sqrt(d), dtype)
-        wo[e] = _normal(rng, (f, d), 1.0 / math.sqrt(f), dtype)
-    return wg, wv, wo
+        wg[e].copy_(_draw(gen, (d, f), 1.0 / math.sqrt(d), dtype))
+        wv[e].copy_(_draw(gen, (d, f), 1.0 / math.sqrt(d), dtype))
+        wo[e].copy_(_draw(gen, (f, d), 1.0 / math.sqrt(f), dtype))
+    return _as_numpy(wg), _as_numpy(wv), _as_numpy(wo)
 
 
 def generate(cfg: Config | str) -> dict:
@@ -148,18 +162,19 @@ def generate(cfg: Config | str) -> dict:
     plus the integer parameters the calls need."""
     if isinstance(cfg, str):
         cfg = get(cfg)
+    gen = torch.Generator().manual_seed(cfg.seed)
     rng = np.random.default_rng(cfg.seed)
     out = dict(config=cfg, dtype=cfg.dtype)
     if cfg.kind == "routed":
-        out["x"] = _normal(rng, (cfg.T, cfg.d), 1.0, cfg.dtype)
-        out["w_router"] = _normal(rng, (cfg.d, cfg.E), 0.02, cfg.dtype)
+        out["x"] = _normal(gen, (cfg.T, cfg.d), 1.0, cfg.dtype)
+        out["w_router"] = _normal(gen, (cfg.d, cfg.E), 0.02, cfg.dtype)
         bias = None
         if cfg.bias == "normal":
-            bias = rng.standard_normal(size=cfg.E, dtype=np.float32) * np.float32(cfg.bias_std)
-        out["w_gate"], out["w_val"], out["w_out"] = _experts(rng, cfg.E, cfg.d, cfg.f, cfg.dtype)
+            bias = _normal(gen, (cfg.E,), cfg.bias_std, "f32")
+        out["w_gate"], out["w_val"], out["w_out"] = _experts(gen, cfg.E, cfg.d, cfg.f, cfg.dtype)
         if cfg.shared:
             (out["shared_w_gate"], out["shared_w_val"],
-             out["shared_w_out"]) = _experts(rng, cfg.shared, cfg.d, cfg.f, cfg.dtype)
+             out["shared_w_out"]) = _experts(gen, cfg.shared, cfg.d, cfg.f, cfg.dtype)
         if cfg.bias == "zipf":
             ranks = rng.permutation(cfg.E) + 1
             bias = (-cfg.zipf_s * np.log(ranks.astype(np.float64))).astype(np.float32)
@@ -174,8 +189,8 @@ def generate(cfg: Config | str) -> dict:
         out["k"] = cfg.k
         out["renorm"] = True
     elif cfg.kind == "recv":
-        out["x_recv"] = _normal(rng, (cfg.N, cfg.d), 1.0, cfg.dtype)
-        out["w_gate"], out["w_val"], out["w_out"] = _experts(rng, cfg.E, cfg.d, cfg.f, cfg.dtype)
+        out["x_recv"] = _normal(gen, (cfg.N, cfg.d), 1.0, cfg.dtype)
+        out["w_gate"], out["w_val"], out["w_out"] = _experts(gen, cfg.E, cfg.d, cfg.f, cfg.dtype)
         p = rng.dirichlet(np.full(cfg.S * cfg.E, cfg.alpha))
         counts = rng.multinomial(cfg.N, p).astype(np.int32)
         out["recv_counts"] = counts.reshape(cfg.S, cfg.E)

@@ -1,0 +1,181 @@
+/*
+ * moe.h -- C ABI of libmoe, the MI355X (gfx950) routed-expert MoE layer that
+ * one expert-parallel rank runs on its share of the tokens.
+ *
+ * The layer, as "Three axes of Parallelism" (section Expert Parallel (EP))
+ * states it: score every token against all experts and keep the top K with
+ * their router weights; count the assignments per expert, take offsets from
+ * the cumulative counts and pack the assignments expert-major; run each
+ * expert's MLP on its contiguous rows; undo the packing, weight each expert
+ * output by its router weight and sum the K outputs of every token. On the
+ * receive side of the exchange the rows arrive sender-major and are reordered
+ * expert-major on the device ("feat(parallelism): expert parallelism for the
+ * Nemotron-3 Nano MoE layers", section Design: the permutation indices are
+ * built with device operations, with no device-to-host readback).
+ *
+ * Conventions shared by every call:
+ *  - Pointers are device pointers to caller-owned memory (e.g. PyTorch
+ *    tensors) unless stated otherwise. The library never allocates or frees
+ *    device memory on these calls and keeps no state between calls; calls
+ *    on different streams are independent.
+ *  - Every tensor is row-major and contiguous. bf16 data are raw 16-bit
+ *    patterns (the upper half of an IEEE binary32). Expert weights use the
+ *    x.W orientation: W_gate, W_val [E,d,f], W_out [E,f,d].
+ *  - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
+ *    work on it and return; none synchronises or copies device -> host.
+ *  - Errors: arguments that are wrong on the host (NULL required pointer,
+ *    non-positive or too large sizes, k > E, too small a workspace) return an
+ *    error code before anything is enqueued. A failed launch returns
+ *    MOE_ERR_HIP. Device-side preconditions (ids in [0,E), counts summing to
+ *    the row total, finite scores) are not checked; when broken the results
+ *    are unspecified, but no kernel reads or writes outside the buffers
+ *    described here.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,
+    MOE_ERR_UNSUPPORTED = 2,
+    MOE_ERR_WORKSPACE = 3,
+    MOE_ERR_HIP = 4
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Static, human-readable text for a status code. */
+const char* moe_status_string(moe_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int moe_version(void);
+
+/*
+ * Router ("Three axes of Parallelism", Expert Parallel (EP) -> Producing
+ * assignments: scores [T,E], top-K expert ids and router weights [T,K]).
+ *   x        [T,d] dtype dt        token activations
+ *   w_router [d,E] dtype dt        router weight
+ *   bias     [E] fp32 or NULL      per-expert score bias
+ *   logits   [T,E] fp32 out or NULL (not written)
+ *   topk_idx [T,k] int32 out       expert ids, slot 0 = highest score
+ *   gates    [T,k] fp32 out        router weights
+ * Scores: logits[t,e] = fl32(sum_i x[t,i]*w[i,e]) (+ bias[e]), the sum taken in
+ * fp32 in index order with one fused multiply-add per term from +0, then one
+ * fp32 bias add; this fixes every score bit so the selection is reproducible.
+ * Selection: experts ordered by (score descending, index ascending).
+ * Weights: renorm != 0 -> softmax over the k selected scores (the full softmax
+ * restricted to the selection and renormalised); renorm == 0 -> the full
+ * softmax probability of each selected expert.
+ * Limits: 1 <= k <= min(E, 32), E <= 1024, T >= 0.
+ */
+moe_status moe_route(const void* x, moe_dtype dt, const void* w_router, const float* bias,
+                     int T, int d, int E, int k, int renorm,
+                     float* logits, int32_t* topk_idx, float* gates, void* stream);
+
+/*
+ * Expert-major packing ("Three axes of Parallelism", Producing assignments:
+ * per-expert counts, offsets from the cumulative counts, every assignment
+ * written to its expert's region; the assignment a = t*k + s is token-major).
+ *   topk_idx [T*k] int32           expert of each assignment
+ *   x        [T,d] dtype dt        token rows
+ *   counts   [E] int32 out
+ *   offsets  [E+1] int32 out       offsets[0] = 0, offsets[E] = T*k
+ *   perm_src [T*k] int32 out       packed row -> assignment a
+ *   dest     [T*k] int32 out       assignment a -> packed row
+ *   x_perm   [T*k,d] dtype dt out  x_perm[dest[a]] = x[a / k]
+ *   ws       device workspace of at least moe_permute_workspace(T,k,E) bytes
+ * Inside an expert's region the assignments keep ascending a (stable), which
+ * is the order the pages' per-expert argwhere produces. An id outside [0,E)
+ * is dropped: dest[a] = -1 and it is in no region.
+ * Limits: T*k < 2^31, E <= 1024, k <= 32.
+ */
+size_t moe_permute_workspace(int T, int k, int E);
+moe_status moe_permute(const int32_t* topk_idx, int T, int k, int E,
+                       const void* x, moe_dtype dt, int d,
+                       int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* dest,
+                       void* x_perm, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Receive-side reorder ("Three axes of Parallelism", Dispatch, expert
+ * computation and combine: recv_matrix[i,j] = rows sender i sent to local
+ * expert j; the received buffer is source-major and is permuted expert-major,
+ * counts = recv_matrix.sum(0), offsets = their cumulative sums; the Modalities
+ * EP page, Design: indices built on the device with no readback).
+ *   recv_counts [S,E_loc] int32, device memory
+ *   x_recv      [N,d] dtype dt     rows sender-major, inside a sender grouped
+ *                                  by local expert ascending
+ *   counts [E_loc], offsets [E_loc+1], perm_src [N], dest [N] int32 out,
+ *   x_perm [N,d] out               x_perm[dest[r]] = x_recv[r]
+ * Rows of one expert keep their arrival (sender) order. N is a host integer
+ * the caller already holds (the one split-count copy of the exchange).
+ * Precondition: sum(recv_counts) == N. Limits: S*E_loc <= 4096.
+ */
+size_t moe_permute_recv_workspace(int S, int E_loc, int N);
+moe_status moe_permute_recv(const int32_t* recv_counts, int S, int E_loc, int N,
+                            const void* x_recv, moe_dtype dt, int d,
+                            int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                            int32_t* dest, void* x_perm, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/*
+ * Grouped SwiGLU expert MLPs ("Three axes of Parallelism", Mapping experts to
+ * EP ranks: W_gate, W_val [E_local,d,f], W_out [E_local,f,d]; Dispatch,
+ * expert computation and combine: E_local independent MLPs on contiguous rows).
+ * For every packed row j of expert e (offsets[e] <= j < offsets[e+1]):
+ *   h = silu(x_perm[j] . W_gate[e]) * (x_perm[j] . W_val[e]),  silu(z) = z*sigmoid(z)
+ *   y[j] = h . W_out[e]
+ *   x_perm [N,d] dtype dt, offsets [E+1] int32 (device, read on the device),
+ *   y      [N,d] dtype y_dt out (MOE_F32 recommended)
+ * Products accumulate in fp32. With dt = MOE_BF16 the hidden activation h is
+ * stored as bf16 (round to nearest even) between the two products; with
+ * MOE_F32 it stays fp32. Experts with no rows cost nothing.
+ * Limits: E <= 4096, N < 2^31. Any d, f >= 1 work; bf16 with d % 256 == 0 and
+ * f % 128 == 0 (and 16-byte aligned pointers) takes the matrix-core path.
+ */
+size_t moe_grouped_ffn_workspace(int N, int d, int f, int E, moe_dtype dt);
+moe_status moe_grouped_ffn(const void* x_perm, moe_dtype dt, int N, int d, int f, int E,
+                           const int32_t* offsets, const void* w_gate, const void* w_val,
+                           const void* w_out, void* y, moe_dtype y_dt,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The two halves of moe_grouped_ffn, for callers that keep h themselves:
+ *   moe_ffn_gate_up: h [N,f] (dtype dt) = silu(x_perm . W_gate[e]) * (x_perm . W_val[e])
+ *   moe_ffn_down:    y [N,d] (dtype y_dt) = h . W_out[e]
+ * Same layouts, limits and row-to-expert mapping as moe_grouped_ffn.
+ */
+moe_status moe_ffn_gate_up(const void* x_perm, moe_dtype dt, int N, int d, int f, int E,
+                           const int32_t* offsets, const void* w_gate, const void* w_val,
+                           void* h, void* stream);
+moe_status moe_ffn_down(const void* h, moe_dtype dt, int N, int f, int d, int E,
+                        const int32_t* offsets, const void* w_out, void* y, moe_dtype y_dt,
+                        void* stream);
+
+/*
+ * Weighted combine ("Three axes of Parallelism", Dispatch, expert computation
+ * and combine: undo the packing, multiply each expert output by its router
+ * weight and sum the K outputs of each token, restoring [T,D]); the gather
+ * form of the scatter-add, deterministic and free of atomics:
+ *   out[t] = sum_{s = 0..k-1, ascending} gates[t*k+s] * y_perm[dest[t*k+s]]  (+ y_shared[t])
+ *   y_perm [*,d] dtype y_dt, dest [T*k] int32, gates [T*k] fp32 or NULL (= 1),
+ *   y_shared [T,d] dtype sh_dt or NULL (always-on shared experts, unweighted),
+ *   out [T,d] dtype out_dt.
+ * Sums run in fp32. With k = 1 and gates = NULL this is the un-permute of a
+ * received buffer back to sender-major order. dest < 0 terms are skipped.
+ */
+moe_status moe_combine(const void* y_perm, moe_dtype y_dt, const int32_t* dest,
+                       const float* gates, int T, int k, int d,
+                       const void* y_shared, moe_dtype sh_dt,
+                       void* out, moe_dtype out_dt, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

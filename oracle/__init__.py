@@ -60,7 +60,7 @@ def lib():
                                     ctypes.c_int, vp]
         L.oracle_expert_ffn_rows.argtypes = [vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                              ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp,
-                                             ctypes.c_int64, vp]
+                                             ctypes.c_int64, ctypes.c_int, vp]
         L.oracle_combine.argtypes = [vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, vp, vp,
                                      vp, vp, vp, vp]
         for name in ("oracle_route", "oracle_permute", "oracle_permute_recv", "oracle_gather",
@@ -160,23 +160,30 @@ def gather(x, perm_src, k: int):
     return out
 
 
-def expert_ffn_rows(x_perm, offsets, wg, wv, wo, rows=None):
+def expert_ffn_rows(x_perm, offsets, wg, wv, wo, rows=None, N=None):
     """SwiGLU expert MLPs evaluated in double on the listed packed rows
-    (all rows if None). Returns float64 [len(rows), d]."""
+    (all rows if None). Returns float64 [len(rows), d]. With ``N`` given,
+    ``x_perm`` holds only the listed rows (row r = packed row rows[r]) of a
+    packed buffer of N rows."""
     x_perm, wg, wv, wo = _c(x_perm), _c(wg), _c(wv), _c(wo)
     xt = _xtype(x_perm)
     for w in (wg, wv, wo):
         if _xtype(w) != xt:
             raise TypeError("activations and expert weights must share an element type")
-    N, d = x_perm.shape
+    compact = N is not None
+    if not compact:
+        N = x_perm.shape[0]
+    d = x_perm.shape[1]
     E, d2, f = wg.shape
     assert d2 == d and wv.shape == wg.shape and wo.shape == (E, f, d)
     off = _c(offsets, np.int32)
     assert off.shape == (E + 1,)
     rows = np.arange(N, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    if compact:
+        assert x_perm.shape[0] == rows.shape[0]
     y = np.empty((rows.shape[0], d), np.float64)
     _check(lib().oracle_expert_ffn_rows(_p(x_perm), xt, N, d, f, E, _p(off), _p(wg), _p(wv),
-                                        _p(wo), _p(rows), rows.shape[0], _p(y)),
+                                        _p(wo), _p(rows), rows.shape[0], int(compact), _p(y)),
            "oracle_expert_ffn_rows")
     return y
 
@@ -214,18 +221,25 @@ def swiglu_shared(x, wg, wv, wo, rows=None):
 def moe_layer(inp: dict, tokens=None):
     """The whole layer on a token-routed workload dict (see
     expert_dispatch_amd.workloads). Returns a dict of every intermediate.
-    With ``tokens`` given, the FFN and combine are evaluated only for the
-    packed rows those tokens need and for those tokens."""
+    With ``tokens`` given, only the packed rows those tokens need are
+    gathered and run through the expert MLPs, and only those tokens are
+    combined; ``x_perm`` then holds the rows listed in ``y_rows``."""
     k = inp["k"]
     logits, idx, gates = route(inp["x"], inp["w_router"], inp.get("bias"), k,
                                inp.get("renorm", True))
     E = inp["w_gate"].shape[0]
     counts, offsets, perm_src, dest = permute(idx, E)
-    x_perm = gather(inp["x"], perm_src, k)
     T = inp["x"].shape[0]
     tok = np.arange(T, dtype=np.int32) if tokens is None else _c(tokens, np.int32)
-    need = np.unique(dest.reshape(T, k)[tok].reshape(-1)).astype(np.int64)
-    y_rows = expert_ffn_rows(x_perm, offsets, inp["w_gate"], inp["w_val"], inp["w_out"], need)
+    if tokens is None:
+        need = np.arange(T * k, dtype=np.int64)
+        x_perm = gather(inp["x"], perm_src, k)
+        y_rows = expert_ffn_rows(x_perm, offsets, inp["w_gate"], inp["w_val"], inp["w_out"])
+    else:
+        need = np.unique(dest.reshape(T, k)[tok].reshape(-1)).astype(np.int64)
+        x_perm = gather(inp["x"], perm_src[need], k)
+        y_rows = expert_ffn_rows(x_perm, offsets, inp["w_gate"], inp["w_val"], inp["w_out"],
+                                 need, N=T * k)
     yrow = np.full(T * k, -1, np.int64)
     yrow[need] = np.arange(need.shape[0])
     shared = None
@@ -240,13 +254,20 @@ def moe_layer(inp: dict, tokens=None):
 
 def moe_recv_layer(inp: dict, rows=None):
     """One EP rank's receive side: reorder, expert MLPs, unweighted un-permute
-    back to sender-major order. ``rows`` restricts the evaluated received rows."""
+    back to sender-major order. ``rows`` restricts the evaluated received rows
+    (``x_perm`` then holds the packed rows listed in ``y_rows``)."""
     N = inp["x_recv"].shape[0]
     counts, offsets, perm_src, dest = permute_recv(inp["recv_counts"], N)
-    x_perm = gather(inp["x_recv"], perm_src, 1)
     r = np.arange(N, dtype=np.int32) if rows is None else _c(rows, np.int32)
-    need = np.unique(dest[r]).astype(np.int64)
-    y_rows = expert_ffn_rows(x_perm, offsets, inp["w_gate"], inp["w_val"], inp["w_out"], need)
+    if rows is None:
+        need = np.arange(N, dtype=np.int64)
+        x_perm = gather(inp["x_recv"], perm_src, 1)
+        y_rows = expert_ffn_rows(x_perm, offsets, inp["w_gate"], inp["w_val"], inp["w_out"])
+    else:
+        need = np.unique(dest[r]).astype(np.int64)
+        x_perm = gather(inp["x_recv"], perm_src[need], 1)
+        y_rows = expert_ffn_rows(x_perm, offsets, inp["w_gate"], inp["w_val"], inp["w_out"],
+                                 need, N=N)
     yrow = np.full(N, -1, np.int64)
     yrow[need] = np.arange(need.shape[0])
     out = combine(r, 1, dest, None, y_rows, yrow, None)

@@ -182,7 +182,7 @@ int oracle_gather(const void* x, int elem_bytes, int64_t d,
 int oracle_expert_ffn_rows(const void* x, int xtype, int64_t N, int d, int f, int E,
                            const int32_t* offsets,
                            const void* wg, const void* wv, const void* wo,
-                           const int64_t* rows, int64_t nrows, double* y)
+                           const int64_t* rows, int64_t nrows, int x_compact, double* y)
 {
     if (!x || !offsets || !wg || !wv || !wo || !rows || !y) return -1;
     if (d <= 0 || f <= 0 || E <= 0 || N < 0) return -1;
@@ -199,12 +199,13 @@ int oracle_expert_ffn_rows(const void* x, int xtype, int64_t N, int d, int f, in
 #pragma omp for schedule(dynamic, 4)
         for (int64_t r = 0; r < nrows; ++r) {
             int64_t j = rows[r];
+            int64_t xr = x_compact ? r : j;
             int e = 0;
             while (!(offsets[e] <= j && j < offsets[e + 1])) ++e;
             size_t wbase = (size_t)e * (size_t)d * (size_t)f;
             for (int c = 0; c < f; ++c) { g[c] = 0.0; v[c] = 0.0; }
             for (int i = 0; i < d; ++i) {
-                double xi = (double)load_f(x, xtype, (size_t)j * d + i);
+                double xi = (double)load_f(x, xtype, (size_t)xr * d + i);
                 size_t wrow = wbase + (size_t)i * f;
                 for (int c = 0; c < f; ++c) {
                     g[c] += xi * (double)load_f(wg, xtype, wrow + c);

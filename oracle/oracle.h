@@ -80,12 +80,13 @@ int oracle_gather(const void* x, int elem_bytes, int64_t d,
  *   h_c = g_c / (1 + exp(-g_c)) * v_c,  y[j,o] = sum_c h_c Wo[e,c,o],
  * all in double with no intermediate rounding. Only the listed rows are
  * evaluated: y is [nrows, d], row r holding packed row rows[r].
- *   x [N,d], Wg/Wv [E,d,f], Wo [E,f,d] (type xtype), offsets [E+1].
+ *   x [N,d] (x_compact == 0) or [nrows,d] holding packed row rows[r] in row r
+ *   (x_compact != 0); Wg/Wv [E,d,f], Wo [E,f,d] (type xtype), offsets [E+1].
  */
 int oracle_expert_ffn_rows(const void* x, int xtype, int64_t N, int d, int f, int E,
                            const int32_t* offsets,
                            const void* wg, const void* wv, const void* wo,
-                           const int64_t* rows, int64_t nrows, double* y);
+                           const int64_t* rows, int64_t nrows, int x_compact, double* y);
 
 /*
  * Weighted combine [Three axes of Parallelism, "Dispatch, expert computation

@@ -1,0 +1,83 @@
+"""The C ABI library loads, exports every entry point include/moe.h declares,
+and rejects bad host-side arguments before touching the device (no compute
+call is made here, so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from expert_dispatch_amd import ops
+    return ops.lib()
+
+
+def test_header_declares_the_path():
+    names = _declared()
+    for n in ("moe_route", "moe_permute", "moe_permute_recv", "moe_grouped_ffn", "moe_combine"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in _declared():
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version(L):
+    assert L.moe_status_string(0) == b"ok"
+    assert L.moe_status_string(3) == b"workspace too small"
+    assert L.moe_version() >= 100
+
+
+def test_workspace_queries(L):
+    assert L.moe_permute_workspace(4096, 8, 128) >= 8 * 128 * 4
+    assert L.moe_grouped_ffn_workspace(32768, 2048, 768, 128, 1) >= 32768 * 768 * 2
+    assert L.moe_grouped_ffn_workspace(512, 64, 128, 8, 0) >= 512 * 128 * 4
+
+
+def test_host_side_errors_return_before_launch(L):
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+    # k > E, k <= 0, E too large, unknown dtype
+    assert L.moe_route(fake, 1, fake, None, 16, 64, 4, 5, 1, None, fake, fake, None) == 1
+    assert L.moe_route(fake, 1, fake, None, 16, 64, 4, 0, 1, None, fake, fake, None) == 1
+    assert L.moe_route(fake, 1, fake, None, 16, 64, 2048, 2, 1, None, fake, fake, None) == 2
+    assert L.moe_route(fake, 7, fake, None, 16, 64, 8, 2, 1, None, fake, fake, None) == 1
+    # required output NULL
+    assert L.moe_route(fake, 1, fake, None, 16, 64, 8, 2, 1, None, None, fake, None) == 1
+    # permute: too small a workspace, NULL workspace
+    need = L.moe_permute_workspace(100, 2, 8)
+    assert L.moe_permute(fake, 100, 2, 8, fake, 1, 64, fake, fake, fake, fake, fake, fake,
+                         need - 1, None) == 3
+    assert L.moe_permute(fake, 100, 2, 8, fake, 1, 64, fake, fake, fake, fake, fake, None,
+                         0, None) == 3
+    # permute_recv: too many cells
+    assert L.moe_permute_recv(fake, 64, 128, 10, fake, 1, 64, fake, fake, fake, fake, fake,
+                              None, 0, None) == 2
+    # grouped ffn: NULL offsets, small workspace, bad y dtype
+    assert L.moe_grouped_ffn(fake, 1, 10, 64, 64, 2, None, fake, fake, fake, fake, 0, fake,
+                             1 << 20, None) == 1
+    assert L.moe_grouped_ffn(fake, 1, 10, 64, 64, 2, fake, fake, fake, fake, fake, 0, fake,
+                             16, None) == 3
+    assert L.moe_grouped_ffn(fake, 1, 10, 64, 64, 2, fake, fake, fake, fake, fake, 9, fake,
+                             1 << 20, None) == 1
+    # combine: k too large
+    assert L.moe_combine(fake, 0, fake, None, 4, 33, 64, None, 0, fake, 0, None) == 2
+
+
+def test_empty_inputs_are_no_ops(L):
+    # T = 0 / N = 0 enqueue nothing and succeed
+    assert L.moe_route(None, 1, None, None, 0, 64, 8, 2, 1, None, None, None, None) == 0
+    assert L.moe_grouped_ffn(None, 1, 0, 64, 64, 2, ctypes.c_void_p(0x1000), None, None, None,
+                             None, 0, None, 0, None) == 0
+    assert L.moe_combine(None, 0, None, None, 0, 2, 64, None, 0, None, 0, None) == 0

@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Integer results (router ids, counts, offsets, permutation, packed rows) must
+match bit for bit, and so must the router scores, whose definition fixes
+every bit. Floating-point results must meet the gate: fp32 max relative
+error 1e-5; bf16 max error 2e-2 of the reference output's RMS (fp32
+accumulation). Reduced configs are compared element by element; the full
+workload shapes are compared on every integer output and on sampled rows of
+the floating-point ones, in the same launch configuration as the benchmark.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from expert_dispatch_amd import ops
+from expert_dispatch_amd import workloads as W
+from util import check_float, sample_rows, to_numpy, to_torch, widen, err_f32
+
+pytestmark = pytest.mark.gpu
+
+SMALL_ROUTED = ["tiny_f32", "odd_f32", "qwen3_small", "dsv2_small", "dsv2_small_empty4",
+                "stress_small"]
+FULL_ROUTED = ["qwen3_30b_a3b", "dsv2_lite", "dsv2_lite_empty4", "stress_zipf"]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@functools.lru_cache(maxsize=2)
+def _inputs(name):
+    return W.generate(W.get(name))
+
+
+def _device(inp):
+    dev = {}
+    for key in ("x", "w_router", "bias", "w_gate", "w_val", "w_out", "x_recv", "recv_counts"):
+        if inp.get(key) is not None:
+            dev[key] = to_torch(inp[key])
+    if inp.get("shared_w_gate") is not None:
+        # q shared experts as one SwiGLU of width q*f
+        dev["shared"] = (to_torch(np.concatenate(list(inp["shared_w_gate"]), axis=1)[None]),
+                         to_torch(np.concatenate(list(inp["shared_w_val"]), axis=1)[None]),
+                         to_torch(np.concatenate(list(inp["shared_w_out"]), axis=0)[None]))
+    return dev
+
+
+def _gpu_routed(dev, k):
+    r = ops.moe_layer(dev["x"], dev["w_router"], dev.get("bias"), k, dev["w_gate"], dev["w_val"],
+                      dev["w_out"], shared=dev.get("shared"))
+    torch.cuda.synchronize()
+    return r
+
+
+def _check_routed(name, full):
+    cfg = W.get(name)
+    say(f"[parity] {name}: generate")
+    inp = _inputs(name)
+    dev = _device(inp)
+    say(f"[parity] {name}: gpu layer")
+    g = _gpu_routed(dev, cfg.k)
+    rng = np.random.default_rng(0)
+    T, k = cfg.T, cfg.k
+    tokens = None
+    if full:
+        tokens = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, size=96)])).astype(np.int32)
+    say(f"[parity] {name}: oracle")
+    o = oracle.moe_layer(inp, tokens=tokens)
+
+    # router: scores fixed bit for bit, ids bit-exact, weights at fp32 tolerance
+    np.testing.assert_array_equal(to_numpy(g["logits"]).view(np.uint32), o["logits"].view(np.uint32))
+    np.testing.assert_array_equal(to_numpy(g["idx"]), o["idx"])
+    e = err_f32(to_numpy(g["gates"]), o["gates"])
+    assert e <= 1e-5, f"gates rel err {e:.3e}"
+    # packing: bit-exact
+    for key in ("counts", "offsets", "perm_src", "dest"):
+        np.testing.assert_array_equal(to_numpy(g[key]), o[key], err_msg=key)
+    # packed rows: bitwise copies
+    if full:
+        rows_t = torch.from_numpy(o["y_rows"]).to("cuda")
+        xp = to_numpy(g["x_perm"].index_select(0, rows_t))
+        y = to_numpy(g["y"].index_select(0, rows_t))
+    else:
+        xp = to_numpy(g["x_perm"])
+        y = to_numpy(g["y"])
+    np.testing.assert_array_equal(xp, o["x_perm"])
+    ey = check_float(y, o["y"], cfg.dtype, f"{name} y_perm")
+    # shared experts (one fused SwiGLU of width 2f vs the sum of two)
+    if o["shared"] is not None:
+        sh = to_numpy(g["y_shared"])[o["tokens"]]
+        check_float(sh, o["shared"], cfg.dtype, f"{name} y_shared")
+    out = to_numpy(g["out"])[o["tokens"]]
+    eo = check_float(out, o["out"], cfg.dtype, f"{name} out")
+    say(f"[parity] {name}: ok  y_err={ey:.3e} out_err={eo:.3e}")
+
+
+@pytest.mark.parametrize("name", SMALL_ROUTED)
+def test_routed_layer_small(name):
+    _check_routed(name, full=False)
+
+
+@pytest.mark.parametrize("name", FULL_ROUTED)
+def test_routed_layer_full(name):
+    _check_routed(name, full=True)
+
+
+def _check_recv(name, full, zero_col=None):
+    cfg = W.get(name)
+    say(f"[parity] {name} recv: generate")
+    inp = _inputs(name)
+    if zero_col is not None:
+        inp = W.zero_expert_column(inp, zero_col)
+    dev = _device(inp)
+    N = cfg.N
+    say(f"[parity] {name} recv: gpu")
+    p = ops.permute_recv(dev["recv_counts"], dev["x_recv"])
+    y = ops.grouped_ffn(p["x_perm"], p["offsets"], dev["w_gate"], dev["w_val"], dev["w_out"])
+    out = ops.combine(y, p["dest"], None, 1)
+    torch.cuda.synchronize()
+    rows = None
+    if full:
+        rng = np.random.default_rng(1)
+        rows = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, size=128)])).astype(np.int32)
+    say(f"[parity] {name} recv: oracle")
+    o = oracle.moe_recv_layer(inp, rows=rows)
+    for key in ("counts", "offsets", "perm_src", "dest"):
+        np.testing.assert_array_equal(to_numpy(p[key]), o[key], err_msg=key)
+    if zero_col is not None:
+        assert int(to_numpy(p["counts"])[zero_col]) == 0
+    if full:
+        rt = torch.from_numpy(o["y_rows"]).to("cuda")
+        xp = to_numpy(p["x_perm"].index_select(0, rt))
+        yy = to_numpy(y.index_select(0, rt))
+        # the packed buffer is a permutation of the received one: check it whole on the device
+        src = dev["x_recv"].index_select(0, p["perm_src"].long())
+        assert torch.equal(src.view(torch.int16), p["x_perm"].view(torch.int16))
+    else:
+        xp = to_numpy(p["x_perm"])
+        yy = to_numpy(y)
+    np.testing.assert_array_equal(xp, o["x_perm"])
+    check_float(yy, o["y"], cfg.dtype, f"{name} y_perm")
+    check_float(to_numpy(out)[o["rows"]], o["out"], cfg.dtype, f"{name} out")
+    say(f"[parity] {name} recv: ok")
+
+
+def test_recv_small():
+    _check_recv("ep_share_small", full=False)
+
+
+def test_recv_small_with_empty_expert():
+    _check_recv("ep_share_small", full=False, zero_col=2)
+
+
+def test_recv_full():
+    _check_recv("ep_rank_share", full=True)
+
+
+def test_recv_full_with_empty_expert():
+    _check_recv("ep_rank_share", full=True, zero_col=5)
+
+
+# ------------------------------------------------------------------- edges
+
+
+def _small_layer(inp, name="edge"):
+    """Full element-by-element parity of a token-routed layer dict."""
+    dev = _device(inp)
+    g = _gpu_routed(dev, inp["k"])
+    o = oracle.moe_layer(inp)
+    np.testing.assert_array_equal(to_numpy(g["idx"]), o["idx"])
+    for key in ("counts", "offsets", "perm_src", "dest"):
+        np.testing.assert_array_equal(to_numpy(g[key]), o[key], err_msg=key)
+    np.testing.assert_array_equal(to_numpy(g["x_perm"]), o["x_perm"])
+    dt = "bf16" if inp["x"].dtype == np.uint16 else "f32"
+    check_float(to_numpy(g["y"]), o["y"], dt, f"{name} y")
+    check_float(to_numpy(g["out"]), o["out"], dt, f"{name} out")
+    return g, o
+
+
+def test_all_tokens_to_one_expert():
+    inp = dict(_inputs("qwen3_small"))
+    b = np.zeros(inp["w_gate"].shape[0], np.float32)
+    b[3] = 1e4
+    for k in (1, 2):
+        g, o = _small_layer(dict(inp, bias=b, k=k), f"one-expert k={k}")
+        assert int(o["counts"][3]) == inp["x"].shape[0]
+
+
+def test_k_equals_E_and_single_expert():
+    inp = dict(_inputs("tiny_f32"))
+    _small_layer(dict(inp, k=8), "k=E")
+    one = dict(inp, k=1, w_router=inp["w_router"][:, :1], w_gate=inp["w_gate"][:1],
+               w_val=inp["w_val"][:1], w_out=inp["w_out"][:1])
+    g, o = _small_layer(one, "E=1")
+    assert (to_numpy(g["gates"]) == 1.0).all()
+
+
+def test_bf16_shapes_off_the_matrix_core_tiles():
+    cfg = W.get("qwen3_small", d=96, f=80, T=70, E=5, k=2, seed=21)
+    _small_layer(W.generate(cfg), "bf16 d=96 f=80")
+
+
+def test_one_token_and_ragged_tiles():
+    cfg = W.get("qwen3_small", T=1, seed=22)
+    _small_layer(W.generate(cfg), "T=1")
+    cfg = W.get("qwen3_small", T=257, E=3, k=2, seed=23)   # 514 rows over 3 experts
+    _small_layer(W.generate(cfg), "T=257 E=3")
+
+
+def test_empty_batch():
+    inp = _inputs("qwen3_small")
+    dev = _device(inp)
+    x0 = dev["x"][:0]
+    logits, idx, gates = ops.route(x0, dev["w_router"], dev["bias"], 4)
+    p = ops.permute(idx, x0, 16)
+    torch.cuda.synchronize()
+    assert to_numpy(p["counts"]).tolist() == [0] * 16
+    assert to_numpy(p["offsets"]).tolist() == [0] * 17
+
+
+def test_unnormalised_router_weights():
+    inp = _inputs("qwen3_small")
+    dev = _device(inp)
+    _, idx, gates = ops.route(dev["x"], dev["w_router"], dev["bias"], 4, renorm=False)
+    torch.cuda.synchronize()
+    _, oi, og = oracle.route(inp["x"], inp["w_router"], inp["bias"], 4, renorm=False)
+    np.testing.assert_array_equal(to_numpy(idx), oi)
+    assert err_f32(to_numpy(gates), og) <= 1e-5
+
+
+def test_deterministic_bitwise():
+    for name in ("qwen3_small", "qwen3_30b_a3b"):
+        inp = _inputs(name)
+        dev = _device(inp)
+        a = _gpu_routed(dev, inp["k"])
+        b = _gpu_routed(dev, inp["k"])
+        for key in ("idx", "dest", "perm_src"):
+            assert torch.equal(a[key], b[key]), key
+        assert torch.equal(a["y"].view(torch.int32), b["y"].view(torch.int32))
+        assert torch.equal(a["out"].view(torch.int32), b["out"].view(torch.int32))
+
+
+def test_bf16_outputs():
+    """y_perm and out stored as bf16 (the narrow-output variant) stay in tolerance."""
+    inp = _inputs("qwen3_small")
+    dev = _device(inp)
+    k = inp["k"]
+    _, idx, gates = ops.route(dev["x"], dev["w_router"], dev["bias"], k)
+    p = ops.permute(idx, dev["x"], 16)
+    y = ops.grouped_ffn(p["x_perm"], p["offsets"], dev["w_gate"], dev["w_val"], dev["w_out"],
+                        y_dtype=torch.bfloat16)
+    out = ops.combine(y, p["dest"], gates, k, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    o = oracle.moe_layer(inp)
+    yb = to_numpy(y)
+    ob = to_numpy(out)
+    # bf16 storage adds at most half an ulp (2^-9 relative) on top of the fp32 result
+    ref_rms = float(np.sqrt(np.mean(o["out"] ** 2)))
+    assert np.max(np.abs(widen(ob) - o["out"])) / ref_rms <= 4e-2
+    assert np.max(np.abs(widen(yb) - o["y"])) / float(np.sqrt(np.mean(o["y"] ** 2))) <= 4e-2

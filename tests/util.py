@@ -1,0 +1,76 @@
+"""Helpers shared by the tests: moving workload arrays to the device and the
+parity metrics. Holds none of the layer's arithmetic."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+# Tolerances of the parity gate: fp32 results within a max relative error of
+# 1e-5, bf16 results (fp32 accumulation) within 2e-2 relative to the RMS of
+# the reference output.
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-2
+
+
+def to_torch(a: np.ndarray, device="cuda"):
+    """numpy fp32 / bf16-bits (uint16) / int32 array -> device tensor."""
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def to_numpy(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def widen(a: np.ndarray) -> np.ndarray:
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def err_f32(got, ref) -> float:
+    """max_i |got_i - ref_i| / max(|ref_i|, rms(ref))."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    den = np.maximum(np.abs(ref), rms if rms > 0 else 1.0)
+    return float(np.max(np.abs(got - ref) / den)) if ref.size else 0.0
+
+
+def err_bf16(got, ref) -> float:
+    """max_i |got_i - ref_i| / rms(ref)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if not ref.size:
+        return 0.0
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    return float(np.max(np.abs(got - ref)) / (rms if rms > 0 else 1.0))
+
+
+def check_float(got, ref, dtype: str, what: str):
+    if dtype == "f32":
+        e = err_f32(got, ref)
+        assert e <= TOL_F32, f"{what}: max rel err {e:.3e} > {TOL_F32}"
+    else:
+        e = err_bf16(got, ref)
+        assert e <= TOL_BF16, f"{what}: max err / rms {e:.3e} > {TOL_BF16}"
+    return e
+
+
+def sample_rows(offsets: np.ndarray, per_expert: int, rng) -> np.ndarray:
+    """First and last packed row of every non-empty expert plus random rows."""
+    rows = []
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi <= lo:
+            continue
+        rows += [lo, hi - 1]
+        if hi - lo > 2:
+            rows += list(rng.integers(lo, hi, size=min(per_expert, hi - lo)))
+    return np.unique(np.array(rows, np.int64))
