@@ -46,7 +46,23 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU work of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (3 launches), the reference "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read_per_launch": n,
+                      "copy_calibration_bytes_written_per_launch": n, "launches": 3}), flush=True)
 
 
 def to_dev(a, torch):
@@ -152,6 +168,9 @@ def cpu_baseline(cfg, inp, target_s: float):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the layer runs on one GPU's share; see DESIGN.md for how it would shard)",
