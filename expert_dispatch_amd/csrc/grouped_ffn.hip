@@ -87,18 +87,34 @@ static long long max_row_tiles(int N, int E, int bm) {
 
 // ------------------------------------------------------ matrix-core kernel
 
-constexpr int BM = 128;
-constexpr int BK = 64;
-constexpr int LDK = BK + 8;   // LDS row stride in bf16 (144 bytes)
-constexpr int BNB = 256;      // B-panel rows (output columns of the block)
+constexpr int BM = 128;       // rows per tile
+constexpr int BK = 64;        // k per pipeline stage
+constexpr int BNB = 256;      // B-panel columns per tile
 constexpr int kMfmaThreads = 256;
 
-__device__ __forceinline__ unsigned pack_lo(unsigned a, unsigned b) {  // low halves
-    return (a & 0xffffu) | (b << 16);
+#define LDS_AS __attribute__((address_space(3)))
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// Workgroup barrier of the pipelined main loop. __syncthreads() carries a
+// workgroup fence, for which the compiler waits on every outstanding global
+// load, draining the prefetched stages held in registers. The loop needs no
+// fence: the LDS writes before the barrier and the LDS reads after it are
+// ordered by the barrier itself, the compiler waits on each register load
+// exactly where its value is written to LDS, and the asm memory clobber keeps
+// the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
-__device__ __forceinline__ unsigned pack_hi(unsigned a, unsigned b) {  // high halves
-    return (a >> 16) | (b & 0xffff0000u);
-}
+
+// Stage layouts in LDS (no padding; XOR swizzles keep the fragment reads
+// conflict-free):
+//  A: [BM rows][BK], 16-byte chunk c of row r stored at chunk c ^ (r & 7);
+//  B: [BK k-rows][BNB columns], N-contiguous as in memory, 16-byte chunk c of
+//     k-row r stored at chunk c ^ 2*(r & 3). B fragments are read with the
+//     gfx950 LDS transpose read (ds_read_b64_tr_b16): in each 16-lane group,
+//     lane j points at k-row j/4, columns 4*(j%4)..+3 of a 4 x 16 block and
+//     receives the 4 k-values of column j.
 
 template <bool GATE_UP, bool Y_BF16>
 __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
@@ -107,8 +123,8 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
     void* __restrict__ C)
 {
     constexpr int BNT = GATE_UP ? 128 : 256;   // output columns per tile
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BNB * LDK];
+    __shared__ __attribute__((aligned(1024))) uint16_t sA[2][BM * BK];
+    __shared__ __attribute__((aligned(1024))) uint16_t sB[2][BK * BNB];
     __shared__ int scratch[kMfmaThreads / kWave + 1];
 
     const int tid = threadIdx.x;
@@ -119,70 +135,67 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
 
     Tile tile;
     {
-        int* s_off = reinterpret_cast<int*>(&sB[0][0]);
-        int* s_pre = s_off + kMaxE + 1;
+        int* s_pre = reinterpret_cast<int*>(&sB[0][0]);   // 4096 ints fit in 32 KB
+        int* s_off = reinterpret_cast<int*>(&sB[1][0]);   // 4097 ints fit in 32 KB
         const bool ok = schedule_tile(offsets, N, E, BM, NC / BNT, s_off, s_pre, scratch, tile);
         if (!ok) return;  // uniform over the block
-        __syncthreads();  // scheduler LDS is reused below
+        __syncthreads();  // the scheduler's LDS is reused below
     }
     const int m0 = tile.m0;
     const int seg_last = tile.seg_end - 1;
     const size_t wbase = (size_t)tile.e * (size_t)K * (size_t)NC;
     const int n0 = tile.n_tile * BNT;
 
-    // global -> register staging
-    // A: 128 rows x 64 k: chunk c = tid + 256 q -> row c/8, 8 k at (c%8)*8
+    // ---- global sources and LDS destinations of this thread's 16-byte chunks
+    // A: chunk id q = tid + 256 i -> row tid/8 + 32 i, chunk tid%8 (8 lanes per
+    // 128-byte row); the swizzle term (row & 7) does not depend on i.
     const uint16_t* a_src[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int c = tid + kMfmaThreads * q;
-        const int row = min(m0 + (c >> 3), seg_last);
-        a_src[q] = A + (size_t)row * K + (c & 7) * 8;
+    for (int i = 0; i < 4; ++i) {
+        const int r = (tid >> 3) + 32 * i;
+        a_src[i] = A + (size_t)min(m0 + r, seg_last) * K + (tid & 7) * 8;
     }
-    // B: an 8x8 block per thread: k rows 8*kb.., columns 8*nb..
-    const int kb = tid & 7;
-    const int nb = tid >> 3;
+    const int a_dst = (tid >> 3) * BK + (((tid & 7) ^ ((tid >> 3) & 7)) * 8);   // + 32 i rows
+    // B: chunk id q = tid + 256 i -> k-row tid/32 + 8 i, chunk tid%32 (32 lanes
+    // per 512-byte row); again the swizzle term (k-row & 3) does not depend on i.
     const uint16_t* b_src;
-    if (GATE_UP)
-        b_src = (nb < 16 ? B0 : B1) + wbase + (size_t)(kb * 8) * NC + n0 + (nb & 15) * 8;
-    else
-        b_src = B0 + wbase + (size_t)(kb * 8) * NC + n0 + nb * 8;
-
-    u32x4 ra[4];
-    u32x4 rb[8];
-    auto load_stage = [&](int kt) {
-        const size_t ko = (size_t)kt * BK;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) ra[q] = *reinterpret_cast<const u32x4*>(a_src[q] + ko);
-        const uint16_t* bs = b_src + ko * NC;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) rb[r] = *reinterpret_cast<const u32x4*>(bs + (size_t)r * NC);
-    };
-    auto store_stage = [&](int buf) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = tid + kMfmaThreads * q;
-            *reinterpret_cast<u32x4*>(&sA[buf][(c >> 3) * LDK + (c & 7) * 8]) = ra[q];
+    {
+        const int c = tid & 31;
+        const uint16_t* base;
+        int col;
+        if (GATE_UP) {
+            base = (c < 16) ? B0 : B1;
+            col = n0 + (c & 15) * 8;
+        } else {
+            base = B0;
+            col = n0 + c * 8;
         }
-        // transpose the 8 (k) x 8 (n) block: column n becomes 8 consecutive k
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-            u32x4 o;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const unsigned lo = rb[2 * q][n >> 1];
-                const unsigned hi = rb[2 * q + 1][n >> 1];
-                o[q] = (n & 1) ? pack_hi(lo, hi) : pack_lo(lo, hi);
-            }
-            *reinterpret_cast<u32x4*>(&sB[buf][(nb * 8 + n) * LDK + kb * 8]) = o;
-        }
-    };
+        b_src = base + wbase + (size_t)(tid >> 5) * NC + col;                      // + 8 i k-rows
+    }
+    const int b_dst = (tid >> 5) * BNB + (((tid & 31) ^ (2 * ((tid >> 5) & 3))) * 8);  // + 8 i k-rows
 
-    int nbase[4];
+    // ---- fragment addressing (element offsets inside a stage buffer)
+    // A (row 64wm + 32mi + lane%32, logical chunk 2ks + lane/32): the mi term
+    // is a constant 32 rows; the ks term goes through the XOR, one base per ks.
+    int a_lane[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int r = 64 * wm + (lane & 31);
+        a_lane[ks] = r * BK + ((((2 * ks + (lane >> 5)) ^ (r & 7))) * 8);
+    }
+    // B: 16-lane group g = lane/16, j = lane%16 points at k-row
+    // 16ks + 8(g/2) + 4h + j/4 and column nbase[q] + 16(g%2) + 4(j%4); the
+    // swizzle term (k-row & 3) = j/4 is lane-constant, so ks and h are
+    // constant offsets and only q needs a per-lane base.
+    const int g = lane >> 4, j = lane & 15;
+    int b_lane[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        if (GATE_UP) nbase[q] = (q < 2) ? (64 * wn + 32 * q) : (128 + 64 * wn + 32 * (q - 2));
-        else nbase[q] = 128 * wn + 32 * q;
+        int nb;
+        if (GATE_UP) nb = (q < 2) ? (64 * wn + 32 * q) : (128 + 64 * wn + 32 * (q - 2));
+        else nb = 128 * wn + 32 * q;
+        const int n = nb + 16 * (g & 1) + 4 * (j & 3);
+        b_lane[q] = (8 * (g >> 1) + (j >> 2)) * BNB + (((n >> 3) ^ (2 * (j >> 2))) * 8) + (n & 7);
     }
 
     f32x16 acc[2][4];
@@ -193,35 +206,76 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][q][r] = 0.0f;
 
-    const int KT = K / BK;
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-
-    const int frow = lane & 31;
-    const int fk = (lane >> 5) * 8;
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) load_stage(kt + 1);
-        const uint16_t* sa = sA[cur];
-        const uint16_t* sb = sB[cur];
+    // two register stages in flight; LDS double buffer
+    u32x4 ra0[4], rb0[8], ra1[4], rb1[8];
+    auto load_regs = [&](int kt, u32x4 (&ra)[4], u32x4 (&rb)[8]) {
+        const size_t ka = (size_t)kt * BK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + ka);
+        const uint16_t* bs = b_src + ka * NC;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bs + (size_t)(8 * i) * NC);
+    };
+    auto store_lds = [&](int buf, const u32x4 (&ra)[4], const u32x4 (&rb)[8]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&sA[buf][a_dst + 32 * i * BK]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(&sB[buf][b_dst + 8 * i * BNB]) = rb[i];
+    };
+    auto compute = [&](int buf) {
+        const uint16_t* sa = sA[buf];
+        const uint16_t* sb = sB[buf];
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             bf16x8 af[2], bfr[4];
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
-                af[mi] = *reinterpret_cast<const bf16x8*>(&sa[(64 * wm + 32 * mi + frow) * LDK + ks * 16 + fk]);
+                af[mi] = *reinterpret_cast<const bf16x8*>(sa + a_lane[ks] + 32 * mi * BK);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                bfr[q] = *reinterpret_cast<const bf16x8*>(&sb[(nbase[q] + frow) * LDK + ks * 16 + fk]);
+            for (int q = 0; q < 4; ++q) {
+                const uint16_t* p = sb + b_lane[q] + 16 * ks * BNB;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * BNB));
+                const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                bfr[q] = __builtin_bit_cast(bf16x8, v);
+            }
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     acc[mi][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[q], acc[mi][q], 0, 0, 0);
+            // keep each substep's fragment reads next to its MFMAs (bounds live registers)
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (kt + 1 < KT) store_stage(cur ^ 1);
-        __syncthreads();
+    };
+
+    const int KT = K / BK;
+    // Loads and LDS writes past the last stage are issued anyway with the
+    // stage index clamped (a valid address, written into a buffer that is
+    // free and never read again): branch-free, so the compiler's wait
+    // analysis sees one straight path and waits only for the stage it stores.
+    auto clampk = [&](int k) { return min(k, KT - 1); };
+    load_regs(0, ra0, rb0);
+    load_regs(clampk(1), ra1, rb1);
+    store_lds(0, ra0, rb0);
+    load_regs(clampk(2), ra0, rb0);
+    // iteration kt: barrier (stage kt is in LDS buffer kt&1 and buffer
+    // (kt+1)&1 is free); write stage kt+1 from its registers; reload those
+    // registers with stage kt+3; compute stage kt. Loads get two iterations.
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
+        lds_barrier();
+        store_lds(1, ra1, rb1);
+        load_regs(clampk(kt + 3), ra1, rb1);
+        compute(0);
+        lds_barrier();
+        store_lds(0, ra0, rb0);
+        load_regs(clampk(kt + 4), ra0, rb0);
+        compute(1);
+    }
+    if (kt < KT) {  // odd number of stages: the last one sits in buffer 0
+        lds_barrier();
+        compute(0);
     }
 
     // epilogue: lane holds column (lane % 32) of each 32x32 accumulator and
@@ -239,9 +293,9 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
                 for (int r = 0; r < 16; ++r) {
                     const int row = m0 + 64 * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
                     if (row <= seg_last) {
-                        const float g = acc[mi][q][r];
+                        const float gv = acc[mi][q][r];
                         const float v = acc[mi][q + 2][r];
-                        const float h = g / (1.0f + __expf(-g)) * v;
+                        const float h = __fdividef(gv, 1.0f + __expf(-gv)) * v;
                         H[(size_t)row * NC + col] = f32_to_bf16(h);
                     }
                 }
