@@ -72,7 +72,7 @@ moe_status moe_route(const void* x, moe_dtype dt, const void* w_router, const fl
     if ((long long)T * E > INT32_MAX || (long long)T * d > (1LL << 40))
         return MOE_ERR_UNSUPPORTED;
     if (T == 0) return MOE_OK;
-    if (!x || !w_router || !topk_idx || !gates) return MOE_ERR_INVALID_ARG;
+    if (!x || !w_router || !logits || !topk_idx || !gates) return MOE_ERR_INVALID_ARG;
     return hip_status(moe::launch_route(x, dt, w_router, bias, T, d, E, k, renorm, logits,
                                         topk_idx, gates, as_stream(stream)));
 }

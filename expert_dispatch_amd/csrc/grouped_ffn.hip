@@ -14,17 +14,19 @@
 //    surplus blocks leave at once;
 //  * XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs,
 //    so block b works on tile (b % 8) * ceil(tiles / 8) + b / 8. Each XCD
-//    then walks a contiguous run of the tile list, in which the row tiles of
-//    one (expert, column tile) are adjacent and share that weight panel
-//    through the XCD's L2;
-//  * block tile 128 rows x 256 B-columns (gate_up: 128 gate + 128 val columns
-//    of the same hidden units), BK = 64, 4 wavefronts of 64 x 128, each a
-//    2 x 4 grid of v_mfma_f32_32x32x16_bf16 accumulators (128 fp32 / lane);
-//  * LDS double buffer (108 KB): A rows K-contiguous; the weight panel, which
-//    is N-contiguous in memory, is transposed 8x8 in registers on its way in
-//    so that both MFMA operands are read with 16-byte LDS loads. Rows are
-//    padded by 16 bytes, which keeps the 16-byte reads and writes free of
-//    bank conflicts;
+//    then walks a contiguous run of the tile list, ordered expert by expert
+//    and, inside an expert, by groups of 4 row tiles that sweep all column
+//    tiles, so the tiles resident on an XCD share row and weight panels
+//    through its L2;
+//  * block tile 256 rows x 256 B-columns (gate_up: 128 gate + 128 val columns
+//    of the same hidden units), BK = 64, 4 wavefronts of 128 x 128, each a
+//    4 x 4 grid of v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 / lane,
+//    held in AGPRs), so every fragment read from LDS feeds four MFMAs;
+//  * a register-staged pipeline: two stages of global loads in flight in
+//    registers while one LDS buffer (of two, 128 KB) is consumed. A is
+//    K-contiguous in LDS; the weight panel stays N-contiguous as in memory and
+//    the MFMA B fragments come from the gfx950 LDS transpose read. XOR
+//    swizzles keep both fragment reads and the staging writes conflict-free;
 //  * the fused epilogue applies SwiGLU on the two accumulator sets of a lane
 //    (gate and val of the same element sit in the same lane and register).
 // A plain fp32-FMA kernel covers fp32 data and shapes the matrix-core path
@@ -36,6 +38,7 @@
 namespace moe {
 
 constexpr int kMaxE = 4096;
+constexpr int kGroupM = 4;   // row tiles per scheduling group inside an expert
 
 // ----------------------------------------------------------- tile scheduler
 
@@ -73,9 +76,15 @@ __device__ bool schedule_tile(const int32_t* __restrict__ offsets, int N, int E,
     const int rows_hi = max(rows_lo, s_off[e + 1]);
     const int mt = (rows_hi - rows_lo + bm - 1) / bm;
     const int local = t - s_pre[e];
+    // inside an expert, groups of kGroupM row tiles sweep all column tiles
+    // (row tile fastest): the tiles resident on an XCD at one time share a
+    // few A row panels and a few weight panels through its L2
+    const int grp = local / (kGroupM * n_tiles);
+    const int within = local - grp * (kGroupM * n_tiles);
+    const int gsz = min(kGroupM, mt - grp * kGroupM);
     tile.e = e;
-    tile.n_tile = local / mt;
-    tile.m0 = rows_lo + (local % mt) * bm;
+    tile.n_tile = within / gsz;
+    tile.m0 = rows_lo + (grp * kGroupM + within % gsz) * bm;
     tile.seg_end = rows_hi;
     return true;
 }
@@ -87,10 +96,12 @@ static long long max_row_tiles(int N, int E, int bm) {
 
 // ------------------------------------------------------ matrix-core kernel
 
-constexpr int BM = 128;       // rows per tile
+constexpr int BM = 256;       // rows per tile
 constexpr int BK = 64;        // k per pipeline stage
 constexpr int BNB = 256;      // B-panel columns per tile
 constexpr int kMfmaThreads = 256;
+constexpr int kMI = BM / 64;   // 32-row accumulator blocks per wavefront (2 x 2 wavefronts)
+constexpr int kAChunks = BM * BK / 8 / kMfmaThreads;   // 16-byte A chunks per thread per stage
 
 #define LDS_AS __attribute__((address_space(3)))
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -149,9 +160,9 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
     // ---- global sources and LDS destinations of this thread's 16-byte chunks
     // A: chunk id q = tid + 256 i -> row tid/8 + 32 i, chunk tid%8 (8 lanes per
     // 128-byte row); the swizzle term (row & 7) does not depend on i.
-    const uint16_t* a_src[4];
+    const uint16_t* a_src[kAChunks];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kAChunks; ++i) {
         const int r = (tid >> 3) + 32 * i;
         a_src[i] = A + (size_t)min(m0 + r, seg_last) * K + (tid & 7) * 8;
     }
@@ -175,12 +186,12 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
     const int b_dst = (tid >> 5) * BNB + (((tid & 31) ^ (2 * ((tid >> 5) & 3))) * 8);  // + 8 i k-rows
 
     // ---- fragment addressing (element offsets inside a stage buffer)
-    // A (row 64wm + 32mi + lane%32, logical chunk 2ks + lane/32): the mi term
+    // A (row (BM/2)wm + 32mi + lane%32, logical chunk 2ks + lane/32): the mi term
     // is a constant 32 rows; the ks term goes through the XOR, one base per ks.
     int a_lane[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        const int r = 64 * wm + (lane & 31);
+        const int r = (BM / 2) * wm + (lane & 31);
         a_lane[ks] = r * BK + ((((2 * ks + (lane >> 5)) ^ (r & 7))) * 8);
     }
     // B: 16-lane group g = lane/16, j = lane%16 points at k-row
@@ -198,27 +209,27 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
         b_lane[q] = (8 * (g >> 1) + (j >> 2)) * BNB + (((n >> 3) ^ (2 * (j >> 2))) * 8) + (n & 7);
     }
 
-    f32x16 acc[2][4];
+    f32x16 acc[kMI][4];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][q][r] = 0.0f;
 
     // two register stages in flight; LDS double buffer
-    u32x4 ra0[4], rb0[8], ra1[4], rb1[8];
-    auto load_regs = [&](int kt, u32x4 (&ra)[4], u32x4 (&rb)[8]) {
+    u32x4 ra0[kAChunks], rb0[8], ra1[kAChunks], rb1[8];
+    auto load_regs = [&](int kt, u32x4 (&ra)[kAChunks], u32x4 (&rb)[8]) {
         const size_t ka = (size_t)kt * BK;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + ka);
+        for (int i = 0; i < kAChunks; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + ka);
         const uint16_t* bs = b_src + ka * NC;
 #pragma unroll
         for (int i = 0; i < 8; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bs + (size_t)(8 * i) * NC);
     };
-    auto store_lds = [&](int buf, const u32x4 (&ra)[4], const u32x4 (&rb)[8]) {
+    auto store_lds = [&](int buf, const u32x4 (&ra)[kAChunks], const u32x4 (&rb)[8]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&sA[buf][a_dst + 32 * i * BK]) = ra[i];
+        for (int i = 0; i < kAChunks; ++i) *reinterpret_cast<u32x4*>(&sA[buf][a_dst + 32 * i * BK]) = ra[i];
 #pragma unroll
         for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(&sB[buf][b_dst + 8 * i * BNB]) = rb[i];
     };
@@ -227,9 +238,9 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
         const uint16_t* sb = sB[buf];
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            bf16x8 af[2], bfr[4];
+            bf16x8 af[kMI], bfr[4];
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
+            for (int mi = 0; mi < kMI; ++mi)
                 af[mi] = *reinterpret_cast<const bf16x8*>(sa + a_lane[ks] + 32 * mi * BK);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -240,7 +251,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
                 bfr[q] = __builtin_bit_cast(bf16x8, v);
             }
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
+            for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     acc[mi][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[q], acc[mi][q], 0, 0, 0);
@@ -285,13 +296,13 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
     if (GATE_UP) {
         uint16_t* H = static_cast<uint16_t*>(C);
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
+        for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int col = n0 + 64 * wn + 32 * q + col_l;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + 64 * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
+                    const int row = m0 + (BM / 2) * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
                     if (row <= seg_last) {
                         const float gv = acc[mi][q][r];
                         const float v = acc[mi][q + 2][r];
@@ -302,13 +313,13 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
             }
     } else {
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
+        for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int col = n0 + 128 * wn + 32 * q + col_l;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + 64 * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
+                    const int row = m0 + (BM / 2) * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
                     if (row <= seg_last) {
                         if (Y_BF16)
                             static_cast<uint16_t*>(C)[(size_t)row * NC + col] = f32_to_bf16(acc[mi][q][r]);

@@ -94,14 +94,13 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def route(x, w_router, bias, k: int, renorm: bool = True, *, want_logits: bool = True,
-          out=None, stream=None):
-    """Router scores (optional), top-k ids and router weights."""
+def route(x, w_router, bias, k: int, renorm: bool = True, *, out=None, stream=None):
+    """Router scores, top-k ids and router weights."""
     _dev(x, "x"); _dev(w_router, "w_router")
     T, d = x.shape
     E = w_router.shape[1]
     if out is None:
-        logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if want_logits else None
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
         idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
         gates = torch.empty((T, k), dtype=torch.float32, device=x.device)
     else:

@@ -63,7 +63,7 @@ int moe_version(void);
  *   x        [T,d] dtype dt        token activations
  *   w_router [d,E] dtype dt        router weight
  *   bias     [E] fp32 or NULL      per-expert score bias
- *   logits   [T,E] fp32 out or NULL (not written)
+ *   logits   [T,E] fp32 out         router scores (required: selection reads them)
  *   topk_idx [T,k] int32 out       expert ids, slot 0 = highest score
  *   gates    [T,k] fp32 out        router weights
  * Scores: logits[t,e] = fl32(sum_i x[t,i]*w[i,e]) (+ bias[e]), the sum taken in

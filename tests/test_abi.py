@@ -49,12 +49,13 @@ def test_workspace_queries(L):
 def test_host_side_errors_return_before_launch(L):
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
     # k > E, k <= 0, E too large, unknown dtype
-    assert L.moe_route(fake, 1, fake, None, 16, 64, 4, 5, 1, None, fake, fake, None) == 1
-    assert L.moe_route(fake, 1, fake, None, 16, 64, 4, 0, 1, None, fake, fake, None) == 1
-    assert L.moe_route(fake, 1, fake, None, 16, 64, 2048, 2, 1, None, fake, fake, None) == 2
-    assert L.moe_route(fake, 7, fake, None, 16, 64, 8, 2, 1, None, fake, fake, None) == 1
-    # required output NULL
-    assert L.moe_route(fake, 1, fake, None, 16, 64, 8, 2, 1, None, None, fake, None) == 1
+    assert L.moe_route(fake, 1, fake, None, 16, 64, 4, 5, 1, fake, fake, fake, None) == 1
+    assert L.moe_route(fake, 1, fake, None, 16, 64, 4, 0, 1, fake, fake, fake, None) == 1
+    assert L.moe_route(fake, 1, fake, None, 16, 64, 2048, 2, 1, fake, fake, fake, None) == 2
+    assert L.moe_route(fake, 7, fake, None, 16, 64, 8, 2, 1, fake, fake, fake, None) == 1
+    # required outputs NULL
+    assert L.moe_route(fake, 1, fake, None, 16, 64, 8, 2, 1, None, fake, fake, None) == 1
+    assert L.moe_route(fake, 1, fake, None, 16, 64, 8, 2, 1, fake, None, fake, None) == 1
     # permute: too small a workspace, NULL workspace
     need = L.moe_permute_workspace(100, 2, 8)
     assert L.moe_permute(fake, 100, 2, 8, fake, 1, 64, fake, fake, fake, fake, fake, fake,
