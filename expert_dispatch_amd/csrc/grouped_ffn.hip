@@ -32,6 +32,7 @@
 // A plain fp32-FMA kernel covers fp32 data and shapes the matrix-core path
 // does not tile.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -97,11 +98,20 @@ static long long max_row_tiles(int N, int E, int bm) {
 // ------------------------------------------------------ matrix-core kernel
 
 constexpr int BM = 256;       // rows per tile
-constexpr int BK = 64;        // k per pipeline stage
+constexpr int BK = 32;        // k per pipeline stage
 constexpr int BNB = 256;      // B-panel columns per tile
 constexpr int kMfmaThreads = 256;
-constexpr int kMI = BM / 64;   // 32-row accumulator blocks per wavefront (2 x 2 wavefronts)
-constexpr int kAChunks = BM * BK / 8 / kMfmaThreads;   // 16-byte A chunks per thread per stage
+constexpr int kMI = BM / 64;  // 32-row accumulator blocks per wavefront (2 x 2 wavefronts)
+constexpr int kAChunks = BM * BK / 8 / kMfmaThreads;    // 16-byte A chunks per thread per stage
+constexpr int kBChunks = BK * BNB / 8 / kMfmaThreads;   // 16-byte B chunks per thread per stage
+constexpr int kRing = 3;      // LDS stage buffers
+#ifndef MOE_GEMM_SETS
+#define MOE_GEMM_SETS 3
+#endif
+constexpr int kSets = MOE_GEMM_SETS;
+#ifndef MOE_GEMM_INTERLEAVE
+#define MOE_GEMM_INTERLEAVE 1
+#endif   // register stages in flight (global-load prefetch distance)
 
 #define LDS_AS __attribute__((address_space(3)))
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -110,22 +120,44 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 // Workgroup barrier of the pipelined main loop. __syncthreads() carries a
 // workgroup fence, for which the compiler waits on every outstanding global
 // load, draining the prefetched stages held in registers. The loop needs no
-// fence: the LDS writes before the barrier and the LDS reads after it are
-// ordered by the barrier itself, the compiler waits on each register load
-// exactly where its value is written to LDS, and the asm memory clobber keeps
-// the compiler from moving LDS accesses across the barrier.
+// fence: this wave's LDS accesses are complete (lgkmcnt(0)) when it arrives,
+// the compiler waits on each register load exactly where its value is
+// written to LDS, and the asm memory clobber keeps the compiler from moving
+// LDS accesses across the barrier.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+// Same, but up to 12 of this wave's most recent LDS operations may still be
+// in flight (LDS operations of a wave complete in order). The main loop issues
+// the fragment reads of the next stage last; they read a buffer no wave
+// writes before the following barrier, so only what precedes them (this
+// step's LDS writes and the reads of the buffer about to be refilled) must
+// be complete here.
+__device__ __forceinline__ void lds_barrier_pending12() {
+    asm volatile("s_waitcnt lgkmcnt(12)\n\ts_barrier" ::: "memory");
+}
 
-// Stage layouts in LDS (no padding; XOR swizzles keep the fragment reads
-// conflict-free):
-//  A: [BM rows][BK], 16-byte chunk c of row r stored at chunk c ^ (r & 7);
-//  B: [BK k-rows][BNB columns], N-contiguous as in memory, 16-byte chunk c of
-//     k-row r stored at chunk c ^ 2*(r & 3). B fragments are read with the
-//     gfx950 LDS transpose read (ds_read_b64_tr_b16): in each 16-lane group,
-//     lane j points at k-row j/4, columns 4*(j%4)..+3 of a 4 x 16 block and
-//     receives the 4 k-values of column j.
+// Stage layouts in LDS (no padding; XOR swizzles of 16-byte chunks inside a
+// row keep the fragment reads and the staging writes free of bank conflicts,
+// both for LDS phases of 8 lanes x 16 bytes over 32 banks and of 16 lanes x
+// 16 bytes (32 lanes x 8 bytes) over 64 banks):
+//  A: [BM rows][BK], chunk c of row r stored at a_swz(c, r);
+//  B: [BK k-rows][BNB columns], N-contiguous as in memory, chunk c of k-row r
+//     stored at b_swz(c, r). B fragments are read with the gfx950 LDS
+//     transpose read (ds_read_b64_tr_b16): in each 16-lane group, lane j
+//     points at k-row j/4, columns 4*(j%4)..+3 of a 4 x 16 block and receives
+//     the 4 k-values of column j.
+__device__ __forceinline__ int a_swz(int c, int r) {
+    return c ^ (((r >> 1) ^ (r >> 3)) & 3);
+}
+__device__ __forceinline__ int b_swz(int c, int r) {
+    return c ^ (2 * (r & 3)) ^ (8 * ((c >> 1) & 1));
+}
+
+struct Frags {
+    bf16x8 a[kMI];
+    bf16x8 b[4];
+};
 
 template <bool GATE_UP, bool Y_BF16>
 __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
@@ -134,9 +166,12 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
     void* __restrict__ C)
 {
     constexpr int BNT = GATE_UP ? 128 : 256;   // output columns per tile
-    __shared__ __attribute__((aligned(1024))) uint16_t sA[2][BM * BK];
-    __shared__ __attribute__((aligned(1024))) uint16_t sB[2][BK * BNB];
+    // one LDS allocation: the A ring, then the B ring (96 KB); the tile
+    // scheduler and the epilogue reuse it as a whole
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[kRing * (BM * BK + BK * BNB)];
     __shared__ int scratch[kMfmaThreads / kWave + 1];
+    auto sA = [&](int buf) { return smem + buf * (BM * BK); };
+    auto sB = [&](int buf) { return smem + kRing * (BM * BK) + buf * (BK * BNB); };
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
@@ -146,8 +181,8 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
 
     Tile tile;
     {
-        int* s_pre = reinterpret_cast<int*>(&sB[0][0]);   // 4096 ints fit in 32 KB
-        int* s_off = reinterpret_cast<int*>(&sB[1][0]);   // 4097 ints fit in 32 KB
+        int* s_pre = reinterpret_cast<int*>(smem);         // 4096 ints
+        int* s_off = s_pre + kMaxE;                        // 4097 ints
         const bool ok = schedule_tile(offsets, N, E, BM, NC / BNT, s_off, s_pre, scratch, tile);
         if (!ok) return;  // uniform over the block
         __syncthreads();  // the scheduler's LDS is reused below
@@ -158,17 +193,17 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
     const int n0 = tile.n_tile * BNT;
 
     // ---- global sources and LDS destinations of this thread's 16-byte chunks
-    // A: chunk id q = tid + 256 i -> row tid/8 + 32 i, chunk tid%8 (8 lanes per
-    // 128-byte row); the swizzle term (row & 7) does not depend on i.
+    // A: chunk q = tid + 256 i -> row tid/4 + 64 i, chunk tid%4 (4 lanes per
+    // 64-byte row); the swizzle term of the row does not depend on i.
     const uint16_t* a_src[kAChunks];
 #pragma unroll
     for (int i = 0; i < kAChunks; ++i) {
-        const int r = (tid >> 3) + 32 * i;
-        a_src[i] = A + (size_t)min(m0 + r, seg_last) * K + (tid & 7) * 8;
+        const int r = (tid >> 2) + 64 * i;
+        a_src[i] = A + (size_t)min(m0 + r, seg_last) * K + (tid & 3) * 8;
     }
-    const int a_dst = (tid >> 3) * BK + (((tid & 7) ^ ((tid >> 3) & 7)) * 8);   // + 32 i rows
-    // B: chunk id q = tid + 256 i -> k-row tid/32 + 8 i, chunk tid%32 (32 lanes
-    // per 512-byte row); again the swizzle term (k-row & 3) does not depend on i.
+    const int a_dst = (tid >> 2) * BK + (a_swz(tid & 3, tid >> 2) * 8);        // + 64 i rows
+    // B: chunk q = tid + 256 i -> k-row tid/32 + 8 i, chunk tid%32 (32 lanes
+    // per 512-byte row); the swizzle term (k-row & 3) does not depend on i.
     const uint16_t* b_src;
     {
         const int c = tid & 31;
@@ -181,23 +216,23 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
             base = B0;
             col = n0 + c * 8;
         }
-        b_src = base + wbase + (size_t)(tid >> 5) * NC + col;                      // + 8 i k-rows
+        b_src = base + wbase + (size_t)(tid >> 5) * NC + col;                   // + 8 i k-rows
     }
-    const int b_dst = (tid >> 5) * BNB + (((tid & 31) ^ (2 * ((tid >> 5) & 3))) * 8);  // + 8 i k-rows
+    const int b_dst = (tid >> 5) * BNB + (b_swz(tid & 31, tid >> 5) * 8);      // + 8 i k-rows
 
     // ---- fragment addressing (element offsets inside a stage buffer)
-    // A (row (BM/2)wm + 32mi + lane%32, logical chunk 2ks + lane/32): the mi term
-    // is a constant 32 rows; the ks term goes through the XOR, one base per ks.
-    int a_lane[4];
+    // A (row (BM/2)wm + 32mi + lane%32, logical chunk 2ks + lane/32): the mi
+    // term is a constant 32 rows (the swizzle term does not change with it).
+    int a_lane[BK / 16];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < BK / 16; ++ks) {
         const int r = (BM / 2) * wm + (lane & 31);
-        a_lane[ks] = r * BK + ((((2 * ks + (lane >> 5)) ^ (r & 7))) * 8);
+        a_lane[ks] = r * BK + (a_swz(2 * ks + (lane >> 5), r) * 8);
     }
     // B: 16-lane group g = lane/16, j = lane%16 points at k-row
-    // 16ks + 8(g/2) + 4h + j/4 and column nbase[q] + 16(g%2) + 4(j%4); the
-    // swizzle term (k-row & 3) = j/4 is lane-constant, so ks and h are
-    // constant offsets and only q needs a per-lane base.
+    // 16ks + 8(g/2) + 4h + j/4 and column nb[q] + 16(g%2) + 4(j%4); the swizzle
+    // term (k-row & 3) = j/4 is lane-constant, so ks and h are constant
+    // offsets and only q needs a per-lane base.
     const int g = lane >> 4, j = lane & 15;
     int b_lane[4];
 #pragma unroll
@@ -206,7 +241,8 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
         if (GATE_UP) nb = (q < 2) ? (64 * wn + 32 * q) : (128 + 64 * wn + 32 * (q - 2));
         else nb = 128 * wn + 32 * q;
         const int n = nb + 16 * (g & 1) + 4 * (j & 3);
-        b_lane[q] = (8 * (g >> 1) + (j >> 2)) * BNB + (((n >> 3) ^ (2 * (j >> 2))) * 8) + (n & 7);
+        const int kr = 8 * (g >> 1) + (j >> 2);
+        b_lane[q] = kr * BNB + (b_swz(n >> 3, kr) * 8) + (n & 7);
     }
 
     f32x16 acc[kMI][4];
@@ -217,101 +253,165 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][q][r] = 0.0f;
 
-    // two register stages in flight; LDS double buffer
-    u32x4 ra0[kAChunks], rb0[8], ra1[kAChunks], rb1[8];
-    auto load_regs = [&](int kt, u32x4 (&ra)[kAChunks], u32x4 (&rb)[8]) {
+    // kSets register stages in flight
+    struct Stage {
+        u32x4 a[kAChunks];
+        u32x4 b[kBChunks];
+    };
+    Stage rs[kSets];
+    auto load_regs = [&](int kt, Stage& r) {
         const size_t ka = (size_t)kt * BK;
 #pragma unroll
-        for (int i = 0; i < kAChunks; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + ka);
+        for (int i = 0; i < kAChunks; ++i) r.a[i] = *reinterpret_cast<const u32x4*>(a_src[i] + ka);
         const uint16_t* bs = b_src + ka * NC;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bs + (size_t)(8 * i) * NC);
+        for (int i = 0; i < kBChunks; ++i) r.b[i] = *reinterpret_cast<const u32x4*>(bs + (size_t)(8 * i) * NC);
     };
-    auto store_lds = [&](int buf, const u32x4 (&ra)[kAChunks], const u32x4 (&rb)[8]) {
+    auto store_lds = [&](int buf, const Stage& r) {
 #pragma unroll
-        for (int i = 0; i < kAChunks; ++i) *reinterpret_cast<u32x4*>(&sA[buf][a_dst + 32 * i * BK]) = ra[i];
+        for (int i = 0; i < kAChunks; ++i) *reinterpret_cast<u32x4*>(sA(buf) + a_dst + 64 * i * BK) = r.a[i];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(&sB[buf][b_dst + 8 * i * BNB]) = rb[i];
+        for (int i = 0; i < kBChunks; ++i) *reinterpret_cast<u32x4*>(sB(buf) + b_dst + 8 * i * BNB) = r.b[i];
     };
-    auto compute = [&](int buf) {
-        const uint16_t* sa = sA[buf];
-        const uint16_t* sb = sB[buf];
+    auto read_frags = [&](int buf, int ks, Frags& f) {
+        const uint16_t* sa = sA(buf);
+        const uint16_t* sb = sB(buf);
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            bf16x8 af[kMI], bfr[4];
+        for (int mi = 0; mi < kMI; ++mi)
+            f.a[mi] = *reinterpret_cast<const bf16x8*>(sa + a_lane[ks] + 32 * mi * BK);
 #pragma unroll
-            for (int mi = 0; mi < kMI; ++mi)
-                af[mi] = *reinterpret_cast<const bf16x8*>(sa + a_lane[ks] + 32 * mi * BK);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint16_t* p = sb + b_lane[q] + 16 * ks * BNB;
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * BNB));
-                const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                bfr[q] = __builtin_bit_cast(bf16x8, v);
-            }
-#pragma unroll
-            for (int mi = 0; mi < kMI; ++mi)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    acc[mi][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[q], acc[mi][q], 0, 0, 0);
-            // keep each substep's fragment reads next to its MFMAs (bounds live registers)
-            __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < 4; ++q) {
+            const uint16_t* p = sb + b_lane[q] + 16 * ks * BNB;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * BNB));
+            const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            f.b[q] = __builtin_bit_cast(bf16x8, v);
         }
+    };
+    auto mfmas = [&](const Frags& f) {
+#pragma unroll
+        for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                acc[mi][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[q], acc[mi][q], 0, 0, 0);
     };
 
     const int KT = K / BK;
     // Loads and LDS writes past the last stage are issued anyway with the
-    // stage index clamped (a valid address, written into a buffer that is
-    // free and never read again): branch-free, so the compiler's wait
-    // analysis sees one straight path and waits only for the stage it stores.
+    // stage index clamped (a valid address, written into a buffer no later
+    // step reads): the loop body stays branch-free, so the compiler's wait
+    // analysis waits only for the stage it stores.
     auto clampk = [&](int k) { return min(k, KT - 1); };
-    load_regs(0, ra0, rb0);
-    load_regs(clampk(1), ra1, rb1);
-    store_lds(0, ra0, rb0);
-    load_regs(clampk(2), ra0, rb0);
-    // iteration kt: barrier (stage kt is in LDS buffer kt&1 and buffer
-    // (kt+1)&1 is free); write stage kt+1 from its registers; reload those
-    // registers with stage kt+3; compute stage kt. Loads get two iterations.
-    int kt = 0;
-    for (; kt + 2 <= KT; kt += 2) {
-        lds_barrier();
-        store_lds(1, ra1, rb1);
-        load_regs(clampk(kt + 3), ra1, rb1);
-        compute(0);
-        lds_barrier();
-        store_lds(0, ra0, rb0);
-        load_regs(clampk(kt + 4), ra0, rb0);
-        compute(1);
-    }
-    if (kt < KT) {  // odd number of stages: the last one sits in buffer 0
-        lds_barrier();
-        compute(0);
-    }
 
-    // epilogue: lane holds column (lane % 32) of each 32x32 accumulator and
-    // rows 8*(r/4) + 4*(lane/32) + r%4 for register r
+    // Pipeline: stage s lives in LDS buffer s % 3 and, before that, in
+    // register set s % 2 (the loop body is two steps, so the set is static
+    // and the buffer index is carried along). Step kt (after a barrier that publishes stage kt+1
+    // and retires every read of buffer (kt-1) % 3):
+    //   read the second k-substep fragments of stage kt,
+    //   MFMAs of stage kt, first k-substep (fragments read in step kt-1),
+    //   write stage kt+2 from its registers into buffer (kt+2) % 3 and
+    //   reload those registers with stage kt+4,
+    //   read the first k-substep fragments of stage kt+1,
+    //   MFMAs of stage kt, second k-substep.
+    // Global loads get two steps to land; LDS reads of a stage start one
+    // step before its MFMAs.
+    Frags f0, f1;
+#pragma unroll
+    for (int i = 0; i < kSets; ++i) load_regs(clampk(i), rs[i]);
+    store_lds(0, rs[0]);
+    load_regs(clampk(kSets), rs[0]);
+    store_lds(1, rs[1]);
+    load_regs(clampk(kSets + 1), rs[1]);
+    lds_barrier();
+    read_frags(0, 0, f0);
+
+    // step kt: stage kt+2 sits in register set (kt+2) % kSets; once written
+    // to LDS that set is reloaded with stage kt+2+kSets
+    auto step = [&](int kt, int buf, Stage& r) {
+        const int nxt = (buf == kRing - 1) ? 0 : buf + 1;
+        const int wr = (nxt == kRing - 1) ? 0 : nxt + 1;
+#if MOE_GEMM_INTERLEAVE
+        lds_barrier_pending12();
+#else
+        lds_barrier();
+#endif
+        read_frags(buf, 1, f1);
+        mfmas(f0);
+        store_lds(wr, r);
+        load_regs(clampk(kt + 2 + kSets), r);
+        read_frags(nxt, 0, f0);
+        mfmas(f1);
+#if MOE_GEMM_INTERLEAVE
+        // issue order: the 12 fragment reads of the second k-substep between
+        // the first 12 MFMAs, then the stage's 8 LDS writes and 8 global loads
+        // and the 12 fragment reads of the next stage spread over the other MFMAs
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#endif
+        return nxt;
+    };
+    int kt = 0, buf = 0;
+    for (; kt + kSets <= KT; kt += kSets) {
+#pragma unroll
+        for (int u = 0; u < kSets; ++u) buf = step(kt + u, buf, rs[(u + 2) % kSets]);
+    }
+#pragma unroll
+    for (int u = 0; u < kSets - 1; ++u)
+        if (kt + u < KT) buf = step(kt + u, buf, rs[(u + 2) % kSets]);
+
+    // Epilogue. A lane holds column lane%32 of each 32x32 accumulator block and
+    // rows 8*(r/4) + 4*(lane/32) + r%4 for register r.
     const int col_l = lane & 31;
     const int row_l = 4 * (lane >> 5);
     if (GATE_UP) {
-        uint16_t* H = static_cast<uint16_t*>(C);
+        // The bf16 h tile is staged row-major through the (now idle) LDS ring
+        // and leaves with 16-byte row-contiguous stores instead of one 2-byte
+        // store per element.
+        lds_barrier();   // every wave is done with the stage buffers
+        // h tile: 256 rows x 128 hidden columns, bf16, row stride 136 elements
+        constexpr int HS = 136;
+        uint16_t* sh = smem;   // 256 * 136 * 2 = 69632 bytes of the 96 KB ring
 #pragma unroll
         for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int col = n0 + 64 * wn + 32 * q + col_l;
+            for (int q = 0; q < 2; ++q)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + (BM / 2) * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
-                    if (row <= seg_last) {
-                        const float gv = acc[mi][q][r];
-                        const float v = acc[mi][q + 2][r];
-                        const float h = __fdividef(gv, 1.0f + __expf(-gv)) * v;
-                        H[(size_t)row * NC + col] = f32_to_bf16(h);
-                    }
+                    const int row = (BM / 2) * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
+                    const int col = 64 * wn + 32 * q + col_l;
+                    const float gv = acc[mi][q][r];
+                    const float v = acc[mi][q + 2][r];
+                    sh[row * HS + col] = f32_to_bf16(__fdividef(gv, 1.0f + __expf(-gv)) * v);
                 }
+        lds_barrier();
+        uint16_t* H = static_cast<uint16_t*>(C);
+        // 256 rows x 16 chunks of 8 columns; thread -> chunk tid%16, rows tid/16 + 16 i
+#pragma unroll
+        for (int i = 0; i < BM / 16; ++i) {
+            const int row = (tid >> 4) + 16 * i;
+            const int c8 = (tid & 15) * 8;
+            if (m0 + row <= seg_last) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(&sh[row * HS + c8]);
+                *reinterpret_cast<u32x4*>(&H[(size_t)(m0 + row) * NC + n0 + c8]) = v;
             }
+        }
     } else {
+        // y: 32 lanes cover 32 consecutive columns of a row per register, so
+        // direct stores already write whole 128-byte row segments
 #pragma unroll
         for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll

@@ -9,8 +9,8 @@
 // multiply-add per term from +0, then one fp32 bias add. That makes the work
 // T*E independent chains of d dependent FMAs on the vector ALUs (a matrix
 // core would sum in its own order). route_scores_kernel tiles the [T,E]
-// score matrix 64 tokens x 32 experts per block; each thread runs the chains
-// of 4 tokens x 2 experts side by side, reading x and W_r from LDS (staged
+// score matrix 32 tokens x 32 experts per block; each thread runs the chains
+// of 2 tokens x 2 experts side by side, reading x and W_r from LDS (staged
 // in 64-wide d-chunks, the next chunk prefetched into registers while the
 // current one is consumed). Zero padding of a chunk past d adds +-0 to a sum
 // that is never -0, so no bit changes. route_topk_kernel then gives each
@@ -23,10 +23,10 @@
 
 namespace moe {
 
-constexpr int kRT = 64;       // tokens per block
+constexpr int kRT = 32;       // tokens per block
 constexpr int kRE = 32;       // experts per block
 constexpr int kRD = 64;       // d-chunk
-constexpr int kRXS = kRD + 4; // x tile row stride (floats): 4 rows of a wave hit distinct banks
+constexpr int kRS = kRD + 4;  // LDS row stride (floats) of both staged tiles
 
 template <typename XT, bool VEC>
 __device__ __forceinline__ void load4(const XT* p, size_t i, bool in, float (&v)[4]) {
@@ -49,26 +49,31 @@ __device__ __forceinline__ void load4(const XT* p, size_t i, bool in, float (&v)
 }
 
 // VEC: d % 4 == 0, E % 4 == 0 and aligned pointers (4-element vector loads).
+// Block: 32 tokens x 32 experts; thread (tx, ty) owns tokens ty, ty+16 and
+// experts tx, tx+16. x is staged [token][i] and W_r transposed to
+// [expert][i], so both operands of four consecutive FMA steps are one
+// 16-byte LDS read; rows are padded to 68 floats, which puts the eight
+// lanes of each 16-byte read phase in distinct banks.
 template <typename XT, bool VEC>
 __global__ __launch_bounds__(256) void route_scores_kernel(
     const XT* __restrict__ x, const XT* __restrict__ w, const float* __restrict__ bias,
     int T, int d, int E, float* __restrict__ logits)
 {
-    __shared__ __attribute__((aligned(16))) float xs[kRT * kRXS];
-    __shared__ __attribute__((aligned(16))) float ws[kRD * kRE];
+    __shared__ __attribute__((aligned(16))) float xs[kRT * kRS];
+    __shared__ __attribute__((aligned(16))) float wt[kRE * kRS];
 
     const int tid = threadIdx.x;
-    const int tx = tid & 15;     // experts e0 + 2tx, e0 + 2tx + 1
-    const int ty = tid >> 4;     // tokens t0 + ty + 16b, b < 4
+    const int tx = tid & 15;
+    const int ty = tid >> 4;
     const int t0 = blockIdx.x * kRT;
     const int e0 = blockIdx.y * kRE;
 
-    // staging assignment: x 64 tokens x 64 values as 4-value groups,
-    // W_r 64 rows x 32 experts as 4-value groups
-    float xr[4][4], wr[2][4];
+    // staging: x 32 tokens x 64 values and W_r 64 rows x 32 experts, each as
+    // 512 groups of 4 consecutive values, two groups of each per thread
+    float xr[2][4], wr[2][4];
     auto load_chunk = [&](int i0) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 2; ++u) {
             const int gq = tid + 256 * u;
             const int tl = gq >> 4, i4 = (gq & 15) * 4;
             const int t = t0 + tl, i = i0 + i4;
@@ -96,24 +101,24 @@ __global__ __launch_bounds__(256) void route_scores_kernel(
     };
     auto store_chunk = [&]() {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 2; ++u) {
             const int gq = tid + 256 * u;
             const int tl = gq >> 4, i4 = (gq & 15) * 4;
             f32x4 v = {xr[u][0], xr[u][1], xr[u][2], xr[u][3]};
-            *reinterpret_cast<f32x4*>(&xs[tl * kRXS + i4]) = v;
+            *reinterpret_cast<f32x4*>(&xs[tl * kRS + i4]) = v;
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int gq = tid + 256 * u;
             const int il = gq >> 3, e4 = (gq & 7) * 4;
-            f32x4 v = {wr[u][0], wr[u][1], wr[u][2], wr[u][3]};
-            *reinterpret_cast<f32x4*>(&ws[il * kRE + e4]) = v;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) wt[(e4 + c) * kRS + il] = wr[u][c];
         }
     };
 
-    float acc[4][2];
+    float acc[2][2];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) { acc[b][0] = 0.0f; acc[b][1] = 0.0f; }
+    for (int b = 0; b < 2; ++b) { acc[b][0] = 0.0f; acc[b][1] = 0.0f; }
 
     load_chunk(0);
     for (int i0 = 0; i0 < d; i0 += kRD) {
@@ -122,30 +127,32 @@ __global__ __launch_bounds__(256) void route_scores_kernel(
         __syncthreads();
         if (i0 + kRD < d) load_chunk(i0 + kRD);
         const int dc = min(kRD, ((d - i0) + 3) & ~3);
+#pragma unroll 4
         for (int i = 0; i < dc; i += 4) {
-            f32x4 xv[4];
+            f32x4 xv[2], wv[2];
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
-                xv[b] = *reinterpret_cast<const f32x4*>(&xs[(ty + 16 * b) * kRXS + i]);
+            for (int b = 0; b < 2; ++b)
+                xv[b] = *reinterpret_cast<const f32x4*>(&xs[(ty + 16 * b) * kRS + i]);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const float2 wv = *reinterpret_cast<const float2*>(&ws[(i + c) * kRE + 2 * tx]);
+            for (int a = 0; a < 2; ++a)
+                wv[a] = *reinterpret_cast<const f32x4*>(&wt[(tx + 16 * a) * kRS + i]);
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    acc[b][0] = __builtin_fmaf(xv[b][c], wv.x, acc[b][0]);
-                    acc[b][1] = __builtin_fmaf(xv[b][c], wv.y, acc[b][1]);
-                }
-            }
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int a = 0; a < 2; ++a)
+                        acc[b][a] = __builtin_fmaf(xv[b][c], wv[a][c], acc[b][a]);
         }
     }
 
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
-        const int e = e0 + 2 * tx + a;
+        const int e = e0 + tx + 16 * a;
         if (e >= E) continue;
         const float bv = bias ? bias[e] : 0.0f;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < 2; ++b) {
             const int t = t0 + ty + 16 * b;
             if (t >= T) continue;
             float l = acc[b][a];
