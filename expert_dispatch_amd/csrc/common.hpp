@@ -16,15 +16,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// bf16 <-> fp32. Widening is exact; narrowing rounds to nearest, ties to even.
+// bf16 <-> fp32. Widening is exact; narrowing rounds to nearest, ties to even
+// (gfx950 converts in one instruction, v_cvt_pk_bf16_f32; NaN stays NaN).
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(static_cast<unsigned>(h) << 16);
 }
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    unsigned u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN stays NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+// Two values at once: low half = a, high half = b.
+__device__ __forceinline__ unsigned f32x2_to_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2_t));
 }
 
 template <typename T> struct Elem;
@@ -104,6 +109,17 @@ __device__ inline int block_exclusive_scan_lds(int* s, int n, int* scratch) {
     const int total = scratch[nt / kWave];
     __syncthreads();
     return total;
+}
+
+// Workgroup barrier for pipelined loops that keep global loads in flight
+// across it. __syncthreads() carries a workgroup fence, for which the
+// compiler waits on every outstanding global load. When the barrier only has
+// to order LDS accesses, this is enough: each wave's LDS operations are
+// complete (lgkmcnt(0)) when it arrives, register values loaded from global
+// memory are waited for exactly where they are used, and the asm memory
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }

@@ -44,7 +44,7 @@ constexpr int kGroupM = 4;   // row tiles per scheduling group inside an expert
 // ----------------------------------------------------------- tile scheduler
 
 struct Tile {
-    int e, m0, seg_end, n_tile;
+    int e, m0, seg_end, n_tile, bm;
 };
 
 // All threads of the block must call it. s_off needs E+1 ints, s_pre E ints.
@@ -87,7 +87,98 @@ __device__ bool schedule_tile(const int32_t* __restrict__ offsets, int N, int E,
     tile.n_tile = within / gsz;
     tile.m0 = rows_lo + (grp * kGroupM + within % gsz) * bm;
     tile.seg_end = rows_hi;
+    tile.bm = bm;
     return true;
+}
+
+// Tile list of the matrix-core kernel, two tile heights in one launch. An
+// expert with n rows gets n / 256 tiles of 256 rows; a remainder above 128
+// rows one more 256-row tile, a remainder of at most 128 rows one 128-row tile
+// (a 256-row tile would be more than half padding there). Every row tile
+// spans all n_tiles column tiles. Tile indices [0, big) are the 256-row tiles
+// (expert by expert; inside an expert groups of kGroupM row tiles sweep all
+// column tiles, row tile fastest), [big, big + small) the 128-row tiles.
+struct TileList {
+    const int* off;     // [E+1] clamped offsets
+    const int* big;     // [E] exclusive prefix of 256-row tiles x n_tiles
+    const int* small;   // [E] exclusive prefix of 128-row tiles x n_tiles
+    int E, n_tiles, total_big, total_small;
+};
+
+// All threads of the block must call it. s_off needs E+1 ints, s_big and
+// s_small E ints each.
+__device__ TileList build_tile_list(const int32_t* __restrict__ offsets, int N, int E,
+                                    int n_tiles, int* s_off, int* s_big, int* s_small,
+                                    int* scratch)
+{
+    const int tid = threadIdx.x;
+    for (int e = tid; e <= E; e += blockDim.x) s_off[e] = min(max(offsets[e], 0), N);
+    __syncthreads();
+    for (int e = tid; e < E; e += blockDim.x) {
+        const int n = max(0, s_off[e + 1] - s_off[e]);
+        const int rem = n & 255;
+        s_big[e] = ((n >> 8) + (rem > 128 ? 1 : 0)) * n_tiles;
+        s_small[e] = (rem > 0 && rem <= 128) ? n_tiles : 0;
+    }
+    __syncthreads();
+    TileList L;
+    L.off = s_off;
+    L.big = s_big;
+    L.small = s_small;
+    L.E = E;
+    L.n_tiles = n_tiles;
+    L.total_big = __builtin_amdgcn_readfirstlane(block_exclusive_scan_lds(s_big, E, scratch));
+    L.total_small = __builtin_amdgcn_readfirstlane(block_exclusive_scan_lds(s_small, E, scratch));
+    return L;
+}
+
+// Largest e with pre[e] <= t (pre is an exclusive prefix over E entries, so
+// experts owning no tile are skipped).
+__device__ __forceinline__ int find_owner(const int* pre, int E, int t) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Tile t of the list, 0 <= t < total_big + total_small.
+__device__ Tile decode_tile(const TileList& L, int t) {
+    Tile tile;
+    if (t < L.total_big) {
+        const int e = find_owner(L.big, L.E, t);
+        const int rows_lo = L.off[e];
+        const int rows_hi = max(rows_lo, L.off[e + 1]);
+        const int n = rows_hi - rows_lo;
+        const int mt = (n >> 8) + ((n & 255) > 128 ? 1 : 0);
+        const int local = t - L.big[e];
+        const int grp = local / (kGroupM * L.n_tiles);
+        const int within = local - grp * (kGroupM * L.n_tiles);
+        const int gsz = min(kGroupM, mt - grp * kGroupM);
+        tile.e = e;
+        tile.n_tile = within / gsz;
+        tile.m0 = rows_lo + (grp * kGroupM + within % gsz) * 256;
+        tile.seg_end = rows_hi;
+        tile.bm = 256;
+    } else {
+        t -= L.total_big;
+        const int e = find_owner(L.small, L.E, t);
+        const int rows_lo = L.off[e];
+        const int rows_hi = max(rows_lo, L.off[e + 1]);
+        tile.e = e;
+        tile.n_tile = t - L.small[e];
+        tile.m0 = rows_lo + ((rows_hi - rows_lo) >> 8) * 256;
+        tile.seg_end = rows_hi;
+        tile.bm = 128;
+    }
+    // uniform over the block: keep the fields in scalar registers
+    tile.e = __builtin_amdgcn_readfirstlane(tile.e);
+    tile.m0 = __builtin_amdgcn_readfirstlane(tile.m0);
+    tile.seg_end = __builtin_amdgcn_readfirstlane(tile.seg_end);
+    tile.n_tile = __builtin_amdgcn_readfirstlane(tile.n_tile);
+    tile.bm = __builtin_amdgcn_readfirstlane(tile.bm);
+    return tile;
 }
 
 static long long max_row_tiles(int N, int E, int bm) {
@@ -97,51 +188,45 @@ static long long max_row_tiles(int N, int E, int bm) {
 
 // ------------------------------------------------------ matrix-core kernel
 
-constexpr int BM = 256;       // rows per tile
+constexpr int BM = 256;       // rows of a full tile (a remainder tile has 128)
 constexpr int BK = 32;        // k per pipeline stage
 constexpr int BNB = 256;      // B-panel columns per tile
 constexpr int kMfmaThreads = 256;
-constexpr int kMI = BM / 64;  // 32-row accumulator blocks per wavefront (2 x 2 wavefronts)
-constexpr int kAChunks = BM * BK / 8 / kMfmaThreads;    // 16-byte A chunks per thread per stage
 constexpr int kBChunks = BK * BNB / 8 / kMfmaThreads;   // 16-byte B chunks per thread per stage
 constexpr int kRing = 3;      // LDS stage buffers
-#ifndef MOE_GEMM_SETS
-#define MOE_GEMM_SETS 3
-#endif
-constexpr int kSets = MOE_GEMM_SETS;
-#ifndef MOE_GEMM_INTERLEAVE
-#define MOE_GEMM_INTERLEAVE 1
-#endif   // register stages in flight (global-load prefetch distance)
+constexpr int kSets = 3;      // register stages in flight (global-load prefetch distance)
 
 #define LDS_AS __attribute__((address_space(3)))
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-// Workgroup barrier of the pipelined main loop. __syncthreads() carries a
-// workgroup fence, for which the compiler waits on every outstanding global
-// load, draining the prefetched stages held in registers. The loop needs no
-// fence: this wave's LDS accesses are complete (lgkmcnt(0)) when it arrives,
-// the compiler waits on each register load exactly where its value is
-// written to LDS, and the asm memory clobber keeps the compiler from moving
-// LDS accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-// Same, but up to 12 of this wave's most recent LDS operations may still be
+// Barrier that lets up to P of this wave's most recent LDS operations still be
 // in flight (LDS operations of a wave complete in order). The main loop issues
 // the fragment reads of the next stage last; they read a buffer no wave
 // writes before the following barrier, so only what precedes them (this
 // step's LDS writes and the reads of the buffer about to be refilled) must
 // be complete here.
-__device__ __forceinline__ void lds_barrier_pending12() {
-    asm volatile("s_waitcnt lgkmcnt(12)\n\ts_barrier" ::: "memory");
+template <int P>
+__device__ __forceinline__ void lds_barrier_pending() {
+    static_assert(P == 10 || P == 12, "pending count");
+    if constexpr (P == 12)
+        asm volatile("s_waitcnt lgkmcnt(12)\n\ts_barrier" ::: "memory");
+    else
+        asm volatile("s_waitcnt lgkmcnt(10)\n\ts_barrier" ::: "memory");
+}
+
+// silu(z) = z * sigmoid(z) with the hardware exp2 and reciprocal (about 1 ulp
+// each; h is rounded to bf16 right after, 2^-9 relative). For z -> -inf,
+// 1 + exp(-z) overflows to +inf and the reciprocal gives 0, so silu -> -0.
+__device__ __forceinline__ float silu_fast(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
 }
 
 // Stage layouts in LDS (no padding; XOR swizzles of 16-byte chunks inside a
 // row keep the fragment reads and the staging writes free of bank conflicts,
 // both for LDS phases of 8 lanes x 16 bytes over 32 banks and of 16 lanes x
 // 16 bytes (32 lanes x 8 bytes) over 64 banks):
-//  A: [BM rows][BK], chunk c of row r stored at a_swz(c, r);
+//  A: [rows][BK], chunk c of row r stored at a_swz(c, r);
 //  B: [BK k-rows][BNB columns], N-contiguous as in memory, chunk c of k-row r
 //     stored at b_swz(c, r). B fragments are read with the gfx950 LDS
 //     transpose read (ds_read_b64_tr_b16): in each 16-lane group, lane j
@@ -154,79 +239,98 @@ __device__ __forceinline__ int b_swz(int c, int r) {
     return c ^ (2 * (r & 3)) ^ (8 * ((c >> 1) & 1));
 }
 
-struct Frags {
-    bf16x8 a[kMI];
-    bf16x8 b[4];
+// LDS of the kernel: the stage ring (96 KB, sized for 256-row tiles; the
+// epilogue reuses it) and the tile list (built once per block, kept).
+constexpr int kSmemElems = kRing * (BM * BK + BK * BNB);
+
+// Global-load stage in registers: 16-byte A and B chunks of one thread (a
+// 128-row tile uses the first half of a[]).
+struct Stage {
+    u32x4 a[BM * BK / 8 / kMfmaThreads];
+    u32x4 b[kBChunks];
 };
 
-template <bool GATE_UP, bool Y_BF16>
-__global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
-    const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int N, int K, int NC,
-    int E, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
-    void* __restrict__ C)
-{
-    constexpr int BNT = GATE_UP ? 128 : 256;   // output columns per tile
-    // one LDS allocation: the A ring, then the B ring (96 KB); the tile
-    // scheduler and the epilogue reuse it as a whole
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[kRing * (BM * BK + BK * BNB)];
-    __shared__ int scratch[kMfmaThreads / kWave + 1];
-    auto sA = [&](int buf) { return smem + buf * (BM * BK); };
-    auto sB = [&](int buf) { return smem + kRing * (BM * BK) + buf * (BK * BNB); };
+// Per-thread global sources of one tile. A: chunk q = tid + 256 i -> row
+// tid/4 + 64 i, chunk tid%4 (4 lanes per 64-byte row); rows past the expert's
+// segment re-read its last row (never stored). B: chunk q = tid + 256 i ->
+// k-row tid/32 + 8 i, chunk tid%32 (32 lanes per 512-byte row; gate_up: 16
+// chunks of W_gate, then 16 of W_val).
+template <bool GATE_UP, int TM>
+struct TileSrc {
+    static constexpr int kAChunks = TM * BK / 8 / kMfmaThreads;
+    const uint16_t* a[kAChunks];
+    const uint16_t* b;
 
-    const int tid = threadIdx.x;
-    const int lane = lane_id();
+    __device__ __forceinline__ TileSrc(const uint16_t* A, int K, int NC, const uint16_t* B0,
+                                       const uint16_t* B1, const Tile& tile) {
+        const int tid = threadIdx.x;
+        const int seg_last = tile.seg_end - 1;
+#pragma unroll
+        for (int i = 0; i < kAChunks; ++i) {
+            const int r = (tid >> 2) + 64 * i;
+            a[i] = A + (size_t)min(tile.m0 + r, seg_last) * K + (tid & 3) * 8;
+        }
+        const size_t wbase = (size_t)tile.e * (size_t)K * (size_t)NC;
+        const int c = tid & 31;
+        if (GATE_UP) {
+            b = ((c < 16) ? B0 : B1) + wbase + (size_t)(tid >> 5) * NC + tile.n_tile * 128 + (c & 15) * 8;
+        } else {
+            b = B0 + wbase + (size_t)(tid >> 5) * NC + tile.n_tile * 256 + c * 8;
+        }
+    }
+    __device__ __forceinline__ void load(int kt, int NC, Stage& r) const {
+        const size_t ka = (size_t)kt * BK;
+#pragma unroll
+        for (int i = 0; i < kAChunks; ++i) r.a[i] = *reinterpret_cast<const u32x4*>(a[i] + ka);
+        const uint16_t* bs = b + ka * NC;
+#pragma unroll
+        for (int i = 0; i < kBChunks; ++i) r.b[i] = *reinterpret_cast<const u32x4*>(bs + (size_t)(8 * i) * NC);
+    }
+};
+
+// One output tile of TM rows (256 or 128) x 256 B-columns. The 4 wavefronts
+// form a 2 x 2 grid, each computing TM/2 x 128 as a (TM/64) x 4 grid of
+// v_mfma_f32_32x32x16_bf16 accumulators held in AGPRs.
+template <bool GATE_UP, bool Y_BF16, int TM>
+__device__ __forceinline__ void ffn_mfma_tile(
+    const uint16_t* __restrict__ A, int K, int NC, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, void* __restrict__ C, const Tile& tile, uint16_t* smem)
+{
+    constexpr int kMI = TM / 64;                               // 32-row blocks per wavefront
+    constexpr int kAChunks = TM * BK / 8 / kMfmaThreads;       // 16-byte A chunks per thread per stage
+    constexpr int kReads = kMI + 8;                            // LDS reads per fragment set
+    constexpr int BNT = GATE_UP ? 128 : 256;                   // output columns per tile
+    auto sA = [&](int buf) { return smem + buf * (TM * BK); };
+    auto sB = [&](int buf) { return smem + kRing * (TM * BK) + buf * (BK * BNB); };
+
+    // The thread index passes through an empty asm statement, so the compiler
+    // recomputes the addresses derived from it for every tile instead of
+    // hoisting them out of the block's tile loop (where they would stay live
+    // next to the full register budget of the main loop).
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int wm = wave >> 1;
     const int wn = wave & 1;
 
-    Tile tile;
-    {
-        int* s_pre = reinterpret_cast<int*>(smem);         // 4096 ints
-        int* s_off = s_pre + kMaxE;                        // 4097 ints
-        const bool ok = schedule_tile(offsets, N, E, BM, NC / BNT, s_off, s_pre, scratch, tile);
-        if (!ok) return;  // uniform over the block
-        __syncthreads();  // the scheduler's LDS is reused below
-    }
     const int m0 = tile.m0;
     const int seg_last = tile.seg_end - 1;
-    const size_t wbase = (size_t)tile.e * (size_t)K * (size_t)NC;
     const int n0 = tile.n_tile * BNT;
+    const TileSrc<GATE_UP, TM> src(A, K, NC, B0, B1, tile);
 
-    // ---- global sources and LDS destinations of this thread's 16-byte chunks
-    // A: chunk q = tid + 256 i -> row tid/4 + 64 i, chunk tid%4 (4 lanes per
-    // 64-byte row); the swizzle term of the row does not depend on i.
-    const uint16_t* a_src[kAChunks];
-#pragma unroll
-    for (int i = 0; i < kAChunks; ++i) {
-        const int r = (tid >> 2) + 64 * i;
-        a_src[i] = A + (size_t)min(m0 + r, seg_last) * K + (tid & 3) * 8;
-    }
-    const int a_dst = (tid >> 2) * BK + (a_swz(tid & 3, tid >> 2) * 8);        // + 64 i rows
-    // B: chunk q = tid + 256 i -> k-row tid/32 + 8 i, chunk tid%32 (32 lanes
-    // per 512-byte row); the swizzle term (k-row & 3) does not depend on i.
-    const uint16_t* b_src;
-    {
-        const int c = tid & 31;
-        const uint16_t* base;
-        int col;
-        if (GATE_UP) {
-            base = (c < 16) ? B0 : B1;
-            col = n0 + (c & 15) * 8;
-        } else {
-            base = B0;
-            col = n0 + c * 8;
-        }
-        b_src = base + wbase + (size_t)(tid >> 5) * NC + col;                   // + 8 i k-rows
-    }
-    const int b_dst = (tid >> 5) * BNB + (b_swz(tid & 31, tid >> 5) * 8);      // + 8 i k-rows
+    // LDS destinations of this thread's chunks: A + 64 i rows, B + 8 i k-rows
+    // (the swizzle terms do not depend on i)
+    const int a_dst = (tid >> 2) * BK + (a_swz(tid & 3, tid >> 2) * 8);
+    const int b_dst = (tid >> 5) * BNB + (b_swz(tid & 31, tid >> 5) * 8);
 
     // ---- fragment addressing (element offsets inside a stage buffer)
-    // A (row (BM/2)wm + 32mi + lane%32, logical chunk 2ks + lane/32): the mi
+    // A (row (TM/2)wm + 32mi + lane%32, logical chunk 2ks + lane/32): the mi
     // term is a constant 32 rows (the swizzle term does not change with it).
     int a_lane[BK / 16];
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-        const int r = (BM / 2) * wm + (lane & 31);
+        const int r = (TM / 2) * wm + (lane & 31);
         a_lane[ks] = r * BK + (a_swz(2 * ks + (lane >> 5), r) * 8);
     }
     // B: 16-lane group g = lane/16, j = lane%16 points at k-row
@@ -253,19 +357,9 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][q][r] = 0.0f;
 
-    // kSets register stages in flight
-    struct Stage {
-        u32x4 a[kAChunks];
-        u32x4 b[kBChunks];
-    };
-    Stage rs[kSets];
-    auto load_regs = [&](int kt, Stage& r) {
-        const size_t ka = (size_t)kt * BK;
-#pragma unroll
-        for (int i = 0; i < kAChunks; ++i) r.a[i] = *reinterpret_cast<const u32x4*>(a_src[i] + ka);
-        const uint16_t* bs = b_src + ka * NC;
-#pragma unroll
-        for (int i = 0; i < kBChunks; ++i) r.b[i] = *reinterpret_cast<const u32x4*>(bs + (size_t)(8 * i) * NC);
+    struct Frags {
+        bf16x8 a[kMI];
+        bf16x8 b[4];
     };
     auto store_lds = [&](int buf, const Stage& r) {
 #pragma unroll
@@ -304,64 +398,86 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
     auto clampk = [&](int k) { return min(k, KT - 1); };
 
     // Pipeline: stage s lives in LDS buffer s % 3 and, before that, in
-    // register set s % 2 (the loop body is two steps, so the set is static
-    // and the buffer index is carried along). Step kt (after a barrier that publishes stage kt+1
-    // and retires every read of buffer (kt-1) % 3):
+    // register set s % 3 (the loop body is three steps, so the set is static
+    // and the buffer index is carried along). Step kt (after a barrier that
+    // publishes stage kt+1 and retires every read of buffer (kt-1) % 3):
     //   read the second k-substep fragments of stage kt,
     //   MFMAs of stage kt, first k-substep (fragments read in step kt-1),
     //   write stage kt+2 from its registers into buffer (kt+2) % 3 and
-    //   reload those registers with stage kt+4,
+    //   reload those registers with stage kt+5,
     //   read the first k-substep fragments of stage kt+1,
     //   MFMAs of stage kt, second k-substep.
-    // Global loads get two steps to land; LDS reads of a stage start one
+    // Global loads get three steps to land; LDS reads of a stage start one
     // step before its MFMAs.
-    Frags f0, f1;
+    Stage rs[kSets];
 #pragma unroll
-    for (int i = 0; i < kSets; ++i) load_regs(clampk(i), rs[i]);
+    for (int i = 0; i < kSets; ++i) src.load(clampk(i), NC, rs[i]);
+    Frags f0, f1;
+    lds_barrier();   // the block's previous tile is done with the ring
     store_lds(0, rs[0]);
-    load_regs(clampk(kSets), rs[0]);
+    src.load(clampk(kSets), NC, rs[0]);
     store_lds(1, rs[1]);
-    load_regs(clampk(kSets + 1), rs[1]);
+    src.load(clampk(kSets + 1), NC, rs[1]);
     lds_barrier();
     read_frags(0, 0, f0);
 
-    // step kt: stage kt+2 sits in register set (kt+2) % kSets; once written
-    // to LDS that set is reloaded with stage kt+2+kSets
     auto step = [&](int kt, int buf, Stage& r) {
         const int nxt = (buf == kRing - 1) ? 0 : buf + 1;
         const int wr = (nxt == kRing - 1) ? 0 : nxt + 1;
-#if MOE_GEMM_INTERLEAVE
-        lds_barrier_pending12();
-#else
-        lds_barrier();
-#endif
+        lds_barrier_pending<kReads>();
         read_frags(buf, 1, f1);
         mfmas(f0);
         store_lds(wr, r);
-        load_regs(clampk(kt + 2 + kSets), r);
+        src.load(clampk(kt + 2 + kSets), NC, r);
         read_frags(nxt, 0, f0);
         mfmas(f1);
-#if MOE_GEMM_INTERLEAVE
-        // issue order: the 12 fragment reads of the second k-substep between
-        // the first 12 MFMAs, then the stage's 8 LDS writes and 8 global loads
-        // and the 12 fragment reads of the next stage spread over the other MFMAs
+        // issue order, so that every MFMA has LDS or global-memory work beside it
+        if constexpr (TM == 256) {
+            // the 12 fragment reads of the second k-substep between the first
+            // 12 MFMAs, the stage's 8 LDS writes and 8 global loads over the
+            // next 8, the 12 fragment reads of the next stage over the last 12
 #pragma unroll
-        for (int i = 0; i < 12; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
+            for (int i = 0; i < 12; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
 #pragma unroll
-        for (int i = 0; i < 12; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int i = 0; i < 12; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        } else {
+            // 16 MFMAs: 10 reads over the first 5, 6 LDS writes and 6 global
+            // loads over the next 3, the 10 reads of the next stage over the
+            // last 8
+#pragma unroll
+            for (int i = 0; i < 5; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 6; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
         }
-#endif
         return nxt;
     };
     int kt = 0, buf = 0;
@@ -377,34 +493,40 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
     // rows 8*(r/4) + 4*(lane/32) + r%4 for register r.
     const int col_l = lane & 31;
     const int row_l = 4 * (lane >> 5);
+    const bool full = m0 + TM - 1 <= seg_last;
     if (GATE_UP) {
         // The bf16 h tile is staged row-major through the (now idle) LDS ring
         // and leaves with 16-byte row-contiguous stores instead of one 2-byte
         // store per element.
         lds_barrier();   // every wave is done with the stage buffers
-        // h tile: 256 rows x 128 hidden columns, bf16, row stride 136 elements
+        // h tile: TM rows x 128 hidden columns, bf16, row stride 136 elements
+        // (256 rows: 69632 bytes of the 96 KB ring)
         constexpr int HS = 136;
-        uint16_t* sh = smem;   // 256 * 136 * 2 = 69632 bytes of the 96 KB ring
+        uint16_t* sh = smem;
 #pragma unroll
         for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
             for (int q = 0; q < 2; ++q)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = (BM / 2) * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
+                for (int r = 0; r < 16; r += 2) {
+                    // rows r and r+1 of a lane are adjacent: one packed conversion
+                    const int row = (TM / 2) * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
                     const int col = 64 * wn + 32 * q + col_l;
-                    const float gv = acc[mi][q][r];
-                    const float v = acc[mi][q + 2][r];
-                    sh[row * HS + col] = f32_to_bf16(__fdividef(gv, 1.0f + __expf(-gv)) * v);
+                    const float g0 = acc[mi][q][r], g1 = acc[mi][q][r + 1];
+                    const float h0 = silu_fast(g0) * acc[mi][q + 2][r];
+                    const float h1 = silu_fast(g1) * acc[mi][q + 2][r + 1];
+                    const unsigned pk = f32x2_to_bf16x2(h0, h1);
+                    sh[row * HS + col] = (uint16_t)pk;
+                    sh[(row + 1) * HS + col] = (uint16_t)(pk >> 16);
                 }
         lds_barrier();
         uint16_t* H = static_cast<uint16_t*>(C);
-        // 256 rows x 16 chunks of 8 columns; thread -> chunk tid%16, rows tid/16 + 16 i
+        // TM rows x 16 chunks of 8 columns; thread -> chunk tid%16, rows tid/16 + 16 i
 #pragma unroll
-        for (int i = 0; i < BM / 16; ++i) {
+        for (int i = 0; i < TM / 16; ++i) {
             const int row = (tid >> 4) + 16 * i;
             const int c8 = (tid & 15) * 8;
-            if (m0 + row <= seg_last) {
+            if (full || m0 + row <= seg_last) {
                 const u32x4 v = *reinterpret_cast<const u32x4*>(&sh[row * HS + c8]);
                 *reinterpret_cast<u32x4*>(&H[(size_t)(m0 + row) * NC + n0 + c8]) = v;
             }
@@ -419,8 +541,8 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
                 const int col = n0 + 128 * wn + 32 * q + col_l;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + (BM / 2) * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
-                    if (row <= seg_last) {
+                    const int row = m0 + (TM / 2) * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
+                    if (full || row <= seg_last) {
                         if (Y_BF16)
                             static_cast<uint16_t*>(C)[(size_t)row * NC + col] = f32_to_bf16(acc[mi][q][r]);
                         else
@@ -428,6 +550,35 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
                     }
                 }
             }
+    }
+}
+
+// Persistent: the grid is a multiple of 8 no larger than the number of
+// compute units; block b works through tiles t_i = i*G + (b%8)*(G/8) + b/8
+// (G = grid size), so in every round each XCD (block b runs on XCD b % 8)
+// takes a contiguous run of the tile list and the tiles of one expert meet
+// on one XCD and share its L2.
+template <bool GATE_UP, bool Y_BF16>
+__global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int N, int K, int NC,
+    int E, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
+    void* __restrict__ C)
+{
+    constexpr int BNT = GATE_UP ? 128 : 256;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[kSmemElems];
+    __shared__ int s_sched[3 * kMaxE + 1];
+    __shared__ int scratch[kMfmaThreads / kWave + 1];
+    const TileList L = build_tile_list(offsets, N, E, NC / BNT, s_sched, s_sched + kMaxE + 1,
+                                       s_sched + 2 * kMaxE + 1, scratch);
+    const int total = L.total_big + L.total_small;
+    const int G = gridDim.x;
+    const int base = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+    for (int t = base; t < total; t += G) {
+        const Tile tile = decode_tile(L, t);
+        if (tile.bm == 256)
+            ffn_mfma_tile<GATE_UP, Y_BF16, 256>(A, K, NC, B0, B1, C, tile, smem);
+        else
+            ffn_mfma_tile<GATE_UP, Y_BF16, 128>(A, K, NC, B0, B1, C, tile, smem);
     }
 }
 
@@ -526,6 +677,25 @@ bool ffn_down_uses_mfma(moe_dtype dt, int f, int d, const void* h, const void* w
     return dt == MOE_BF16 && f % BK == 0 && d % 256 == 0 && aligned16(h) && aligned16(wo);
 }
 
+// Persistent grid: one block per compute unit (the kernel's LDS and registers
+// allow no second one), rounded down to a multiple of 8, and no more blocks
+// than there can be tiles (sum_e ceil(n_e / 128) row tiles at most).
+static unsigned mfma_grid(int N, int E, int n_tiles) {
+    static int cus[64] = {0};
+    int dev = 0;
+    hipGetDevice(&dev);
+    int& c = cus[dev & 63];
+    if (c == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        c = v;
+    }
+    const long long cap = std::max(8, c / 8 * 8);
+    const long long tiles = max_row_tiles(N, E, 128) * n_tiles;
+    return (unsigned)std::max(8LL, std::min(cap, (tiles + 7) / 8 * 8));
+}
+
 static unsigned grid_for(long long tiles) {
     long long g = (tiles + 7) / 8 * 8;
     return (unsigned)std::max(8LL, g);
@@ -536,8 +706,7 @@ hipError_t launch_gate_up(const void* x, moe_dtype dt, int N, int d, int f, int 
                           hipStream_t st)
 {
     if (ffn_gate_up_uses_mfma(dt, d, f, x, wg, wv, h)) {
-        const long long tiles = max_row_tiles(N, E, BM) * (f / 128);
-        ffn_mfma_kernel<true, false><<<grid_for(tiles), kMfmaThreads, 0, st>>>(
+        ffn_mfma_kernel<true, false><<<mfma_grid(N, E, f / 128), kMfmaThreads, 0, st>>>(
             (const uint16_t*)x, offsets, N, d, f, E, (const uint16_t*)wg, (const uint16_t*)wv, h);
     } else {
         const long long tiles = max_row_tiles(N, E, GBM) * ((f + GBN - 1) / GBN);
@@ -558,12 +727,12 @@ hipError_t launch_down(const void* h, moe_dtype dt, int N, int f, int d, int E,
                        hipStream_t st)
 {
     if (ffn_down_uses_mfma(dt, f, d, h, wo) && aligned16(y)) {
-        const long long tiles = max_row_tiles(N, E, BM) * (d / 256);
+        const unsigned grid = mfma_grid(N, E, d / 256);
         if (y_dt == MOE_BF16)
-            ffn_mfma_kernel<false, true><<<grid_for(tiles), kMfmaThreads, 0, st>>>(
+            ffn_mfma_kernel<false, true><<<grid, kMfmaThreads, 0, st>>>(
                 (const uint16_t*)h, offsets, N, f, d, E, (const uint16_t*)wo, nullptr, y);
         else
-            ffn_mfma_kernel<false, false><<<grid_for(tiles), kMfmaThreads, 0, st>>>(
+            ffn_mfma_kernel<false, false><<<grid, kMfmaThreads, 0, st>>>(
                 (const uint16_t*)h, offsets, N, f, d, E, (const uint16_t*)wo, nullptr, y);
     } else {
         const long long tiles = max_row_tiles(N, E, GBM) * ((d + GBN - 1) / GBN);

@@ -9,151 +9,225 @@
 // multiply-add per term from +0, then one fp32 bias add. That makes the work
 // T*E independent chains of d dependent FMAs on the vector ALUs (a matrix
 // core would sum in its own order). route_scores_kernel tiles the [T,E]
-// score matrix 32 tokens x 32 experts per block; each thread runs the chains
-// of 2 tokens x 2 experts side by side, reading x and W_r from LDS (staged
-// in 64-wide d-chunks, the next chunk prefetched into registers while the
-// current one is consumed). Zero padding of a chunk past d adds +-0 to a sum
-// that is never -0, so no bit changes. route_topk_kernel then gives each
+// score matrix 64 tokens x 32 experts per block; each thread runs the chains
+// of 2 tokens x 4 experts side by side, reading x and W_r from LDS (staged
+// in 128-wide d-chunks, double-buffered, loaded into registers ahead). Zero
+// padding of a chunk past d adds +-0 to a sum that is never -0, so no bit
+// changes. route_topk_kernel then gives each
 // token one wavefront: its E <= 1024 scores spread over the 64 lanes, k
 // rounds of a wave-wide arg-max under (score descending, index ascending),
 // then the softmax weights.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 
 namespace moe {
 
-constexpr int kRT = 32;       // tokens per block
+constexpr int kRT = 64;       // tokens per block
 constexpr int kRE = 32;       // experts per block
-constexpr int kRD = 64;       // d-chunk
-constexpr int kRS = kRD + 4;  // LDS row stride (floats) of both staged tiles
-
-template <typename XT, bool VEC>
-__device__ __forceinline__ void load4(const XT* p, size_t i, bool in, float (&v)[4]) {
-    if (!in) { v[0] = v[1] = v[2] = v[3] = 0.0f; return; }
-    if constexpr (VEC) {
-        if constexpr (sizeof(XT) == 2) {
-            const u32x2 u = *reinterpret_cast<const u32x2*>(p + i);
-            v[0] = __uint_as_float(u[0] << 16);
-            v[1] = __uint_as_float(u[0] & 0xffff0000u);
-            v[2] = __uint_as_float(u[1] << 16);
-            v[3] = __uint_as_float(u[1] & 0xffff0000u);
-        } else {
-            const f32x4 u = *reinterpret_cast<const f32x4*>(p + i);
-            v[0] = u[0]; v[1] = u[1]; v[2] = u[2]; v[3] = u[3];
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = Elem<XT>::load(p, i + q);
-    }
-}
+constexpr int kRD = 128;      // d-chunk
+constexpr int kRS = kRD + 4;  // x tile row stride (floats)
+constexpr int kXU = kRT * kRD / 1024;  // x groups of 4 per thread per chunk
+constexpr int kWU = kRD * kRE / 1024;  // W_r groups of 4 per thread per chunk
+constexpr int kRG = 8;        // steps per register group
+constexpr int kRBuf = kRT * kRS + kRD * kRE;  // floats per LDS buffer
 
 // VEC: d % 4 == 0, E % 4 == 0 and aligned pointers (4-element vector loads).
-// Block: 32 tokens x 32 experts; thread (tx, ty) owns tokens ty, ty+16 and
-// experts tx, tx+16. x is staged [token][i] and W_r transposed to
-// [expert][i], so both operands of four consecutive FMA steps are one
-// 16-byte LDS read; rows are padded to 68 floats, which puts the eight
-// lanes of each 16-byte read phase in distinct banks.
+// Block: 64 tokens x 32 experts; thread (eg, tg) = (tid % 8, tid / 8) owns
+// experts 4eg..4eg+3 and tokens tg, tg+32: eight FMA chains. x is staged
+// [token][i] (rows padded to 132 floats: the 8 token rows a wavefront reads
+// at once fall in distinct banks) and W_r as it is laid out, [i][expert], so
+// one 16-byte LDS read gives four steps of a token or one step of four
+// experts, and the staging writes are plain 16-byte stores.
+//
+// Pipeline: chunk c + 3 is loaded into registers while chunk c + 1 is written
+// to the second LDS buffer and chunk c is consumed from the first (one
+// barrier per chunk). Inside a chunk the LDS reads of the next 8 steps are
+// issued before the 64 FMAs of the current 8 (scheduling barriers keep that
+// order), so one wavefront per SIMD keeps its ALU fed.
 template <typename XT, bool VEC>
 __global__ __launch_bounds__(256) void route_scores_kernel(
     const XT* __restrict__ x, const XT* __restrict__ w, const float* __restrict__ bias,
     int T, int d, int E, float* __restrict__ logits)
 {
-    __shared__ __attribute__((aligned(16))) float xs[kRT * kRS];
-    __shared__ __attribute__((aligned(16))) float wt[kRE * kRS];
+    __shared__ __attribute__((aligned(16))) float smem[2 * kRBuf];
 
     const int tid = threadIdx.x;
-    const int tx = tid & 15;
-    const int ty = tid >> 4;
+    const int eg = tid & 7;
+    const int tg = tid >> 3;
     const int t0 = blockIdx.x * kRT;
     const int e0 = blockIdx.y * kRE;
+    const int nchunks = (d + kRD - 1) / kRD;
 
-    // staging: x 32 tokens x 64 values and W_r 64 rows x 32 experts, each as
-    // 512 groups of 4 consecutive values, two groups of each per thread
-    float xr[2][4], wr[2][4];
-    auto load_chunk = [&](int i0) {
+    // staging: x 64 tokens x 128 values (8 groups of 4 per thread) and W_r
+    // 128 rows x 32 experts (4 groups of 4 per thread). The vector path loads raw
+    // bits from clamped (always valid) addresses with no branch and converts /
+    // zeroes out-of-range groups when writing to LDS.
+    using Raw = typename std::conditional<sizeof(XT) == 2, u32x2, f32x4>::type;
+    struct Chunk {
+        Raw x[kXU], w[kWU];
+        bool xin[kXU], win[kWU];
+    };
+    Chunk ch[2];
+    float xr[kXU][4], wr[kWU][4];
+    auto load_chunk = [&](int c, Chunk& cr) {
+        const int i0 = c * kRD;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < kXU; ++u) {
             const int gq = tid + 256 * u;
-            const int tl = gq >> 4, i4 = (gq & 15) * 4;
+            const int tl = gq / (kRD / 4), i4 = (gq % (kRD / 4)) * 4;
             const int t = t0 + tl, i = i0 + i4;
             if (VEC) {
-                load4<XT, true>(x, (size_t)t * d + i, t < T && i < d, xr[u]);
+                cr.xin[u] = t < T && i < d;
+                cr.x[u] = *reinterpret_cast<const Raw*>(x + (size_t)min(t, T - 1) * d + min(i, d - 4));
             } else {
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    xr[u][c] = (t < T && i + c < d) ? Elem<XT>::load(x, (size_t)t * d + i + c) : 0.0f;
+                for (int q = 0; q < 4; ++q)
+                    xr[u][q] = (t < T && i + q < d) ? Elem<XT>::load(x, (size_t)t * d + i + q) : 0.0f;
             }
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < kWU; ++u) {
             const int gq = tid + 256 * u;
             const int il = gq >> 3, e4 = (gq & 7) * 4;
             const int i = i0 + il, e = e0 + e4;
             if (VEC) {
-                load4<XT, true>(w, (size_t)i * E + e, i < d && e < E, wr[u]);
+                cr.win[u] = i < d && e < E;
+                cr.w[u] = *reinterpret_cast<const Raw*>(w + (size_t)min(i, d - 1) * E + min(e, E - 4));
             } else {
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    wr[u][c] = (i < d && e + c < E) ? Elem<XT>::load(w, (size_t)i * E + e + c) : 0.0f;
+                for (int q = 0; q < 4; ++q)
+                    wr[u][q] = (i < d && e + q < E) ? Elem<XT>::load(w, (size_t)i * E + e + q) : 0.0f;
             }
         }
     };
-    auto store_chunk = [&]() {
+    auto unpack = [&](const Raw& r, bool in, float (&v)[4]) {
+        if constexpr (sizeof(XT) == 2) {
+            v[0] = __uint_as_float(r[0] << 16);
+            v[1] = __uint_as_float(r[0] & 0xffff0000u);
+            v[2] = __uint_as_float(r[1] << 16);
+            v[3] = __uint_as_float(r[1] & 0xffff0000u);
+        } else {
+            v[0] = r[0]; v[1] = r[1]; v[2] = r[2]; v[3] = r[3];
+        }
+        if (!in) v[0] = v[1] = v[2] = v[3] = 0.0f;
+    };
+    auto store_chunk = [&](int c, const Chunk& cr) {
+        if (!VEC) load_chunk(c, ch[0]);
+        float* xs = smem + (c & 1) * kRBuf;
+        float* ws = xs + kRT * kRS;
+        if (VEC) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+            for (int u = 0; u < kXU; ++u) unpack(cr.x[u], cr.xin[u], xr[u]);
+#pragma unroll
+            for (int u = 0; u < kWU; ++u) unpack(cr.w[u], cr.win[u], wr[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kXU; ++u) {
             const int gq = tid + 256 * u;
-            const int tl = gq >> 4, i4 = (gq & 15) * 4;
+            const int tl = gq / (kRD / 4), i4 = (gq % (kRD / 4)) * 4;
             f32x4 v = {xr[u][0], xr[u][1], xr[u][2], xr[u][3]};
             *reinterpret_cast<f32x4*>(&xs[tl * kRS + i4]) = v;
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < kWU; ++u) {
             const int gq = tid + 256 * u;
             const int il = gq >> 3, e4 = (gq & 7) * 4;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) wt[(e4 + c) * kRS + il] = wr[u][c];
+            f32x4 v = {wr[u][0], wr[u][1], wr[u][2], wr[u][3]};
+            *reinterpret_cast<f32x4*>(&ws[il * kRE + e4]) = v;
         }
     };
 
-    float acc[2][2];
+    float acc[2][4];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) { acc[b][0] = 0.0f; acc[b][1] = 0.0f; }
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) acc[b][a] = 0.0f;
 
-    load_chunk(0);
-    for (int i0 = 0; i0 < d; i0 += kRD) {
-        __syncthreads();          // previous chunk fully consumed
-        store_chunk();
-        __syncthreads();
-        if (i0 + kRD < d) load_chunk(i0 + kRD);
-        const int dc = min(kRD, ((d - i0) + 3) & ~3);
-#pragma unroll 4
-        for (int i = 0; i < dc; i += 4) {
-            f32x4 xv[2], wv[2];
+    // one group: x of 2 tokens x 8 steps, W_r of 8 steps x 4 experts
+    struct Group {
+        f32x4 x[2][2];
+        f32x4 w[kRG];
+    };
+    auto read_group = [&](const float* xs, const float* ws, int i, Group& g) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                g.x[b][h] = *reinterpret_cast<const f32x4*>(&xs[(tg + 32 * b) * kRS + i + 4 * h]);
+#pragma unroll
+        for (int q = 0; q < kRG; ++q)
+            g.w[q] = *reinterpret_cast<const f32x4*>(&ws[(i + q) * kRE + 4 * eg]);
+    };
+    auto fma_group = [&](const Group& g) {
+#pragma unroll
+        for (int q = 0; q < kRG; ++q)
 #pragma unroll
             for (int b = 0; b < 2; ++b)
-                xv[b] = *reinterpret_cast<const f32x4*>(&xs[(ty + 16 * b) * kRS + i]);
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
-                wv[a] = *reinterpret_cast<const f32x4*>(&wt[(tx + 16 * a) * kRS + i]);
+                for (int a = 0; a < 4; ++a)
+                    acc[b][a] = __builtin_fmaf(g.x[b][q >> 2][q & 3], g.w[q][a], acc[b][a]);
+    };
+    auto compute_chunk = [&](int c) {
+        const float* xs = smem + (c & 1) * kRBuf;
+        const float* ws = xs + kRT * kRS;
+        Group g[2];
+        if ((c + 1) * kRD <= d) {
+            // full chunk: 8 groups, reads one group ahead
+            read_group(xs, ws, 0, g[0]);
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-#pragma unroll
-                    for (int a = 0; a < 2; ++a)
-                        acc[b][a] = __builtin_fmaf(xv[b][c], wv[a][c], acc[b][a]);
+            for (int j = 0; j < kRD / kRG; ++j) {
+                if (j + 1 < kRD / kRG) read_group(xs, ws, (j + 1) * kRG, g[(j + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                fma_group(g[j & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            // last, partial chunk: groups up to d rounded up to 8 (the tile
+            // holds zeros past d)
+            const int n = (d - c * kRD + kRG - 1) / kRG;
+            for (int j = 0; j < n; ++j) {
+                read_group(xs, ws, j * kRG, g[0]);
+                fma_group(g[0]);
+            }
         }
+    };
+
+    if (VEC) {
+        load_chunk(0, ch[0]);
+        load_chunk(1, ch[1]);
     }
+    store_chunk(0, ch[0]);
+    if (VEC) load_chunk(2, ch[0]);
+    lds_barrier();
+    // chunk c: store c + 1 (register set (c + 1) % 2), load c + 3 into the
+    // same set, consume c, barrier. Unrolled by two so the sets are fixed and
+    // with no exit in between (an exit there would merge into the loop head
+    // and make the compiler wait for every load in flight). Loads and stores
+    // are unconditional: past the last chunk the loads read clamped, valid
+    // addresses and the zeros stored go to a buffer nobody reads.
+    int c = 0;
+    for (; c + 1 < nchunks; c += 2) {
+        store_chunk(c + 1, ch[1]);
+        if (VEC) load_chunk(c + 3, ch[1]);
+        compute_chunk(c);
+        lds_barrier();
+        store_chunk(c + 2, ch[0]);
+        if (VEC) load_chunk(c + 4, ch[0]);
+        compute_chunk(c + 1);
+        lds_barrier();
+    }
+    if (c < nchunks) compute_chunk(c);  // odd count: the last chunk is already stored
 
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-        const int e = e0 + tx + 16 * a;
+    for (int a = 0; a < 4; ++a) {
+        const int e = e0 + 4 * eg + a;
         if (e >= E) continue;
         const float bv = bias ? bias[e] : 0.0f;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-            const int t = t0 + ty + 16 * b;
+            const int t = t0 + tg + 32 * b;
             if (t >= T) continue;
             float l = acc[b][a];
             if (bias) l = l + bv;
