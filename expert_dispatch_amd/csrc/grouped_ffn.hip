@@ -555,7 +555,7 @@ __device__ __forceinline__ void ffn_mfma_tile(
 
 // Persistent: the grid is a multiple of 8 no larger than the number of
 // compute units; block b works through tiles t_i = i*G + (b%8)*(G/8) + b/8
-// (G = grid size), so in every round each XCD (block b runs on XCD b % 8)
+// (G = grid size), so in every pass i each XCD (block b runs on XCD b % 8)
 // takes a contiguous run of the tile list and the tiles of one expert meet
 // on one XCD and share its L2.
 template <bool GATE_UP, bool Y_BF16>
