@@ -45,6 +45,7 @@ constexpr int kGroupM = 4;   // row tiles per scheduling group inside an expert
 
 struct Tile {
     int e, m0, seg_end, n_tile, bm;
+    int stream;   // matrix-core kernel: the tile's weight panel is read by no other tile
 };
 
 // All threads of the block must call it. s_off needs E+1 ints, s_pre E ints.
@@ -161,6 +162,7 @@ __device__ Tile decode_tile(const TileList& L, int t) {
         tile.m0 = rows_lo + (grp * kGroupM + within % gsz) * 256;
         tile.seg_end = rows_hi;
         tile.bm = 256;
+        tile.stream = mt < 2;
     } else {
         t -= L.total_big;
         const int e = find_owner(L.small, L.E, t);
@@ -171,6 +173,9 @@ __device__ Tile decode_tile(const TileList& L, int t) {
         tile.m0 = rows_lo + ((rows_hi - rows_lo) >> 8) * 256;
         tile.seg_end = rows_hi;
         tile.bm = 128;
+        // remainder tiles run after all 256-row tiles: whatever the expert's
+        // other tiles read is long gone from L2
+        tile.stream = 1;
     }
     // uniform over the block: keep the fields in scalar registers
     tile.e = __builtin_amdgcn_readfirstlane(tile.e);
@@ -178,6 +183,7 @@ __device__ Tile decode_tile(const TileList& L, int t) {
     tile.seg_end = __builtin_amdgcn_readfirstlane(tile.seg_end);
     tile.n_tile = __builtin_amdgcn_readfirstlane(tile.n_tile);
     tile.bm = __builtin_amdgcn_readfirstlane(tile.bm);
+    tile.stream = __builtin_amdgcn_readfirstlane(tile.stream);
     return tile;
 }
 
@@ -255,7 +261,7 @@ struct Stage {
 // segment re-read its last row (never stored). B: chunk q = tid + 256 i ->
 // k-row tid/32 + 8 i, chunk tid%32 (32 lanes per 512-byte row; gate_up: 16
 // chunks of W_gate, then 16 of W_val).
-template <bool GATE_UP, int TM>
+template <bool GATE_UP, int TM, bool STREAM>
 struct TileSrc {
     static constexpr int kAChunks = TM * BK / 8 / kMfmaThreads;
     const uint16_t* a[kAChunks];
@@ -282,16 +288,23 @@ struct TileSrc {
         const size_t ka = (size_t)kt * BK;
 #pragma unroll
         for (int i = 0; i < kAChunks; ++i) r.a[i] = *reinterpret_cast<const u32x4*>(a[i] + ka);
+        // STREAM: no other tile reads this weight panel; a non-temporal load
+        // keeps it from pushing the A rows (read again by the next stage) out
+        // of the caches. Otherwise the panel is left in L2 for the expert's
+        // other row tiles.
         const uint16_t* bs = b + ka * NC;
 #pragma unroll
-        for (int i = 0; i < kBChunks; ++i) r.b[i] = *reinterpret_cast<const u32x4*>(bs + (size_t)(8 * i) * NC);
+        for (int i = 0; i < kBChunks; ++i) {
+            const u32x4* p = reinterpret_cast<const u32x4*>(bs + (size_t)(8 * i) * NC);
+            r.b[i] = STREAM ? __builtin_nontemporal_load(p) : *p;
+        }
     }
 };
 
 // One output tile of TM rows (256 or 128) x 256 B-columns. The 4 wavefronts
 // form a 2 x 2 grid, each computing TM/2 x 128 as a (TM/64) x 4 grid of
 // v_mfma_f32_32x32x16_bf16 accumulators held in AGPRs.
-template <bool GATE_UP, bool Y_BF16, int TM>
+template <bool GATE_UP, bool Y_BF16, int TM, bool STREAM>
 __device__ __forceinline__ void ffn_mfma_tile(
     const uint16_t* __restrict__ A, int K, int NC, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, void* __restrict__ C, const Tile& tile, uint16_t* smem)
@@ -317,7 +330,7 @@ __device__ __forceinline__ void ffn_mfma_tile(
     const int m0 = tile.m0;
     const int seg_last = tile.seg_end - 1;
     const int n0 = tile.n_tile * BNT;
-    const TileSrc<GATE_UP, TM> src(A, K, NC, B0, B1, tile);
+    const TileSrc<GATE_UP, TM, STREAM> src(A, K, NC, B0, B1, tile);
 
     // LDS destinations of this thread's chunks: A + 64 i rows, B + 8 i k-rows
     // (the swizzle terms do not depend on i)
@@ -575,10 +588,12 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
     const int base = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
     for (int t = base; t < total; t += G) {
         const Tile tile = decode_tile(L, t);
-        if (tile.bm == 256)
-            ffn_mfma_tile<GATE_UP, Y_BF16, 256>(A, K, NC, B0, B1, C, tile, smem);
+        if (tile.bm == 128)
+            ffn_mfma_tile<GATE_UP, Y_BF16, 128, true>(A, K, NC, B0, B1, C, tile, smem);
+        else if (tile.stream)
+            ffn_mfma_tile<GATE_UP, Y_BF16, 256, true>(A, K, NC, B0, B1, C, tile, smem);
         else
-            ffn_mfma_tile<GATE_UP, Y_BF16, 128>(A, K, NC, B0, B1, C, tile, smem);
+            ffn_mfma_tile<GATE_UP, Y_BF16, 256, false>(A, K, NC, B0, B1, C, tile, smem);
     }
 }
 
