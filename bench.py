@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="qwen3_30b_a3b")
+    ap.add_argument("--y-dtype", choices=("f32", "bf16"), default="bf16",
+                    help="storage type of the expert outputs y_perm between the down GEMM "
+                         "and the combine (bf16 inputs only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU work of the oracle baseline sample")
@@ -73,12 +76,13 @@ def to_dev(a, torch):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def stage_work(cfg, counts, es):
+def stage_work(cfg, counts, es, ys=4):
     """Algorithmic flops and bytes of one launch of each stage: what the method
     must compute or move (s = element size, TK = T*k rows, n_act = experts with
     rows). Router 2*T*d*E flop; packing (T + TK)*d*s bytes + indices; gate_up
     4*TK*d*f flop over TK*d*s + n_act*2*d*f*s + TK*f*s bytes; down 2*TK*f*d flop
-    over TK*f*s + n_act*f*d*s + TK*d*4 bytes; combine TK*d*4 + T*d*4 bytes."""
+    over TK*f*s + n_act*f*d*s + TK*d*ys bytes; combine TK*d*ys + T*d*4 bytes
+    (ys = element size of the stored expert outputs)."""
     T, k, d, f, E = cfg.T, cfg.k, cfg.d, cfg.f, cfg.E
     rows = cfg.rows
     active = int((counts > 0).sum())
@@ -93,7 +97,7 @@ def stage_work(cfg, counts, es):
     w["gate_up"] = dict(flops=4.0 * rows * d * f,
                         bytes=rows * d * es + active * 2 * d * f * es + rows * f * es)
     w["down"] = dict(flops=2.0 * rows * f * d,
-                     bytes=rows * f * es + active * f * d * es + rows * d * 4)
+                     bytes=rows * f * es + active * f * d * es + rows * d * ys)
     if cfg.shared:
         fs = cfg.shared * f
         w["shared_gate_up"] = dict(flops=4.0 * T * d * fs,
@@ -101,7 +105,7 @@ def stage_work(cfg, counts, es):
         w["shared_down"] = dict(flops=2.0 * T * fs * d, bytes=T * fs * es + fs * d * es + T * d * 4)
     units = T if cfg.kind == "routed" else rows
     w["combine"] = dict(flops=2.0 * rows * d,
-                        bytes=rows * d * 4 + units * d * 4 + rows * 8
+                        bytes=rows * d * ys + units * d * 4 + rows * 8
                         + (units * d * 4 if cfg.shared else 0), bound="hbm")
     mfma_peak = PEAK_MFMA_BF16_TFS if es == 2 else PEAK_MFMA_F32_TFS
     for name, v in w.items():
@@ -211,7 +215,8 @@ def main():
         x_perm=torch.empty((rows, d), dtype=xdt, device=cuda),
     )
     h = torch.empty((rows, f), dtype=xdt, device=cuda)
-    y = torch.empty((rows, d), dtype=torch.float32, device=cuda)
+    ys = 2 if (args.y_dtype == "bf16" and es == 2) else 4
+    y = torch.empty((rows, d), dtype=torch.bfloat16 if ys == 2 else torch.float32, device=cuda)
     units = cfg.units
     out = torch.empty((units, d), dtype=torch.float32, device=cuda)
     shared = None
@@ -288,7 +293,7 @@ def main():
                                         for s in range(args.steps)]) * 1e3)
 
     counts = bufs["counts"].cpu().numpy()
-    work = stage_work(cfg, counts, es)
+    work = stage_work(cfg, counts, es, ys)
     stage_rep = {}
     for name in stages:
         r = roofline_entry(work[name], stage_us[name], es)
@@ -317,7 +322,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if es == 2 else "f32",
         "data": "synthetic (seeded Gaussian inputs and weights of the stated shapes)",
-        "config": {"workload": cfg.name, "description": cfg.description, "T": cfg.T,
+        "config": {"workload": cfg.name, "description": cfg.description,
+                   "y_perm_dtype": "bf16" if ys == 2 else "f32", "T": cfg.T,
                    "k": cfg.k, "N": cfg.N, "d": d, "f": f, "E": E, "shared": cfg.shared,
                    "rows": rows, "load_max_over_mean": round(float(counts.max() / max(counts.mean(), 1e-9)), 3),
                    "empty_experts": int((counts == 0).sum())},

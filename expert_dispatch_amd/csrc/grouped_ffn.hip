@@ -544,9 +544,33 @@ __device__ __forceinline__ void ffn_mfma_tile(
                 *reinterpret_cast<u32x4*>(&H[(size_t)(m0 + row) * NC + n0 + c8]) = v;
             }
         }
+    } else if (Y_BF16) {
+        // y in bf16: registers r, r+1 of a lane are rows i, i+1 of one column and
+        // neighbouring lanes hold neighbouring columns, so a swap between lane
+        // pairs (DPP quad_perm [1,0,3,2]) gives every even lane columns c, c+1 of
+        // row i and every odd lane columns c-1, c of row i+1: one 4-byte store
+        // per two values
+        const bool odd = lane & 1;
+        uint16_t* Y = static_cast<uint16_t*>(C);
+#pragma unroll
+        for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = n0 + 128 * wn + 32 * q + col_l - (odd ? 1 : 0);
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const int row = m0 + (TM / 2) * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3) + (odd ? 1 : 0);
+                    const float x = acc[mi][q][r], y = acc[mi][q][r + 1];
+                    const float xs = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+                    const float ys = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0xB1, 0xF, 0xF, false));
+                    const unsigned pk = f32x2_to_bf16x2(odd ? ys : x, odd ? y : xs);
+                    if (full || row <= seg_last)
+                        *reinterpret_cast<unsigned*>(&Y[(size_t)row * NC + col]) = pk;
+                }
+            }
     } else {
-        // y: 32 lanes cover 32 consecutive columns of a row per register, so
-        // direct stores already write whole 128-byte row segments
+        // y in fp32: 32 lanes cover 32 consecutive columns of a row per
+        // register, so direct stores already write whole 128-byte row segments
 #pragma unroll
         for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
@@ -555,12 +579,8 @@ __device__ __forceinline__ void ffn_mfma_tile(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = m0 + (TM / 2) * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
-                    if (full || row <= seg_last) {
-                        if (Y_BF16)
-                            static_cast<uint16_t*>(C)[(size_t)row * NC + col] = f32_to_bf16(acc[mi][q][r]);
-                        else
-                            static_cast<float*>(C)[(size_t)row * NC + col] = acc[mi][q][r];
-                    }
+                    if (full || row <= seg_last)
+                        static_cast<float*>(C)[(size_t)row * NC + col] = acc[mi][q][r];
                 }
             }
     }

@@ -217,18 +217,21 @@ def combine(y_perm, dest, gates, k: int, *, y_shared=None, out_dtype=torch.float
 
 
 def moe_layer(x, w_router, bias, k: int, w_gate, w_val, w_out, *, shared=None,
-              out_dtype=torch.float32, stream=None):
+              y_dtype=torch.float32, out_dtype=torch.float32, stream=None):
     """The whole token-routed layer: route -> permute -> grouped FFN -> combine.
     ``shared`` = (w_gate, w_val, w_out) of the always-on shared experts
-    concatenated along f (one SwiGLU of width q*f equals the sum of q)."""
+    concatenated along f (one SwiGLU of width q*f equals the sum of q).
+    ``y_dtype`` is the storage type of the expert outputs between the down
+    GEMM and the combine."""
     E = w_gate.shape[0]
     logits, idx, gates = route(x, w_router, bias, k, stream=stream)
     p = permute(idx, x, E, stream=stream)
-    y = grouped_ffn(p["x_perm"], p["offsets"], w_gate, w_val, w_out, stream=stream)
+    y = grouped_ffn(p["x_perm"], p["offsets"], w_gate, w_val, w_out, y_dtype=y_dtype,
+                    stream=stream)
     y_sh = None
     if shared is not None:
         T = x.shape[0]
         off = torch.tensor([0, T], dtype=torch.int32, device=x.device)
-        y_sh = grouped_ffn(x, off, *shared, stream=stream)
+        y_sh = grouped_ffn(x, off, *shared, y_dtype=y_dtype, stream=stream)
     out = combine(y, p["dest"], gates, k, y_shared=y_sh, out_dtype=out_dtype, stream=stream)
     return dict(logits=logits, idx=idx, gates=gates, y=y, y_shared=y_sh, out=out, **p)

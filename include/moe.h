@@ -132,10 +132,12 @@ moe_status moe_permute_recv(const int32_t* recv_counts, int S, int E_loc, int N,
  *   h = silu(x_perm[j] . W_gate[e]) * (x_perm[j] . W_val[e]),  silu(z) = z*sigmoid(z)
  *   y[j] = h . W_out[e]
  *   x_perm [N,d] dtype dt, offsets [E+1] int32 (device, read on the device),
- *   y      [N,d] dtype y_dt out (MOE_F32 recommended)
+ *   y      [N,d] dtype y_dt out
  * Products accumulate in fp32. With dt = MOE_BF16 the hidden activation h is
  * stored as bf16 (round to nearest even) between the two products; with
- * MOE_F32 it stays fp32. Experts with no rows cost nothing.
+ * MOE_F32 it stays fp32. y is rounded once to y_dt: MOE_BF16 halves the bytes
+ * the down product writes and the combine reads, MOE_F32 keeps the fp32 sums.
+ * Experts with no rows cost nothing.
  * Limits: E <= 4096, N < 2^31. Any d, f >= 1 work; bf16 with d % 256 == 0 and
  * f % 128 == 0 (and 16-byte aligned pointers) takes the matrix-core path.
  */

@@ -50,20 +50,20 @@ def _device(inp):
     return dev
 
 
-def _gpu_routed(dev, k):
+def _gpu_routed(dev, k, y_dtype=torch.float32):
     r = ops.moe_layer(dev["x"], dev["w_router"], dev.get("bias"), k, dev["w_gate"], dev["w_val"],
-                      dev["w_out"], shared=dev.get("shared"))
+                      dev["w_out"], shared=dev.get("shared"), y_dtype=y_dtype)
     torch.cuda.synchronize()
     return r
 
 
-def _check_routed(name, full):
+def _check_routed(name, full, y_dtype=torch.float32):
     cfg = W.get(name)
     say(f"[parity] {name}: generate")
     inp = _inputs(name)
     dev = _device(inp)
-    say(f"[parity] {name}: gpu layer")
-    g = _gpu_routed(dev, cfg.k)
+    say(f"[parity] {name}: gpu layer (y {y_dtype})")
+    g = _gpu_routed(dev, cfg.k, y_dtype)
     rng = np.random.default_rng(0)
     T, k = cfg.T, cfg.k
     tokens = None
@@ -107,6 +107,12 @@ def test_routed_layer_small(name):
 @pytest.mark.parametrize("name", FULL_ROUTED)
 def test_routed_layer_full(name):
     _check_routed(name, full=True)
+
+
+@pytest.mark.parametrize("name", ["qwen3_30b_a3b", "dsv2_lite"])
+def test_routed_layer_full_bf16_expert_outputs(name):
+    """The bench's launch configuration: expert outputs stored as bf16."""
+    _check_routed(name, full=True, y_dtype=torch.bfloat16)
 
 
 def _check_recv(name, full, zero_col=None):

@@ -54,6 +54,9 @@ def err_bf16(got, ref) -> float:
 
 
 def check_float(got, ref, dtype: str, what: str):
+    """Parity gate of one float output; bf16 bit patterns (uint16) are widened
+    to their values first."""
+    got = widen(got) if isinstance(got, np.ndarray) and got.dtype == np.uint16 else got
     if dtype == "f32":
         e = err_f32(got, ref)
         assert e <= TOL_F32, f"{what}: max rel err {e:.3e} > {TOL_F32}"
