@@ -9,7 +9,9 @@
 // page (Design) builds those indices on the device with no readback.
 //
 // Token-routed packing, three launches and no host synchronisation:
-//  1. perm_hist:  per-chunk expert histogram in LDS (4096 assignments/block);
+//  1. perm_hist:  per-chunk expert histogram in LDS (1024 or 4096 assignments
+//                 per block: small batches get more blocks, large ones fewer
+//                 chunk histograms for every ranking block to sum);
 //  2. perm_rank:  every block re-derives the global offsets and its own base
 //                 per expert from the chunk histograms, then ranks its
 //                 assignments stably with wave ballots (a bit-sliced match of
@@ -28,17 +30,21 @@
 namespace moe {
 
 constexpr int kPermThreads = 256;
-constexpr int kPermChunk = 4096;                       // assignments per block
-constexpr int kPermIters = kPermChunk / kPermThreads;  // 16 per lane
 constexpr int kPermMaxE = 1024;
+constexpr int kPermSmallTK = 65536;   // up to this many assignments: 1024-chunks
 
+// assignments per ranking block
+static int perm_chunk(long long TK) { return TK <= kPermSmallTK ? 1024 : 4096; }
+
+template <int CHUNK>
 __global__ __launch_bounds__(kPermThreads) void perm_hist_kernel(
     const int32_t* __restrict__ idx, int TK, int E, int32_t* __restrict__ bc)
 {
+    constexpr int kPermIters = CHUNK / kPermThreads;
     __shared__ int h[kPermMaxE];
     for (int e = threadIdx.x; e < E; e += kPermThreads) h[e] = 0;
     __syncthreads();
-    const int base = blockIdx.x * kPermChunk;
+    const int base = blockIdx.x * CHUNK;
 #pragma unroll 4
     for (int q = 0; q < kPermIters; ++q) {
         const int a = base + threadIdx.x + q * kPermThreads;
@@ -51,12 +57,14 @@ __global__ __launch_bounds__(kPermThreads) void perm_hist_kernel(
     for (int e = threadIdx.x; e < E; e += kPermThreads) bc[(size_t)blockIdx.x * E + e] = h[e];
 }
 
+template <int CHUNK>
 __global__ __launch_bounds__(kPermThreads) void perm_rank_kernel(
     const int32_t* __restrict__ idx, int TK, int E, int nbits,
     const int32_t* __restrict__ bc, int nb,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm_src, int32_t* __restrict__ dest)
 {
+    constexpr int kPermIters = CHUNK / kPermThreads;   // per lane
     __shared__ int s_off[kPermMaxE];       // global offsets
     __shared__ int s_base[kPermMaxE];      // offsets + assignments of earlier blocks
     __shared__ int s_wcnt[4][kPermMaxE];   // per-wave running counts, then wave bases
@@ -91,9 +99,9 @@ __global__ __launch_bounds__(kPermThreads) void perm_rank_kernel(
     if (blockIdx.x == 0 && tid == 0) offsets[E] = total;
     __syncthreads();
 
-    // stable ranks inside this wave's 1024 consecutive assignments
+    // stable ranks inside this wave's CHUNK/4 consecutive assignments
     volatile int* wc = s_wcnt[w];
-    const int a0 = blockIdx.x * kPermChunk + w * (kPermChunk / 4);
+    const int a0 = blockIdx.x * CHUNK + w * (CHUNK / 4);
     int loc[kPermIters];
     int key[kPermIters];
 #pragma unroll
@@ -256,7 +264,8 @@ static int ceil_log2(int v) {
 
 size_t permute_ws_bytes(int T, int k, int E) {
     const long long TK = (long long)T * k;
-    const long long nb = std::max(1LL, (TK + kPermChunk - 1) / kPermChunk);
+    const long long chunk = perm_chunk(TK);
+    const long long nb = std::max(1LL, (TK + chunk - 1) / chunk);
     return align_up((size_t)(nb * E) * sizeof(int32_t), 256);
 }
 
@@ -265,11 +274,18 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, const void* x
                           void* x_perm, void* ws, hipStream_t st)
 {
     const int TK = T * k;
-    const int nb = std::max(1, (TK + kPermChunk - 1) / kPermChunk);
+    const int chunk = perm_chunk(TK);
+    const int nb = std::max(1, (TK + chunk - 1) / chunk);
     int32_t* bc = static_cast<int32_t*>(ws);
-    perm_hist_kernel<<<nb, kPermThreads, 0, st>>>(idx, TK, E, bc);
-    perm_rank_kernel<<<nb, kPermThreads, 0, st>>>(idx, TK, E, ceil_log2(E), bc, nb, counts,
-                                                  offsets, perm_src, dest);
+    if (chunk == 1024) {
+        perm_hist_kernel<1024><<<nb, kPermThreads, 0, st>>>(idx, TK, E, bc);
+        perm_rank_kernel<1024><<<nb, kPermThreads, 0, st>>>(idx, TK, E, ceil_log2(E), bc, nb,
+                                                            counts, offsets, perm_src, dest);
+    } else {
+        perm_hist_kernel<4096><<<nb, kPermThreads, 0, st>>>(idx, TK, E, bc);
+        perm_rank_kernel<4096><<<nb, kPermThreads, 0, st>>>(idx, TK, E, ceil_log2(E), bc, nb,
+                                                            counts, offsets, perm_src, dest);
+    }
     if (T > 0) {
         const size_t row_bytes = (size_t)d * es;
         const dim3 grid((T + 3) / 4);
