@@ -54,6 +54,8 @@ def lib():
         L.oracle_route.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int64, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
         L.oracle_permute.argtypes = [vp, ctypes.c_int64, ctypes.c_int, vp, vp, vp, vp]
+        L.oracle_permute_capacity.argtypes = [vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int64,
+                                              vp, vp, vp, vp, vp]
         L.oracle_permute_recv.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
                                           vp, vp, vp, vp]
         L.oracle_gather.argtypes = [vp, ctypes.c_int, ctypes.c_int64, vp, ctypes.c_int64,
@@ -63,7 +65,8 @@ def lib():
                                              ctypes.c_int64, ctypes.c_int, vp]
         L.oracle_combine.argtypes = [vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, vp, vp,
                                      vp, vp, vp, vp]
-        for name in ("oracle_route", "oracle_permute", "oracle_permute_recv", "oracle_gather",
+        for name in ("oracle_route", "oracle_permute", "oracle_permute_capacity",
+                     "oracle_permute_recv", "oracle_gather",
                      "oracle_expert_ffn_rows", "oracle_combine"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -133,6 +136,23 @@ def permute(idx, E: int):
     _check(lib().oracle_permute(_p(flat), TK, E, _p(counts), _p(offsets), _p(perm_src),
                                 _p(dest)), "oracle_permute")
     return counts, offsets, perm_src, dest
+
+
+def permute_capacity(idx, E: int, capacity: int):
+    """Fixed-capacity packing: each expert keeps its first ``capacity``
+    assignments in ascending a = t*k+s. Returns (routed [E], counts [E],
+    offsets [E+1], perm_src [kept], dest [TK]) int32; dest = -1 when dropped."""
+    flat = _c(np.asarray(idx).reshape(-1), np.int32)
+    TK = flat.shape[0]
+    routed = np.empty(E, np.int32)
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    perm_src = np.empty(max(TK, 1), np.int32)
+    dest = np.empty(TK, np.int32)
+    _check(lib().oracle_permute_capacity(_p(flat), TK, E, int(capacity), _p(routed), _p(counts),
+                                         _p(offsets), _p(perm_src), _p(dest)),
+           "oracle_permute_capacity")
+    return routed, counts, offsets, perm_src[:int(offsets[E])].copy(), dest
 
 
 def permute_recv(recv_counts, N: int):
@@ -218,38 +238,47 @@ def swiglu_shared(x, wg, wv, wo, rows=None):
     return total
 
 
-def moe_layer(inp: dict, tokens=None):
+def moe_layer(inp: dict, tokens=None, capacity=None):
     """The whole layer on a token-routed workload dict (see
     expert_dispatch_amd.workloads). Returns a dict of every intermediate.
     With ``tokens`` given, only the packed rows those tokens need are
     gathered and run through the expert MLPs, and only those tokens are
-    combined; ``x_perm`` then holds the rows listed in ``y_rows``."""
+    combined; ``x_perm`` then holds the rows listed in ``y_rows``. With
+    ``capacity`` given, the packing keeps at most that many assignments per
+    expert (see permute_capacity); ``routed`` then holds the counts before
+    the cap."""
     k = inp["k"]
     logits, idx, gates = route(inp["x"], inp["w_router"], inp.get("bias"), k,
                                inp.get("renorm", True))
     E = inp["w_gate"].shape[0]
-    counts, offsets, perm_src, dest = permute(idx, E)
+    if capacity is None:
+        counts, offsets, perm_src, dest = permute(idx, E)
+        routed = counts
+    else:
+        routed, counts, offsets, perm_src, dest = permute_capacity(idx, E, capacity)
     T = inp["x"].shape[0]
+    kept = int(offsets[E])
     tok = np.arange(T, dtype=np.int32) if tokens is None else _c(tokens, np.int32)
     if tokens is None:
-        need = np.arange(T * k, dtype=np.int64)
+        need = np.arange(kept, dtype=np.int64)
         x_perm = gather(inp["x"], perm_src, k)
         y_rows = expert_ffn_rows(x_perm, offsets, inp["w_gate"], inp["w_val"], inp["w_out"])
     else:
         need = np.unique(dest.reshape(T, k)[tok].reshape(-1)).astype(np.int64)
+        need = need[need >= 0]
         x_perm = gather(inp["x"], perm_src[need], k)
         y_rows = expert_ffn_rows(x_perm, offsets, inp["w_gate"], inp["w_val"], inp["w_out"],
-                                 need, N=T * k)
-    yrow = np.full(T * k, -1, np.int64)
+                                 need, N=kept)
+    yrow = np.full(max(kept, 1), -1, np.int64)
     yrow[need] = np.arange(need.shape[0])
     shared = None
     if inp.get("shared_w_gate") is not None:
         shared = swiglu_shared(inp["x"], inp["shared_w_gate"], inp["shared_w_val"],
                                inp["shared_w_out"], tok.astype(np.int64))
     out = combine(tok, k, dest, gates, y_rows, yrow, shared)
-    return dict(logits=logits, idx=idx, gates=gates, counts=counts, offsets=offsets,
-                perm_src=perm_src, dest=dest, x_perm=x_perm, y_rows=need, y=y_rows,
-                shared=shared, tokens=tok, out=out)
+    return dict(logits=logits, idx=idx, gates=gates, counts=counts, routed=routed,
+                offsets=offsets, perm_src=perm_src, dest=dest, x_perm=x_perm, y_rows=need,
+                y=y_rows, shared=shared, tokens=tok, out=out)
 
 
 def moe_recv_layer(inp: dict, rows=None):

@@ -140,6 +140,36 @@ int oracle_permute(const int32_t* idx, int64_t TK, int E,
     return 0;
 }
 
+int oracle_permute_capacity(const int32_t* idx, int64_t TK, int E, int64_t capacity,
+                            int32_t* routed, int32_t* counts, int32_t* offsets,
+                            int32_t* perm_src, int32_t* dest)
+{
+    if (!idx || !routed || !counts || !offsets || !perm_src || !dest) return -1;
+    if (TK < 0 || E <= 0 || TK > INT32_MAX || capacity < 0) return -1;
+    for (int64_t a = 0; a < TK; ++a)
+        if (idx[a] < 0 || idx[a] >= E) return -2;
+    for (int e = 0; e < E; ++e) routed[e] = 0;
+    for (int64_t a = 0; a < TK; ++a) routed[idx[a]] += 1;
+    for (int e = 0; e < E; ++e) counts[e] = routed[e] < capacity ? routed[e] : (int32_t)capacity;
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    for (int64_t a = 0; a < TK; ++a) dest[a] = -1;
+    /* for each expert: its assignments in ascending a, the first `capacity`
+     * of them into its slice of the packed buffer */
+    for (int e = 0; e < E; ++e) {
+        int64_t j = offsets[e];
+        int64_t kept = 0;
+        for (int64_t a = 0; a < TK && kept < counts[e]; ++a) {
+            if (idx[a] != e) continue;
+            perm_src[j] = (int32_t)a;
+            dest[a] = (int32_t)j;
+            ++j;
+            ++kept;
+        }
+    }
+    return 0;
+}
+
 int oracle_permute_recv(const int32_t* recv, int S, int E_loc, int64_t N,
                         int32_t* counts, int32_t* offsets,
                         int32_t* perm_src, int32_t* dest)
@@ -245,6 +275,7 @@ int oracle_combine(const int32_t* tokens, int64_t ntok, int k, int64_t d,
         for (int s = 0; s < k; ++s) {
             int64_t a = t * k + s;
             int64_t j = dest[a];
+            if (j < 0) continue;   /* dropped by a capacity: contributes nothing */
             int64_t row = yrow ? yrow[j] : j;
             if (row < 0) { bad = 1; continue; }
             double gw = gates ? gates[a] : 1.0;

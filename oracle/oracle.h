@@ -55,6 +55,23 @@ int oracle_permute(const int32_t* idx, int64_t TK, int E,
                    int32_t* perm_src, int32_t* dest);
 
 /*
+ * Fixed-capacity packing (a routing variant; the Modalities EP page, "Not
+ * done yet / follow-ups", and "Three axes of Parallelism", "Discussion,
+ * Future work", name fixed-capacity dispatch and capacity load balancing
+ * without defining them). Reading: every expert keeps the first `capacity`
+ * of its assignments in ascending a = t*k+s; the others are dropped.
+ * routed[e] = assignments with idx == e (before the cap),
+ * counts[e] = min(routed[e], capacity), offsets from counts as in
+ * oracle_permute; expert e's region holds its kept assignments in ascending
+ * a; dest[a] = -1 for a dropped assignment. capacity >= max routed[e] gives
+ * exactly oracle_permute. Fails (-1) on capacity < 0, (-2) on an id outside
+ * [0,E).
+ */
+int oracle_permute_capacity(const int32_t* idx, int64_t TK, int E, int64_t capacity,
+                            int32_t* routed, int32_t* counts, int32_t* offsets,
+                            int32_t* perm_src, int32_t* dest);
+
+/*
  * Receive-side reorder [Three axes of Parallelism, "Dispatch, expert
  * computation and combine"; Modalities PR "expert parallelism for the
  * Nemotron-3 Nano MoE layers", section "Design"]: recv[i,j] rows came from
@@ -95,6 +112,7 @@ int oracle_expert_ffn_rows(const void* x, int xtype, int64_t N, int d, int f, in
  *   out[r,:] = sum_{s ascending} g[t,s] * y[dest[t*k+s],:] (+ shared[r,:])
  * for t = tokens[r]. gates NULL means weight 1. yrow maps a packed row to its
  * row in y (NULL: y is indexed by the packed row itself; -1: missing -> -3).
+ * A term with dest = -1 (an assignment dropped by a capacity) adds nothing.
  */
 int oracle_combine(const int32_t* tokens, int64_t ntok, int k, int64_t d,
                    const int32_t* dest, const double* gates,

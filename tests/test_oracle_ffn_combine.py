@@ -172,3 +172,44 @@ def test_recv_layer_identity_round_trip():
     out = oracle.combine(np.arange(N, dtype=np.int32), 1, r["dest"], None, ident)
     np.testing.assert_array_equal(out, _widen(inp["x_recv"]))
     assert r["out"].shape == (N, inp["x_recv"].shape[1])
+
+
+@pytest.mark.parametrize("name,cap", [("tiny_f32", 8), ("dsv2_small", 9)])
+def test_capacity_layer_dense_bruteforce(name, cap):
+    """Fixed-capacity routing against every expert on every token, masked by
+    the assignments each expert keeps (its first `cap` in (token, slot)
+    order): dropped assignments add nothing."""
+    inp = W.generate(W.get(name))
+    T = min(inp["x"].shape[0], 48)
+    inp = dict(inp, x=inp["x"][:T])
+    r = oracle.moe_layer(inp, capacity=cap)
+    E, k = inp["w_gate"].shape[0], inp["k"]
+    assert (r["dest"] < 0).any(), "the cap should drop something here"
+    X = torch.from_numpy(_widen(inp["x"]))
+    dense = torch.zeros(T, X.shape[1], dtype=torch.float64)
+    for e in range(E):
+        G, V, O = (torch.from_numpy(_widen(inp[n][e])) for n in ("w_gate", "w_val", "w_out"))
+        ye = (torch.nn.functional.silu(X @ G) * (X @ V)) @ O
+        wgt = np.zeros(T)
+        seen = 0
+        for t in range(T):
+            for s in range(k):
+                if r["idx"][t, s] == e:
+                    if seen < cap:
+                        wgt[t] = r["gates"][t, s]
+                    seen += 1
+        dense += torch.from_numpy(wgt)[:, None] * ye
+    if inp.get("shared_w_gate") is not None:
+        for q in range(inp["shared_w_gate"].shape[0]):
+            G, V, O = (torch.from_numpy(_widen(inp["shared_" + n][q]))
+                       for n in ("w_gate", "w_val", "w_out"))
+            dense += (torch.nn.functional.silu(X @ G) * (X @ V)) @ O
+    np.testing.assert_allclose(r["out"], dense.numpy(), rtol=1e-10, atol=1e-11)
+
+
+def test_capacity_sampled_layer_equals_full_layer():
+    inp = W.generate(W.get("dsv2_small"))
+    full = oracle.moe_layer(inp, capacity=30)
+    toks = np.array([0, 5, 17, 100, 279], np.int32)
+    part = oracle.moe_layer(inp, tokens=toks, capacity=30)
+    np.testing.assert_array_equal(part["out"], full["out"][toks])

@@ -108,3 +108,53 @@ def test_gather_reads_each_token_for_each_slot():
     T = inp["x"].shape[0]
     for a in range(0, T * k, 5):
         np.testing.assert_array_equal(xp[dest[a]], inp["x"][a // k])
+
+
+def _capacity_reference(flat, E, cap):
+    """Each expert keeps its first `cap` assignments in ascending flat order
+    (written out with Python lists, one expert at a time)."""
+    kept, dest = [], np.full(flat.shape[0], -1, np.int64)
+    routed = np.bincount(flat, minlength=E)
+    for e in range(E):
+        mine = [a for a in range(flat.shape[0]) if flat[a] == e][:cap]
+        for a in mine:
+            dest[a] = len(kept)
+            kept.append(a)
+    counts = np.minimum(routed, cap)
+    return routed, counts, np.concatenate([[0], np.cumsum(counts)]), np.array(kept, np.int64), dest
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_capacity_pack_bruteforce(seed):
+    rng = np.random.default_rng(seed)
+    T, k, E = int(rng.integers(1, 40)), int(rng.integers(1, 4)), int(rng.integers(1, 7))
+    k = min(k, E)
+    # skewed ids so some experts overflow
+    flat = np.minimum(rng.geometric(0.4, size=T * k) - 1, E - 1).astype(np.int32)
+    for cap in (0, 1, 2, 5, T * k):
+        r = oracle.permute_capacity(flat.reshape(T, k), E, cap)
+        ref = _capacity_reference(flat, E, cap)
+        for got, want, what in zip(r, ref, ("routed", "counts", "offsets", "perm_src", "dest")):
+            np.testing.assert_array_equal(got, want, err_msg=f"{what} cap={cap}")
+        assert (r[4] < 0).sum() == int(np.maximum(ref[0] - cap, 0).sum())
+
+
+@pytest.mark.parametrize("name", ["qwen3_small", "stress_small"])
+def test_capacity_at_least_every_count_is_the_plain_pack(name):
+    inp = W.generate(W.get(name))
+    _, idx, _ = oracle.route(inp["x"], inp["w_router"], inp["bias"], inp["k"])
+    E = inp["w_gate"].shape[0]
+    plain = oracle.permute(idx, E)
+    cap = int(plain[0].max())
+    routed, counts, offsets, perm_src, dest = oracle.permute_capacity(idx, E, cap)
+    np.testing.assert_array_equal(routed, plain[0])
+    for got, want in zip((counts, offsets, perm_src, dest), plain):
+        np.testing.assert_array_equal(got, want)
+    # one below the largest count drops exactly the largest expert's last assignment
+    routed, counts, offsets, perm_src, dest = oracle.permute_capacity(idx, E, cap - 1)
+    assert (dest < 0).sum() == int((plain[0] == cap).sum())
+
+
+def test_capacity_rejects_negative():
+    with pytest.raises(RuntimeError):
+        oracle.permute_capacity(np.zeros((2, 1), np.int32), 1, -1)
