@@ -43,7 +43,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="qwen3_30b_a3b")
-    ap.add_argument("--y-dtype", choices=("f32", "bf16"), default="bf16",
+    ap.add_argument("--capacity-factor", type=float, default=None,
+                    help="fixed-capacity packing: each expert keeps at most "
+                         "ceil(factor * T * k / E) assignments (token-routed workloads)")
+    ap.add_argument("--y-dtype", choices=("f32", "bf16"), default="f32",
                     help="storage type of the expert outputs y_perm between the down GEMM "
                          "and the combine (bf16 inputs only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -76,7 +79,7 @@ def to_dev(a, torch):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def stage_work(cfg, counts, es, ys=4):
+def stage_work(cfg, counts, es, ys=4, kept=None):
     """Algorithmic flops and bytes of one launch of each stage: what the method
     must compute or move (s = element size, TK = T*k rows, n_act = experts with
     rows). Router 2*T*d*E flop; packing (T + TK)*d*s bytes + indices; gate_up
@@ -84,14 +87,14 @@ def stage_work(cfg, counts, es, ys=4):
     over TK*f*s + n_act*f*d*s + TK*d*ys bytes; combine TK*d*ys + T*d*4 bytes
     (ys = element size of the stored expert outputs)."""
     T, k, d, f, E = cfg.T, cfg.k, cfg.d, cfg.f, cfg.E
-    rows = cfg.rows
+    rows = cfg.rows if kept is None else kept   # packed rows the experts process
     active = int((counts > 0).sum())
     w = {}
     if cfg.kind == "routed":
         w["route"] = dict(flops=2.0 * T * d * E,
                           bytes=T * d * es + d * E * es + E * 4 + T * E * 4 + 2 * T * k * 4,
                           bound="alu")
-        w["permute"] = dict(flops=0.0, bytes=(T + rows) * d * es + 4 * rows * 4, bound="hbm")
+        w["permute"] = dict(flops=0.0, bytes=(T + rows) * d * es + 4 * cfg.rows * 4, bound="hbm")
     else:
         w["permute_recv"] = dict(flops=0.0, bytes=2 * rows * d * es + 2 * rows * 4, bound="hbm")
     w["gate_up"] = dict(flops=4.0 * rows * d * f,
@@ -226,6 +229,10 @@ def main():
         gates = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=cuda)
         ws = torch.empty(max(1, ops.permute_workspace(cfg.T, cfg.k, E)), dtype=torch.uint8,
                          device=cuda)
+        cap = None
+        if args.capacity_factor is not None:
+            cap = int(np.ceil(args.capacity_factor * cfg.T * cfg.k / E))
+            bufs["routed"] = torch.empty(E, dtype=torch.int32, device=cuda)
         if cfg.shared:
             shared = dict(
                 wg=to_dev(np.concatenate(list(inp["shared_w_gate"]), axis=1)[None], torch),
@@ -245,7 +252,7 @@ def main():
         if cfg.kind == "routed":
             ops.route(dev["x"], dev["w_router"], dev["bias"], cfg.k, out=(logits, idx, gates))
             if ev is not None: ev[1].record()
-            ops.permute(idx, dev["x"], E, out=bufs, workspace=ws)
+            ops.permute(idx, dev["x"], E, capacity=cap, out=bufs, workspace=ws)
             i = 2
         else:
             ops.permute_recv(dev["recv_counts"], dev["x_recv"], out=bufs)
@@ -293,7 +300,8 @@ def main():
                                         for s in range(args.steps)]) * 1e3)
 
     counts = bufs["counts"].cpu().numpy()
-    work = stage_work(cfg, counts, es, ys)
+    kept = int(counts.sum())
+    work = stage_work(cfg, counts, es, ys, kept)
     stage_rep = {}
     for name in stages:
         r = roofline_entry(work[name], stage_us[name], es)
@@ -323,7 +331,8 @@ def main():
         "dtype": "bf16" if es == 2 else "f32",
         "data": "synthetic (seeded Gaussian inputs and weights of the stated shapes)",
         "config": {"workload": cfg.name, "description": cfg.description,
-                   "y_perm_dtype": "bf16" if ys == 2 else "f32", "T": cfg.T,
+                   "y_perm_dtype": "bf16" if ys == 2 else "f32",
+                   "capacity_factor": args.capacity_factor, "kept_rows": kept, "T": cfg.T,
                    "k": cfg.k, "N": cfg.N, "d": d, "f": f, "E": E, "shared": cfg.shared,
                    "rows": rows, "load_max_over_mean": round(float(counts.max() / max(counts.mean(), 1e-9)), 3),
                    "empty_experts": int((counts == 0).sum())},

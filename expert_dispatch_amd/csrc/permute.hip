@@ -57,16 +57,18 @@ __global__ __launch_bounds__(kPermThreads) void perm_hist_kernel(
     for (int e = threadIdx.x; e < E; e += kPermThreads) bc[(size_t)blockIdx.x * E + e] = h[e];
 }
 
+// cap: assignments an expert keeps (its first cap in ascending a; INT_MAX =
+// all); routed (may be null) receives the per-expert counts before the cap.
 template <int CHUNK>
 __global__ __launch_bounds__(kPermThreads) void perm_rank_kernel(
-    const int32_t* __restrict__ idx, int TK, int E, int nbits,
+    const int32_t* __restrict__ idx, int TK, int E, int nbits, int cap,
     const int32_t* __restrict__ bc, int nb,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ routed, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm_src, int32_t* __restrict__ dest)
 {
     constexpr int kPermIters = CHUNK / kPermThreads;   // per lane
-    __shared__ int s_off[kPermMaxE];       // global offsets
-    __shared__ int s_base[kPermMaxE];      // offsets + assignments of earlier blocks
+    __shared__ int s_off[kPermMaxE];       // offsets of the kept assignments
+    __shared__ int s_base[kPermMaxE];      // assignments of earlier blocks (rank base)
     __shared__ int s_wcnt[4][kPermMaxE];   // per-wave running counts, then wave bases
     __shared__ int scratch[kPermThreads / kWave + 1];
 
@@ -81,22 +83,22 @@ __global__ __launch_bounds__(kPermThreads) void perm_rank_kernel(
             tot += c;
             if (b < (int)blockIdx.x) pre += c;
         }
-        s_off[e] = tot;
+        const int kept = min(tot, cap);
+        s_off[e] = kept;
         s_base[e] = pre;
+        if (blockIdx.x == 0) {
+            counts[e] = kept;
+            if (routed) routed[e] = tot;
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) s_wcnt[q][e] = 0;
     }
     __syncthreads();
     const int total = block_exclusive_scan_lds(s_off, E, scratch);
-    for (int e = tid; e < E; e += kPermThreads) {
-        s_base[e] += s_off[e];
-        if (blockIdx.x == 0) {
-            const int next = (e + 1 < E) ? s_off[e + 1] : total;
-            counts[e] = next - s_off[e];
-            offsets[e] = s_off[e];
-        }
+    if (blockIdx.x == 0) {
+        for (int e = tid; e < E; e += kPermThreads) offsets[e] = s_off[e];
+        if (tid == 0) offsets[E] = total;
     }
-    if (blockIdx.x == 0 && tid == 0) offsets[E] = total;
     __syncthreads();
 
     // stable ranks inside this wave's CHUNK/4 consecutive assignments
@@ -143,8 +145,9 @@ __global__ __launch_bounds__(kPermThreads) void perm_rank_kernel(
         const int e = key[it];
         int j = -1;
         if (e >= 0) {
-            j = s_base[e] + s_wcnt[w][e] + loc[it];
-            if (j >= TK) j = -1;
+            const int r = s_base[e] + s_wcnt[w][e] + loc[it];   // rank inside expert e
+            j = r < cap ? s_off[e] + r : -1;
+            if (j >= total) j = -1;
         }
         dest[a] = j;
         if (j >= 0) perm_src[j] = a;
@@ -269,9 +272,10 @@ size_t permute_ws_bytes(int T, int k, int E) {
     return align_up((size_t)(nb * E) * sizeof(int32_t), 256);
 }
 
-hipError_t launch_permute(const int32_t* idx, int T, int k, int E, const void* x, int es, int d,
-                          int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* dest,
-                          void* x_perm, void* ws, hipStream_t st)
+hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int cap, const void* x,
+                          int es, int d, int32_t* routed, int32_t* counts, int32_t* offsets,
+                          int32_t* perm_src, int32_t* dest, void* x_perm, void* ws,
+                          hipStream_t st)
 {
     const int TK = T * k;
     const int chunk = perm_chunk(TK);
@@ -279,12 +283,14 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, const void* x
     int32_t* bc = static_cast<int32_t*>(ws);
     if (chunk == 1024) {
         perm_hist_kernel<1024><<<nb, kPermThreads, 0, st>>>(idx, TK, E, bc);
-        perm_rank_kernel<1024><<<nb, kPermThreads, 0, st>>>(idx, TK, E, ceil_log2(E), bc, nb,
-                                                            counts, offsets, perm_src, dest);
+        perm_rank_kernel<1024><<<nb, kPermThreads, 0, st>>>(idx, TK, E, ceil_log2(E), cap, bc,
+                                                            nb, routed, counts, offsets,
+                                                            perm_src, dest);
     } else {
         perm_hist_kernel<4096><<<nb, kPermThreads, 0, st>>>(idx, TK, E, bc);
-        perm_rank_kernel<4096><<<nb, kPermThreads, 0, st>>>(idx, TK, E, ceil_log2(E), bc, nb,
-                                                            counts, offsets, perm_src, dest);
+        perm_rank_kernel<4096><<<nb, kPermThreads, 0, st>>>(idx, TK, E, ceil_log2(E), cap, bc,
+                                                            nb, routed, counts, offsets,
+                                                            perm_src, dest);
     }
     if (T > 0) {
         const size_t row_bytes = (size_t)d * es;

@@ -43,6 +43,7 @@ def lib():
     sigs = {
         "moe_route": [vp, i, vp, vp, i, i, i, i, i, vp, vp, vp, vp],
         "moe_permute": [vp, i, i, i, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp],
+        "moe_permute_capacity": [vp, i, i, i, i, vp, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_permute_recv": [vp, i, i, i, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_grouped_ffn": [vp, i, i, i, i, i, vp, vp, vp, vp, vp, i, vp, sz, vp],
         "moe_ffn_gate_up": [vp, i, i, i, i, i, vp, vp, vp, vp, vp],
@@ -115,8 +116,10 @@ def permute_workspace(T: int, k: int, E: int) -> int:
     return int(lib().moe_permute_workspace(T, k, E))
 
 
-def permute(topk_idx, x, E: int, *, out=None, workspace=None, stream=None):
-    """Expert-major packing. Returns dict(counts, offsets, perm_src, dest, x_perm)."""
+def permute(topk_idx, x, E: int, *, capacity=None, out=None, workspace=None, stream=None):
+    """Expert-major packing. Returns dict(counts, offsets, perm_src, dest, x_perm);
+    with ``capacity`` (fixed-capacity packing) also ``routed``, the counts
+    before the cap."""
     _dev(topk_idx, "topk_idx"); _dev(x, "x")
     T, k = topk_idx.shape
     d = x.shape[1]
@@ -127,13 +130,21 @@ def permute(topk_idx, x, E: int, *, out=None, workspace=None, stream=None):
                    perm_src=torch.empty(T * k, dtype=torch.int32, device=dev),
                    dest=torch.empty(T * k, dtype=torch.int32, device=dev),
                    x_perm=torch.empty((T * k, d), dtype=x.dtype, device=dev))
+        if capacity is not None:
+            out["routed"] = torch.empty(E, dtype=torch.int32, device=dev)
     nbytes = permute_workspace(T, k, E)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    _check("moe_permute", lib().moe_permute(
-        _p(topk_idx), T, k, E, _p(x), _dt(x), d, _p(out["counts"]), _p(out["offsets"]),
-        _p(out["perm_src"]), _p(out["dest"]), _p(out["x_perm"]), _p(workspace),
-        workspace.numel(), _stream(stream)))
+    if capacity is None:
+        _check("moe_permute", lib().moe_permute(
+            _p(topk_idx), T, k, E, _p(x), _dt(x), d, _p(out["counts"]), _p(out["offsets"]),
+            _p(out["perm_src"]), _p(out["dest"]), _p(out["x_perm"]), _p(workspace),
+            workspace.numel(), _stream(stream)))
+    else:
+        _check("moe_permute_capacity", lib().moe_permute_capacity(
+            _p(topk_idx), T, k, E, int(capacity), _p(x), _dt(x), d, _p(out.get("routed")),
+            _p(out["counts"]), _p(out["offsets"]), _p(out["perm_src"]), _p(out["dest"]),
+            _p(out["x_perm"]), _p(workspace), workspace.numel(), _stream(stream)))
     return out
 
 
@@ -216,16 +227,17 @@ def combine(y_perm, dest, gates, k: int, *, y_shared=None, out_dtype=torch.float
     return out
 
 
-def moe_layer(x, w_router, bias, k: int, w_gate, w_val, w_out, *, shared=None,
+def moe_layer(x, w_router, bias, k: int, w_gate, w_val, w_out, *, shared=None, capacity=None,
               y_dtype=torch.float32, out_dtype=torch.float32, stream=None):
     """The whole token-routed layer: route -> permute -> grouped FFN -> combine.
     ``shared`` = (w_gate, w_val, w_out) of the always-on shared experts
     concatenated along f (one SwiGLU of width q*f equals the sum of q).
     ``y_dtype`` is the storage type of the expert outputs between the down
-    GEMM and the combine."""
+    GEMM and the combine. ``capacity``: fixed-capacity packing (at most that
+    many rows per expert; dropped assignments add nothing to their token)."""
     E = w_gate.shape[0]
     logits, idx, gates = route(x, w_router, bias, k, stream=stream)
-    p = permute(idx, x, E, stream=stream)
+    p = permute(idx, x, E, capacity=capacity, stream=stream)
     y = grouped_ffn(p["x_perm"], p["offsets"], w_gate, w_val, w_out, y_dtype=y_dtype,
                     stream=stream)
     y_sh = None

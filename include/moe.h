@@ -103,6 +103,27 @@ moe_status moe_permute(const int32_t* topk_idx, int T, int k, int E,
                        void* x_perm, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Fixed-capacity packing, a routing variant the pages name but do not define
+ * (Modalities EP PR, "Not done yet / follow-ups": fixed-capacity dispatchers;
+ * "Three axes of Parallelism", "Discussion, Future work": capacity load
+ * balancing). Every expert keeps the first `capacity` of its assignments in
+ * ascending a = t*k+s (the packing's stable order); the others are dropped.
+ * Same arguments and workspace as moe_permute, plus:
+ *   capacity  >= 0 host integer, the most rows an expert keeps
+ *   routed    [E] int32 out or NULL: assignments per expert before the cap
+ *             (the load statistics)
+ * counts[e] = min(routed[e], capacity); offsets from counts; perm_src is
+ * defined for packed rows j < offsets[E]; dest[a] = -1 and no x_perm row for
+ * a dropped assignment (moe_combine then skips it). capacity >= T*k is the
+ * plain packing. Errors: capacity < 0 -> MOE_ERR_INVALID_ARG.
+ */
+moe_status moe_permute_capacity(const int32_t* topk_idx, int T, int k, int E, int capacity,
+                                const void* x, moe_dtype dt, int d, int32_t* routed,
+                                int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                                int32_t* dest, void* x_perm, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/*
  * Receive-side reorder ("Three axes of Parallelism", Dispatch, expert
  * computation and combine: recv_matrix[i,j] = rows sender i sent to local
  * expert j; the received buffer is source-major and is permuted expert-major,
