@@ -48,7 +48,8 @@ def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
 @dataclasses.dataclass(frozen=True)
 class Config:
     name: str
-    kind: str            # "routed" (tokens pass the router) or "recv" (received buffer)
+    kind: str            # "routed" (tokens pass the router), "recv" (received buffer) or
+                         # "gathered" (one rank of the all-gather / reduce-scatter layout)
     dtype: str           # "f32" or "bf16"
     d: int
     f: int
@@ -63,19 +64,21 @@ class Config:
     empty: int = 0       # experts forced to receive no token
     N: int = 0           # recv: received rows
     S: int = 0           # recv: senders
-    E_global: int = 0    # recv: experts over the whole EP group
+    E_global: int = 0    # recv / gathered: experts over the whole EP group
+    e_first: int = 0     # gathered: first global expert this rank owns
     alpha: float = 0.3   # recv: Dirichlet concentration
     description: str = ""
 
     @property
     def rows(self) -> int:
-        """Rows the grouped FFN processes (T*k assignments or N received rows)."""
-        return self.T * self.k if self.kind == "routed" else self.N
+        """Rows the grouped FFN can process: T*k assignments (at most, for a
+        rank's expert range) or N received rows."""
+        return self.N if self.kind == "recv" else self.T * self.k
 
     @property
     def units(self) -> int:
-        """Tokens (routed) or received rows (recv) one layer pass handles."""
-        return self.T if self.kind == "routed" else self.N
+        """Tokens (routed / gathered) or received rows (recv) one layer pass handles."""
+        return self.N if self.kind == "recv" else self.T
 
 
 CONFIGS = {
@@ -98,6 +101,12 @@ CONFIGS = {
                description="one EP rank's received buffer: N=16384 rows sender-major over "
                            "4 senders x 16 local experts (of 64), SwiGLU 2048->1024->2048, "
                            "Dirichlet(0.3) cell counts"),
+        Config("ag_rs_rank", "gathered", "bf16", d=2048, f=768, E=16, seed=6, T=32768, k=8,
+               E_global=128, e_first=80, bias="normal",
+               description="one rank of an 8-rank all-gather / reduce-scatter EP group at the "
+                           "Qwen3-30B-A3B shape: 32768 gathered tokens (8x4096), replicated "
+                           "router over 128 experts, top-8, local experts 80..95, SwiGLU "
+                           "2048->768->2048, partial outputs"),
         Config("stress_zipf", "routed", "bf16", d=4096, f=1536, E=64, seed=5, T=32768, k=8,
                bias="zipf",
                description="large-batch stress: T=32768, d=4096, E=64, top-8, SwiGLU "
@@ -118,6 +127,9 @@ CONFIGS = {
                bias="zipf", description="reduced Zipf stress layer"),
         Config("odd_f32", "routed", "f32", d=48, f=80, E=5, seed=16, T=37, k=3,
                description="fp32 layer with dims that are not tile multiples"),
+        Config("ag_rs_small", "gathered", "bf16", d=256, f=384, E=4, seed=17, T=300, k=4,
+               E_global=16, e_first=8, bias="normal",
+               description="reduced all-gather / reduce-scatter rank: experts 8..11 of 16"),
     ]
 }
 
@@ -188,6 +200,15 @@ def generate(cfg: Config | str) -> dict:
         out["bias"] = bias
         out["k"] = cfg.k
         out["renorm"] = True
+    elif cfg.kind == "gathered":
+        out["x"] = _normal(gen, (cfg.T, cfg.d), 1.0, cfg.dtype)
+        out["w_router"] = _normal(gen, (cfg.d, cfg.E_global), 0.02, cfg.dtype)
+        out["bias"] = (_normal(gen, (cfg.E_global,), cfg.bias_std, "f32")
+                       if cfg.bias == "normal" else None)
+        out["w_gate"], out["w_val"], out["w_out"] = _experts(gen, cfg.E, cfg.d, cfg.f, cfg.dtype)
+        out["k"] = cfg.k
+        out["renorm"] = True
+        out["e_first"] = cfg.e_first
     elif cfg.kind == "recv":
         out["x_recv"] = _normal(gen, (cfg.N, cfg.d), 1.0, cfg.dtype)
         out["w_gate"], out["w_val"], out["w_out"] = _experts(gen, cfg.E, cfg.d, cfg.f, cfg.dtype)

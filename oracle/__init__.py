@@ -56,6 +56,8 @@ def lib():
         L.oracle_permute.argtypes = [vp, ctypes.c_int64, ctypes.c_int, vp, vp, vp, vp]
         L.oracle_permute_capacity.argtypes = [vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int64,
                                               vp, vp, vp, vp, vp]
+        L.oracle_permute_range.argtypes = [vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                           vp, vp, vp, vp]
         L.oracle_permute_recv.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
                                           vp, vp, vp, vp]
         L.oracle_gather.argtypes = [vp, ctypes.c_int, ctypes.c_int64, vp, ctypes.c_int64,
@@ -66,6 +68,7 @@ def lib():
         L.oracle_combine.argtypes = [vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, vp, vp,
                                      vp, vp, vp, vp]
         for name in ("oracle_route", "oracle_permute", "oracle_permute_capacity",
+                     "oracle_permute_range",
                      "oracle_permute_recv", "oracle_gather",
                      "oracle_expert_ffn_rows", "oracle_combine"):
             getattr(L, name).restype = ctypes.c_int
@@ -153,6 +156,22 @@ def permute_capacity(idx, E: int, capacity: int):
                                          _p(offsets), _p(perm_src), _p(dest)),
            "oracle_permute_capacity")
     return routed, counts, offsets, perm_src[:int(offsets[E])].copy(), dest
+
+
+def permute_range(idx, e_first: int, E_loc: int):
+    """Packing of the expert range [e_first, e_first + E_loc) (one rank of the
+    all-gather layout). Returns (counts [E_loc], offsets [E_loc+1],
+    perm_src [kept], dest [TK]) int32; dest = -1 outside the range."""
+    flat = _c(np.asarray(idx).reshape(-1), np.int32)
+    TK = flat.shape[0]
+    counts = np.empty(E_loc, np.int32)
+    offsets = np.empty(E_loc + 1, np.int32)
+    perm_src = np.empty(max(TK, 1), np.int32)
+    dest = np.empty(TK, np.int32)
+    _check(lib().oracle_permute_range(_p(flat), TK, int(e_first), int(E_loc), _p(counts),
+                                      _p(offsets), _p(perm_src), _p(dest)),
+           "oracle_permute_range")
+    return counts, offsets, perm_src[:int(offsets[E_loc])].copy(), dest
 
 
 def permute_recv(recv_counts, N: int):
@@ -279,6 +298,38 @@ def moe_layer(inp: dict, tokens=None, capacity=None):
     return dict(logits=logits, idx=idx, gates=gates, counts=counts, routed=routed,
                 offsets=offsets, perm_src=perm_src, dest=dest, x_perm=x_perm, y_rows=need,
                 y=y_rows, shared=shared, tokens=tok, out=out)
+
+
+def moe_partial_layer(inp: dict, e_first: int, tokens=None):
+    """One rank of the all-gather / reduce-scatter layout on a gathered-token
+    workload: the replicated router over every token, the rank's local experts
+    (inp["w_gate"] etc. hold them, global ids e_first..) over the assignments
+    routed to them, and the combine into this rank's partial output (the
+    reduce-scatter then sums the partials of all ranks)."""
+    k = inp["k"]
+    logits, idx, gates = route(inp["x"], inp["w_router"], inp.get("bias"), k,
+                               inp.get("renorm", True))
+    E_loc = inp["w_gate"].shape[0]
+    counts, offsets, perm_src, dest = permute_range(idx, e_first, E_loc)
+    T = inp["x"].shape[0]
+    kept = int(offsets[E_loc])
+    tok = np.arange(T, dtype=np.int32) if tokens is None else _c(tokens, np.int32)
+    if tokens is None:
+        need = np.arange(kept, dtype=np.int64)
+        x_perm = gather(inp["x"], perm_src, k)
+        y_rows = expert_ffn_rows(x_perm, offsets, inp["w_gate"], inp["w_val"], inp["w_out"])
+    else:
+        need = np.unique(dest.reshape(T, k)[tok].reshape(-1)).astype(np.int64)
+        need = need[need >= 0]
+        x_perm = gather(inp["x"], perm_src[need], k)
+        y_rows = expert_ffn_rows(x_perm, offsets, inp["w_gate"], inp["w_val"], inp["w_out"],
+                                 need, N=kept)
+    yrow = np.full(max(kept, 1), -1, np.int64)
+    yrow[need] = np.arange(need.shape[0])
+    out = combine(tok, k, dest, gates, y_rows, yrow, None)
+    return dict(logits=logits, idx=idx, gates=gates, counts=counts, offsets=offsets,
+                perm_src=perm_src, dest=dest, x_perm=x_perm, y_rows=need, y=y_rows,
+                tokens=tok, out=out)
 
 
 def moe_recv_layer(inp: dict, rows=None):

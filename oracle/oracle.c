@@ -170,6 +170,32 @@ int oracle_permute_capacity(const int32_t* idx, int64_t TK, int E, int64_t capac
     return 0;
 }
 
+int oracle_permute_range(const int32_t* idx, int64_t TK, int e_first, int E_loc,
+                         int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* dest)
+{
+    if (!idx || !counts || !offsets || !perm_src || !dest) return -1;
+    if (TK < 0 || TK > INT32_MAX || E_loc <= 0 || e_first < 0) return -1;
+    for (int e = 0; e < E_loc; ++e) counts[e] = 0;
+    for (int64_t a = 0; a < TK; ++a) {
+        int64_t l = (int64_t)idx[a] - e_first;
+        if (l >= 0 && l < E_loc) counts[l] += 1;
+    }
+    offsets[0] = 0;
+    for (int e = 0; e < E_loc; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    for (int64_t a = 0; a < TK; ++a) dest[a] = -1;
+    /* for each local expert: its assignments in ascending a, into its slice */
+    for (int e = 0; e < E_loc; ++e) {
+        int64_t j = offsets[e];
+        for (int64_t a = 0; a < TK; ++a) {
+            if ((int64_t)idx[a] - e_first != e) continue;
+            perm_src[j] = (int32_t)a;
+            dest[a] = (int32_t)j;
+            ++j;
+        }
+    }
+    return 0;
+}
+
 int oracle_permute_recv(const int32_t* recv, int S, int E_loc, int64_t N,
                         int32_t* counts, int32_t* offsets,
                         int32_t* perm_src, int32_t* dest)

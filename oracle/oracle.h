@@ -72,6 +72,19 @@ int oracle_permute_capacity(const int32_t* idx, int64_t TK, int E, int64_t capac
                             int32_t* perm_src, int32_t* dest);
 
 /*
+ * Packing of one rank's expert range in the all-gather / reduce-scatter
+ * layout [SpecForge PR "expert parallelism for MoE drafters on the FSDP2
+ * backend", "What this adds": all-gather the group's tokens, run the
+ * replicated router on them, compute only the locally owned experts for all
+ * of them, reduce-scatter the partial outputs]: the rank owns global experts
+ * [e_first, e_first + E_loc). An assignment whose id lies in that range goes
+ * to local expert idx - e_first, packed as in oracle_permute; any other is
+ * dropped (dest = -1). Fails (-1) on a bad range.
+ */
+int oracle_permute_range(const int32_t* idx, int64_t TK, int e_first, int E_loc,
+                         int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* dest);
+
+/*
  * Receive-side reorder [Three axes of Parallelism, "Dispatch, expert
  * computation and combine"; Modalities PR "expert parallelism for the
  * Nemotron-3 Nano MoE layers", section "Design"]: recv[i,j] rows came from

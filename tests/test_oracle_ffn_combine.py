@@ -213,3 +213,28 @@ def test_capacity_sampled_layer_equals_full_layer():
     toks = np.array([0, 5, 17, 100, 279], np.int32)
     part = oracle.moe_layer(inp, tokens=toks, capacity=30)
     np.testing.assert_array_equal(part["out"], full["out"][toks])
+
+
+def test_partial_layers_of_all_ranks_sum_to_the_full_layer():
+    """All-gather / reduce-scatter layout: the reduce-scatter sums the ranks'
+    partial outputs, which must give the layer over all experts."""
+    inp = W.generate(W.get("qwen3_small"))
+    full = oracle.moe_layer(inp)
+    E = inp["w_gate"].shape[0]
+    R = 4
+    E_loc = E // R
+    total = np.zeros_like(full["out"])
+    for r in range(R):
+        e0 = r * E_loc
+        part = dict(inp, w_gate=inp["w_gate"][e0:e0 + E_loc], w_val=inp["w_val"][e0:e0 + E_loc],
+                    w_out=inp["w_out"][e0:e0 + E_loc])
+        total += oracle.moe_partial_layer(part, e0)["out"]
+    np.testing.assert_allclose(total, full["out"], rtol=1e-12, atol=1e-12)
+
+
+def test_partial_layer_sampled_equals_full():
+    inp = W.generate(W.get("ag_rs_small"))
+    full = oracle.moe_partial_layer(inp, inp["e_first"])
+    toks = np.array([0, 7, 150, 299], np.int32)
+    part = oracle.moe_partial_layer(inp, inp["e_first"], tokens=toks)
+    np.testing.assert_array_equal(part["out"], full["out"][toks])

@@ -158,3 +158,27 @@ def test_capacity_at_least_every_count_is_the_plain_pack(name):
 def test_capacity_rejects_negative():
     with pytest.raises(RuntimeError):
         oracle.permute_capacity(np.zeros((2, 1), np.int32), 1, -1)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_range_packing_is_the_ranks_slice_of_the_global_packing(seed):
+    """All-gather layout: rank r owns experts [r*E_loc, (r+1)*E_loc). Its packing
+    is exactly its experts' slice of the global packing, shifted to start at 0,
+    and every assignment is kept by exactly one rank."""
+    rng = np.random.default_rng(seed)
+    R, E_loc, T, k = 4, 3, 57, 3
+    E = R * E_loc
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    g_counts, g_off, g_src, g_dest = oracle.permute(idx, E)
+    owners = np.zeros(T * k, np.int64)
+    for r in range(R):
+        e0 = r * E_loc
+        counts, offsets, perm_src, dest = oracle.permute_range(idx, e0, E_loc)
+        np.testing.assert_array_equal(counts, g_counts[e0:e0 + E_loc])
+        lo, hi = g_off[e0], g_off[e0 + E_loc]
+        np.testing.assert_array_equal(perm_src, g_src[lo:hi])
+        mine = (idx.reshape(-1) >= e0) & (idx.reshape(-1) < e0 + E_loc)
+        np.testing.assert_array_equal(dest[mine], g_dest[mine] - lo)
+        assert (dest[~mine] == -1).all()
+        owners += mine
+    assert (owners == 1).all()
