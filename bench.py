@@ -7,7 +7,9 @@ One step = one pass of the whole hot path over one batch: router (scores,
 top-k, weights) -> expert-major packing -> grouped SwiGLU gate/up -> down ->
 weighted combine (plus the shared experts where the workload has them; the
 receive-side workload runs the device reorder instead of router + packing and
-un-permutes back to sender-major order). Inputs are seeded synthetic tensors
+un-permutes back to sender-major order; the gathered-token workload routes every
+gathered token over the whole expert set, packs only the rank's own experts and
+combines into the rank's partial output). Inputs are seeded synthetic tensors
 already resident in HBM; every buffer is allocated before timing, so the timed
 region is kernel launches only. Per-stage times come from HIP events recorded
 on the stream the kernels are launched on. Prints one JSON line on stdout.
@@ -49,6 +51,9 @@ def parse():
     ap.add_argument("--y-dtype", choices=("f32", "bf16"), default="f32",
                     help="storage type of the expert outputs y_perm between the down GEMM "
                          "and the combine (bf16 inputs only)")
+    ap.add_argument("--partial-dtype", choices=("f32", "bf16"), default="bf16",
+                    help="gathered-token workload: type of the partial output that the "
+                         "reduce-scatter would sum")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU work of the oracle baseline sample")
@@ -79,13 +84,16 @@ def to_dev(a, torch):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def stage_work(cfg, counts, es, ys=4, kept=None):
+def stage_work(cfg, counts, es, ys=4, kept=None, os_=4, touched=None):
     """Algorithmic flops and bytes of one launch of each stage: what the method
     must compute or move (s = element size, TK = T*k rows, n_act = experts with
     rows). Router 2*T*d*E flop; packing (T + TK)*d*s bytes + indices; gate_up
     4*TK*d*f flop over TK*d*s + n_act*2*d*f*s + TK*f*s bytes; down 2*TK*f*d flop
-    over TK*f*s + n_act*f*d*s + TK*d*ys bytes; combine TK*d*ys + T*d*4 bytes
-    (ys = element size of the stored expert outputs)."""
+    over TK*f*s + n_act*f*d*s + TK*d*ys bytes; combine TK*d*ys + T*d*os bytes
+    (ys, os = element sizes of the stored expert outputs and of the layer
+    output). For a rank of the all-gather layout the router spans the whole
+    expert set, TK is the rank's kept assignments, and the packing reads only
+    the ``touched`` tokens that have at least one of them."""
     T, k, d, f, E = cfg.T, cfg.k, cfg.d, cfg.f, cfg.E
     rows = cfg.rows if kept is None else kept   # packed rows the experts process
     active = int((counts > 0).sum())
@@ -95,6 +103,14 @@ def stage_work(cfg, counts, es, ys=4, kept=None):
                           bytes=T * d * es + d * E * es + E * 4 + T * E * 4 + 2 * T * k * 4,
                           bound="alu")
         w["permute"] = dict(flops=0.0, bytes=(T + rows) * d * es + 4 * cfg.rows * 4, bound="hbm")
+    elif cfg.kind == "gathered":
+        Eg = cfg.E_global
+        w["route"] = dict(flops=2.0 * T * d * Eg,
+                          bytes=T * d * es + d * Eg * es + Eg * 4 + T * Eg * 4 + 2 * T * k * 4,
+                          bound="alu")
+        # idx read + dest written for every assignment, perm_src for the kept
+        w["permute"] = dict(flops=0.0, bytes=(touched + rows) * d * es + 2 * T * k * 4 + rows * 4,
+                            bound="hbm")
     else:
         w["permute_recv"] = dict(flops=0.0, bytes=2 * rows * d * es + 2 * rows * 4, bound="hbm")
     w["gate_up"] = dict(flops=4.0 * rows * d * f,
@@ -106,9 +122,10 @@ def stage_work(cfg, counts, es, ys=4, kept=None):
         w["shared_gate_up"] = dict(flops=4.0 * T * d * fs,
                                    bytes=T * d * es + 2 * d * fs * es + T * fs * es)
         w["shared_down"] = dict(flops=2.0 * T * fs * d, bytes=T * fs * es + fs * d * es + T * d * 4)
-    units = T if cfg.kind == "routed" else rows
+    units = cfg.units
+    idx_bytes = T * k * 8 if cfg.kind == "gathered" else rows * 8
     w["combine"] = dict(flops=2.0 * rows * d,
-                        bytes=rows * d * ys + units * d * 4 + rows * 8
+                        bytes=rows * d * ys + units * d * os_ + idx_bytes
                         + (units * d * 4 if cfg.shared else 0), bound="hbm")
     mfma_peak = PEAK_MFMA_BF16_TFS if es == 2 else PEAK_MFMA_F32_TFS
     for name, v in w.items():
@@ -162,6 +179,13 @@ def cpu_baseline(cfg, inp, target_s: float):
             oracle.moe_layer(sub)
             return time.perf_counter() - t
         total = cfg.T
+    elif cfg.kind == "gathered":
+        def run(n):
+            sub = dict(inp, x=inp["x"][:n])
+            t = time.perf_counter()
+            oracle.moe_partial_layer(sub, cfg.e_first)
+            return time.perf_counter() - t
+        total = cfg.T
     else:
         def run(n):
             t = time.perf_counter()
@@ -177,7 +201,7 @@ def cpu_baseline(cfg, inp, target_s: float):
     while n == total and t < 0.6 * target_s and reps < 30:
         t += run(n)
         reps += 1
-    unit_name = "tokens" if cfg.kind == "routed" else "rows"
+    unit_name = {"routed": "tokens", "gathered": "gathered tokens"}.get(cfg.kind, "rows")
     what = (f"all {total}" if n == total else f"first {n} of {total}")
     return dict(value=reps * n / t, unit=f"{unit_name}/s", cores=oracle.num_threads(), kind="oracle",
                 sample=f"{what} {unit_name} of the same workload (same weights), whole layer "
@@ -221,16 +245,20 @@ def main():
     ys = 2 if (args.y_dtype == "bf16" and es == 2) else 4
     y = torch.empty((rows, d), dtype=torch.bfloat16 if ys == 2 else torch.float32, device=cuda)
     units = cfg.units
-    out = torch.empty((units, d), dtype=torch.float32, device=cuda)
+    gathered = cfg.kind == "gathered"
+    os_ = 2 if (gathered and args.partial_dtype == "bf16") else 4
+    out = torch.empty((units, d), dtype=torch.bfloat16 if os_ == 2 else torch.float32, device=cuda)
     shared = None
-    if cfg.kind == "routed":
-        logits = torch.empty((cfg.T, E), dtype=torch.float32, device=cuda)
+    e_first = cfg.e_first if gathered else None
+    if cfg.kind in ("routed", "gathered"):
+        Er = cfg.E_global if gathered else E   # experts the router scores
+        logits = torch.empty((cfg.T, Er), dtype=torch.float32, device=cuda)
         idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=cuda)
         gates = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=cuda)
         ws = torch.empty(max(1, ops.permute_workspace(cfg.T, cfg.k, E)), dtype=torch.uint8,
                          device=cuda)
         cap = None
-        if args.capacity_factor is not None:
+        if args.capacity_factor is not None and not gathered:
             cap = int(np.ceil(args.capacity_factor * cfg.T * cfg.k / E))
             bufs["routed"] = torch.empty(E, dtype=torch.int32, device=cuda)
         if cfg.shared:
@@ -242,17 +270,17 @@ def main():
                 h=torch.empty((cfg.T, cfg.shared * f), dtype=xdt, device=cuda),
                 y=torch.empty((cfg.T, d), dtype=torch.float32, device=cuda))
 
-    stages = (["route", "permute"] if cfg.kind == "routed" else ["permute_recv"]) + \
+    stages = (["route", "permute"] if cfg.kind != "recv" else ["permute_recv"]) + \
         ["gate_up", "down"] + (["shared_gate_up", "shared_down"] if shared else []) + ["combine"]
 
     def step(ev=None):
         i = 0
         if ev is not None:
             ev[0].record()
-        if cfg.kind == "routed":
+        if cfg.kind != "recv":
             ops.route(dev["x"], dev["w_router"], dev["bias"], cfg.k, out=(logits, idx, gates))
             if ev is not None: ev[1].record()
-            ops.permute(idx, dev["x"], E, capacity=cap, out=bufs, workspace=ws)
+            ops.permute(idx, dev["x"], E, capacity=cap, e_first=e_first, out=bufs, workspace=ws)
             i = 2
         else:
             ops.permute_recv(dev["recv_counts"], dev["x_recv"], out=bufs)
@@ -271,7 +299,7 @@ def main():
             if ev is not None: ev[i + 1].record()
             i += 2
             y_sh = shared["y"]
-        if cfg.kind == "routed":
+        if cfg.kind != "recv":
             ops.combine(y, bufs["dest"], gates, cfg.k, y_shared=y_sh, out=out)
         else:
             ops.combine(y, bufs["dest"], None, 1, out=out)
@@ -301,7 +329,10 @@ def main():
 
     counts = bufs["counts"].cpu().numpy()
     kept = int(counts.sum())
-    work = stage_work(cfg, counts, es, ys, kept)
+    touched = None
+    if gathered:
+        touched = int((bufs["dest"].view(cfg.T, cfg.k) >= 0).any(dim=1).sum().item())
+    work = stage_work(cfg, counts, es, ys, kept, os_, touched)
     stage_rep = {}
     for name in stages:
         r = roofline_entry(work[name], stage_us[name], es)
@@ -320,7 +351,8 @@ def main():
     res = {
         "metric": METRIC,
         "value": round(value, 1),
-        "unit": "tokens/s" if cfg.kind == "routed" else "received rows/s",
+        "unit": {"routed": "tokens/s", "gathered": "gathered tokens/s"}.get(cfg.kind,
+                                                                           "received rows/s"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -332,10 +364,14 @@ def main():
         "data": "synthetic (seeded Gaussian inputs and weights of the stated shapes)",
         "config": {"workload": cfg.name, "description": cfg.description,
                    "y_perm_dtype": "bf16" if ys == 2 else "f32",
-                   "capacity_factor": args.capacity_factor, "kept_rows": kept, "T": cfg.T,
+                   "capacity_factor": None if gathered else args.capacity_factor,
+                   "kept_rows": kept, "T": cfg.T,
                    "k": cfg.k, "N": cfg.N, "d": d, "f": f, "E": E, "shared": cfg.shared,
                    "rows": rows, "load_max_over_mean": round(float(counts.max() / max(counts.mean(), 1e-9)), 3),
                    "empty_experts": int((counts == 0).sum())},
+        **({"partial": {"E_global": cfg.E_global, "e_first": cfg.e_first,
+                        "partial_dtype": "bf16" if os_ == 2 else "f32",
+                        "tokens_with_local_expert": touched}} if gathered else {}),
         "roofline": {"kernel": dominant, "bound": dom["bound"], "achieved": round(dom["achieved"], 1),
                      "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4),
                      "traffic": traffic},

@@ -10,8 +10,8 @@ hipError_t launch_route(const void* x, moe_dtype dt, const void* w, const float*
                         int d, int E, int k, int renorm, float* logits, int32_t* idx,
                         float* gates, hipStream_t st);
 size_t permute_ws_bytes(int T, int k, int E);
-hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int cap, const void* x,
-                          int es, int d, int32_t* routed,
+hipError_t launch_permute(const int32_t* idx, int T, int k, int e_base, int E, int cap,
+                          const void* x, int es, int d, int32_t* routed,
                           int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* dest,
                           void* x_perm, void* ws, hipStream_t st);
 hipError_t launch_permute_recv(const int32_t* recv, int S, int E, int N, const void* x, int es,
@@ -92,7 +92,7 @@ moe_status moe_permute(const int32_t* topk_idx, int T, int k, int E, const void*
     if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
     if (T > 0 && (!topk_idx || !x || !perm_src || !dest || !x_perm)) return MOE_ERR_INVALID_ARG;
     if (!ws || ws_bytes < moe::permute_ws_bytes(T, k, E)) return MOE_ERR_WORKSPACE;
-    return hip_status(moe::launch_permute(topk_idx, T, k, E, INT32_MAX, x, elem_size(dt), d,
+    return hip_status(moe::launch_permute(topk_idx, T, k, 0, E, INT32_MAX, x, elem_size(dt), d,
                                           nullptr, counts, offsets, perm_src, dest, x_perm, ws,
                                           as_stream(stream)));
 }
@@ -109,9 +109,25 @@ moe_status moe_permute_capacity(const int32_t* topk_idx, int T, int k, int E, in
     if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
     if (T > 0 && (!topk_idx || !x || !perm_src || !dest || !x_perm)) return MOE_ERR_INVALID_ARG;
     if (!ws || ws_bytes < moe::permute_ws_bytes(T, k, E)) return MOE_ERR_WORKSPACE;
-    return hip_status(moe::launch_permute(topk_idx, T, k, E, capacity, x, elem_size(dt), d,
+    return hip_status(moe::launch_permute(topk_idx, T, k, 0, E, capacity, x, elem_size(dt), d,
                                           routed, counts, offsets, perm_src, dest, x_perm, ws,
                                           as_stream(stream)));
+}
+
+moe_status moe_permute_range(const int32_t* topk_idx, int T, int k, int e_first, int E_loc,
+                             const void* x, moe_dtype dt, int d, int32_t* counts,
+                             int32_t* offsets, int32_t* perm_src, int32_t* dest, void* x_perm,
+                             void* ws, size_t ws_bytes, void* stream)
+{
+    if (!valid_dtype(dt) || T < 0 || k <= 0 || E_loc <= 0 || e_first < 0 || d <= 0)
+        return MOE_ERR_INVALID_ARG;
+    if (E_loc > kMaxRouteE || k > kMaxK || (long long)T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
+    if (T > 0 && (!topk_idx || !x || !perm_src || !dest || !x_perm)) return MOE_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < moe::permute_ws_bytes(T, k, E_loc)) return MOE_ERR_WORKSPACE;
+    return hip_status(moe::launch_permute(topk_idx, T, k, e_first, E_loc, INT32_MAX, x,
+                                          elem_size(dt), d, nullptr, counts, offsets, perm_src,
+                                          dest, x_perm, ws, as_stream(stream)));
 }
 
 size_t moe_permute_recv_workspace(int S, int E_loc, int N) {

@@ -36,9 +36,11 @@ constexpr int kPermSmallTK = 65536;   // up to this many assignments: 1024-chunk
 // assignments per ranking block
 static int perm_chunk(long long TK) { return TK <= kPermSmallTK ? 1024 : 4096; }
 
+// e_base: the packing covers global expert ids [e_base, e_base + E) (an
+// expert-parallel rank's range); any other id is dropped.
 template <int CHUNK>
 __global__ __launch_bounds__(kPermThreads) void perm_hist_kernel(
-    const int32_t* __restrict__ idx, int TK, int E, int32_t* __restrict__ bc)
+    const int32_t* __restrict__ idx, int TK, int e_base, int E, int32_t* __restrict__ bc)
 {
     constexpr int kPermIters = CHUNK / kPermThreads;
     __shared__ int h[kPermMaxE];
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(kPermThreads) void perm_hist_kernel(
     for (int q = 0; q < kPermIters; ++q) {
         const int a = base + threadIdx.x + q * kPermThreads;
         if (a < TK) {
-            const int e = idx[a];
+            const int e = idx[a] - e_base;
             if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
         }
     }
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(kPermThreads) void perm_hist_kernel(
 // all); routed (may be null) receives the per-expert counts before the cap.
 template <int CHUNK>
 __global__ __launch_bounds__(kPermThreads) void perm_rank_kernel(
-    const int32_t* __restrict__ idx, int TK, int E, int nbits, int cap,
+    const int32_t* __restrict__ idx, int TK, int e_base, int E, int nbits, int cap,
     const int32_t* __restrict__ bc, int nb,
     int32_t* __restrict__ routed, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm_src, int32_t* __restrict__ dest)
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(kPermThreads) void perm_rank_kernel(
 #pragma unroll
     for (int it = 0; it < kPermIters; ++it) {
         const int a = a0 + it * kWave + lane;
-        int e = (a < TK) ? idx[a] : -1;
+        int e = (a < TK) ? idx[a] - e_base : -1;
         const bool valid = (unsigned)e < (unsigned)E;
         if (!valid) e = -1;
         unsigned long long m = ballot(valid);
@@ -272,23 +274,23 @@ size_t permute_ws_bytes(int T, int k, int E) {
     return align_up((size_t)(nb * E) * sizeof(int32_t), 256);
 }
 
-hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int cap, const void* x,
-                          int es, int d, int32_t* routed, int32_t* counts, int32_t* offsets,
-                          int32_t* perm_src, int32_t* dest, void* x_perm, void* ws,
-                          hipStream_t st)
+hipError_t launch_permute(const int32_t* idx, int T, int k, int e_base, int E, int cap,
+                          const void* x, int es, int d, int32_t* routed, int32_t* counts,
+                          int32_t* offsets, int32_t* perm_src, int32_t* dest, void* x_perm,
+                          void* ws, hipStream_t st)
 {
     const int TK = T * k;
     const int chunk = perm_chunk(TK);
     const int nb = std::max(1, (TK + chunk - 1) / chunk);
     int32_t* bc = static_cast<int32_t*>(ws);
     if (chunk == 1024) {
-        perm_hist_kernel<1024><<<nb, kPermThreads, 0, st>>>(idx, TK, E, bc);
-        perm_rank_kernel<1024><<<nb, kPermThreads, 0, st>>>(idx, TK, E, ceil_log2(E), cap, bc,
+        perm_hist_kernel<1024><<<nb, kPermThreads, 0, st>>>(idx, TK, e_base, E, bc);
+        perm_rank_kernel<1024><<<nb, kPermThreads, 0, st>>>(idx, TK, e_base, E, ceil_log2(E), cap, bc,
                                                             nb, routed, counts, offsets,
                                                             perm_src, dest);
     } else {
-        perm_hist_kernel<4096><<<nb, kPermThreads, 0, st>>>(idx, TK, E, bc);
-        perm_rank_kernel<4096><<<nb, kPermThreads, 0, st>>>(idx, TK, E, ceil_log2(E), cap, bc,
+        perm_hist_kernel<4096><<<nb, kPermThreads, 0, st>>>(idx, TK, e_base, E, bc);
+        perm_rank_kernel<4096><<<nb, kPermThreads, 0, st>>>(idx, TK, e_base, E, ceil_log2(E), cap, bc,
                                                             nb, routed, counts, offsets,
                                                             perm_src, dest);
     }

@@ -44,6 +44,7 @@ def lib():
         "moe_route": [vp, i, vp, vp, i, i, i, i, i, vp, vp, vp, vp],
         "moe_permute": [vp, i, i, i, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_permute_capacity": [vp, i, i, i, i, vp, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "moe_permute_range": [vp, i, i, i, i, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_permute_recv": [vp, i, i, i, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_grouped_ffn": [vp, i, i, i, i, i, vp, vp, vp, vp, vp, i, vp, sz, vp],
         "moe_ffn_gate_up": [vp, i, i, i, i, i, vp, vp, vp, vp, vp],
@@ -116,10 +117,12 @@ def permute_workspace(T: int, k: int, E: int) -> int:
     return int(lib().moe_permute_workspace(T, k, E))
 
 
-def permute(topk_idx, x, E: int, *, capacity=None, out=None, workspace=None, stream=None):
+def permute(topk_idx, x, E: int, *, capacity=None, e_first=None, out=None, workspace=None,
+            stream=None):
     """Expert-major packing. Returns dict(counts, offsets, perm_src, dest, x_perm);
     with ``capacity`` (fixed-capacity packing) also ``routed``, the counts
-    before the cap."""
+    before the cap. With ``e_first`` only global experts [e_first, e_first + E)
+    are packed (one rank of the all-gather layout)."""
     _dev(topk_idx, "topk_idx"); _dev(x, "x")
     T, k = topk_idx.shape
     d = x.shape[1]
@@ -135,7 +138,12 @@ def permute(topk_idx, x, E: int, *, capacity=None, out=None, workspace=None, str
     nbytes = permute_workspace(T, k, E)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    if capacity is None:
+    if e_first is not None:
+        _check("moe_permute_range", lib().moe_permute_range(
+            _p(topk_idx), T, k, int(e_first), E, _p(x), _dt(x), d, _p(out["counts"]),
+            _p(out["offsets"]), _p(out["perm_src"]), _p(out["dest"]), _p(out["x_perm"]),
+            _p(workspace), workspace.numel(), _stream(stream)))
+    elif capacity is None:
         _check("moe_permute", lib().moe_permute(
             _p(topk_idx), T, k, E, _p(x), _dt(x), d, _p(out["counts"]), _p(out["offsets"]),
             _p(out["perm_src"]), _p(out["dest"]), _p(out["x_perm"]), _p(workspace),
@@ -225,6 +233,20 @@ def combine(y_perm, dest, gates, k: int, *, y_shared=None, out_dtype=torch.float
         _p(y_perm), _dt(y_perm), _p(dest), _p(gates), T, k, d, _p(y_shared), sh_dt, _p(out),
         _dt(out), _stream(stream)))
     return out
+
+
+def moe_partial_layer(x, w_router, bias, k: int, e_first: int, w_gate, w_val, w_out, *,
+                      y_dtype=torch.float32, out_dtype=torch.float32, stream=None):
+    """One rank of the all-gather / reduce-scatter layout: the replicated router
+    over the gathered tokens, the rank's local experts (global ids e_first..,
+    weights w_gate etc.), the combine into this rank's partial output."""
+    E_loc = w_gate.shape[0]
+    logits, idx, gates = route(x, w_router, bias, k, stream=stream)
+    p = permute(idx, x, E_loc, e_first=e_first, stream=stream)
+    y = grouped_ffn(p["x_perm"], p["offsets"], w_gate, w_val, w_out, y_dtype=y_dtype,
+                    stream=stream)
+    out = combine(y, p["dest"], gates, k, out_dtype=out_dtype, stream=stream)
+    return dict(logits=logits, idx=idx, gates=gates, y=y, out=out, **p)
 
 
 def moe_layer(x, w_router, bias, k: int, w_gate, w_val, w_out, *, shared=None, capacity=None,

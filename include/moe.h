@@ -124,6 +124,25 @@ moe_status moe_permute_capacity(const int32_t* topk_idx, int T, int k, int E, in
                                 void* stream);
 
 /*
+ * Packing of one rank's expert range in the all-gather / reduce-scatter
+ * layout (SpecForge PR "expert parallelism for MoE drafters on the FSDP2
+ * backend", What this adds: all-gather the group's tokens, run the
+ * replicated router on them, compute only the locally owned experts for all
+ * of them, reduce-scatter the partial outputs). The rank owns global experts
+ * [e_first, e_first + E_loc): an assignment with an id in that range goes to
+ * local expert id - e_first; any other is dropped (dest = -1, no packed row;
+ * moe_combine skips it, so its output is this rank's partial sum).
+ * Arguments as moe_permute with counts [E_loc], offsets [E_loc+1]; the
+ * workspace is moe_permute_workspace(T, k, E_loc). perm_src is defined for
+ * packed rows j < offsets[E_loc].
+ * Limits: e_first >= 0, 1 <= E_loc <= 1024, k <= 32.
+ */
+moe_status moe_permute_range(const int32_t* topk_idx, int T, int k, int e_first, int E_loc,
+                             const void* x, moe_dtype dt, int d, int32_t* counts,
+                             int32_t* offsets, int32_t* perm_src, int32_t* dest, void* x_perm,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Receive-side reorder ("Three axes of Parallelism", Dispatch, expert
  * computation and combine: recv_matrix[i,j] = rows sender i sent to local
  * expert j; the received buffer is source-major and is permuted expert-major,

@@ -25,7 +25,8 @@ def L():
 
 def test_header_declares_the_path():
     names = _declared()
-    for n in ("moe_route", "moe_permute", "moe_permute_capacity", "moe_permute_recv",
+    for n in ("moe_route", "moe_permute", "moe_permute_capacity", "moe_permute_range",
+              "moe_permute_recv",
               "moe_grouped_ffn", "moe_combine"):
         assert n in names
 
@@ -68,6 +69,11 @@ def test_host_side_errors_return_before_launch(L):
                                   fake, fake, fake, need, None) == 1
     assert L.moe_permute_capacity(fake, 100, 2, 8, 10, fake, 1, 64, None, fake, fake, fake,
                                   fake, fake, fake, need - 1, None) == 3
+    # range packing: negative first expert, E_loc too large
+    assert L.moe_permute_range(fake, 100, 2, -1, 8, fake, 1, 64, fake, fake, fake, fake, fake,
+                               fake, need, None) == 1
+    assert L.moe_permute_range(fake, 100, 2, 0, 2048, fake, 1, 64, fake, fake, fake, fake, fake,
+                               fake, need, None) == 2
     # permute_recv: too many cells
     assert L.moe_permute_recv(fake, 64, 128, 10, fake, 1, 64, fake, fake, fake, fake, fake,
                               None, 0, None) == 2

@@ -18,7 +18,8 @@ import torch
 import oracle
 from expert_dispatch_amd import ops
 from expert_dispatch_amd import workloads as W
-from util import check_float, err_bf16, sample_rows, to_numpy, to_torch, widen, err_f32
+from util import (check_bf16_stored, check_float, err_bf16, err_f32, sample_rows, to_numpy,
+                  to_torch, widen)
 
 pytestmark = pytest.mark.gpu
 
@@ -147,6 +148,57 @@ def test_capacity_zero_drops_everything():
 @pytest.mark.parametrize("name,factor", [("qwen3_30b_a3b", 1.0), ("stress_zipf", 1.25)])
 def test_capacity_layer_full(name, factor):
     _check_routed(name, full=True, capacity=_capacity(name, factor))
+
+
+def _check_partial(name, full, out_dtype):
+    """One rank of the all-gather / reduce-scatter layout against the oracle;
+    the partial output in fp32 or bf16 (the reduce-scatter's wire format)."""
+    cfg = W.get(name)
+    say(f"[parity] {name}: generate")
+    inp = _inputs(name)
+    dev = _device(inp)
+    say(f"[parity] {name}: gpu partial layer (experts {cfg.e_first}..{cfg.e_first + cfg.E - 1}, "
+        f"partials {out_dtype})")
+    g = ops.moe_partial_layer(dev["x"], dev["w_router"], dev.get("bias"), cfg.k, cfg.e_first,
+                              dev["w_gate"], dev["w_val"], dev["w_out"], out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    T, k = cfg.T, cfg.k
+    tokens = None
+    if full:
+        rng = np.random.default_rng(0)
+        tokens = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, size=96)])).astype(np.int32)
+    say(f"[parity] {name}: oracle")
+    o = oracle.moe_partial_layer(inp, cfg.e_first, tokens=tokens)
+    kept = int(o["offsets"][-1])
+    np.testing.assert_array_equal(to_numpy(g["logits"]).view(np.uint32), o["logits"].view(np.uint32))
+    np.testing.assert_array_equal(to_numpy(g["idx"]), o["idx"])
+    for key in ("counts", "offsets", "dest"):
+        np.testing.assert_array_equal(to_numpy(g[key]), o[key], err_msg=key)
+    np.testing.assert_array_equal(to_numpy(g["perm_src"])[:kept], o["perm_src"][:kept])
+    if full:
+        rows_t = torch.from_numpy(o["y_rows"]).to("cuda")
+        xp = to_numpy(g["x_perm"].index_select(0, rows_t))
+        y = to_numpy(g["y"].index_select(0, rows_t))
+    else:
+        xp = to_numpy(g["x_perm"])[:kept]
+        y = to_numpy(g["y"])[:kept]
+    np.testing.assert_array_equal(xp, o["x_perm"])
+    ey = check_float(y, o["y"], cfg.dtype, f"{name} y_perm")
+    out = to_numpy(g["out"])[o["tokens"]]
+    if out_dtype == torch.bfloat16:
+        eo = check_bf16_stored(out, o["out"], f"{name} partial out (bf16)")
+    else:
+        eo = check_float(out, o["out"], cfg.dtype, f"{name} partial out")
+    say(f"[parity] {name}: keeps {kept} of {T * k} assignments; ok y_err={ey:.3e} out_err={eo:.3e}")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_partial_layer_small(out_dtype):
+    _check_partial("ag_rs_small", full=False, out_dtype=out_dtype)
+
+
+def test_partial_layer_full():
+    _check_partial("ag_rs_rank", full=True, out_dtype=torch.bfloat16)
 
 
 def _check_recv(name, full, zero_col=None):

@@ -66,6 +66,27 @@ def check_float(got, ref, dtype: str, what: str):
     return e
 
 
+U_BF16 = 2.0 ** -8   # unit roundoff of bf16 (8 significant bits, round to nearest)
+
+
+def check_bf16_stored(got, ref, what: str):
+    """Parity gate of an output the method stores in bf16 (a partial sum on its
+    way to the reduce-scatter). The stored value is the computed one rounded
+    once more, which moves it by at most U_BF16 of its own magnitude; that
+    rounding is taken off each element's error before the usual bf16 bar:
+    max_i (|got_i - ref_i| - U*|ref_i|)+ / (1 + U) <= TOL_BF16 * rms(ref)."""
+    got = widen(got) if got.dtype == np.uint16 else np.asarray(got, np.float64)
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if not ref.size:
+        return 0.0
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    excess = np.maximum(np.abs(got - ref) - U_BF16 * np.abs(ref), 0.0) / (1 + U_BF16)
+    e = float(excess.max()) / max(rms, 1e-30)
+    assert e <= TOL_BF16, f"{what}: max (err - rounding) / rms {e:.3e} > {TOL_BF16}"
+    return e
+
+
 def sample_rows(offsets: np.ndarray, per_expert: int, rng) -> np.ndarray:
     """First and last packed row of every non-empty expert plus random rows."""
     rows = []
