@@ -16,7 +16,11 @@ Sources followed (page title, section):
     MLPs, and the weighted sum of the K expert outputs per token.
   * same page, Mapping experts to EP ranks: W_gate, W_val [E,d,f], W_out [E,f,d].
   * "feat(parallelism): expert parallelism for the Nemotron-3 Nano MoE layers",
-    Design: the device-built permutation indices for the received buffer.
+    Design: the device-built permutation indices for the received buffer, and
+    autograd through the index_select / index_copy permutation pair.
+  * "Three axes of Parallelism", EP backward pass: expert gradients divided by
+    the EP group size. The backward itself is the chain rule on the forward
+    definitions (no page writes it out); see oracle.h.
 """
 from __future__ import annotations
 
@@ -67,10 +71,22 @@ def lib():
                                              ctypes.c_int64, ctypes.c_int, vp]
         L.oracle_combine.argtypes = [vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, vp, vp,
                                      vp, vp, vp, vp]
+        i64, i32 = ctypes.c_int64, ctypes.c_int
+        L.oracle_route_backward.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, vp]
+        L.oracle_router_grads.argtypes = [vp, vp, i32, i64, i32, i32, vp, vp, i64, vp, vp]
+        L.oracle_combine_backward_gates.argtypes = [vp, i64, i32, i64, vp, vp, vp, vp, vp]
+        L.oracle_combine_backward_rows.argtypes = [vp, vp, i64, i32, i64, vp, vp, vp]
+        L.oracle_expert_ffn_backward_rows.argtypes = [vp, i32, i64, i32, i32, i32, vp, vp, vp,
+                                                      vp, vp, i64, i32, vp, vp, vp, vp]
+        L.oracle_expert_weight_grads.argtypes = [vp, i32, i64, i32, i32, i32, vp, vp, vp, vp,
+                                                 vp, vp, vp, i64, ctypes.c_double, vp, vp, vp]
         for name in ("oracle_route", "oracle_permute", "oracle_permute_capacity",
                      "oracle_permute_range",
                      "oracle_permute_recv", "oracle_gather",
-                     "oracle_expert_ffn_rows", "oracle_combine"):
+                     "oracle_expert_ffn_rows", "oracle_combine",
+                     "oracle_route_backward", "oracle_router_grads",
+                     "oracle_combine_backward_gates", "oracle_combine_backward_rows",
+                     "oracle_expert_ffn_backward_rows", "oracle_expert_weight_grads"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -353,3 +369,194 @@ def moe_recv_layer(inp: dict, rows=None):
     out = combine(r, 1, dest, None, y_rows, yrow, None)
     return dict(counts=counts, offsets=offsets, perm_src=perm_src, dest=dest, x_perm=x_perm,
                 y_rows=need, y=y_rows, rows=r, out=out)
+
+
+# ------------------------------------------------------------------ backward
+
+def widen(a) -> np.ndarray:
+    """fp32 or bf16-bit-pattern (uint16) array -> float64, exactly."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def route_backward(logits, idx, gates, d_gates, renorm: bool = True):
+    """d_logits [T,E] float64 from the router-weight gradients d_gates [T,k]."""
+    logits = _c(logits, np.float32)
+    idx = _c(idx, np.int32)
+    T, E = logits.shape
+    k = idx.shape[1]
+    g = _c(gates, np.float64)
+    dg = _c(d_gates, np.float64)
+    out = np.empty((T, E), np.float64)
+    _check(lib().oracle_route_backward(_p(logits), _p(idx), _p(g), _p(dg), T, E, k,
+                                       int(bool(renorm)), _p(out)), "oracle_route_backward")
+    return out
+
+
+def router_grads(x, w, d_logits, want_dx=True, want_dw=True):
+    """(d_x [T,d], d_w [d,E]) of the router scores, float64; x holds the
+    tokens d_logits belongs to (row for row)."""
+    x, w = _c(x), _c(w)
+    xt = _xtype(x)
+    T, d = x.shape
+    E = w.shape[1]
+    dl = _c(d_logits, np.float64)
+    assert dl.shape == (T, E)
+    tok = np.arange(T, dtype=np.int32)
+    dx = np.empty((T, d), np.float64) if want_dx else None
+    dw = np.empty((d, E), np.float64) if want_dw else None
+    _check(lib().oracle_router_grads(_p(x), _p(w), xt, T, d, E, _p(dl), _p(tok), T, _p(dx),
+                                     _p(dw)), "oracle_router_grads")
+    return dx, dw
+
+
+def combine_backward_gates(tokens, k: int, dest, y, yrow, d_out_rows):
+    tokens = _c(tokens, np.int32)
+    dest = _c(np.asarray(dest).reshape(-1), np.int32)
+    y = _c(y, np.float64)
+    yr = None if yrow is None else _c(yrow, np.int64)
+    do = _c(d_out_rows, np.float64)
+    d = do.shape[1]
+    out = np.empty((tokens.shape[0], k), np.float64)
+    _check(lib().oracle_combine_backward_gates(_p(tokens), tokens.shape[0], k, d, _p(dest),
+                                               _p(y), _p(yr), _p(do), _p(out)),
+           "oracle_combine_backward_gates")
+    return out
+
+
+def combine_backward_rows(perm_src, rows, k: int, gates, d_out):
+    ps = _c(perm_src, np.int32)
+    rows = _c(rows, np.int64)
+    g = None if gates is None else _c(np.asarray(gates).reshape(-1), np.float64)
+    do = _c(d_out, np.float64)
+    d = do.shape[1]
+    out = np.empty((rows.shape[0], d), np.float64)
+    _check(lib().oracle_combine_backward_rows(_p(ps), _p(rows), rows.shape[0], k, d, _p(g),
+                                              _p(do), _p(out)), "oracle_combine_backward_rows")
+    return out
+
+
+def expert_ffn_backward_rows(x_perm, offsets, wg, wv, wo, d_y, rows=None, N=None):
+    """(act, d_act, d_x) of the listed packed rows, float64: act = [a | v]
+    [n,2f], d_act = [da | dv] [n,2f], d_x [n,d]. ``rows`` and ``N`` as in
+    expert_ffn_rows; d_y [n,d] the rows' output gradients."""
+    x_perm, wg, wv, wo = _c(x_perm), _c(wg), _c(wv), _c(wo)
+    xt = _xtype(x_perm)
+    compact = N is not None
+    if not compact:
+        N = x_perm.shape[0]
+    d = x_perm.shape[1]
+    E, _, f = wg.shape
+    off = _c(offsets, np.int32)
+    rows = np.arange(N, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    dy = _c(d_y, np.float64)
+    n = rows.shape[0]
+    act = np.empty((n, 2 * f), np.float64)
+    dact = np.empty((n, 2 * f), np.float64)
+    dx = np.empty((n, d), np.float64)
+    _check(lib().oracle_expert_ffn_backward_rows(_p(x_perm), xt, N, d, f, E, _p(off), _p(wg),
+                                                 _p(wv), _p(wo), _p(rows), n, int(compact),
+                                                 _p(dy), _p(act), _p(dact), _p(dx)),
+           "oracle_expert_ffn_backward_rows")
+    return act, dact, dx
+
+
+def expert_weight_grads(x_perm, offsets, wg, wv, wo, d_y, pairs, scale: float = 1.0):
+    """Weight gradients of the listed (expert, hidden column) pairs:
+    (dWg[e][:,c], dWv[e][:,c], dWo[e][c,:]), each float64 [P,d]. x_perm and
+    d_y hold every packed row."""
+    x_perm, wg, wv, wo = _c(x_perm), _c(wg), _c(wv), _c(wo)
+    xt = _xtype(x_perm)
+    N, d = x_perm.shape
+    E, _, f = wg.shape
+    off = _c(offsets, np.int32)
+    pairs = np.asarray(pairs, np.int64).reshape(-1, 2)
+    pe = _c(pairs[:, 0], np.int32)
+    pc = _c(pairs[:, 1], np.int32)
+    P = pe.shape[0]
+    dy = _c(d_y, np.float64)
+    assert dy.shape == (N, d)
+    outs = [np.empty((P, d), np.float64) for _ in range(3)]
+    _check(lib().oracle_expert_weight_grads(_p(x_perm), xt, N, d, f, E, _p(off), _p(wg),
+                                            _p(wv), _p(wo), _p(dy), _p(pe), _p(pc), P,
+                                            float(scale), *(_p(o) for o in outs)),
+           "oracle_expert_weight_grads")
+    return tuple(outs)
+
+
+def all_pairs(E: int, f: int) -> np.ndarray:
+    """Every (expert, hidden column) pair, expert-major."""
+    e, c = np.meshgrid(np.arange(E), np.arange(f), indexing="ij")
+    return np.stack([e.reshape(-1), c.reshape(-1)], axis=1)
+
+
+def moe_backward(inp: dict, d_out, tokens=None, pairs=None, scale: float = 1.0,
+                 capacity=None, e_first=None):
+    """Gradients of the loss L = sum(out * d_out) through the layer (or, with
+    ``e_first``, through one rank's partial output), in double.
+
+    With ``tokens`` None every token is evaluated: d_x [T,d], d_gates [T,k],
+    d_logits [T,E] and the router weight gradient d_w_router [d,E]. With
+    ``tokens`` given only those tokens' input and router gradients are formed
+    (from the packed rows they use, listed in ``y_rows``); d_w_router is then
+    None. ``pairs`` lists (expert, hidden column) pairs whose expert weight
+    gradients are formed over all packed rows (all_pairs(E, f) for all of
+    them), multiplied by ``scale``. Shared experts, where the workload has
+    them, add their input gradient to d_x; their weight gradients are the
+    same functions on the token rows (expert_weight_grads with offsets [0,T])."""
+    k = inp["k"]
+    renorm = inp.get("renorm", True)
+    x = inp["x"]
+    T = x.shape[0]
+    logits, idx, gates = route(x, inp["w_router"], inp.get("bias"), k, renorm)
+    E = inp["w_gate"].shape[0]
+    if e_first is not None:
+        counts, offsets, perm_src, dest = permute_range(idx, e_first, E)
+    elif capacity is not None:
+        _, counts, offsets, perm_src, dest = permute_capacity(idx, E, capacity)
+    else:
+        counts, offsets, perm_src, dest = permute(idx, E)
+    kept = int(offsets[E])
+    dout = widen(d_out)
+    full = tokens is None
+    tok = np.arange(T, dtype=np.int32) if full else _c(tokens, np.int32)
+    if full:
+        need = np.arange(kept, dtype=np.int64)
+    else:
+        need = np.unique(dest.reshape(T, k)[tok].reshape(-1)).astype(np.int64)
+        need = need[need >= 0]
+    wg, wv, wo = inp["w_gate"], inp["w_val"], inp["w_out"]
+    xp = gather(x, perm_src[need], k)
+    y = expert_ffn_rows(xp, offsets, wg, wv, wo, need, N=kept)
+    yrow = np.full(max(kept, 1), -1, np.int64)
+    yrow[need] = np.arange(need.shape[0])
+    # combine: out[t] = sum_s g[t,s] y[dest[t,s]]
+    d_gates = combine_backward_gates(tok, k, dest, y, yrow, dout[tok])
+    d_y = combine_backward_rows(perm_src, need, k, gates, dout)
+    act, d_act, d_xp = expert_ffn_backward_rows(xp, offsets, wg, wv, wo, d_y, need, N=kept)
+    # the packing's backward: each token sums the input gradients of its rows
+    d_x = combine(tok, k, dest, None, d_xp, yrow)
+    # router
+    d_logits = route_backward(logits[tok], idx[tok], gates[tok], d_gates, renorm)
+    dxr, dwr = router_grads(x[tok], inp["w_router"], d_logits, True, full)
+    d_x += dxr
+    if inp.get("shared_w_gate") is not None:
+        sg, sv, so = inp["shared_w_gate"], inp["shared_w_val"], inp["shared_w_out"]
+        for q in range(sg.shape[0]):
+            _, _, dxs = expert_ffn_backward_rows(x, np.array([0, T], np.int32), sg[q:q + 1],
+                                                 sv[q:q + 1], so[q:q + 1], dout[tok],
+                                                 tok.astype(np.int64))
+            d_x += dxs
+    res = dict(logits=logits, idx=idx, gates=gates, counts=counts, offsets=offsets,
+               perm_src=perm_src, dest=dest, tokens=tok, y_rows=need, y=y, d_y=d_y, act=act,
+               d_act=d_act, d_x_perm=d_xp, d_gates=d_gates, d_logits=d_logits, d_x=d_x,
+               d_w_router=dwr)
+    if pairs is not None:
+        xall = gather(x, perm_src, k)
+        dyall = combine_backward_rows(perm_src, np.arange(kept, dtype=np.int64), k, gates, dout)
+        res["pairs"] = np.asarray(pairs, np.int64).reshape(-1, 2)
+        res["d_w_gate"], res["d_w_val"], res["d_w_out"] = expert_weight_grads(
+            xall, offsets, wg, wv, wo, dyall, res["pairs"], scale)
+    return res

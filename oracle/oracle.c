@@ -315,3 +315,253 @@ int oracle_combine(const int32_t* tokens, int64_t ntok, int k, int64_t d,
     }
     return bad ? -3 : 0;
 }
+
+/* ---------------------------------------------------------------- backward
+ *
+ * The gradients of a scalar loss through the layer, by the chain rule on the
+ * definitions above, in double. The selection (top-k ids, packing) is
+ * piecewise constant in its inputs and passes no gradient; everything else
+ * is differentiated as written.
+ */
+
+int oracle_route_backward(const float* logits, const int32_t* idx, const double* gates,
+                          const double* d_gates, int64_t T, int E, int k, int renorm,
+                          double* d_logits)
+{
+    if (!logits || !idx || !gates || !d_gates || !d_logits) return -1;
+    if (T < 0 || E <= 0 || k <= 0 || k > E) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const int32_t* id = idx + (size_t)t * k;
+        const double* g = gates + (size_t)t * k;
+        const double* dg = d_gates + (size_t)t * k;
+        double* dl = d_logits + (size_t)t * E;
+        /* sum over the selected of g * dg: the part every logit shares */
+        double gdg = 0.0;
+        for (int s = 0; s < k; ++s) gdg += g[s] * dg[s];
+        for (int e = 0; e < E; ++e) dl[e] = 0.0;
+        if (renorm) {
+            /* g_s = exp(l_{e_s}) / sum_r exp(l_{e_r}):
+             * dg_s/dl_{e_r} = g_s (delta_sr - g_r) */
+            for (int s = 0; s < k; ++s) dl[id[s]] = g[s] * (dg[s] - gdg);
+        } else {
+            /* g_s = p_{e_s}, p = softmax over all E: dp_a/dl_b = p_a (delta_ab - p_b) */
+            const float* l = logits + (size_t)t * E;
+            double m = (double)l[id[0]];
+            double denom = 0.0;
+            for (int e = 0; e < E; ++e) denom += exp((double)l[e] - m);
+            for (int e = 0; e < E; ++e) dl[e] = -(exp((double)l[e] - m) / denom) * gdg;
+            for (int s = 0; s < k; ++s) dl[id[s]] += g[s] * dg[s];
+        }
+    }
+    return 0;
+}
+
+int oracle_router_grads(const void* x, const void* w, int xtype, int64_t T, int d, int E,
+                        const double* d_logits, const int32_t* tokens, int64_t ntok,
+                        double* d_x, double* d_w)
+{
+    if (!x || !w || !d_logits || d <= 0 || E <= 0 || T < 0) return -1;
+    if (d_x) {
+        if (!tokens) return -1;
+        /* d_x[r,i] = sum_e d_logits[t,e] W_r[i,e] */
+#pragma omp parallel for schedule(static)
+        for (int64_t r = 0; r < ntok; ++r) {
+            int64_t t = tokens[r];
+            const double* dl = d_logits + (size_t)t * E;
+            for (int i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (int e = 0; e < E; ++e) acc += dl[e] * (double)load_f(w, xtype, (size_t)i * E + e);
+                d_x[(size_t)r * d + i] = acc;
+            }
+        }
+    }
+    if (d_w) {
+        /* d_w[i,e] = sum_t x[t,i] d_logits[t,e] */
+#pragma omp parallel for schedule(static)
+        for (int i = 0; i < d; ++i) {
+            double* o = d_w + (size_t)i * E;
+            for (int e = 0; e < E; ++e) o[e] = 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                double xi = (double)load_f(x, xtype, (size_t)t * d + i);
+                const double* dl = d_logits + (size_t)t * E;
+                for (int e = 0; e < E; ++e) o[e] += xi * dl[e];
+            }
+        }
+    }
+    return 0;
+}
+
+int oracle_combine_backward_gates(const int32_t* tokens, int64_t ntok, int k, int64_t d,
+                                  const int32_t* dest, const double* y, const int64_t* yrow,
+                                  const double* d_out, double* d_gates)
+{
+    if (!tokens || !dest || !y || !d_out || !d_gates || k <= 0 || d <= 0) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t r = 0; r < ntok; ++r) {
+        int64_t t = tokens[r];
+        const double* go = d_out + (size_t)r * d;
+        for (int s = 0; s < k; ++s) {
+            int64_t j = dest[t * k + s];
+            double acc = 0.0;
+            if (j >= 0) {
+                int64_t row = yrow ? yrow[j] : j;
+                if (row < 0) { bad = 1; continue; }
+                const double* yr = y + (size_t)row * d;
+                for (int64_t c = 0; c < d; ++c) acc += go[c] * yr[c];
+            }
+            d_gates[(size_t)r * k + s] = acc;
+        }
+    }
+    return bad ? -3 : 0;
+}
+
+int oracle_combine_backward_rows(const int32_t* perm_src, const int64_t* rows, int64_t nrows,
+                                 int k, int64_t d, const double* gates, const double* d_out,
+                                 double* d_y)
+{
+    if (!perm_src || !rows || !d_out || !d_y || k <= 0 || d <= 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t a = perm_src[rows[r]];
+        double gw = gates ? gates[a] : 1.0;
+        const double* go = d_out + (size_t)(a / k) * d;
+        for (int64_t c = 0; c < d; ++c) d_y[(size_t)r * d + c] = gw * go[c];
+    }
+    return 0;
+}
+
+/* expert of packed row j */
+static int expert_of(const int32_t* offsets, int E, int64_t j)
+{
+    int e = 0;
+    while (e < E && !(offsets[e] <= j && j < offsets[e + 1])) ++e;
+    return e;
+}
+
+int oracle_expert_ffn_backward_rows(const void* x, int xtype, int64_t N, int d, int f, int E,
+                                    const int32_t* offsets,
+                                    const void* wg, const void* wv, const void* wo,
+                                    const int64_t* rows, int64_t nrows, int x_compact,
+                                    const double* d_y, double* act, double* d_act, double* d_x)
+{
+    if (!x || !offsets || !wg || !wv || !wo || !rows || !d_y) return -1;
+    if (d <= 0 || f <= 0 || E <= 0 || N < 0) return -1;
+    if (offsets[0] != 0 || offsets[E] != N) return -2;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= N) return -2;
+
+#pragma omp parallel
+    {
+        double* a = (double*)malloc(sizeof(double) * (size_t)f);
+        double* v = (double*)malloc(sizeof(double) * (size_t)f);
+        double* dh = (double*)malloc(sizeof(double) * (size_t)f);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < nrows; ++r) {
+            int64_t j = rows[r];
+            int64_t xr = x_compact ? r : j;
+            int e = expert_of(offsets, E, j);
+            size_t wbase = (size_t)e * (size_t)d * (size_t)f;
+            /* forward pre-activations, as in oracle_expert_ffn_rows */
+            for (int c = 0; c < f; ++c) { a[c] = 0.0; v[c] = 0.0; }
+            for (int i = 0; i < d; ++i) {
+                double xi = (double)load_f(x, xtype, (size_t)xr * d + i);
+                size_t wrow = wbase + (size_t)i * f;
+                for (int c = 0; c < f; ++c) {
+                    a[c] += xi * (double)load_f(wg, xtype, wrow + c);
+                    v[c] += xi * (double)load_f(wv, xtype, wrow + c);
+                }
+            }
+            /* y = h Wo  ->  dh_c = sum_o dy_o Wo[c,o] */
+            const double* dy = d_y + (size_t)r * d;
+            for (int c = 0; c < f; ++c) {
+                size_t wrow = wbase + (size_t)c * d;
+                double acc = 0.0;
+                for (int o = 0; o < d; ++o) acc += dy[o] * (double)load_f(wo, xtype, wrow + o);
+                dh[c] = acc;
+            }
+            if (act)
+                for (int c = 0; c < f; ++c) {
+                    act[(size_t)r * 2 * f + c] = a[c];
+                    act[(size_t)r * 2 * f + f + c] = v[c];
+                }
+            /* h = silu(a) v, silu(a) = a s, s = 1/(1+exp(-a)), silu'(a) = s (1 + a (1 - s)):
+             * da = dh v silu'(a), dv = dh silu(a); stored over a and v */
+            for (int c = 0; c < f; ++c) {
+                double s = 1.0 / (1.0 + exp(-a[c]));
+                double da = dh[c] * v[c] * (s * (1.0 + a[c] * (1.0 - s)));
+                double dv = dh[c] * (a[c] * s);
+                a[c] = da;
+                v[c] = dv;
+            }
+            if (d_act)
+                for (int c = 0; c < f; ++c) {
+                    d_act[(size_t)r * 2 * f + c] = a[c];
+                    d_act[(size_t)r * 2 * f + f + c] = v[c];
+                }
+            /* a = x Wg, v = x Wv  ->  dx_i = sum_c da_c Wg[i,c] + dv_c Wv[i,c] */
+            if (d_x)
+                for (int i = 0; i < d; ++i) {
+                    size_t wrow = wbase + (size_t)i * f;
+                    double acc = 0.0;
+                    for (int c = 0; c < f; ++c)
+                        acc += a[c] * (double)load_f(wg, xtype, wrow + c)
+                             + v[c] * (double)load_f(wv, xtype, wrow + c);
+                    d_x[(size_t)r * d + i] = acc;
+                }
+        }
+        free(a);
+        free(v);
+        free(dh);
+    }
+    return 0;
+}
+
+int oracle_expert_weight_grads(const void* x, int xtype, int64_t N, int d, int f, int E,
+                               const int32_t* offsets,
+                               const void* wg, const void* wv, const void* wo,
+                               const double* d_y, const int32_t* pair_e, const int32_t* pair_c,
+                               int64_t npairs, double scale,
+                               double* dwg, double* dwv, double* dwo)
+{
+    if (!x || !offsets || !wg || !wv || !wo || !d_y || !pair_e || !pair_c) return -1;
+    if (!dwg || !dwv || !dwo || d <= 0 || f <= 0 || E <= 0 || N < 0) return -1;
+    if (offsets[0] != 0 || offsets[E] != N) return -2;
+    for (int64_t p = 0; p < npairs; ++p)
+        if (pair_e[p] < 0 || pair_e[p] >= E || pair_c[p] < 0 || pair_c[p] >= f) return -2;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t p = 0; p < npairs; ++p) {
+        int e = pair_e[p], c = pair_c[p];
+        size_t wbase = (size_t)e * (size_t)d * (size_t)f;
+        double* og = dwg + (size_t)p * d;
+        double* ov = dwv + (size_t)p * d;
+        double* oo = dwo + (size_t)p * d;
+        for (int i = 0; i < d; ++i) { og[i] = 0.0; ov[i] = 0.0; oo[i] = 0.0; }
+        for (int64_t j = offsets[e]; j < offsets[e + 1]; ++j) {
+            /* column c of this row's pre-activations and of dh */
+            double a = 0.0, v = 0.0, dh = 0.0;
+            for (int i = 0; i < d; ++i) {
+                double xi = (double)load_f(x, xtype, (size_t)j * d + i);
+                a += xi * (double)load_f(wg, xtype, wbase + (size_t)i * f + c);
+                v += xi * (double)load_f(wv, xtype, wbase + (size_t)i * f + c);
+            }
+            const double* dy = d_y + (size_t)j * d;
+            for (int o = 0; o < d; ++o) dh += dy[o] * (double)load_f(wo, xtype, wbase + (size_t)c * d + o);
+            double s = 1.0 / (1.0 + exp(-a));
+            double h = a * s * v;
+            double da = dh * v * (s * (1.0 + a * (1.0 - s)));
+            double dv = dh * (a * s);
+            /* a = x Wg[:,c]: dWg[i,c] += x_i da; likewise Wv; y = h Wo: dWo[c,o] += h dy_o */
+            for (int i = 0; i < d; ++i) {
+                double xi = (double)load_f(x, xtype, (size_t)j * d + i);
+                og[i] += xi * da;
+                ov[i] += xi * dv;
+            }
+            for (int o = 0; o < d; ++o) oo[o] += h * dy[o];
+        }
+        for (int i = 0; i < d; ++i) { og[i] *= scale; ov[i] *= scale; oo[i] *= scale; }
+    }
+    return 0;
+}

@@ -132,6 +132,89 @@ int oracle_combine(const int32_t* tokens, int64_t ntok, int k, int64_t d,
                    const double* y, const int64_t* yrow,
                    const double* shared, double* out);
 
+/* ----------------------------------------------------------------------
+ * Backward. The pages' systems train the layer: autograd flows through the
+ * exchanges and the index_select / index_copy permutation pair [Modalities
+ * PR "expert parallelism for the Nemotron-3 Nano MoE layers", "Design"], and
+ * expert gradients are divided by the EP group size before clipping and the
+ * optimizer [Three axes of Parallelism, "EP backward pass"]. No page writes
+ * the gradients out; these are the chain rule applied to the definitions
+ * above, in double. The selection (ids, packing) is piecewise constant and
+ * passes no gradient. Pinned against torch float64 autograd of a dense
+ * formulation and against central finite differences of the forward.
+ * -------------------------------------------------------------------- */
+
+/*
+ * Router weights -> logits (also the gradient of a trainable bias):
+ *   renorm != 0: g_s = softmax over the k selected logits, so
+ *     d_logits[t,e_s] = g_s (dg_s - sum_r g_r dg_r), 0 for unselected e;
+ *   renorm == 0: g_s = p_{e_s} with p the softmax over all E, so
+ *     d_logits[t,e] = p_e ([e = e_s] dg_s - sum_r g_r dg_r).
+ *   logits [T,E] fp32 and idx, gates [T,k] as oracle_route wrote them,
+ *   d_gates [T,k] in, d_logits [T,E] out.
+ */
+int oracle_route_backward(const float* logits, const int32_t* idx, const double* gates,
+                          const double* d_gates, int64_t T, int E, int k, int renorm,
+                          double* d_logits);
+
+/*
+ * Router scores -> inputs: d_x[r,i] = sum_e d_logits[t,e] w[i,e] for
+ * t = tokens[r] (d_x [ntok,d], may be NULL), d_w[i,e] = sum over all T tokens
+ * of x[t,i] d_logits[t,e] (d_w [d,E], may be NULL).
+ */
+int oracle_router_grads(const void* x, const void* w, int xtype, int64_t T, int d, int E,
+                        const double* d_logits, const int32_t* tokens, int64_t ntok,
+                        double* d_x, double* d_w);
+
+/*
+ * Combine -> router weights: d_gates[r,s] = sum_c d_out[r,c] y[dest[t*k+s],c]
+ * for t = tokens[r] (0 for a dropped assignment); d_out [ntok,d] holds the
+ * listed tokens' output gradients; y and yrow as in oracle_combine.
+ */
+int oracle_combine_backward_gates(const int32_t* tokens, int64_t ntok, int k, int64_t d,
+                                  const int32_t* dest, const double* y, const int64_t* yrow,
+                                  const double* d_out, double* d_gates);
+
+/*
+ * Combine -> expert outputs: for packed row j = rows[r] holding flat
+ * assignment a = perm_src[j], d_y[r,:] = g[a] * d_out[a / k,:] (gates NULL:
+ * weight 1). d_out [T,d] is the whole output gradient.
+ */
+int oracle_combine_backward_rows(const int32_t* perm_src, const int64_t* rows, int64_t nrows,
+                                 int k, int64_t d, const double* gates, const double* d_out,
+                                 double* d_y);
+
+/*
+ * Expert SwiGLU MLP backward for the listed packed rows (x, layouts and
+ * x_compact as in oracle_expert_ffn_rows), d_y [nrows,d] their output
+ * gradients. With a = x Wg[e], v = x Wv[e], s = 1/(1+exp(-a)):
+ *   dh = d_y Wo[e]^T,  da = dh v s (1 + a (1 - s)),  dv = dh a s,
+ *   d_x = da Wg[e]^T + dv Wv[e]^T.
+ * act [nrows,2f] gets (a, v), d_act [nrows,2f] gets (da, dv), d_x [nrows,d];
+ * each may be NULL.
+ */
+int oracle_expert_ffn_backward_rows(const void* x, int xtype, int64_t N, int d, int f, int E,
+                                    const int32_t* offsets,
+                                    const void* wg, const void* wv, const void* wo,
+                                    const int64_t* rows, int64_t nrows, int x_compact,
+                                    const double* d_y, double* act, double* d_act, double* d_x);
+
+/*
+ * Expert weight gradients of the listed (expert e, hidden column c) pairs,
+ * summed over every packed row j of expert e and multiplied by `scale` (1/P
+ * for an EP group of P ranks):
+ *   dWg[e][:,c] = scale sum_j x[j,:] da[j,c],  dWv[e][:,c] = scale sum_j x[j,:] dv[j,c],
+ *   dWo[e][c,:] = scale sum_j h[j,c] d_y[j,:].
+ * x [N,d] packed rows, d_y [N,d] all packed rows' output gradients;
+ * dwg, dwv, dwo [npairs,d] out.
+ */
+int oracle_expert_weight_grads(const void* x, int xtype, int64_t N, int d, int f, int E,
+                               const int32_t* offsets,
+                               const void* wg, const void* wv, const void* wo,
+                               const double* d_y, const int32_t* pair_e, const int32_t* pair_c,
+                               int64_t npairs, double scale,
+                               double* dwg, double* dwv, double* dwo);
+
 #ifdef __cplusplus
 }
 #endif
