@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["api.hip", "route.hip", "permute.hip", "grouped_ffn.hip", "combine.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "grouped_ffn.hip", "grouped_bwd.hip",
+           "combine.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 CFLAGS = [

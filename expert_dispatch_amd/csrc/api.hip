@@ -19,13 +19,26 @@ hipError_t launch_permute_recv(const int32_t* recv, int S, int E, int N, const v
                                int32_t* dest, void* x_perm, hipStream_t st);
 hipError_t launch_gate_up(const void* x, moe_dtype dt, int N, int d, int f, int E,
                           const int32_t* offsets, const void* wg, const void* wv, void* h,
-                          hipStream_t st);
+                          void* act, hipStream_t st);
 hipError_t launch_down(const void* h, moe_dtype dt, int N, int f, int d, int E,
                        const int32_t* offsets, const void* wo, void* y, moe_dtype y_dt,
                        hipStream_t st);
 hipError_t launch_combine(const void* y, moe_dtype y_dt, const int32_t* dest, const float* gates,
                           int T, int k, int d, const void* sh, moe_dtype sh_dt, void* out,
                           moe_dtype out_dt, hipStream_t st);
+hipError_t launch_combine_bwd(const void* d_out, moe_dtype g_dt, const void* y, moe_dtype y_dt,
+                              const int32_t* dest, const float* gates, int T, int k, int d,
+                              void* d_y, moe_dtype dy_dt, float* d_gates, hipStream_t st);
+hipError_t launch_route_bwd(const float* logits, const int32_t* idx, const float* gates,
+                            const float* d_gates, int T, int E, int k, int renorm,
+                            float* d_logits, uint16_t* d_logits_bf16, hipStream_t st);
+hipError_t launch_nt(int epi, const void* A, moe_dtype dt, int rows, int K, int K0, int N, int E,
+                     const int32_t* offsets, const void* B0, const void* B1, void* C,
+                     const void* act, hipStream_t st);
+hipError_t launch_tn(const void* A, int lda, int M, const void* B, int ldb, int Nc, int pair,
+                     moe_dtype dt, int rows, int E, const int32_t* offsets, float scale,
+                     float* C0, float* C1, hipStream_t st);
+enum NtEpi { kNtSwigluBwd = 0, kNtStoreF32 = 1, kNtAccumF32 = 2, kNtStoreBf16 = 3 };
 }  // namespace moe
 
 namespace {
@@ -173,7 +186,7 @@ moe_status moe_ffn_gate_up(const void* x_perm, moe_dtype dt, int N, int d, int f
     if (N == 0) return MOE_OK;
     if (!x_perm || !w_gate || !w_val || !h) return MOE_ERR_INVALID_ARG;
     return hip_status(moe::launch_gate_up(x_perm, dt, N, d, f, E, offsets, w_gate, w_val, h,
-                                          as_stream(stream)));
+                                          nullptr, as_stream(stream)));
 }
 
 moe_status moe_ffn_down(const void* h, moe_dtype dt, int N, int f, int d, int E,
@@ -201,7 +214,8 @@ moe_status moe_grouped_ffn(const void* x_perm, moe_dtype dt, int N, int d, int f
     if (!x_perm || !w_gate || !w_val || !w_out || !y) return MOE_ERR_INVALID_ARG;
     if (!ws || ws_bytes < h_bytes(N, f, dt)) return MOE_ERR_WORKSPACE;
     hipStream_t st = as_stream(stream);
-    hipError_t e = moe::launch_gate_up(x_perm, dt, N, d, f, E, offsets, w_gate, w_val, ws, st);
+    hipError_t e = moe::launch_gate_up(x_perm, dt, N, d, f, E, offsets, w_gate, w_val, ws,
+                                       nullptr, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
     return hip_status(moe::launch_down(ws, dt, N, f, d, E, offsets, w_out, y, y_dt, st));
 }
@@ -219,6 +233,127 @@ moe_status moe_combine(const void* y_perm, moe_dtype y_dt, const int32_t* dest,
     return hip_status(moe::launch_combine(y_perm, y_dt, dest, gates, T, k, d, y_shared,
                                           y_shared ? sh_dt : MOE_F32, out, out_dt,
                                           as_stream(stream)));
+}
+
+// ------------------------------------------------------------------ backward
+
+moe_status moe_ffn_gate_up_train(const void* x_perm, moe_dtype dt, int N, int d, int f, int E,
+                                 const int32_t* offsets, const void* w_gate, const void* w_val,
+                                 void* h, void* act, void* stream)
+{
+    moe_status s = check_ffn(dt, N, d, f, E, offsets);
+    if (s != MOE_OK) return s;
+    if (N == 0) return MOE_OK;
+    if (!x_perm || !w_gate || !w_val || !h || !act) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_gate_up(x_perm, dt, N, d, f, E, offsets, w_gate, w_val, h, act,
+                                          as_stream(stream)));
+}
+
+moe_status moe_combine_backward(const void* d_out, moe_dtype d_out_dt, const void* y_perm,
+                                moe_dtype y_dt, const int32_t* dest, const float* gates,
+                                int T, int k, int d, void* d_y, moe_dtype d_y_dt,
+                                float* d_gates, void* stream)
+{
+    if (!valid_dtype(d_out_dt) || !valid_dtype(y_dt) || !valid_dtype(d_y_dt) || T < 0 ||
+        k <= 0 || d <= 0)
+        return MOE_ERR_INVALID_ARG;
+    if (k > kMaxK || (long long)T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!d_out || !y_perm || !dest || !gates || !d_y || !d_gates) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_combine_bwd(d_out, d_out_dt, y_perm, y_dt, dest, gates, T, k, d,
+                                              d_y, d_y_dt, d_gates, as_stream(stream)));
+}
+
+moe_status moe_ffn_down_backward(const void* d_y, moe_dtype dt, int N, int d, int f, int E,
+                                 const int32_t* offsets, const void* w_out, const void* act,
+                                 void* d_act, void* stream)
+{
+    moe_status s = check_ffn(dt, N, d, f, E, offsets);
+    if (s != MOE_OK) return s;
+    if (N == 0) return MOE_OK;
+    if (!d_y || !w_out || !act || !d_act) return MOE_ERR_INVALID_ARG;
+    // dh [N,f] = d_y [N,d] . W_out[e]^T, W_out[e] [f,d] read as [N = f][K = d]
+    return hip_status(moe::launch_nt(moe::kNtSwigluBwd, d_y, dt, N, d, d, f, E, offsets, w_out,
+                                     nullptr, d_act, act, as_stream(stream)));
+}
+
+moe_status moe_ffn_gate_up_backward(const void* d_act, moe_dtype dt, int N, int d, int f, int E,
+                                    const int32_t* offsets, const void* w_gate,
+                                    const void* w_val, void* d_x_perm, moe_dtype dx_dt,
+                                    int accumulate, void* stream)
+{
+    moe_status s = check_ffn(dt, N, d, f, E, offsets);
+    if (s != MOE_OK) return s;
+    if (!valid_dtype(dx_dt)) return MOE_ERR_INVALID_ARG;
+    if (accumulate && dx_dt != MOE_F32) return MOE_ERR_UNSUPPORTED;
+    if (dt == MOE_F32 && dx_dt != MOE_F32) return MOE_ERR_UNSUPPORTED;
+    if (N == 0) return MOE_OK;
+    if (!d_act || !w_gate || !w_val || !d_x_perm) return MOE_ERR_INVALID_ARG;
+    // d_x [N,d] = d_act [N,2f] . [W_gate[e] ; W_val[e]]^T: K = 2f, the first f
+    // from W_gate[e] [d,f] read as [N = d][K = f], the rest from W_val[e]
+    const int epi = accumulate ? moe::kNtAccumF32 : (dx_dt == MOE_BF16 ? moe::kNtStoreBf16
+                                                                       : moe::kNtStoreF32);
+    return hip_status(moe::launch_nt(epi, d_act, dt, N, 2 * f, f, d, E, offsets, w_gate, w_val,
+                                     d_x_perm, nullptr, as_stream(stream)));
+}
+
+moe_status moe_ffn_weight_grads(const void* x_perm, const void* h, const void* d_y,
+                                const void* d_act, moe_dtype dt, int N, int d, int f, int E,
+                                const int32_t* offsets, float scale, float* d_w_gate,
+                                float* d_w_val, float* d_w_out, void* stream)
+{
+    moe_status s = check_ffn(dt, N, d, f, E, offsets);
+    if (s != MOE_OK) return s;
+    if (!d_w_gate || !d_w_val || !d_w_out) return MOE_ERR_INVALID_ARG;
+    if (N > 0 && (!x_perm || !h || !d_y || !d_act)) return MOE_ERR_INVALID_ARG;
+    hipStream_t st = as_stream(stream);
+    // dW_out[e] [f,d] = h_e^T . d_y_e
+    hipError_t e = moe::launch_tn(h, f, f, d_y, d, d, 0, dt, N, E, offsets, scale, d_w_out,
+                                  nullptr, st);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    // [dW_gate | dW_val][e] [d,f] = x_e^T . d_act_e[:, 0:f | f:2f]
+    return hip_status(moe::launch_tn(x_perm, d, d, d_act, 2 * f, f, f, dt, N, E, offsets, scale,
+                                     d_w_gate, d_w_val, st));
+}
+
+moe_status moe_route_backward(const float* logits, const int32_t* topk_idx, const float* gates,
+                              const float* d_gates, int T, int E, int k, int renorm,
+                              float* d_logits, void* d_logits_bf16, void* stream)
+{
+    if (T < 0 || E <= 0 || k <= 0 || k > E) return MOE_ERR_INVALID_ARG;
+    if (k > kMaxK || (long long)T * E > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_idx || !gates || !d_gates) return MOE_ERR_INVALID_ARG;
+    if (!d_logits && !d_logits_bf16) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_route_bwd(logits, topk_idx, gates, d_gates, T, E, k, renorm,
+                                            d_logits, static_cast<uint16_t*>(d_logits_bf16),
+                                            as_stream(stream)));
+}
+
+moe_status moe_router_backward(const void* x, const void* w_router, moe_dtype dt,
+                               const void* d_logits, int T, int d, int E, float* d_x,
+                               int accumulate, float* d_w_router, void* stream)
+{
+    if (!valid_dtype(dt) || T < 0 || d <= 0 || E <= 0) return MOE_ERR_INVALID_ARG;
+    if ((long long)T * std::max(d, E) > (1LL << 40) || (long long)T * E > INT32_MAX)
+        return MOE_ERR_UNSUPPORTED;
+    if (!d_x && !d_w_router) return MOE_OK;
+    if (T > 0 && (!x || !w_router || !d_logits)) return MOE_ERR_INVALID_ARG;
+    hipStream_t st = as_stream(stream);
+    if (d_x && T > 0) {
+        // d_x [T,d] (+)= d_logits [T,E] . W_r^T, W_r [d,E] read as [N = d][K = E]
+        hipError_t e = moe::launch_nt(accumulate ? moe::kNtAccumF32 : moe::kNtStoreF32, d_logits,
+                                      dt, T, E, E, d, 1, nullptr, w_router, nullptr, d_x, nullptr,
+                                      st);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    if (d_w_router) {
+        // d_w_router [d,E] = x^T . d_logits over all T rows (T = 0: zeros)
+        hipError_t e = moe::launch_tn(x, d, d, d_logits, E, E, 0, dt, T, 1, nullptr, 1.0f,
+                                      d_w_router, nullptr, st);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    return MOE_OK;
 }
 
 }  // extern "C"

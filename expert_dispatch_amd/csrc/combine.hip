@@ -152,4 +152,112 @@ hipError_t launch_combine(const void* y, moe_dtype y_dt, const int32_t* dest, co
     return launch_combine_s<float>(sh_dt, out_dt, y, dest, gates, T, k, d, sh, out, st);
 }
 
+// ------------------------------------------------------------------ backward
+//
+// Gradient of the combine: with out[t] = sum_s g[t,s] y[dest[t*k+s]],
+//   d_y[dest[t*k+s]] = g[t,s] d_out[t]    (written in the activation type: the
+//                                          input of the expert backward GEMMs)
+//   d_g[t,s]        = <d_out[t], y[dest[t*k+s]]>
+// One wavefront per token: for each slot it streams d_out[t] (cached after
+// the first slot) and the slot's y row, writes the scaled row and reduces the
+// dot product over the wave. A dropped assignment (dest < 0) gets d_g = 0 and
+// no row.
+template <typename GT, typename YT, typename DT, bool VEC>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(
+    const GT* __restrict__ d_out, const YT* __restrict__ y, const int32_t* __restrict__ dest,
+    const float* __restrict__ gates, int T, int k, int d, DT* __restrict__ d_y,
+    float* __restrict__ d_gates)
+{
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T) return;
+    const int lane = lane_id();
+    const long long rows = (long long)T * k;
+    int my_j = -1;
+    float my_g = 0.0f;
+    if (lane < k) {
+        my_j = dest[(size_t)t * k + lane];
+        if (my_j < 0 || my_j >= rows) my_j = -1;
+        my_g = gates[(size_t)t * k + lane];
+    }
+    const GT* go = d_out + (size_t)t * d;
+    for (int s = 0; s < k; ++s) {
+        const int j = __shfl(my_j, s, kWave);
+        const float g = __shfl(my_g, s, kWave);
+        float dot = 0.0f;
+        if (j >= 0) {
+            const YT* yr = y + (size_t)j * d;
+            DT* dyr = d_y + (size_t)j * d;
+            if constexpr (VEC) {
+                for (int c = lane * 4; c < d; c += kWave * 4) {
+                    float o[4], v[4], w[4];
+                    Vec4<GT>::load(go + c, o);
+                    Vec4<YT>::load(yr + c, v);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        dot = __builtin_fmaf(o[q], v[q], dot);
+                        w[q] = g * o[q];
+                    }
+                    Vec4<DT>::store(dyr + c, w);
+                }
+            } else {
+                for (int c = lane; c < d; c += kWave) {
+                    const float o = Elem<GT>::load(go, c);
+                    dot = __builtin_fmaf(o, Elem<YT>::load(yr, c), dot);
+                    Elem<DT>::store(dyr, c, g * o);
+                }
+            }
+        }
+        dot = wave_sum_f32(dot);
+        if (lane == 0) d_gates[(size_t)t * k + s] = dot;
+    }
+}
+
+template <typename GT, typename YT, typename DT>
+static hipError_t launch_combine_bwd_t(const void* d_out, const void* y, const int32_t* dest,
+                                       const float* gates, int T, int k, int d, void* d_y,
+                                       float* d_gates, hipStream_t st)
+{
+    const dim3 grid((T + 3) / 4);
+    auto al = [](const void* p, size_t a) { return (uintptr_t)p % a == 0; };
+    const bool vec = d % 4 == 0 && al(d_out, 4 * sizeof(GT)) && al(y, 4 * sizeof(YT)) &&
+                     al(d_y, 4 * sizeof(DT));
+    if (vec)
+        combine_bwd_kernel<GT, YT, DT, true><<<grid, 256, 0, st>>>(
+            (const GT*)d_out, (const YT*)y, dest, gates, T, k, d, (DT*)d_y, d_gates);
+    else
+        combine_bwd_kernel<GT, YT, DT, false><<<grid, 256, 0, st>>>(
+            (const GT*)d_out, (const YT*)y, dest, gates, T, k, d, (DT*)d_y, d_gates);
+    return hipGetLastError();
+}
+
+template <typename GT, typename YT>
+static hipError_t launch_combine_bwd_d(moe_dtype dy_dt, const void* d_out, const void* y,
+                                       const int32_t* dest, const float* gates, int T, int k,
+                                       int d, void* d_y, float* d_gates, hipStream_t st)
+{
+    if (dy_dt == MOE_BF16)
+        return launch_combine_bwd_t<GT, YT, uint16_t>(d_out, y, dest, gates, T, k, d, d_y, d_gates, st);
+    return launch_combine_bwd_t<GT, YT, float>(d_out, y, dest, gates, T, k, d, d_y, d_gates, st);
+}
+
+template <typename GT>
+static hipError_t launch_combine_bwd_y(moe_dtype y_dt, moe_dtype dy_dt, const void* d_out,
+                                       const void* y, const int32_t* dest, const float* gates,
+                                       int T, int k, int d, void* d_y, float* d_gates,
+                                       hipStream_t st)
+{
+    if (y_dt == MOE_BF16)
+        return launch_combine_bwd_d<GT, uint16_t>(dy_dt, d_out, y, dest, gates, T, k, d, d_y, d_gates, st);
+    return launch_combine_bwd_d<GT, float>(dy_dt, d_out, y, dest, gates, T, k, d, d_y, d_gates, st);
+}
+
+hipError_t launch_combine_bwd(const void* d_out, moe_dtype g_dt, const void* y, moe_dtype y_dt,
+                              const int32_t* dest, const float* gates, int T, int k, int d,
+                              void* d_y, moe_dtype dy_dt, float* d_gates, hipStream_t st)
+{
+    if (g_dt == MOE_BF16)
+        return launch_combine_bwd_y<uint16_t>(y_dt, dy_dt, d_out, y, dest, gates, T, k, d, d_y, d_gates, st);
+    return launch_combine_bwd_y<float>(y_dt, dy_dt, d_out, y, dest, gates, T, k, d, d_y, d_gates, st);
+}
+
 }  // namespace moe

@@ -1,0 +1,657 @@
+// Backward of the grouped SwiGLU expert MLPs (and of the router's score
+// product), as grouped matrix-core GEMMs.
+//
+// The pages' systems train the layer: gradients flow back through the expert
+// MLPs and the permutation pair, and an expert's weight gradient is divided
+// by the EP group size ("Three axes of Parallelism", EP backward pass). With
+// a = x.W_gate[e], v = x.W_val[e], h = silu(a) * v, y = h.W_out[e] on the rows
+// of expert e, the chain rule gives two product shapes:
+//
+//  * data gradients, rows grouped by expert, C = A . B_e^T (both operands
+//    K-contiguous in memory):
+//      dh   = dy . W_out[e]^T            (K = d),  fused SwiGLU backward:
+//             da = dh * v * silu'(a), dv = dh * silu(a)  -> d_act = [da | dv]
+//      dx   = [da | dv] . [W_gate[e] ; W_val[e]]^T   (K = 2f, two sources)
+//      router: dx += dl . W_r^T          (one group, K = E)
+//  * weight gradients, one output tile per (expert, m, n) with the expert's
+//    rows as the reduction, C_e = scale * A_e^T . B_e (both operands row-major
+//    with the rows as K):
+//      dW_out[e]            = h^T . dy
+//      [dW_gate | dW_val][e] = x^T . [da | dv]   (paired column tiles)
+//      router: dW_r          = x^T . dl         (one group of all T rows)
+//
+// Both shapes reuse the forward's machinery: 256 threads as a 2 x 2 grid of
+// wavefronts, v_mfma_f32_32x32x16_bf16 with fp32 accumulators, BK = 32 stages
+// through a three-buffer LDS ring fed by three register stages of 16-byte
+// global loads. A K-contiguous operand is staged [rows][32] with the a_swz
+// swizzle and read as plain 16-byte fragments; a row-major operand whose rows
+// are the reduction is staged [32][256] with b_swz and read with the gfx950
+// LDS transpose read. Rows of the data-gradient kernel are scheduled by the
+// forward's device-side tile list (256-row tiles, 128-row remainder tiles);
+// the weight-gradient kernel has a fixed E x M/256 x N/256 tile grid, every
+// expert's tiles contiguous on one XCD, and a reduction of ceil(n_e/32)
+// stages (rows past the expert's end load as zeros; an expert with no rows
+// writes zeros). A plain fp32-FMA kernel covers fp32 data and shapes the
+// matrix-core path does not tile.
+#include "mfma_common.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kT = 256;     // threads
+constexpr int kK = 32;      // k per stage
+constexpr int kN = 256;     // columns per tile
+constexpr int kRingB = 3;   // LDS stage buffers
+constexpr int kSetsB = 3;   // register stages in flight
+
+// sigmoid with the hardware exp2 and reciprocal
+__device__ __forceinline__ float sigmoid_fast(float z) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
+
+// SwiGLU backward of one element: h = silu(a) * v, silu(a) = a s, s = sigmoid(a),
+// silu'(a) = s (1 + a (1 - s)).
+__device__ __forceinline__ void swiglu_bwd(float dh, float a, float v, float& da, float& dv) {
+    const float s = sigmoid_fast(a);
+    da = dh * v * (s * (1.0f + a * (1.0f - s)));
+    dv = dh * (a * s);
+}
+
+}  // namespace
+
+enum NtEpi { kNtSwigluBwd = 0, kNtStoreF32 = 1, kNtAccumF32 = 2, kNtStoreBf16 = 3 };
+
+// ----------------------------------------------- data gradients: C = A . B^T
+
+struct NtArgs {
+    const uint16_t* A;    // [rows, K], row stride K
+    int K;                // reduction length (multiple of 32)
+    const uint16_t* B0;   // per expert [N, K0]: B(k, n) = B0[e][n][k] for k < K0
+    const uint16_t* B1;   // per expert [N, K - K0]: B(k, n) = B1[e][n][k - K0]
+    int K0;               // multiple of 32
+    int N;                // output columns
+    void* C;              // swiglu-bwd: d_act [rows, 2N] bf16; else [rows, N]
+    const uint16_t* act;  // swiglu-bwd: [rows, 2N] bf16, (a | v)
+};
+
+struct NtStage {
+    u32x4 a[4];
+    u32x4 b[4];
+};
+
+template <int EPI, int TM>
+__device__ __forceinline__ void nt_tile(const NtArgs& p, const Tile& tile, uint16_t* smem)
+{
+    constexpr int kMI = TM / 64;                 // 32-row blocks per wavefront
+    constexpr int kAC = TM * kK / 8 / kT;        // 16-byte A chunks per thread per stage
+    constexpr int kBC = kN * kK / 8 / kT;        // 16-byte B chunks per thread per stage
+    auto sA = [&](int b) { return smem + b * (TM * kK); };
+    auto sB = [&](int b) { return smem + kRingB * (TM * kK) + b * (kN * kK); };
+
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int m0 = tile.m0, seg_last = tile.seg_end - 1;
+    const int n0 = tile.n_tile * kN;
+    const int K = p.K, KT = K / kK, KT0 = p.K0 / kK, K1 = K - p.K0;
+
+    // sources: A chunk i -> row tid/4 + 64 i (rows past the segment re-read
+    // its last row, never stored), 16-byte chunk tid%4 of the stage's 64
+    // bytes; B chunk i -> output column n0 + tid/4 + 64 i (clamped to N-1)
+    const uint16_t* ap[kAC];
+#pragma unroll
+    for (int i = 0; i < kAC; ++i)
+        ap[i] = p.A + (size_t)min(m0 + (tid >> 2) + 64 * i, seg_last) * K + (tid & 3) * 8;
+    const uint16_t* bp0[kBC];
+    const uint16_t* bp1[kBC];
+#pragma unroll
+    for (int i = 0; i < kBC; ++i) {
+        const size_t n = (size_t)tile.e * p.N + min(n0 + (tid >> 2) + 64 * i, p.N - 1);
+        bp0[i] = p.B0 + n * p.K0 + (tid & 3) * 8;
+        bp1[i] = (K1 > 0 ? p.B1 + n * K1 : p.B0) + (tid & 3) * 8;
+    }
+    auto load = [&](int kt, NtStage& r) {
+#pragma unroll
+        for (int i = 0; i < kAC; ++i) r.a[i] = *reinterpret_cast<const u32x4*>(ap[i] + (size_t)kt * kK);
+        const bool first = kt < KT0;
+#pragma unroll
+        for (int i = 0; i < kBC; ++i) {
+            const uint16_t* q = first ? bp0[i] + (size_t)kt * kK : bp1[i] + (size_t)(kt - KT0) * kK;
+            r.b[i] = *reinterpret_cast<const u32x4*>(q);
+        }
+    };
+    // LDS destinations (the swizzle term does not change with + 64 rows)
+    const int dst = (tid >> 2) * kK + a_swz(tid & 3, tid >> 2) * 8;
+    auto store = [&](int buf, const NtStage& r) {
+#pragma unroll
+        for (int i = 0; i < kAC; ++i) *reinterpret_cast<u32x4*>(sA(buf) + dst + 64 * i * kK) = r.a[i];
+#pragma unroll
+        for (int i = 0; i < kBC; ++i) *reinterpret_cast<u32x4*>(sB(buf) + dst + 64 * i * kK) = r.b[i];
+    };
+    // fragments: row (or column) base + lane%32, 16-byte chunk 2 ks + lane/32;
+    // + 32 rows per block (the swizzle term does not change with it)
+    int a_lane[2], b_lane[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int ra = (TM / 2) * wm + (lane & 31);
+        const int rb = 128 * wn + (lane & 31);
+        a_lane[ks] = ra * kK + a_swz(2 * ks + (lane >> 5), ra) * 8;
+        b_lane[ks] = rb * kK + a_swz(2 * ks + (lane >> 5), rb) * 8;
+    }
+    f32x16 acc[kMI][4];
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mi][q][r] = 0.0f;
+    auto compute = [&](int buf) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 fa[kMI], fb[4];
+#pragma unroll
+            for (int mi = 0; mi < kMI; ++mi)
+                fa[mi] = *reinterpret_cast<const bf16x8*>(sA(buf) + a_lane[ks] + 32 * mi * kK);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                fb[q] = *reinterpret_cast<const bf16x8*>(sB(buf) + b_lane[ks] + 32 * q * kK);
+#pragma unroll
+            for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[mi][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[q], acc[mi][q], 0, 0, 0);
+        }
+    };
+
+    // Stage s lives in register set s % 3, then LDS buffer s % 3. Step kt:
+    // MFMAs of stage kt, store stage kt+2 into the buffer stage kt-1 used
+    // (every wave passed the barrier after its last read), reload the set
+    // with stage kt+5, barrier. Loads past the last stage re-read it.
+    auto clampk = [&](int k) { return min(k, KT - 1); };
+    NtStage rs[kSetsB];
+#pragma unroll
+    for (int i = 0; i < kSetsB; ++i) load(clampk(i), rs[i]);
+    lds_barrier();   // the block's previous tile is done with the ring
+    store(0, rs[0]);
+    load(clampk(3), rs[0]);
+    store(1, rs[1]);
+    load(clampk(4), rs[1]);
+    lds_barrier();
+    auto step = [&](int kt, int buf, NtStage& r) {
+        compute(buf);
+        store(buf == 0 ? 2 : buf - 1, r);
+        load(clampk(kt + 5), r);
+        lds_barrier();
+        return buf == kRingB - 1 ? 0 : buf + 1;
+    };
+    int kt = 0, buf = 0;
+    for (; kt + kSetsB <= KT; kt += kSetsB) {
+#pragma unroll
+        for (int u = 0; u < kSetsB; ++u) buf = step(kt + u, buf, rs[(u + 2) % kSetsB]);
+    }
+#pragma unroll
+    for (int u = 0; u < kSetsB - 1; ++u)
+        if (kt + u < KT) buf = step(kt + u, buf, rs[(u + 2) % kSetsB]);
+
+    // Epilogue. A lane holds column lane%32 of each 32 x 32 block and rows
+    // 8 (r/4) + 4 (lane/32) + r%4 for register r.
+    const int col_l = lane & 31;
+    const int row_l = 4 * (lane >> 5);
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int col = n0 + 128 * wn + 32 * q + col_l;
+            if (col >= p.N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + (TM / 2) * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
+                if (row > seg_last) continue;
+                const float v = acc[mi][q][r];
+                if constexpr (EPI == kNtSwigluBwd) {
+                    const size_t o = (size_t)row * 2 * p.N + col;
+                    float da, dv;
+                    swiglu_bwd(v, bf16_to_f32(p.act[o]), bf16_to_f32(p.act[o + p.N]), da, dv);
+                    uint16_t* D = static_cast<uint16_t*>(p.C);
+                    D[o] = f32_to_bf16(da);
+                    D[o + p.N] = f32_to_bf16(dv);
+                } else if constexpr (EPI == kNtStoreF32) {
+                    static_cast<float*>(p.C)[(size_t)row * p.N + col] = v;
+                } else if constexpr (EPI == kNtAccumF32) {
+                    static_cast<float*>(p.C)[(size_t)row * p.N + col] += v;
+                } else {
+                    static_cast<uint16_t*>(p.C)[(size_t)row * p.N + col] = f32_to_bf16(v);
+                }
+            }
+        }
+}
+
+// LDS: ring of three stages sized for 256-row tiles (96 KB) + the tile list.
+constexpr int kNtSmem = kRingB * (256 * kK + kN * kK);
+
+template <int EPI>
+__global__ __launch_bounds__(kT, 1) void nt_mfma_kernel(NtArgs p, const int32_t* __restrict__ offsets,
+                                                       int rows, int E)
+{
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[kNtSmem];
+    __shared__ int s_sched[3 * kMaxE + 1];
+    __shared__ int scratch[kT / kWave + 1];
+    const TileList L = build_tile_list(offsets, rows, E, (p.N + kN - 1) / kN, s_sched,
+                                       s_sched + kMaxE + 1, s_sched + 2 * kMaxE + 1, scratch);
+    const int total = L.total_big + L.total_small;
+    const int G = gridDim.x;
+    const int base = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+    for (int t = base; t < total; t += G) {
+        const Tile tile = decode_tile(L, t);
+        if (tile.bm == 128) nt_tile<EPI, 128>(p, tile, smem);
+        else nt_tile<EPI, 256>(p, tile, smem);
+    }
+}
+
+// ---------------------------------------- weight gradients: C_e = s A_e^T B_e
+
+struct TnArgs {
+    const uint16_t* A;  // [rows, lda]: A(k = row j, m) = A[j][m], m < M
+    int lda, M;
+    const uint16_t* B;  // [rows, ldb]: B(k = row j, n) = B[j][n]
+    int ldb, Nc;        // Nc: output columns (per half when paired)
+    int pair;           // > 0: paired tiles; tile column c < 128 is B column n0 + c
+                        // (-> C0), c >= 128 is B column pair + n0 + c - 128 (-> C1)
+    float* C0;          // [E, M, Nc] fp32
+    float* C1;          // paired: second output [E, M, Nc]
+    float scale;
+};
+
+struct TnStage {
+    u32x4 a[4];
+    u32x4 b[4];
+};
+
+__global__ __launch_bounds__(kT, 1) void tn_mfma_kernel(TnArgs p, const int32_t* __restrict__ offsets,
+                                                       int rows, int E)
+{
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[kRingB * 2 * kK * kN];
+    auto sA = [&](int b) { return smem + b * (kK * kN); };
+    auto sB = [&](int b) { return smem + kRingB * (kK * kN) + b * (kK * kN); };
+
+    const int mt_n = (p.M + kN - 1) / kN;
+    const int ncols = p.pair > 0 ? 128 : kN;
+    const int nt_n = (p.Nc + ncols - 1) / ncols;
+    const int per_e = mt_n * nt_n;
+    const int tiles = E * per_e;
+    // XCD-aware order: blocks of one XCD (b % 8) take a contiguous run of the
+    // expert-major tile list, so an expert's tiles share its rows through L2
+    const int per_xcd = (tiles + 7) / 8;
+    const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (blockIdx.x / 8 >= per_xcd || t >= tiles) return;
+    const int e = t / per_e;
+    const int mt = (t % per_e) / nt_n;
+    const int nt = t % nt_n;
+    const int m0 = mt * kN, n0 = nt * ncols;
+    const int j0 = offsets ? min(max(offsets[e], 0), rows) : 0;
+    const int j1 = offsets ? max(j0, min(offsets[e + 1], rows)) : rows;
+    // stages of 32 rows, rounded up to a whole number of 3-step loop bodies
+    // (the rows past the expert's end load as zeros and add nothing)
+    const int KT = (j1 - j0 + 3 * kK - 1) / (3 * kK) * 3;
+
+    int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mi][q][r] = 0.0f;
+
+    if (KT > 0) {
+        // chunk i of a stage: k-row tid/32 + 8 i, 16-byte chunk c = tid%32 of the
+        // 256 columns (columns clamped inside the operand; rows past the
+        // expert's end load as zeros)
+        const int c = tid & 31;
+        const int acol = min(m0 + 8 * c, p.M - 8);
+        int bcol;
+        if (p.pair > 0) bcol = (c < 16) ? min(n0 + 8 * c, p.Nc - 8) : p.pair + min(n0 + 8 * (c - 16), p.Nc - 8);
+        else bcol = min(n0 + 8 * c, p.Nc - 8);
+        auto load = [&](int kt, TnStage& r) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = j0 + kt * kK + (tid >> 5) + 8 * i;
+                const int jc = min(j, j1 - 1);
+                const u32x4 va = *reinterpret_cast<const u32x4*>(p.A + (size_t)jc * p.lda + acol);
+                const u32x4 vb = *reinterpret_cast<const u32x4*>(p.B + (size_t)jc * p.ldb + bcol);
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                r.a[i] = j < j1 ? va : z;
+                r.b[i] = j < j1 ? vb : z;
+            }
+        };
+        const int dst = (tid >> 5) * kN + b_swz(c, tid >> 5) * 8;
+        auto store = [&](int buf, const TnStage& r) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                *reinterpret_cast<u32x4*>(sA(buf) + dst + 8 * i * kN) = r.a[i];
+                *reinterpret_cast<u32x4*>(sB(buf) + dst + 8 * i * kN) = r.b[i];
+            }
+        };
+        // transpose-read fragments: in each 16-lane group g, lane j points at
+        // k-row 8 (g/2) + j/4 and columns base + 16 (g%2) + 4 (j%4)..+3
+        const int g = lane >> 4, jl = lane & 15;
+        const int kr = 8 * (g >> 1) + (jl >> 2);
+        int a_lane[4], b_lane[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int m = 128 * wm + 32 * q + 16 * (g & 1) + 4 * (jl & 3);
+            const int n = 128 * wn + 32 * q + 16 * (g & 1) + 4 * (jl & 3);
+            a_lane[q] = kr * kN + b_swz(m >> 3, kr) * 8 + (m & 7);
+            b_lane[q] = kr * kN + b_swz(n >> 3, kr) * 8 + (n & 7);
+        }
+        auto tr8 = [&](const uint16_t* s) {
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(s));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(s + 4 * kN));
+            const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            return __builtin_bit_cast(bf16x8, v);
+        };
+        auto compute = [&](int buf) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                bf16x8 fa[4], fb[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    fa[q] = tr8(sA(buf) + a_lane[q] + 16 * ks * kN);
+                    fb[q] = tr8(sB(buf) + b_lane[q] + 16 * ks * kN);
+                }
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        acc[mi][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[q], acc[mi][q], 0, 0, 0);
+            }
+        };
+        auto clampk = [&](int k) { return min(k, KT - 1); };
+        TnStage rs[kSetsB];
+#pragma unroll
+        for (int i = 0; i < kSetsB; ++i) load(clampk(i), rs[i]);
+        store(0, rs[0]);
+        load(clampk(3), rs[0]);
+        store(1, rs[1]);
+        load(clampk(4), rs[1]);
+        lds_barrier();
+        auto step = [&](int kt, int buf, TnStage& r) {
+            compute(buf);
+            store(buf == 0 ? 2 : buf - 1, r);
+            load(clampk(kt + 5), r);
+            lds_barrier();
+            return buf == kRingB - 1 ? 0 : buf + 1;
+        };
+        int buf = 0;
+        for (int kt = 0; kt < KT; kt += kSetsB) {
+#pragma unroll
+            for (int u = 0; u < kSetsB; ++u) buf = step(kt + u, buf, rs[(u + 2) % kSetsB]);
+        }
+    }
+
+    // Epilogue: 32 lanes write 32 consecutive fp32 of one row per register.
+    const int col_l = lane & 31;
+    const int row_l = 4 * (lane >> 5);
+    float* C = p.C0;
+    int cbase = n0 + 128 * wn;
+    if (p.pair > 0) {
+        // wavefront column half wn: 0 -> first output, 1 -> second
+        C = wn ? p.C1 : p.C0;
+        cbase = n0;
+    }
+    C += (size_t)e * p.M * p.Nc;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int col = cbase + 32 * q + col_l;
+            if (col >= p.Nc) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + 128 * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
+                if (row < p.M) C[(size_t)row * p.Nc + col] = p.scale * acc[mi][q][r];
+            }
+        }
+}
+
+// ------------------------------------------------------------ generic kernels
+
+constexpr int kGM = 64, kGN = 64, kGK = 16;
+
+// Data gradients, any shape and element type: 64 x 64 output tiles of the
+// row-grouped product, one thread 4 x 4 outputs.
+template <typename XT, int EPI>
+__global__ __launch_bounds__(256) void nt_generic_kernel(
+    const XT* __restrict__ A, int K, const XT* __restrict__ B0, const XT* __restrict__ B1, int K0,
+    int N, void* __restrict__ C, const XT* __restrict__ act, const int32_t* __restrict__ offsets,
+    int rows, int E)
+{
+    __shared__ float sA[kGM][kGK + 1];
+    __shared__ float sB[kGK][kGN + 1];
+    __shared__ int s_sched[2 * kMaxE + 1];
+    __shared__ int scratch[256 / kWave + 1];
+    Tile tile;
+    if (!schedule_tile(offsets, rows, E, kGM, (N + kGN - 1) / kGN, s_sched, s_sched + kMaxE + 1,
+                       scratch, tile))
+        return;
+    const int tid = threadIdx.x;
+    const int tx = tid % 16, ty = tid / 16;
+    const int m0 = tile.m0, seg_last = tile.seg_end - 1;
+    const int n0 = tile.n_tile * kGN;
+    const int K1 = K - K0;
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    for (int k0 = 0; k0 < K; k0 += kGK) {
+        for (int q = tid; q < kGM * kGK; q += 256) {
+            const int r = q / kGK, kk = q % kGK;
+            const int kx = k0 + kk;
+            sA[r][kk] = kx < K ? Elem<XT>::load(A, (size_t)min(m0 + r, seg_last) * K + kx) : 0.f;
+        }
+        for (int q = tid; q < kGK * kGN; q += 256) {
+            const int kk = q / kGN, c = q % kGN;
+            const int kx = k0 + kk, n = n0 + c;
+            float v = 0.f;
+            if (kx < K && n < N) {
+                const size_t nr = (size_t)tile.e * N + n;
+                v = kx < K0 ? Elem<XT>::load(B0, nr * K0 + kx) : Elem<XT>::load(B1, nr * K1 + (kx - K0));
+            }
+            sB[kk][c] = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < kGK; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = sA[ty * 4 + i][kk];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = sB[kk][tx * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = m0 + ty * 4 + i;
+        if (row > seg_last) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = n0 + tx * 4 + j;
+            if (col >= N) continue;
+            const float v = acc[i][j];
+            if constexpr (EPI == kNtSwigluBwd) {
+                const size_t o = (size_t)row * 2 * N + col;
+                float da, dv;
+                swiglu_bwd(v, Elem<XT>::load(act, o), Elem<XT>::load(act, o + N), da, dv);
+                Elem<XT>::store(static_cast<XT*>(C), o, da);
+                Elem<XT>::store(static_cast<XT*>(C), o + N, dv);
+            } else if constexpr (EPI == kNtStoreF32) {
+                static_cast<float*>(C)[(size_t)row * N + col] = v;
+            } else if constexpr (EPI == kNtAccumF32) {
+                static_cast<float*>(C)[(size_t)row * N + col] += v;
+            } else {
+                Elem<uint16_t>::store(static_cast<uint16_t*>(C), (size_t)row * N + col, v);
+            }
+        }
+    }
+}
+
+// Weight gradients, any shape and element type: one 64 x 64 tile of
+// C_e = scale * A_e^T B_e per block.
+template <typename XT>
+__global__ __launch_bounds__(256) void tn_generic_kernel(
+    const XT* __restrict__ A, int lda, int M, const XT* __restrict__ B, int ldb, int Nc, int pair,
+    float* __restrict__ C0, float* __restrict__ C1, float scale,
+    const int32_t* __restrict__ offsets, int rows, int E)
+{
+    __shared__ float sA[kGK][kGM + 1];
+    __shared__ float sB[kGK][kGN + 1];
+    const int mt_n = (M + kGM - 1) / kGM;
+    const int halves = pair > 0 ? 2 : 1;
+    const int nt_n = (Nc + kGN - 1) / kGN;
+    const int per_e = mt_n * nt_n * halves;
+    const int t = blockIdx.x;
+    if (t >= E * per_e) return;
+    const int e = t / per_e;
+    const int rest = t % per_e;
+    const int half = rest / (mt_n * nt_n);
+    const int mt = (rest % (mt_n * nt_n)) / nt_n;
+    const int nt = rest % nt_n;
+    const int m0 = mt * kGM, n0 = nt * kGN;
+    const int bcol0 = half ? pair : 0;
+    const int j0 = offsets ? min(max(offsets[e], 0), rows) : 0;
+    const int j1 = offsets ? max(j0, min(offsets[e + 1], rows)) : rows;
+    const int tid = threadIdx.x;
+    const int tx = tid % 16, ty = tid / 16;
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    for (int k0 = j0; k0 < j1; k0 += kGK) {
+        for (int q = tid; q < kGK * kGM; q += 256) {
+            const int kk = q / kGM, c = q % kGM;
+            const int j = k0 + kk, m = m0 + c;
+            sA[kk][c] = (j < j1 && m < M) ? Elem<XT>::load(A, (size_t)j * lda + m) : 0.f;
+        }
+        for (int q = tid; q < kGK * kGN; q += 256) {
+            const int kk = q / kGN, c = q % kGN;
+            const int j = k0 + kk, n = n0 + c;
+            sB[kk][c] = (j < j1 && n < Nc) ? Elem<XT>::load(B, (size_t)j * ldb + bcol0 + n) : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < kGK; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = sA[kk][ty * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = sB[kk][tx * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+    float* C = (half ? C1 : C0) + (size_t)e * M * Nc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + ty * 4 + i;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + tx * 4 + j;
+            if (n < Nc) C[(size_t)m * Nc + n] = scale * acc[i][j];
+        }
+    }
+}
+
+// ----------------------------------------------------------------- launches
+
+static bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// C[rows, N] = A[rows, K] . B_e^T on the rows of each group (offsets NULL:
+// one group of all rows), with epilogue `epi`.
+hipError_t launch_nt(int epi, const void* A, moe_dtype dt, int rows, int K, int K0, int N, int E,
+                     const int32_t* offsets, const void* B0, const void* B1, void* C,
+                     const void* act, hipStream_t st)
+{
+    const bool mfma = dt == MOE_BF16 && K % kK == 0 && K0 % kK == 0 && K0 > 0 && N % 8 == 0 &&
+                      al16(A) && al16(B0) && al16(B1) && (epi != kNtSwigluBwd || N % 2 == 0);
+    if (mfma) {
+        NtArgs p{(const uint16_t*)A, K, (const uint16_t*)B0, (const uint16_t*)B1, K0, N, C,
+                 (const uint16_t*)act};
+        const unsigned g = mfma_grid(rows, E, (N + kN - 1) / kN);
+        switch (epi) {
+        case kNtSwigluBwd: nt_mfma_kernel<kNtSwigluBwd><<<g, kT, 0, st>>>(p, offsets, rows, E); break;
+        case kNtStoreF32: nt_mfma_kernel<kNtStoreF32><<<g, kT, 0, st>>>(p, offsets, rows, E); break;
+        case kNtAccumF32: nt_mfma_kernel<kNtAccumF32><<<g, kT, 0, st>>>(p, offsets, rows, E); break;
+        default: nt_mfma_kernel<kNtStoreBf16><<<g, kT, 0, st>>>(p, offsets, rows, E); break;
+        }
+        return hipGetLastError();
+    }
+    const long long tiles = max_row_tiles(rows, E, kGM) * ((N + kGN - 1) / kGN);
+    const unsigned g = (unsigned)std::max(8LL, (tiles + 7) / 8 * 8);
+#define NT_GEN(XT)                                                                                  \
+    switch (epi) {                                                                                  \
+    case kNtSwigluBwd: nt_generic_kernel<XT, kNtSwigluBwd><<<g, 256, 0, st>>>(                     \
+        (const XT*)A, K, (const XT*)B0, (const XT*)B1, K0, N, C, (const XT*)act, offsets, rows, E); \
+        break;                                                                                      \
+    case kNtStoreF32: nt_generic_kernel<XT, kNtStoreF32><<<g, 256, 0, st>>>(                       \
+        (const XT*)A, K, (const XT*)B0, (const XT*)B1, K0, N, C, (const XT*)act, offsets, rows, E); \
+        break;                                                                                      \
+    case kNtAccumF32: nt_generic_kernel<XT, kNtAccumF32><<<g, 256, 0, st>>>(                       \
+        (const XT*)A, K, (const XT*)B0, (const XT*)B1, K0, N, C, (const XT*)act, offsets, rows, E); \
+        break;                                                                                      \
+    default: nt_generic_kernel<XT, kNtStoreBf16><<<g, 256, 0, st>>>(                               \
+        (const XT*)A, K, (const XT*)B0, (const XT*)B1, K0, N, C, (const XT*)act, offsets, rows, E); \
+        break;                                                                                      \
+    }
+    if (dt == MOE_BF16) { NT_GEN(uint16_t) } else { NT_GEN(float) }
+#undef NT_GEN
+    return hipGetLastError();
+}
+
+// C_e[M, Nc] = scale * A_e^T B_e over the rows of each group (offsets NULL:
+// one group of all rows); pair > 0: B columns [0, Nc) -> C0 and
+// [pair, pair + Nc) -> C1.
+hipError_t launch_tn(const void* A, int lda, int M, const void* B, int ldb, int Nc, int pair,
+                     moe_dtype dt, int rows, int E, const int32_t* offsets, float scale,
+                     float* C0, float* C1, hipStream_t st)
+{
+    const bool mfma = dt == MOE_BF16 && lda % 8 == 0 && ldb % 8 == 0 && M % 8 == 0 &&
+                      Nc % 8 == 0 && pair % 8 == 0 && M >= 8 && Nc >= 8 && al16(A) && al16(B);
+    if (mfma) {
+        TnArgs p{(const uint16_t*)A, lda, M, (const uint16_t*)B, ldb, Nc, pair, C0, C1, scale};
+        const long long tiles = (long long)E * ((M + kN - 1) / kN) *
+                                ((Nc + (pair > 0 ? 128 : kN) - 1) / (pair > 0 ? 128 : kN));
+        const unsigned g = (unsigned)std::max(8LL, (tiles + 7) / 8 * 8);
+        tn_mfma_kernel<<<g, kT, 0, st>>>(p, offsets, rows, E);
+        return hipGetLastError();
+    }
+    const long long tiles = (long long)E * ((M + kGM - 1) / kGM) * ((Nc + kGN - 1) / kGN) *
+                            (pair > 0 ? 2 : 1);
+    if (dt == MOE_BF16)
+        tn_generic_kernel<uint16_t><<<(unsigned)tiles, 256, 0, st>>>(
+            (const uint16_t*)A, lda, M, (const uint16_t*)B, ldb, Nc, pair, C0, C1, scale, offsets,
+            rows, E);
+    else
+        tn_generic_kernel<float><<<(unsigned)tiles, 256, 0, st>>>(
+            (const float*)A, lda, M, (const float*)B, ldb, Nc, pair, C0, C1, scale, offsets, rows, E);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -34,163 +34,9 @@
 #include <algorithm>
 #include <type_traits>
 
-#include "common.hpp"
+#include "mfma_common.hpp"
 
 namespace moe {
-
-constexpr int kMaxE = 4096;
-constexpr int kGroupM = 4;   // row tiles per scheduling group inside an expert
-
-// ----------------------------------------------------------- tile scheduler
-
-struct Tile {
-    int e, m0, seg_end, n_tile, bm;
-    int stream;   // matrix-core kernel: the tile's weight panel is read by no other tile
-};
-
-// All threads of the block must call it. s_off needs E+1 ints, s_pre E ints.
-__device__ bool schedule_tile(const int32_t* __restrict__ offsets, int N, int E, int bm,
-                              int n_tiles, int* s_off, int* s_pre, int* scratch, Tile& tile)
-{
-    const int tid = threadIdx.x;
-    for (int e = tid; e <= E; e += blockDim.x) s_off[e] = min(max(offsets[e], 0), N);
-    __syncthreads();
-    for (int e = tid; e < E; e += blockDim.x) {
-        const int lo = s_off[e];
-        const int hi = max(lo, s_off[e + 1]);
-        s_pre[e] = (hi - lo + bm - 1) / bm * n_tiles;
-    }
-    __syncthreads();
-    const int total = block_exclusive_scan_lds(s_pre, E, scratch);
-    const int per_xcd = (total + 7) / 8;
-    const int b = blockIdx.x;
-    const int slot = b / 8;
-    if (slot >= per_xcd) return false;
-    const int t = (b % 8) * per_xcd + slot;
-    if (t >= total) return false;
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_pre[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    const int e = lo;
-    const int rows_lo = s_off[e];
-    const int rows_hi = max(rows_lo, s_off[e + 1]);
-    const int mt = (rows_hi - rows_lo + bm - 1) / bm;
-    const int local = t - s_pre[e];
-    // inside an expert, groups of kGroupM row tiles sweep all column tiles
-    // (row tile fastest): the tiles resident on an XCD at one time share a
-    // few A row panels and a few weight panels through its L2
-    const int grp = local / (kGroupM * n_tiles);
-    const int within = local - grp * (kGroupM * n_tiles);
-    const int gsz = min(kGroupM, mt - grp * kGroupM);
-    tile.e = e;
-    tile.n_tile = within / gsz;
-    tile.m0 = rows_lo + (grp * kGroupM + within % gsz) * bm;
-    tile.seg_end = rows_hi;
-    tile.bm = bm;
-    return true;
-}
-
-// Tile list of the matrix-core kernel, two tile heights in one launch. An
-// expert with n rows gets n / 256 tiles of 256 rows; a remainder above 128
-// rows one more 256-row tile, a remainder of at most 128 rows one 128-row tile
-// (a 256-row tile would be more than half padding there). Every row tile
-// spans all n_tiles column tiles. Tile indices [0, big) are the 256-row tiles
-// (expert by expert; inside an expert groups of kGroupM row tiles sweep all
-// column tiles, row tile fastest), [big, big + small) the 128-row tiles.
-struct TileList {
-    const int* off;     // [E+1] clamped offsets
-    const int* big;     // [E] exclusive prefix of 256-row tiles x n_tiles
-    const int* small;   // [E] exclusive prefix of 128-row tiles x n_tiles
-    int E, n_tiles, total_big, total_small;
-};
-
-// All threads of the block must call it. s_off needs E+1 ints, s_big and
-// s_small E ints each.
-__device__ TileList build_tile_list(const int32_t* __restrict__ offsets, int N, int E,
-                                    int n_tiles, int* s_off, int* s_big, int* s_small,
-                                    int* scratch)
-{
-    const int tid = threadIdx.x;
-    for (int e = tid; e <= E; e += blockDim.x) s_off[e] = min(max(offsets[e], 0), N);
-    __syncthreads();
-    for (int e = tid; e < E; e += blockDim.x) {
-        const int n = max(0, s_off[e + 1] - s_off[e]);
-        const int rem = n & 255;
-        s_big[e] = ((n >> 8) + (rem > 128 ? 1 : 0)) * n_tiles;
-        s_small[e] = (rem > 0 && rem <= 128) ? n_tiles : 0;
-    }
-    __syncthreads();
-    TileList L;
-    L.off = s_off;
-    L.big = s_big;
-    L.small = s_small;
-    L.E = E;
-    L.n_tiles = n_tiles;
-    L.total_big = __builtin_amdgcn_readfirstlane(block_exclusive_scan_lds(s_big, E, scratch));
-    L.total_small = __builtin_amdgcn_readfirstlane(block_exclusive_scan_lds(s_small, E, scratch));
-    return L;
-}
-
-// Largest e with pre[e] <= t (pre is an exclusive prefix over E entries, so
-// experts owning no tile are skipped).
-__device__ __forceinline__ int find_owner(const int* pre, int E, int t) {
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (pre[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
-// Tile t of the list, 0 <= t < total_big + total_small.
-__device__ Tile decode_tile(const TileList& L, int t) {
-    Tile tile;
-    if (t < L.total_big) {
-        const int e = find_owner(L.big, L.E, t);
-        const int rows_lo = L.off[e];
-        const int rows_hi = max(rows_lo, L.off[e + 1]);
-        const int n = rows_hi - rows_lo;
-        const int mt = (n >> 8) + ((n & 255) > 128 ? 1 : 0);
-        const int local = t - L.big[e];
-        const int grp = local / (kGroupM * L.n_tiles);
-        const int within = local - grp * (kGroupM * L.n_tiles);
-        const int gsz = min(kGroupM, mt - grp * kGroupM);
-        tile.e = e;
-        tile.n_tile = within / gsz;
-        tile.m0 = rows_lo + (grp * kGroupM + within % gsz) * 256;
-        tile.seg_end = rows_hi;
-        tile.bm = 256;
-        tile.stream = mt < 2;
-    } else {
-        t -= L.total_big;
-        const int e = find_owner(L.small, L.E, t);
-        const int rows_lo = L.off[e];
-        const int rows_hi = max(rows_lo, L.off[e + 1]);
-        tile.e = e;
-        tile.n_tile = t - L.small[e];
-        tile.m0 = rows_lo + ((rows_hi - rows_lo) >> 8) * 256;
-        tile.seg_end = rows_hi;
-        tile.bm = 128;
-        // remainder tiles run after all 256-row tiles: whatever the expert's
-        // other tiles read is long gone from L2
-        tile.stream = 1;
-    }
-    // uniform over the block: keep the fields in scalar registers
-    tile.e = __builtin_amdgcn_readfirstlane(tile.e);
-    tile.m0 = __builtin_amdgcn_readfirstlane(tile.m0);
-    tile.seg_end = __builtin_amdgcn_readfirstlane(tile.seg_end);
-    tile.n_tile = __builtin_amdgcn_readfirstlane(tile.n_tile);
-    tile.bm = __builtin_amdgcn_readfirstlane(tile.bm);
-    tile.stream = __builtin_amdgcn_readfirstlane(tile.stream);
-    return tile;
-}
-
-static long long max_row_tiles(int N, int E, int bm) {
-    // sum_e ceil(n_e / bm) <= (N + E * (bm - 1)) / bm
-    return ((long long)N + (long long)E * (bm - 1)) / bm;
-}
 
 // ------------------------------------------------------ matrix-core kernel
 
@@ -201,10 +47,6 @@ constexpr int kMfmaThreads = 256;
 constexpr int kBChunks = BK * BNB / 8 / kMfmaThreads;   // 16-byte B chunks per thread per stage
 constexpr int kRing = 3;      // LDS stage buffers
 constexpr int kSets = 3;      // register stages in flight (global-load prefetch distance)
-
-#define LDS_AS __attribute__((address_space(3)))
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 // Barrier that lets up to P of this wave's most recent LDS operations still be
 // in flight (LDS operations of a wave complete in order). The main loop issues
@@ -219,30 +61,6 @@ __device__ __forceinline__ void lds_barrier_pending() {
         asm volatile("s_waitcnt lgkmcnt(12)\n\ts_barrier" ::: "memory");
     else
         asm volatile("s_waitcnt lgkmcnt(10)\n\ts_barrier" ::: "memory");
-}
-
-// silu(z) = z * sigmoid(z) with the hardware exp2 and reciprocal (about 1 ulp
-// each; h is rounded to bf16 right after, 2^-9 relative). For z -> -inf,
-// 1 + exp(-z) overflows to +inf and the reciprocal gives 0, so silu -> -0.
-__device__ __forceinline__ float silu_fast(float z) {
-    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
-}
-
-// Stage layouts in LDS (no padding; XOR swizzles of 16-byte chunks inside a
-// row keep the fragment reads and the staging writes free of bank conflicts,
-// both for LDS phases of 8 lanes x 16 bytes over 32 banks and of 16 lanes x
-// 16 bytes (32 lanes x 8 bytes) over 64 banks):
-//  A: [rows][BK], chunk c of row r stored at a_swz(c, r);
-//  B: [BK k-rows][BNB columns], N-contiguous as in memory, chunk c of k-row r
-//     stored at b_swz(c, r). B fragments are read with the gfx950 LDS
-//     transpose read (ds_read_b64_tr_b16): in each 16-lane group, lane j
-//     points at k-row j/4, columns 4*(j%4)..+3 of a 4 x 16 block and receives
-//     the 4 k-values of column j.
-__device__ __forceinline__ int a_swz(int c, int r) {
-    return c ^ (((r >> 1) ^ (r >> 3)) & 3);
-}
-__device__ __forceinline__ int b_swz(int c, int r) {
-    return c ^ (2 * (r & 3)) ^ (8 * ((c >> 1) & 1));
 }
 
 // LDS of the kernel: the stage ring (96 KB, sized for 256-row tiles; the
@@ -304,10 +122,11 @@ struct TileSrc {
 // One output tile of TM rows (256 or 128) x 256 B-columns. The 4 wavefronts
 // form a 2 x 2 grid, each computing TM/2 x 128 as a (TM/64) x 4 grid of
 // v_mfma_f32_32x32x16_bf16 accumulators held in AGPRs.
-template <bool GATE_UP, bool Y_BF16, int TM, bool STREAM>
+template <bool GATE_UP, bool Y_BF16, int TM, bool STREAM, bool SAVE>
 __device__ __forceinline__ void ffn_mfma_tile(
     const uint16_t* __restrict__ A, int K, int NC, const uint16_t* __restrict__ B0,
-    const uint16_t* __restrict__ B1, void* __restrict__ C, const Tile& tile, uint16_t* smem)
+    const uint16_t* __restrict__ B1, void* __restrict__ C, uint16_t* __restrict__ act,
+    const Tile& tile, uint16_t* smem)
 {
     constexpr int kMI = TM / 64;                               // 32-row blocks per wavefront
     constexpr int kAChunks = TM * BK / 8 / kMfmaThreads;       // 16-byte A chunks per thread per stage
@@ -510,39 +329,50 @@ __device__ __forceinline__ void ffn_mfma_tile(
     if (GATE_UP) {
         // The bf16 h tile is staged row-major through the (now idle) LDS ring
         // and leaves with 16-byte row-contiguous stores instead of one 2-byte
-        // store per element.
-        lds_barrier();   // every wave is done with the stage buffers
+        // store per element. With `act` (training) the pre-activations a and v
+        // of the tile follow the same way, into act[:, 0:f] and act[:, f:2f].
         // h tile: TM rows x 128 hidden columns, bf16, row stride 136 elements
         // (256 rows: 69632 bytes of the 96 KB ring)
         constexpr int HS = 136;
         uint16_t* sh = smem;
+        // which = 0: h, 1: a, 2: v
+        auto stage_out = [&](int which, uint16_t* dst, int ld, int col0) {
+            lds_barrier();   // every wave is done with the ring (stages or the last tile)
 #pragma unroll
-        for (int mi = 0; mi < kMI; ++mi)
+            for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+                for (int q = 0; q < 2; ++q)
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    // rows r and r+1 of a lane are adjacent: one packed conversion
-                    const int row = (TM / 2) * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
-                    const int col = 64 * wn + 32 * q + col_l;
-                    const float g0 = acc[mi][q][r], g1 = acc[mi][q][r + 1];
-                    const float h0 = silu_fast(g0) * acc[mi][q + 2][r];
-                    const float h1 = silu_fast(g1) * acc[mi][q + 2][r + 1];
-                    const unsigned pk = f32x2_to_bf16x2(h0, h1);
-                    sh[row * HS + col] = (uint16_t)pk;
-                    sh[(row + 1) * HS + col] = (uint16_t)(pk >> 16);
+                    for (int r = 0; r < 16; r += 2) {
+                        // rows r and r+1 of a lane are adjacent: one packed conversion
+                        const int row = (TM / 2) * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
+                        const int col = 64 * wn + 32 * q + col_l;
+                        const float g0 = acc[mi][q][r], g1 = acc[mi][q][r + 1];
+                        const float v0 = acc[mi][q + 2][r], v1 = acc[mi][q + 2][r + 1];
+                        float o0, o1;
+                        if (which == 0) { o0 = silu_fast(g0) * v0; o1 = silu_fast(g1) * v1; }
+                        else if (which == 1) { o0 = g0; o1 = g1; }
+                        else { o0 = v0; o1 = v1; }
+                        const unsigned pk = f32x2_to_bf16x2(o0, o1);
+                        sh[row * HS + col] = (uint16_t)pk;
+                        sh[(row + 1) * HS + col] = (uint16_t)(pk >> 16);
+                    }
+            lds_barrier();
+            // TM rows x 16 chunks of 8 columns; thread -> chunk tid%16, rows tid/16 + 16 i
+#pragma unroll
+            for (int i = 0; i < TM / 16; ++i) {
+                const int row = (tid >> 4) + 16 * i;
+                const int c8 = (tid & 15) * 8;
+                if (full || m0 + row <= seg_last) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(&sh[row * HS + c8]);
+                    *reinterpret_cast<u32x4*>(&dst[(size_t)(m0 + row) * ld + col0 + c8]) = v;
                 }
-        lds_barrier();
-        uint16_t* H = static_cast<uint16_t*>(C);
-        // TM rows x 16 chunks of 8 columns; thread -> chunk tid%16, rows tid/16 + 16 i
-#pragma unroll
-        for (int i = 0; i < TM / 16; ++i) {
-            const int row = (tid >> 4) + 16 * i;
-            const int c8 = (tid & 15) * 8;
-            if (full || m0 + row <= seg_last) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(&sh[row * HS + c8]);
-                *reinterpret_cast<u32x4*>(&H[(size_t)(m0 + row) * NC + n0 + c8]) = v;
             }
+        };
+        stage_out(0, static_cast<uint16_t*>(C), NC, n0);
+        if constexpr (SAVE) {
+            stage_out(1, act, 2 * NC, n0);
+            stage_out(2, act, 2 * NC, NC + n0);
         }
     } else if (Y_BF16) {
         // y in bf16: registers r, r+1 of a lane are rows i, i+1 of one column and
@@ -591,11 +421,11 @@ __device__ __forceinline__ void ffn_mfma_tile(
 // (G = grid size), so in every pass i each XCD (block b runs on XCD b % 8)
 // takes a contiguous run of the tile list and the tiles of one expert meet
 // on one XCD and share its L2.
-template <bool GATE_UP, bool Y_BF16>
+template <bool GATE_UP, bool Y_BF16, bool SAVE>
 __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int N, int K, int NC,
     int E, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
-    void* __restrict__ C)
+    void* __restrict__ C, uint16_t* __restrict__ act)
 {
     constexpr int BNT = GATE_UP ? 128 : 256;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[kSmemElems];
@@ -609,11 +439,11 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
     for (int t = base; t < total; t += G) {
         const Tile tile = decode_tile(L, t);
         if (tile.bm == 128)
-            ffn_mfma_tile<GATE_UP, Y_BF16, 128, true>(A, K, NC, B0, B1, C, tile, smem);
+            ffn_mfma_tile<GATE_UP, Y_BF16, 128, true, SAVE>(A, K, NC, B0, B1, C, act, tile, smem);
         else if (tile.stream)
-            ffn_mfma_tile<GATE_UP, Y_BF16, 256, true>(A, K, NC, B0, B1, C, tile, smem);
+            ffn_mfma_tile<GATE_UP, Y_BF16, 256, true, SAVE>(A, K, NC, B0, B1, C, act, tile, smem);
         else
-            ffn_mfma_tile<GATE_UP, Y_BF16, 256, false>(A, K, NC, B0, B1, C, tile, smem);
+            ffn_mfma_tile<GATE_UP, Y_BF16, 256, false, SAVE>(A, K, NC, B0, B1, C, act, tile, smem);
     }
 }
 
@@ -624,7 +454,8 @@ constexpr int GBM = 64, GBN = 64, GBK = 16;
 template <typename XT, typename OT, bool GATE_UP>
 __global__ __launch_bounds__(256) void ffn_generic_kernel(
     const XT* __restrict__ A, const int32_t* __restrict__ offsets, int N, int K, int NC, int E,
-    const XT* __restrict__ B0, const XT* __restrict__ B1, OT* __restrict__ C)
+    const XT* __restrict__ B0, const XT* __restrict__ B1, OT* __restrict__ C,
+    OT* __restrict__ act)
 {
     __shared__ float sAg[GBM][GBK + 1];
     __shared__ float sB0[GBK][GBN];
@@ -693,7 +524,13 @@ __global__ __launch_bounds__(256) void ffn_generic_kernel(
             const int col = n0 + tx * 4 + j;
             if (col >= NC) continue;
             float v = acc0[i][j];
-            if (GATE_UP) v = v / (1.0f + __expf(-v)) * acc1[i][j];
+            if (GATE_UP) {
+                if (act) {
+                    Elem<OT>::store(act, (size_t)row * 2 * NC + col, v);
+                    Elem<OT>::store(act, (size_t)row * 2 * NC + NC + col, acc1[i][j]);
+                }
+                v = v / (1.0f + __expf(-v)) * acc1[i][j];
+            }
             Elem<OT>::store(C, (size_t)row * NC + col, v);
         }
     }
@@ -712,25 +549,6 @@ bool ffn_down_uses_mfma(moe_dtype dt, int f, int d, const void* h, const void* w
     return dt == MOE_BF16 && f % BK == 0 && d % 256 == 0 && aligned16(h) && aligned16(wo);
 }
 
-// Persistent grid: one block per compute unit (the kernel's LDS and registers
-// allow no second one), rounded down to a multiple of 8, and no more blocks
-// than there can be tiles (sum_e ceil(n_e / 128) row tiles at most).
-static unsigned mfma_grid(int N, int E, int n_tiles) {
-    static int cus[64] = {0};
-    int dev = 0;
-    hipGetDevice(&dev);
-    int& c = cus[dev & 63];
-    if (c == 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-            v = 256;
-        c = v;
-    }
-    const long long cap = std::max(8, c / 8 * 8);
-    const long long tiles = max_row_tiles(N, E, 128) * n_tiles;
-    return (unsigned)std::max(8LL, std::min(cap, (tiles + 7) / 8 * 8));
-}
-
 static unsigned grid_for(long long tiles) {
     long long g = (tiles + 7) / 8 * 8;
     return (unsigned)std::max(8LL, g);
@@ -738,21 +556,28 @@ static unsigned grid_for(long long tiles) {
 
 hipError_t launch_gate_up(const void* x, moe_dtype dt, int N, int d, int f, int E,
                           const int32_t* offsets, const void* wg, const void* wv, void* h,
-                          hipStream_t st)
+                          void* act, hipStream_t st)
 {
-    if (ffn_gate_up_uses_mfma(dt, d, f, x, wg, wv, h)) {
-        ffn_mfma_kernel<true, false><<<mfma_grid(N, E, f / 128), kMfmaThreads, 0, st>>>(
-            (const uint16_t*)x, offsets, N, d, f, E, (const uint16_t*)wg, (const uint16_t*)wv, h);
+    if (ffn_gate_up_uses_mfma(dt, d, f, x, wg, wv, h) && aligned16(act)) {
+        const unsigned g = mfma_grid(N, E, f / 128);
+        if (act)
+            ffn_mfma_kernel<true, false, true><<<g, kMfmaThreads, 0, st>>>(
+                (const uint16_t*)x, offsets, N, d, f, E, (const uint16_t*)wg, (const uint16_t*)wv,
+                h, (uint16_t*)act);
+        else
+            ffn_mfma_kernel<true, false, false><<<g, kMfmaThreads, 0, st>>>(
+                (const uint16_t*)x, offsets, N, d, f, E, (const uint16_t*)wg, (const uint16_t*)wv,
+                h, nullptr);
     } else {
         const long long tiles = max_row_tiles(N, E, GBM) * ((f + GBN - 1) / GBN);
         if (dt == MOE_BF16)
             ffn_generic_kernel<uint16_t, uint16_t, true><<<grid_for(tiles), 256, 0, st>>>(
                 (const uint16_t*)x, offsets, N, d, f, E, (const uint16_t*)wg,
-                (const uint16_t*)wv, (uint16_t*)h);
+                (const uint16_t*)wv, (uint16_t*)h, (uint16_t*)act);
         else
             ffn_generic_kernel<float, float, true><<<grid_for(tiles), 256, 0, st>>>(
                 (const float*)x, offsets, N, d, f, E, (const float*)wg, (const float*)wv,
-                (float*)h);
+                (float*)h, (float*)act);
     }
     return hipGetLastError();
 }
@@ -764,11 +589,11 @@ hipError_t launch_down(const void* h, moe_dtype dt, int N, int f, int d, int E,
     if (ffn_down_uses_mfma(dt, f, d, h, wo) && aligned16(y)) {
         const unsigned grid = mfma_grid(N, E, d / 256);
         if (y_dt == MOE_BF16)
-            ffn_mfma_kernel<false, true><<<grid, kMfmaThreads, 0, st>>>(
-                (const uint16_t*)h, offsets, N, f, d, E, (const uint16_t*)wo, nullptr, y);
+            ffn_mfma_kernel<false, true, false><<<grid, kMfmaThreads, 0, st>>>(
+                (const uint16_t*)h, offsets, N, f, d, E, (const uint16_t*)wo, nullptr, y, nullptr);
         else
-            ffn_mfma_kernel<false, false><<<grid, kMfmaThreads, 0, st>>>(
-                (const uint16_t*)h, offsets, N, f, d, E, (const uint16_t*)wo, nullptr, y);
+            ffn_mfma_kernel<false, false, false><<<grid, kMfmaThreads, 0, st>>>(
+                (const uint16_t*)h, offsets, N, f, d, E, (const uint16_t*)wo, nullptr, y, nullptr);
     } else {
         const long long tiles = max_row_tiles(N, E, GBM) * ((d + GBN - 1) / GBN);
         const unsigned g = grid_for(tiles);
@@ -776,18 +601,20 @@ hipError_t launch_down(const void* h, moe_dtype dt, int N, int f, int d, int E,
             if (y_dt == MOE_BF16)
                 ffn_generic_kernel<uint16_t, uint16_t, false><<<g, 256, 0, st>>>(
                     (const uint16_t*)h, offsets, N, f, d, E, (const uint16_t*)wo, nullptr,
-                    (uint16_t*)y);
+                    (uint16_t*)y, nullptr);
             else
                 ffn_generic_kernel<uint16_t, float, false><<<g, 256, 0, st>>>(
                     (const uint16_t*)h, offsets, N, f, d, E, (const uint16_t*)wo, nullptr,
-                    (float*)y);
+                    (float*)y, nullptr);
         } else {
             if (y_dt == MOE_BF16)
                 ffn_generic_kernel<float, uint16_t, false><<<g, 256, 0, st>>>(
-                    (const float*)h, offsets, N, f, d, E, (const float*)wo, nullptr, (uint16_t*)y);
+                    (const float*)h, offsets, N, f, d, E, (const float*)wo, nullptr, (uint16_t*)y,
+                    nullptr);
             else
                 ffn_generic_kernel<float, float, false><<<g, 256, 0, st>>>(
-                    (const float*)h, offsets, N, f, d, E, (const float*)wo, nullptr, (float*)y);
+                    (const float*)h, offsets, N, f, d, E, (const float*)wo, nullptr, (float*)y,
+                    nullptr);
         }
     }
     return hipGetLastError();

@@ -294,6 +294,69 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     }
 }
 
+// Backward of the router weights, one wavefront per token. With g the
+// weights of the k selected experts and dg their gradients, gdg = sum_s g_s dg_s:
+//  renorm:    g = softmax over the selected logits, so
+//             d_l[e_s] = g_s (dg_s - gdg) and 0 for every other expert;
+//  otherwise: g_s = p_{e_s} with p the softmax over all E, so
+//             d_l[e] = p_e ([e = e_s] dg_s - gdg).
+// The selection itself is piecewise constant and passes no gradient. d_l is
+// written in fp32 and, if asked, as a bf16 copy for the matrix-core products
+// with x and W_r.
+__global__ __launch_bounds__(256) void route_bwd_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ gates, const float* __restrict__ d_gates, int T, int E, int k,
+    int renorm, float* __restrict__ d_logits, uint16_t* __restrict__ d_logits_bf16)
+{
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T) return;
+    const int lane = lane_id();
+    int my_e = -1;
+    float my_g = 0.0f, my_dg = 0.0f;
+    if (lane < k) {
+        my_e = topk_idx[(size_t)t * k + lane];
+        my_g = gates[(size_t)t * k + lane];
+        my_dg = d_gates[(size_t)t * k + lane];
+    }
+    const float gdg = wave_sum_f32(my_g * my_dg);
+    const float* l = logits + (size_t)t * E;
+    float m = 0.0f, denom = 1.0f;
+    if (!renorm) {
+        // the softmax over all E from the top logit (slot 0 holds it)
+        m = l[min(max(__shfl(my_e, 0, kWave), 0), E - 1)];
+        float part = 0.0f;
+        for (int e = lane; e < E; e += kWave) part += expf(l[e] - m);
+        denom = wave_sum_f32(part);
+    }
+    for (int e0 = 0; e0 < E; e0 += kWave) {
+        const int e = e0 + lane;
+        // the slot that selected e, if any
+        float sel_g = 0.0f, sel_dg = 0.0f;
+        bool sel = false;
+        for (int s = 0; s < k; ++s) {
+            const int es = __shfl(my_e, s, kWave);
+            const float gs = __shfl(my_g, s, kWave);
+            const float dgs = __shfl(my_dg, s, kWave);
+            if (es == e) { sel = true; sel_g = gs; sel_dg = dgs; }
+        }
+        if (e >= E) continue;
+        float v;
+        if (renorm) v = sel ? sel_g * (sel_dg - gdg) : 0.0f;
+        else v = (expf(l[e] - m) / denom) * ((sel ? sel_dg : 0.0f) - gdg);
+        if (d_logits) d_logits[(size_t)t * E + e] = v;
+        if (d_logits_bf16) d_logits_bf16[(size_t)t * E + e] = f32_to_bf16(v);
+    }
+}
+
+hipError_t launch_route_bwd(const float* logits, const int32_t* idx, const float* gates,
+                            const float* d_gates, int T, int E, int k, int renorm,
+                            float* d_logits, uint16_t* d_logits_bf16, hipStream_t st)
+{
+    route_bwd_kernel<<<(T + 3) / 4, 256, 0, st>>>(logits, idx, gates, d_gates, T, E, k, renorm,
+                                                  d_logits, d_logits_bf16);
+    return hipGetLastError();
+}
+
 template <typename XT>
 static hipError_t launch_scores_t(const void* x, const void* w, const float* bias, int T, int d,
                                   int E, float* logits, hipStream_t st)

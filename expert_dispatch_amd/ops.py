@@ -50,6 +50,14 @@ def lib():
         "moe_ffn_gate_up": [vp, i, i, i, i, i, vp, vp, vp, vp, vp],
         "moe_ffn_down": [vp, i, i, i, i, i, vp, vp, vp, i, vp],
         "moe_combine": [vp, i, vp, vp, i, i, i, vp, i, vp, i, vp],
+        "moe_ffn_gate_up_train": [vp, i, i, i, i, i, vp, vp, vp, vp, vp, vp],
+        "moe_combine_backward": [vp, i, vp, i, vp, vp, i, i, i, vp, i, vp, vp],
+        "moe_ffn_down_backward": [vp, i, i, i, i, i, vp, vp, vp, vp, vp],
+        "moe_ffn_gate_up_backward": [vp, i, i, i, i, i, vp, vp, vp, vp, i, i, vp],
+        "moe_ffn_weight_grads": [vp, vp, vp, vp, i, i, i, i, i, vp, ctypes.c_float, vp, vp, vp,
+                                 vp],
+        "moe_route_backward": [vp, vp, vp, vp, i, i, i, i, vp, vp, vp],
+        "moe_router_backward": [vp, vp, i, vp, i, i, i, vp, i, vp, vp],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -269,3 +277,172 @@ def moe_layer(x, w_router, bias, k: int, w_gate, w_val, w_out, *, shared=None, c
         y_sh = grouped_ffn(x, off, *shared, y_dtype=y_dtype, stream=stream)
     out = combine(y, p["dest"], gates, k, y_shared=y_sh, out_dtype=out_dtype, stream=stream)
     return dict(logits=logits, idx=idx, gates=gates, y=y, y_shared=y_sh, out=out, **p)
+
+
+# ------------------------------------------------------------------ backward
+
+def ffn_gate_up_train(x_perm, offsets, w_gate, w_val, *, h=None, act=None, stream=None):
+    """h = silu(x W_gate[e]) * (x W_val[e]) and the pre-activations act = [a | v]
+    [N,2f] that the backward needs."""
+    for t, n in ((x_perm, "x_perm"), (offsets, "offsets"), (w_gate, "w_gate"), (w_val, "w_val")):
+        _dev(t, n)
+    N, d = x_perm.shape
+    E, _, f = w_gate.shape
+    if h is None:
+        h = torch.empty((N, f), dtype=x_perm.dtype, device=x_perm.device)
+    if act is None:
+        act = torch.empty((N, 2 * f), dtype=x_perm.dtype, device=x_perm.device)
+    _check("moe_ffn_gate_up_train", lib().moe_ffn_gate_up_train(
+        _p(x_perm), _dt(x_perm), N, d, f, E, _p(offsets), _p(w_gate), _p(w_val), _p(h), _p(act),
+        _stream(stream)))
+    return h, act
+
+
+def ffn_down(h, offsets, w_out, *, y=None, y_dtype=torch.float32, stream=None):
+    N, f = h.shape
+    E, _, d = w_out.shape
+    if y is None:
+        y = torch.empty((N, d), dtype=y_dtype, device=h.device)
+    _check("moe_ffn_down", lib().moe_ffn_down(_p(h), _dt(h), N, f, d, E, _p(offsets), _p(w_out),
+                                              _p(y), _dt(y), _stream(stream)))
+    return y
+
+
+def combine_backward(d_out, y_perm, dest, gates, k: int, *, d_y=None, d_y_dtype=None,
+                     d_gates=None, stream=None):
+    """d_y[dest[t,s]] = gates[t,s] d_out[t]; d_gates[t,s] = <d_out[t], y_perm[dest[t,s]]>."""
+    _dev(d_out, "d_out"); _dev(y_perm, "y_perm"); _dev(dest, "dest"); _dev(gates, "gates")
+    T, d = d_out.shape
+    if d_y is None:
+        d_y = torch.empty((y_perm.shape[0], d), dtype=d_y_dtype or d_out.dtype,
+                          device=d_out.device)
+    if d_gates is None:
+        d_gates = torch.empty((T, k), dtype=torch.float32, device=d_out.device)
+    _check("moe_combine_backward", lib().moe_combine_backward(
+        _p(d_out), _dt(d_out), _p(y_perm), _dt(y_perm), _p(dest), _p(gates), T, k, d, _p(d_y),
+        _dt(d_y), _p(d_gates), _stream(stream)))
+    return d_y, d_gates
+
+
+def ffn_down_backward(d_y, offsets, w_out, act, *, d_act=None, stream=None):
+    """d_act = [da | dv]: the SwiGLU backward of dh = d_y W_out[e]^T."""
+    N, d = d_y.shape
+    E, f, _ = w_out.shape
+    if d_act is None:
+        d_act = torch.empty((N, 2 * f), dtype=d_y.dtype, device=d_y.device)
+    _check("moe_ffn_down_backward", lib().moe_ffn_down_backward(
+        _p(d_y), _dt(d_y), N, d, f, E, _p(offsets), _p(w_out), _p(act), _p(d_act),
+        _stream(stream)))
+    return d_act
+
+
+def ffn_gate_up_backward(d_act, offsets, w_gate, w_val, *, d_x=None, dx_dtype=torch.float32,
+                         accumulate=False, stream=None):
+    """d_x = da W_gate[e]^T + dv W_val[e]^T (added into d_x with accumulate)."""
+    N = d_act.shape[0]
+    E, d, f = w_gate.shape
+    if d_x is None:
+        d_x = torch.empty((N, d), dtype=dx_dtype, device=d_act.device)
+    _check("moe_ffn_gate_up_backward", lib().moe_ffn_gate_up_backward(
+        _p(d_act), _dt(d_act), N, d, f, E, _p(offsets), _p(w_gate), _p(w_val), _p(d_x), _dt(d_x),
+        int(bool(accumulate)), _stream(stream)))
+    return d_x
+
+
+def ffn_weight_grads(x_perm, h, d_y, d_act, offsets, E: int, *, scale: float = 1.0, out=None,
+                     stream=None):
+    """(dW_gate [E,d,f], dW_val [E,d,f], dW_out [E,f,d]) in fp32, times ``scale``."""
+    N, d = x_perm.shape
+    f = h.shape[1]
+    dev = x_perm.device
+    if out is None:
+        out = (torch.empty((E, d, f), dtype=torch.float32, device=dev),
+               torch.empty((E, d, f), dtype=torch.float32, device=dev),
+               torch.empty((E, f, d), dtype=torch.float32, device=dev))
+    dwg, dwv, dwo = out
+    _check("moe_ffn_weight_grads", lib().moe_ffn_weight_grads(
+        _p(x_perm), _p(h), _p(d_y), _p(d_act), _dt(x_perm), N, d, f, E, _p(offsets),
+        float(scale), _p(dwg), _p(dwv), _p(dwo), _stream(stream)))
+    return dwg, dwv, dwo
+
+
+def route_backward(logits, idx, gates, d_gates, renorm: bool = True, *, lp_dtype=None,
+                   stream=None):
+    """d_logits [T,E] fp32, plus a bf16 copy when ``lp_dtype`` is bfloat16."""
+    T, E = logits.shape
+    k = idx.shape[1]
+    d_l = torch.empty((T, E), dtype=torch.float32, device=logits.device)
+    d_lp = None
+    if lp_dtype == torch.bfloat16:
+        d_lp = torch.empty((T, E), dtype=torch.bfloat16, device=logits.device)
+    _check("moe_route_backward", lib().moe_route_backward(
+        _p(logits), _p(idx), _p(gates), _p(d_gates), T, E, k, int(bool(renorm)), _p(d_l),
+        _p(d_lp), _stream(stream)))
+    return d_l, d_lp
+
+
+def router_backward(x, w_router, d_logits, *, d_x=None, accumulate=False, want_dw=True,
+                    stream=None):
+    """d_x (+)= d_logits W_r^T; dW_r = x^T d_logits (fp32). d_logits in x's dtype."""
+    T, d = x.shape
+    E = w_router.shape[1]
+    dw = torch.empty((d, E), dtype=torch.float32, device=x.device) if want_dw else None
+    _check("moe_router_backward", lib().moe_router_backward(
+        _p(x), _p(w_router), _dt(x), _p(d_logits), T, d, E, _p(d_x), int(bool(accumulate)),
+        _p(dw), _stream(stream)))
+    return d_x, dw
+
+
+def moe_layer_train(x, w_router, bias, k: int, w_gate, w_val, w_out, *, shared=None,
+                    capacity=None, e_first=None, renorm=True, y_dtype=torch.float32,
+                    stream=None):
+    """Forward of the layer keeping what the backward needs (the pre-activations
+    of every SwiGLU besides the forward's intermediates)."""
+    E = w_gate.shape[0]
+    logits, idx, gates = route(x, w_router, bias, k, renorm, stream=stream)
+    p = permute(idx, x, E, capacity=capacity, e_first=e_first, stream=stream)
+    h, act = ffn_gate_up_train(p["x_perm"], p["offsets"], w_gate, w_val, stream=stream)
+    y = ffn_down(h, p["offsets"], w_out, y_dtype=y_dtype, stream=stream)
+    sv = dict(logits=logits, idx=idx, gates=gates, h=h, act=act, y=y, renorm=renorm, k=k, **p)
+    y_sh = None
+    if shared is not None:
+        T = x.shape[0]
+        off = torch.tensor([0, T], dtype=torch.int32, device=x.device)
+        h_sh, act_sh = ffn_gate_up_train(x, off, shared[0], shared[1], stream=stream)
+        y_sh = ffn_down(h_sh, off, shared[2], y_dtype=y_dtype, stream=stream)
+        sv.update(shared_off=off, h_shared=h_sh, act_shared=act_sh, y_shared=y_sh)
+    sv["out"] = combine(y, p["dest"], gates, k, y_shared=y_sh, stream=stream)
+    return sv
+
+
+def moe_layer_backward(sv, d_out, x, w_router, w_gate, w_val, w_out, *, shared=None,
+                       scale: float = 1.0, dx_perm_dtype=torch.float32, stream=None):
+    """Gradients of sum(out * d_out) through the layer given the saved forward
+    ``sv`` of moe_layer_train. Expert weight gradients are multiplied by
+    ``scale`` (1/P for an EP group of P ranks)."""
+    k = sv["k"]
+    E = w_gate.shape[0]
+    T = x.shape[0]
+    g = {}
+    d_y, d_gates = combine_backward(d_out, sv["y"], sv["dest"], sv["gates"], k,
+                                    d_y_dtype=x.dtype, stream=stream)
+    d_act = ffn_down_backward(d_y, sv["offsets"], w_out, sv["act"], stream=stream)
+    g["d_w_gate"], g["d_w_val"], g["d_w_out"] = ffn_weight_grads(
+        sv["x_perm"], sv["h"], d_y, d_act, sv["offsets"], E, scale=scale, stream=stream)
+    d_xp = ffn_gate_up_backward(d_act, sv["offsets"], w_gate, w_val, dx_dtype=dx_perm_dtype,
+                                stream=stream)
+    d_x = combine(d_xp, sv["dest"], None, k, out_dtype=torch.float32, stream=stream)
+    if shared is not None:
+        off = sv["shared_off"]
+        d_act_sh = ffn_down_backward(d_out.to(x.dtype), off, shared[2], sv["act_shared"],
+                                     stream=stream)
+        g["d_shared"] = ffn_weight_grads(x, sv["h_shared"], d_out.to(x.dtype), d_act_sh, off, 1,
+                                         stream=stream)
+        ffn_gate_up_backward(d_act_sh, off, shared[0], shared[1], d_x=d_x, accumulate=True,
+                             stream=stream)
+    d_l, d_lp = route_backward(sv["logits"], sv["idx"], sv["gates"], d_gates, sv["renorm"],
+                               lp_dtype=x.dtype, stream=stream)
+    _, g["d_w_router"] = router_backward(x, w_router, d_lp if d_lp is not None else d_l,
+                                         d_x=d_x, accumulate=True, stream=stream)
+    g.update(d_x=d_x, d_gates=d_gates, d_logits=d_l, d_y=d_y, d_act=d_act, d_x_perm=d_xp)
+    return g

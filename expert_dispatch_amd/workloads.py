@@ -220,6 +220,16 @@ def generate(cfg: Config | str) -> dict:
     return out
 
 
+def output_gradient(cfg: Config | str) -> np.ndarray:
+    """A seeded upstream gradient dL/dout [T,d] for a backward pass, Gaussian
+    with unit variance, in the workload's activation type (its own generator,
+    so the layer's inputs are the same with or without it)."""
+    if isinstance(cfg, str):
+        cfg = get(cfg)
+    gen = torch.Generator().manual_seed(1_000_003 * (cfg.seed + 1))
+    return _normal(gen, (cfg.T, cfg.d), 1.0, cfg.dtype)
+
+
 def zero_expert_column(inp: dict, j: int) -> dict:
     """Receive-side variant with local expert j emptied: its rows are moved to
     the next expert of the same sender, so the total stays N."""

@@ -217,6 +217,118 @@ moe_status moe_combine(const void* y_perm, moe_dtype y_dt, const int32_t* dest,
                        const void* y_shared, moe_dtype sh_dt,
                        void* out, moe_dtype out_dt, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Backward (training). The pages' systems train the layer: autograd runs
+ * through the index_select / index_copy permutation pair ("feat(parallelism):
+ * expert parallelism for the Nemotron-3 Nano MoE layers", Design), and an
+ * expert owner divides its expert gradients by the EP group size before
+ * clipping and the optimizer ("Three axes of Parallelism", EP backward pass).
+ * The calls below are the chain rule on the forward definitions; the
+ * selection (ids, packing) is piecewise constant and passes no gradient. A
+ * training step keeps what the forward computed (logits, ids, weights, dest,
+ * offsets, x_perm, h, y_perm and the pre-activations from
+ * moe_ffn_gate_up_train) and, given d_out = dL/dout [T,d], runs:
+ *   moe_combine_backward      -> d_y [rows,d], d_gates [T,k]
+ *   moe_ffn_down_backward     -> d_act [rows,2f]
+ *   moe_ffn_weight_grads      -> dW_gate, dW_val, dW_out (x 1/P_EP)
+ *   moe_ffn_gate_up_backward  -> d_x_perm [rows,d]
+ *   moe_combine(d_x_perm, dest, gates = NULL, k) -> d_x [T,d] (the permutation's
+ *                                backward: every token sums its rows' gradients)
+ *   moe_route_backward        -> d_logits [T,E]
+ *   moe_router_backward       -> d_x += d_logits . W_r^T, dW_r = x^T . d_logits
+ * Products run on the matrix cores in bf16 with fp32 accumulation when dt is
+ * MOE_BF16 and the sizes tile (d, f multiples of 32; otherwise, and for fp32,
+ * a plain fp32 kernel). Same limits as the forward calls.
+ * ---------------------------------------------------------------------- */
+
+/*
+ * moe_ffn_gate_up for training: as moe_ffn_gate_up, and also stores the
+ * pre-activations act [N,2f] (dtype dt): act[j,0:f] = x_perm[j] . W_gate[e],
+ * act[j,f:2f] = x_perm[j] . W_val[e] (rounded once to dt), which the backward
+ * of the SwiGLU needs.
+ */
+moe_status moe_ffn_gate_up_train(const void* x_perm, moe_dtype dt, int N, int d, int f, int E,
+                                 const int32_t* offsets, const void* w_gate, const void* w_val,
+                                 void* h, void* act, void* stream);
+
+/*
+ * Backward of moe_combine (weights given):
+ *   d_y[dest[t*k+s],:] = gates[t*k+s] * d_out[t,:]     (rows with dest < 0: none)
+ *   d_gates[t*k+s]     = sum_c d_out[t,c] * y_perm[dest[t*k+s],c]   (0 if dest < 0)
+ *   d_out [T,d] dtype d_out_dt; y_perm [*,d] dtype y_dt; d_y [*,d] dtype d_y_dt
+ *   (rows the packing kept; the others are not written); d_gates [T*k] fp32.
+ * Each token's slots are handled by one wavefront; no atomics.
+ */
+moe_status moe_combine_backward(const void* d_out, moe_dtype d_out_dt, const void* y_perm,
+                                moe_dtype y_dt, const int32_t* dest, const float* gates,
+                                int T, int k, int d, void* d_y, moe_dtype d_y_dt,
+                                float* d_gates, void* stream);
+
+/*
+ * Backward of moe_ffn_down and of the SwiGLU, fused: for packed row j of
+ * expert e, dh = d_y[j] . W_out[e]^T, and with a, v = act[j,0:f], act[j,f:2f],
+ * s = sigmoid(a):
+ *   d_act[j,0:f]  = da = dh * v * s * (1 + a (1 - s))
+ *   d_act[j,f:2f] = dv = dh * a * s
+ *   d_y [N,d], act [N,2f], d_act [N,2f] dtype dt; W_out [E,f,d]; offsets as
+ *   in moe_grouped_ffn.
+ */
+moe_status moe_ffn_down_backward(const void* d_y, moe_dtype dt, int N, int d, int f, int E,
+                                 const int32_t* offsets, const void* w_out, const void* act,
+                                 void* d_act, void* stream);
+
+/*
+ * Backward of moe_ffn_gate_up to its input:
+ *   d_x_perm[j] = d_act[j,0:f] . W_gate[e]^T + d_act[j,f:2f] . W_val[e]^T
+ *   d_act [N,2f] dtype dt, W_gate/W_val [E,d,f], d_x_perm [N,d] dtype dx_dt.
+ * accumulate != 0 (dx_dt MOE_F32 only) adds into d_x_perm instead of
+ * overwriting it (shared experts add their input gradient to the tokens').
+ */
+moe_status moe_ffn_gate_up_backward(const void* d_act, moe_dtype dt, int N, int d, int f, int E,
+                                    const int32_t* offsets, const void* w_gate,
+                                    const void* w_val, void* d_x_perm, moe_dtype dx_dt,
+                                    int accumulate, void* stream);
+
+/*
+ * Expert weight gradients, summed over each expert's packed rows and
+ * multiplied by `scale` (1/P for an EP group of P ranks; 1 on one GPU):
+ *   dW_out[e]  = scale * h_e^T . d_y_e          [E,f,d]
+ *   dW_gate[e] = scale * x_e^T . d_act_e[:,0:f]  [E,d,f]
+ *   dW_val[e]  = scale * x_e^T . d_act_e[:,f:2f] [E,d,f]
+ *   x_perm [N,d], h [N,f], d_y [N,d], d_act [N,2f] dtype dt; outputs fp32.
+ * Every expert's gradients are written, zeros for an expert with no rows.
+ */
+moe_status moe_ffn_weight_grads(const void* x_perm, const void* h, const void* d_y,
+                                const void* d_act, moe_dtype dt, int N, int d, int f, int E,
+                                const int32_t* offsets, float scale, float* d_w_gate,
+                                float* d_w_val, float* d_w_out, void* stream);
+
+/*
+ * Backward of the router weights to the logits (moe_route's renorm flag):
+ * with g the weights of the k selected experts, dg = d_gates,
+ * gdg = sum_s g_s dg_s:
+ *   renorm != 0: d_logits[t,e_s] = g_s (dg_s - gdg), 0 for unselected experts;
+ *   renorm == 0: d_logits[t,e] = p_e ([e = e_s] dg_s - gdg), p = softmax over E.
+ *   logits [T,E], gates, d_gates [T*k] fp32, topk_idx [T*k] as moe_route wrote
+ *   them; d_logits [T,E] fp32 (may be NULL); d_logits_bf16 [T,E] bf16 copy
+ *   for moe_router_backward on bf16 data (may be NULL).
+ * This is also the gradient of a trainable bias (summed over tokens).
+ */
+moe_status moe_route_backward(const float* logits, const int32_t* topk_idx, const float* gates,
+                              const float* d_gates, int T, int E, int k, int renorm,
+                              float* d_logits, void* d_logits_bf16, void* stream);
+
+/*
+ * Backward of the router scores l = x . W_r:
+ *   d_x[t]  (+)= d_logits[t] . W_r^T   [T,d] fp32 (accumulate != 0 adds)
+ *   d_w_router  = x^T . d_logits        [d,E] fp32
+ *   x [T,d], W_r [d,E] and d_logits [T,E] in dtype dt (bf16: the copy
+ *   moe_route_backward writes). Either output may be NULL.
+ */
+moe_status moe_router_backward(const void* x, const void* w_router, moe_dtype dt,
+                               const void* d_logits, int T, int d, int E, float* d_x,
+                               int accumulate, float* d_w_router, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -86,6 +86,24 @@ def test_host_side_errors_return_before_launch(L):
                              1 << 20, None) == 1
     # combine: k too large
     assert L.moe_combine(fake, 0, fake, None, 4, 33, 64, None, 0, fake, 0, None) == 2
+    # backward: combine without weights, k = 0
+    assert L.moe_combine_backward(fake, 1, fake, 0, fake, None, 4, 2, 64, fake, 1, fake, None) == 1
+    assert L.moe_combine_backward(fake, 1, fake, 0, fake, fake, 4, 0, 64, fake, 1, fake, None) == 1
+    # gate_up backward: accumulating into bf16, fp32 data into a bf16 gradient, NULL d_x
+    assert L.moe_ffn_gate_up_backward(fake, 1, 10, 64, 64, 2, fake, fake, fake, fake, 1, 1,
+                                      None) == 2
+    assert L.moe_ffn_gate_up_backward(fake, 0, 10, 64, 64, 2, fake, fake, fake, fake, 1, 0,
+                                      None) == 2
+    assert L.moe_ffn_gate_up_backward(fake, 1, 10, 64, 64, 2, fake, fake, fake, None, 0, 0,
+                                      None) == 1
+    # down backward: NULL saved pre-activations; training forward: NULL act
+    assert L.moe_ffn_down_backward(fake, 1, 10, 64, 64, 2, fake, fake, None, fake, None) == 1
+    assert L.moe_ffn_gate_up_train(fake, 1, 10, 64, 64, 2, fake, fake, fake, fake, None,
+                                   None) == 1
+    # router backward: no output asked for, k > E, NULL inputs with rows
+    assert L.moe_route_backward(fake, fake, fake, fake, 4, 8, 2, 1, None, None, None) == 1
+    assert L.moe_route_backward(fake, fake, fake, fake, 4, 8, 9, 1, fake, None, None) == 1
+    assert L.moe_router_backward(None, fake, 1, fake, 4, 64, 8, fake, 0, None, None) == 1
 
 
 def test_empty_inputs_are_no_ops(L):
@@ -94,3 +112,6 @@ def test_empty_inputs_are_no_ops(L):
     assert L.moe_grouped_ffn(None, 1, 0, 64, 64, 2, ctypes.c_void_p(0x1000), None, None, None,
                              None, 0, None, 0, None) == 0
     assert L.moe_combine(None, 0, None, None, 0, 2, 64, None, 0, None, 0, None) == 0
+    assert L.moe_combine_backward(None, 1, None, 0, None, None, 0, 2, 64, None, 1, None,
+                                  None) == 0
+    assert L.moe_route_backward(None, None, None, None, 0, 8, 2, 1, None, None, None) == 0

@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 import torch
 
-from util import TOL_BF16, check_bf16_stored
+from util import GRAD_L2_BF16, GRAD_MAX_BF16, TOL_BF16, check_bf16_stored, check_grad
 
 
 def _round_bf16(a: np.ndarray) -> np.ndarray:
@@ -25,3 +25,23 @@ def test_error_beyond_rounding_fails():
     got[17] += 3 * TOL_BF16 * np.sqrt(np.mean(ref * ref))
     with pytest.raises(AssertionError):
         check_bf16_stored(_round_bf16(got), ref, "planted")
+
+
+def test_gradient_gate_passes_independent_roundings():
+    # four independent bf16 roundings of relative size 2^-8 per element
+    rng = np.random.default_rng(5)
+    ref = rng.standard_normal(200_000)
+    got = ref * np.prod(1 + rng.uniform(-2.0 ** -8, 2.0 ** -8, size=(4, ref.size)), axis=0)
+    check_grad(got, ref, "bf16", "four roundings")
+
+
+def test_gradient_gate_catches_a_wrong_tile_and_a_scale_error():
+    rng = np.random.default_rng(6)
+    ref = rng.standard_normal((256, 512))
+    bad = ref.copy()
+    bad[128:160, 256:288] *= 1.3   # one 32 x 32 block off by 30 %
+    with pytest.raises(AssertionError):
+        check_grad(bad, ref, "bf16", "wrong tile")
+    with pytest.raises(AssertionError):
+        check_grad(ref * (1 + 1.5 * GRAD_L2_BF16), ref, "bf16", "scaled")
+    assert GRAD_MAX_BF16 > TOL_BF16

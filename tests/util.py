@@ -87,6 +87,41 @@ def check_bf16_stored(got, ref, what: str):
     return e
 
 
+GRAD_L2_BF16 = 2e-2     # backward, bf16 data: ||got - ref||_2 / ||ref||_2
+GRAD_MAX_BF16 = 1e-1    # backward, bf16 data: max |got - ref| / rms(ref)
+
+
+def check_grad(got, ref, dtype: str, what: str, stored_bf16: bool = False):
+    """Parity gate of one gradient of the backward. fp32 data: the forward's
+    max relative error 1e-5. bf16 data: a training step rounds every tensor it
+    hands from one kernel to the next (d_y, the saved pre-activations, d_act;
+    h and the inputs of every product), so a gradient element carries several
+    independent roundings of relative size up to 2^-8, and the largest error
+    over 10^5..10^6 elements sits several standard deviations out. The gate is
+    the forward's 2e-2 applied norm-wise (relative L2 error of the whole
+    tensor) plus a max-error guard of 0.1 RMS, which any misplaced tile or
+    dropped term exceeds; a bf16-stored tensor first has its own storage
+    rounding (U_BF16 |ref|) taken off each element, as in check_bf16_stored."""
+    got = widen(got) if isinstance(got, np.ndarray) and got.dtype == np.uint16 else got
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if dtype == "f32":
+        e = err_f32(got, ref)
+        assert e <= TOL_F32, f"{what}: max rel err {e:.3e} > {TOL_F32}"
+        return e
+    if not ref.size:
+        return 0.0
+    diff = np.abs(got - ref)
+    l2 = float(np.sqrt(np.sum(diff * diff) / max(np.sum(ref * ref), 1e-300)))
+    assert l2 <= GRAD_L2_BF16, f"{what}: relative L2 error {l2:.3e} > {GRAD_L2_BF16}"
+    if stored_bf16:
+        diff = np.maximum(diff - U_BF16 * np.abs(ref), 0.0) / (1 + U_BF16)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    mx = float(diff.max()) / max(rms, 1e-300)
+    assert mx <= GRAD_MAX_BF16, f"{what}: max err / rms {mx:.3e} > {GRAD_MAX_BF16}"
+    return l2
+
+
 def sample_rows(offsets: np.ndarray, per_expert: int, rng) -> np.ndarray:
     """First and last packed row of every non-empty expert plus random rows."""
     rows = []
