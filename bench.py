@@ -54,6 +54,10 @@ def parse():
     ap.add_argument("--partial-dtype", choices=("f32", "bf16"), default="bf16",
                     help="gathered-token workload: type of the partial output that the "
                          "reduce-scatter would sum")
+    ap.add_argument("--backward", action="store_true",
+                    help="time a training step instead: the forward keeping what the "
+                         "backward needs, then the backward of sum(out * d_out) with a "
+                         "seeded d_out (token-routed workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU work of the oracle baseline sample")
@@ -208,10 +212,188 @@ def cpu_baseline(cfg, inp, target_s: float):
                        f"in the oracle, {reps} run(s), {t:.1f} s")
 
 
+def backward_work(cfg, counts, es):
+    """Algorithmic flops and bytes of the backward stages (bf16 data, fp32
+    gradients of the weights, fp32 expert outputs y). rows = kept packed rows,
+    n_act = experts with rows."""
+    T, k, d, f, E = cfg.T, cfg.k, cfg.d, cfg.f, cfg.E
+    rows = int(counts.sum())
+    active = int((counts > 0).sum())
+    w = {}
+    # d_out read once per token, y read and d_y written per row, weights and dest
+    w["combine_bwd"] = dict(flops=4.0 * rows * d,
+                            bytes=T * d * es + rows * d * 4 + rows * d * es + T * k * 12)
+    w["down_bwd"] = dict(flops=2.0 * rows * d * f,
+                         bytes=rows * d * es + active * f * d * es + 2 * rows * 2 * f * es)
+    w["weight_grads"] = dict(flops=6.0 * rows * d * f,
+                             bytes=rows * (f + d + d + 2 * f) * es + 3 * E * d * f * 4)
+    w["gate_up_bwd"] = dict(flops=4.0 * rows * d * f,
+                            bytes=rows * 2 * f * es + active * 2 * d * f * es + rows * d * 4)
+    w["unpermute"] = dict(flops=1.0 * rows * d, bytes=rows * d * 4 + T * d * 4 + T * k * 4,
+                          bound="hbm")
+    w["route_bwd"] = dict(flops=6.0 * T * E, bytes=T * E * 4 + T * k * 16 + T * E * 6,
+                          bound="hbm")
+    w["router_bwd"] = dict(flops=4.0 * T * d * E,
+                           bytes=T * d * es + d * E * es + T * E * es + T * d * 8 + d * E * 4)
+    for v in w.values():
+        if "bound" not in v:
+            ai = v["flops"] / max(v["bytes"], 1)
+            v["bound"] = "mfma" if ai * PEAK_HBM_GBS * 1e9 > PEAK_MFMA_BF16_TFS * 1e12 else "hbm"
+    return w
+
+
+def main_backward(args):
+    """One training step of the layer: forward (keeping the pre-activations)
+    and backward, every buffer allocated before timing."""
+    import torch
+    from expert_dispatch_amd import ops
+    from expert_dispatch_amd import workloads as W
+
+    cfg = W.get(args.config)
+    if cfg.kind != "routed" or cfg.dtype != "bf16" or cfg.shared:
+        print("bench.py --backward times the token-routed bf16 workloads without shared "
+              "experts", file=sys.stderr)
+        sys.exit(2)
+    es = 2
+    log(f"[bench] generating {cfg.name} (training step)")
+    inp = W.generate(cfg)
+    torch.cuda.set_device(0)
+    dev = {k: to_dev(inp.get(k), torch) for k in ("x", "w_router", "bias", "w_gate", "w_val",
+                                                  "w_out")}
+    d_out = to_dev(W.output_gradient(cfg), torch)
+    T, k, d, f, E = cfg.T, cfg.k, cfg.d, cfg.f, cfg.E
+    rows = T * k
+    cuda = torch.device("cuda")
+    bf = torch.bfloat16
+    f32 = torch.float32
+    b = dict(
+        logits=torch.empty((T, E), dtype=f32, device=cuda),
+        idx=torch.empty((T, k), dtype=torch.int32, device=cuda),
+        gates=torch.empty((T, k), dtype=f32, device=cuda),
+        counts=torch.empty(E, dtype=torch.int32, device=cuda),
+        offsets=torch.empty(E + 1, dtype=torch.int32, device=cuda),
+        perm_src=torch.empty(rows, dtype=torch.int32, device=cuda),
+        dest=torch.empty(rows, dtype=torch.int32, device=cuda),
+        x_perm=torch.empty((rows, d), dtype=bf, device=cuda),
+        h=torch.empty((rows, f), dtype=bf, device=cuda),
+        act=torch.empty((rows, 2 * f), dtype=bf, device=cuda),
+        y=torch.empty((rows, d), dtype=f32, device=cuda),
+        out=torch.empty((T, d), dtype=f32, device=cuda),
+        d_y=torch.empty((rows, d), dtype=bf, device=cuda),
+        d_gates=torch.empty((T, k), dtype=f32, device=cuda),
+        d_act=torch.empty((rows, 2 * f), dtype=bf, device=cuda),
+        d_xp=torch.empty((rows, d), dtype=f32, device=cuda),
+        d_x=torch.empty((T, d), dtype=f32, device=cuda),
+        dwg=torch.empty((E, d, f), dtype=f32, device=cuda),
+        dwv=torch.empty((E, d, f), dtype=f32, device=cuda),
+        dwo=torch.empty((E, f, d), dtype=f32, device=cuda),
+        d_l=torch.empty((T, E), dtype=f32, device=cuda),
+        d_lp=torch.empty((T, E), dtype=bf, device=cuda),
+        d_wr=torch.empty((d, E), dtype=f32, device=cuda),
+    )
+    ws = torch.empty(max(1, ops.permute_workspace(T, k, E)), dtype=torch.uint8, device=cuda)
+    stages = ["route", "permute", "gate_up", "down", "combine", "combine_bwd", "down_bwd",
+              "weight_grads", "gate_up_bwd", "unpermute", "route_bwd", "router_bwd"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        ops.route(dev["x"], dev["w_router"], dev["bias"], k, out=(b["logits"], b["idx"], b["gates"]))
+        mark(1)
+        ops.permute(b["idx"], dev["x"], E, out=b, workspace=ws)
+        mark(2)
+        ops.ffn_gate_up_train(b["x_perm"], b["offsets"], dev["w_gate"], dev["w_val"], h=b["h"],
+                              act=b["act"])
+        mark(3)
+        ops.ffn_down(b["h"], b["offsets"], dev["w_out"], y=b["y"])
+        mark(4)
+        ops.combine(b["y"], b["dest"], b["gates"], k, out=b["out"])
+        mark(5)
+        ops.combine_backward(d_out, b["y"], b["dest"], b["gates"], k, d_y=b["d_y"],
+                             d_gates=b["d_gates"])
+        mark(6)
+        ops.ffn_down_backward(b["d_y"], b["offsets"], dev["w_out"], b["act"], d_act=b["d_act"])
+        mark(7)
+        ops.ffn_weight_grads(b["x_perm"], b["h"], b["d_y"], b["d_act"], b["offsets"], E,
+                             out=(b["dwg"], b["dwv"], b["dwo"]))
+        mark(8)
+        ops.ffn_gate_up_backward(b["d_act"], b["offsets"], dev["w_gate"], dev["w_val"],
+                                 d_x=b["d_xp"])
+        mark(9)
+        ops.combine(b["d_xp"], b["dest"], None, k, out=b["d_x"])
+        mark(10)
+        ops.route_backward(b["logits"], b["idx"], b["gates"], b["d_gates"], True,
+                           d_logits=b["d_l"], d_logits_lp=b["d_lp"])
+        mark(11)
+        ops.router_backward(dev["x"], dev["w_router"], b["d_lp"], d_x=b["d_x"], accumulate=True,
+                            d_w=b["d_wr"])
+        mark(12)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+           for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} training steps")
+    torch.cuda.synchronize()
+    t0.record()
+    for s_ in range(args.steps):
+        step(evs[s_])
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    stage_us = {n: float(np.mean([evs[s_][j].elapsed_time(evs[s_][j + 1])
+                                  for s_ in range(args.steps)]) * 1e3)
+                for j, n in enumerate(stages)}
+    counts = b["counts"].cpu().numpy()
+    fw = stage_work(cfg, counts, es, 4, int(counts.sum()))
+    bw = backward_work(cfg, counts, es)
+    work = dict(fw, **bw)
+    rep = {}
+    for n in stages:
+        r = roofline_entry(work[n], stage_us[n], es)
+        rep[n] = dict(us=round(stage_us[n], 2), bound=r["bound"], achieved=round(r["achieved"], 1),
+                      unit=r["unit"], frac=round(r["frac"], 4))
+    bwd = stages[5:]
+    dominant = max(bwd, key=lambda n: stage_us[n])
+    dom = roofline_entry(work[dominant], stage_us[dominant], es)
+    res = {
+        "metric": "MoE-layer training step (forward + backward) tokens/sec at 1 GPU",
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "forward_ms": round(sum(stage_us[n] for n in stages[:5]) / 1e3, 5),
+        "backward_ms": round(sum(stage_us[n] for n in bwd) / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian inputs, weights and output gradient)",
+        "config": {"workload": cfg.name, "T": T, "k": k, "d": d, "f": f, "E": E,
+                   "kept_rows": int(counts.sum())},
+        "roofline": {"kernel": dominant, "bound": dom["bound"], "achieved": round(dom["achieved"], 1),
+                     "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4),
+                     "traffic": None},
+        "stages": rep,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.backward:
+        if args.gpus != 1:
+            print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported",
+                  file=sys.stderr)
+            sys.exit(2)
+        main_backward(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

@@ -367,13 +367,15 @@ def ffn_weight_grads(x_perm, h, d_y, d_act, offsets, E: int, *, scale: float = 1
 
 
 def route_backward(logits, idx, gates, d_gates, renorm: bool = True, *, lp_dtype=None,
-                   stream=None):
+                   d_logits=None, d_logits_lp=None, stream=None):
     """d_logits [T,E] fp32, plus a bf16 copy when ``lp_dtype`` is bfloat16."""
     T, E = logits.shape
     k = idx.shape[1]
-    d_l = torch.empty((T, E), dtype=torch.float32, device=logits.device)
-    d_lp = None
-    if lp_dtype == torch.bfloat16:
+    d_l = d_logits
+    if d_l is None:
+        d_l = torch.empty((T, E), dtype=torch.float32, device=logits.device)
+    d_lp = d_logits_lp
+    if d_lp is None and lp_dtype == torch.bfloat16:
         d_lp = torch.empty((T, E), dtype=torch.bfloat16, device=logits.device)
     _check("moe_route_backward", lib().moe_route_backward(
         _p(logits), _p(idx), _p(gates), _p(d_gates), T, E, k, int(bool(renorm)), _p(d_l),
@@ -382,11 +384,13 @@ def route_backward(logits, idx, gates, d_gates, renorm: bool = True, *, lp_dtype
 
 
 def router_backward(x, w_router, d_logits, *, d_x=None, accumulate=False, want_dw=True,
-                    stream=None):
+                    d_w=None, stream=None):
     """d_x (+)= d_logits W_r^T; dW_r = x^T d_logits (fp32). d_logits in x's dtype."""
     T, d = x.shape
     E = w_router.shape[1]
-    dw = torch.empty((d, E), dtype=torch.float32, device=x.device) if want_dw else None
+    dw = d_w
+    if dw is None and want_dw:
+        dw = torch.empty((d, E), dtype=torch.float32, device=x.device)
     _check("moe_router_backward", lib().moe_router_backward(
         _p(x), _p(w_router), _dt(x), _p(d_logits), T, d, E, _p(d_x), int(bool(accumulate)),
         _p(dw), _stream(stream)))
