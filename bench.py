@@ -292,6 +292,8 @@ def main_backward(args):
         d_wr=torch.empty((d, E), dtype=f32, device=cuda),
     )
     ws = torch.empty(max(1, ops.permute_workspace(T, k, E)), dtype=torch.uint8, device=cuda)
+    rws = torch.empty(max(1, ops.router_backward_workspace(T, d, E)), dtype=torch.uint8,
+                      device=cuda)
     stages = ["route", "permute", "gate_up", "down", "combine", "combine_bwd", "down_bwd",
               "weight_grads", "gate_up_bwd", "unpermute", "route_bwd", "router_bwd"]
 
@@ -328,7 +330,7 @@ def main_backward(args):
                            d_logits=b["d_l"], d_logits_lp=b["d_lp"])
         mark(11)
         ops.router_backward(dev["x"], dev["w_router"], b["d_lp"], d_x=b["d_x"], accumulate=True,
-                            d_w=b["d_wr"])
+                            d_w=b["d_wr"], workspace=rws)
         mark(12)
 
     log(f"[bench] warmup {args.warmup}")

@@ -37,7 +37,9 @@ hipError_t launch_nt(int epi, const void* A, moe_dtype dt, int rows, int K, int 
                      const void* act, hipStream_t st);
 hipError_t launch_tn(const void* A, int lda, int M, const void* B, int ldb, int Nc, int pair,
                      moe_dtype dt, int rows, int E, const int32_t* offsets, float scale,
-                     float* C0, float* C1, hipStream_t st);
+                     float* C0, float* C1, hipStream_t st, int split);
+int router_splits(int T, int& split);
+hipError_t launch_sum_splits(const float* part, int S, long long n, float* out, hipStream_t st);
 enum NtEpi { kNtSwigluBwd = 0, kNtStoreF32 = 1, kNtAccumF32 = 2, kNtStoreBf16 = 3 };
 }  // namespace moe
 
@@ -309,11 +311,11 @@ moe_status moe_ffn_weight_grads(const void* x_perm, const void* h, const void* d
     hipStream_t st = as_stream(stream);
     // dW_out[e] [f,d] = h_e^T . d_y_e
     hipError_t e = moe::launch_tn(h, f, f, d_y, d, d, 0, dt, N, E, offsets, scale, d_w_out,
-                                  nullptr, st);
+                                  nullptr, st, 0);
     if (e != hipSuccess) return MOE_ERR_HIP;
     // [dW_gate | dW_val][e] [d,f] = x_e^T . d_act_e[:, 0:f | f:2f]
     return hip_status(moe::launch_tn(x_perm, d, d, d_act, 2 * f, f, f, dt, N, E, offsets, scale,
-                                     d_w_gate, d_w_val, st));
+                                     d_w_gate, d_w_val, st, 0));
 }
 
 moe_status moe_route_backward(const float* logits, const int32_t* topk_idx, const float* gates,
@@ -330,9 +332,18 @@ moe_status moe_route_backward(const float* logits, const int32_t* topk_idx, cons
                                             as_stream(stream)));
 }
 
+size_t moe_router_backward_workspace(int T, int d, int E)
+{
+    if (T <= 0 || d <= 0 || E <= 0) return 0;
+    int split = 0;
+    const int S = moe::router_splits(T, split);
+    return S > 1 ? (size_t)S * d * E * sizeof(float) : 0;
+}
+
 moe_status moe_router_backward(const void* x, const void* w_router, moe_dtype dt,
                                const void* d_logits, int T, int d, int E, float* d_x,
-                               int accumulate, float* d_w_router, void* stream)
+                               int accumulate, float* d_w_router, void* ws, size_t ws_bytes,
+                               void* stream)
 {
     if (!valid_dtype(dt) || T < 0 || d <= 0 || E <= 0) return MOE_ERR_INVALID_ARG;
     if ((long long)T * std::max(d, E) > (1LL << 40) || (long long)T * E > INT32_MAX)
@@ -348,10 +359,24 @@ moe_status moe_router_backward(const void* x, const void* w_router, moe_dtype dt
         if (e != hipSuccess) return MOE_ERR_HIP;
     }
     if (d_w_router) {
-        // d_w_router [d,E] = x^T . d_logits over all T rows (T = 0: zeros)
-        hipError_t e = moe::launch_tn(x, d, d, d_logits, E, E, 0, dt, T, 1, nullptr, 1.0f,
-                                      d_w_router, nullptr, st);
-        if (e != hipSuccess) return MOE_ERR_HIP;
+        // d_w_router [d,E] = x^T . d_logits over all T rows (T = 0: zeros). A
+        // large T is split into row groups whose partial products land in the
+        // workspace and are then summed in group order.
+        int split = 0;
+        const int S = T > 0 ? moe::router_splits(T, split) : 1;
+        if (S > 1) {
+            if (!ws || ws_bytes < moe_router_backward_workspace(T, d, E)) return MOE_ERR_WORKSPACE;
+            float* part = static_cast<float*>(ws);
+            hipError_t e = moe::launch_tn(x, d, d, d_logits, E, E, 0, dt, T, S, nullptr, 1.0f,
+                                          part, nullptr, st, split);
+            if (e != hipSuccess) return MOE_ERR_HIP;
+            e = moe::launch_sum_splits(part, S, (long long)d * E, d_w_router, st);
+            if (e != hipSuccess) return MOE_ERR_HIP;
+        } else {
+            hipError_t e = moe::launch_tn(x, d, d, d_logits, E, E, 0, dt, T, 1, nullptr, 1.0f,
+                                          d_w_router, nullptr, st, 0);
+            if (e != hipSuccess) return MOE_ERR_HIP;
+        }
     }
     return MOE_OK;
 }

@@ -50,6 +50,15 @@ __device__ __forceinline__ float sigmoid_fast(float z) {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
 }
 
+// Barrier that leaves this wavefront's P most recent LDS operations in flight
+// (LDS operations of a wavefront complete in order; lgkmcnt counts to 15).
+// The main loops issue the next stage's first fragment reads last in a step;
+// they read a buffer no wavefront writes before the following barrier.
+template <int P>
+__device__ __forceinline__ void lds_barrier_keep() {
+    asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" :: "n"(P < 15 ? P : 15) : "memory");
+}
+
 // SwiGLU backward of one element: h = silu(a) * v, silu(a) = a s, s = sigmoid(a),
 // silu'(a) = s (1 + a (1 - s)).
 __device__ __forceinline__ void swiglu_bwd(float dh, float a, float v, float& da, float& dv) {
@@ -148,28 +157,33 @@ __device__ __forceinline__ void nt_tile(const NtArgs& p, const Tile& tile, uint1
         for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][q][r] = 0.0f;
-    auto compute = [&](int buf) {
+    struct Frags {
+        bf16x8 a[kMI];
+        bf16x8 b[4];
+    };
+    auto read_frags = [&](int buf, int ks, Frags& fr) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 fa[kMI], fb[4];
+        for (int mi = 0; mi < kMI; ++mi)
+            fr.a[mi] = *reinterpret_cast<const bf16x8*>(sA(buf) + a_lane[ks] + 32 * mi * kK);
 #pragma unroll
-            for (int mi = 0; mi < kMI; ++mi)
-                fa[mi] = *reinterpret_cast<const bf16x8*>(sA(buf) + a_lane[ks] + 32 * mi * kK);
+        for (int q = 0; q < 4; ++q)
+            fr.b[q] = *reinterpret_cast<const bf16x8*>(sB(buf) + b_lane[ks] + 32 * q * kK);
+    };
+    auto mfmas = [&](const Frags& fr) {
+#pragma unroll
+        for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                fb[q] = *reinterpret_cast<const bf16x8*>(sB(buf) + b_lane[ks] + 32 * q * kK);
-#pragma unroll
-            for (int mi = 0; mi < kMI; ++mi)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    acc[mi][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[q], acc[mi][q], 0, 0, 0);
-        }
+                acc[mi][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.a[mi], fr.b[q], acc[mi][q], 0, 0, 0);
     };
 
-    // Stage s lives in register set s % 3, then LDS buffer s % 3. Step kt:
-    // MFMAs of stage kt, store stage kt+2 into the buffer stage kt-1 used
-    // (every wave passed the barrier after its last read), reload the set
-    // with stage kt+5, barrier. Loads past the last stage re-read it.
+    // Stage s lives in register set s % 3, then LDS buffer s % 3. Step kt,
+    // after a barrier that publishes stage kt+1 and retires every read of
+    // buffer (kt-1) % 3: read the second k-substep of stage kt, MFMAs of the
+    // first (read in the step before), store stage kt+2 into buffer
+    // (kt-1) % 3 and reload its register set with stage kt+5, read the first
+    // k-substep of stage kt+1, MFMAs of the second. Loads past the last stage
+    // re-read it.
     auto clampk = [&](int k) { return min(k, KT - 1); };
     NtStage rs[kSetsB];
 #pragma unroll
@@ -180,12 +194,19 @@ __device__ __forceinline__ void nt_tile(const NtArgs& p, const Tile& tile, uint1
     store(1, rs[1]);
     load(clampk(4), rs[1]);
     lds_barrier();
+    Frags f0, f1;
+    read_frags(0, 0, f0);
     auto step = [&](int kt, int buf, NtStage& r) {
-        compute(buf);
-        store(buf == 0 ? 2 : buf - 1, r);
+        const int nxt = buf == kRingB - 1 ? 0 : buf + 1;
+        const int wr = nxt == kRingB - 1 ? 0 : nxt + 1;
+        lds_barrier_keep<kMI + 4>();
+        read_frags(buf, 1, f1);
+        mfmas(f0);
+        store(wr, r);
         load(clampk(kt + 5), r);
-        lds_barrier();
-        return buf == kRingB - 1 ? 0 : buf + 1;
+        read_frags(nxt, 0, f0);
+        mfmas(f1);
+        return nxt;
     };
     int kt = 0, buf = 0;
     for (; kt + kSetsB <= KT; kt += kSetsB) {
@@ -200,6 +221,57 @@ __device__ __forceinline__ void nt_tile(const NtArgs& p, const Tile& tile, uint1
     // 8 (r/4) + 4 (lane/32) + r%4 for register r.
     const int col_l = lane & 31;
     const int row_l = 4 * (lane >> 5);
+    if constexpr (EPI == kNtSwigluBwd) {
+        // The SwiGLU backward reads a and v and writes da and dv, two bf16
+        // tensors each: done element by element from the accumulator layout
+        // that is four 2-byte accesses per element. Instead every wavefront
+        // stages its dh rows, 32 at a time, row-major in its own slice of the
+        // idle ring (fp32, row stride 136: the two rows a register spans fall
+        // in different banks), and reads them back as 8 consecutive columns
+        // per lane, so that a, v, da and dv move in 16-byte chunks.
+        constexpr int SS = 136;
+        lds_barrier();   // every wavefront is done with the stage buffers
+        float* sw = reinterpret_cast<float*>(smem) + wave * (32 * SS);
+        const int rr0 = lane >> 4;           // row within a group of 4
+        const int c8 = (lane & 15) * 8;      // 8 columns of the wavefront's 128
+        const int col = n0 + 128 * wn + c8;
+        uint16_t* D = static_cast<uint16_t*>(p.C);
+#pragma unroll
+        for (int mi = 0; mi < kMI; ++mi) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    sw[(8 * (r >> 2) + row_l + (r & 3)) * SS + 32 * q + col_l] = acc[mi][q][r];
+            // LDS operations of a wavefront complete in order: the reads below
+            // see these writes, and the next block's writes follow the reads
+#pragma unroll 2
+            for (int it = 0; it < 8; ++it) {
+                const int rr = rr0 + 4 * it;
+                const int row = m0 + (TM / 2) * wm + 32 * mi + rr;
+                const f32x4 h0 = *reinterpret_cast<const f32x4*>(&sw[rr * SS + c8]);
+                const f32x4 h1 = *reinterpret_cast<const f32x4*>(&sw[rr * SS + c8 + 4]);
+                if (row > seg_last || col >= p.N) continue;
+                const size_t o = (size_t)row * 2 * p.N + col;
+                const u32x4 av = *reinterpret_cast<const u32x4*>(p.act + o);
+                const u32x4 vv = *reinterpret_cast<const u32x4*>(p.act + o + p.N);
+                const float dh[8] = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+                u32x4 da_out, dv_out;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    float da0, dv0, da1, dv1;
+                    swiglu_bwd(dh[2 * w], __uint_as_float(av[w] << 16), __uint_as_float(vv[w] << 16), da0, dv0);
+                    swiglu_bwd(dh[2 * w + 1], __uint_as_float(av[w] & 0xffff0000u),
+                               __uint_as_float(vv[w] & 0xffff0000u), da1, dv1);
+                    da_out[w] = f32x2_to_bf16x2(da0, da1);
+                    dv_out[w] = f32x2_to_bf16x2(dv0, dv1);
+                }
+                *reinterpret_cast<u32x4*>(D + o) = da_out;
+                *reinterpret_cast<u32x4*>(D + o + p.N) = dv_out;
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
@@ -211,14 +283,7 @@ __device__ __forceinline__ void nt_tile(const NtArgs& p, const Tile& tile, uint1
                 const int row = m0 + (TM / 2) * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
                 if (row > seg_last) continue;
                 const float v = acc[mi][q][r];
-                if constexpr (EPI == kNtSwigluBwd) {
-                    const size_t o = (size_t)row * 2 * p.N + col;
-                    float da, dv;
-                    swiglu_bwd(v, bf16_to_f32(p.act[o]), bf16_to_f32(p.act[o + p.N]), da, dv);
-                    uint16_t* D = static_cast<uint16_t*>(p.C);
-                    D[o] = f32_to_bf16(da);
-                    D[o + p.N] = f32_to_bf16(dv);
-                } else if constexpr (EPI == kNtStoreF32) {
+                if constexpr (EPI == kNtStoreF32) {
                     static_cast<float*>(p.C)[(size_t)row * p.N + col] = v;
                 } else if constexpr (EPI == kNtAccumF32) {
                     static_cast<float*>(p.C)[(size_t)row * p.N + col] += v;
@@ -263,21 +328,47 @@ struct TnArgs {
     float* C0;          // [E, M, Nc] fp32
     float* C1;          // paired: second output [E, M, Nc]
     float scale;
+    int split;          // offsets NULL and split > 0: group e is rows [e*split, (e+1)*split)
 };
 
+// Rows [j0, j1) of group e: the expert's segment, all rows, or one split.
+__device__ __forceinline__ void group_rows(const int32_t* offsets, int split, int rows, int e,
+                                           int& j0, int& j1) {
+    if (offsets) {
+        j0 = min(max(offsets[e], 0), rows);
+        j1 = max(j0, min(offsets[e + 1], rows));
+    } else if (split > 0) {
+        j0 = min(e * split, rows);
+        j1 = min(j0 + split, rows);
+    } else {
+        j0 = 0;
+        j1 = rows;
+    }
+}
+
+// One output tile of TM (256 or 128) x 256 per block. TM = 256 holds 256
+// fp32 accumulators per lane (one block per CU); TM = 128 holds 128, so two
+// blocks share a CU and one block's epilogue stores overlap the other's
+// loads and products.
+template <int TM>
 struct TnStage {
-    u32x4 a[4];
+    u32x4 a[TM / 64];
     u32x4 b[4];
 };
 
-__global__ __launch_bounds__(kT, 1) void tn_mfma_kernel(TnArgs p, const int32_t* __restrict__ offsets,
-                                                       int rows, int E)
+template <int TM>
+__global__ __launch_bounds__(kT, TM == 256 ? 1 : 2) void tn_mfma_kernel(
+    TnArgs p, const int32_t* __restrict__ offsets, int rows, int E)
 {
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[kRingB * 2 * kK * kN];
-    auto sA = [&](int b) { return smem + b * (kK * kN); };
-    auto sB = [&](int b) { return smem + kRingB * (kK * kN) + b * (kK * kN); };
+    constexpr int kMI = TM / 64;          // 32-row blocks per wavefront (= A chunks per thread)
+    constexpr int kAT = TM / 8;           // threads per A k-row (16-byte chunks)
+    constexpr int kAR = kT / kAT;         // A k-rows per pass
+    constexpr int kS = TM == 256 ? 3 : 2; // register stages in flight (two blocks per CU: two)
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[kRingB * kK * (TM + kN)];
+    auto sA = [&](int b) { return smem + b * (kK * TM); };
+    auto sB = [&](int b) { return smem + kRingB * (kK * TM) + b * (kK * kN); };
 
-    const int mt_n = (p.M + kN - 1) / kN;
+    const int mt_n = (p.M + TM - 1) / TM;
     const int ncols = p.pair > 0 ? 128 : kN;
     const int nt_n = (p.Nc + ncols - 1) / ncols;
     const int per_e = mt_n * nt_n;
@@ -290,109 +381,148 @@ __global__ __launch_bounds__(kT, 1) void tn_mfma_kernel(TnArgs p, const int32_t*
     const int e = t / per_e;
     const int mt = (t % per_e) / nt_n;
     const int nt = t % nt_n;
-    const int m0 = mt * kN, n0 = nt * ncols;
-    const int j0 = offsets ? min(max(offsets[e], 0), rows) : 0;
-    const int j1 = offsets ? max(j0, min(offsets[e + 1], rows)) : rows;
-    // stages of 32 rows, rounded up to a whole number of 3-step loop bodies
+    const int m0 = mt * TM, n0 = nt * ncols;
+    int j0, j1;
+    group_rows(offsets, p.split, rows, e, j0, j1);
+    // stages of 32 rows, rounded up to a whole number of kS-step loop bodies
     // (the rows past the expert's end load as zeros and add nothing)
-    const int KT = (j1 - j0 + 3 * kK - 1) / (3 * kK) * 3;
+    const int KT = (j1 - j0 + kS * kK - 1) / (kS * kK) * kS;
 
     int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int wm = wave >> 1, wn = wave & 1;
 
-    f32x16 acc[4][4];
+    f32x16 acc[kMI][4];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][q][r] = 0.0f;
 
     if (KT > 0) {
-        // chunk i of a stage: k-row tid/32 + 8 i, 16-byte chunk c = tid%32 of the
-        // 256 columns (columns clamped inside the operand; rows past the
-        // expert's end load as zeros)
-        const int c = tid & 31;
-        const int acol = min(m0 + 8 * c, p.M - 8);
+        // A chunk i: k-row tid/kAT + kAR i, 16-byte chunk tid%kAT of the TM
+        // columns; B chunk i: k-row tid/32 + 8 i, chunk tid%32 of the 256
+        // columns (columns clamped inside the operand; rows past the expert's
+        // end load as zeros)
+        const int ca = tid % kAT, cb = tid & 31;
+        const int acol = min(m0 + 8 * ca, p.M - 8);
         int bcol;
-        if (p.pair > 0) bcol = (c < 16) ? min(n0 + 8 * c, p.Nc - 8) : p.pair + min(n0 + 8 * (c - 16), p.Nc - 8);
-        else bcol = min(n0 + 8 * c, p.Nc - 8);
-        auto load = [&](int kt, TnStage& r) {
+        if (p.pair > 0) bcol = (cb < 16) ? min(n0 + 8 * cb, p.Nc - 8) : p.pair + min(n0 + 8 * (cb - 16), p.Nc - 8);
+        else bcol = min(n0 + 8 * cb, p.Nc - 8);
+        // Rows past the expert's end read its last row and are zeroed when
+        // the stage goes to LDS (a select right after the load would make
+        // the wavefront wait for that load there and then).
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        auto load = [&](int kt, TnStage<TM>& r) {
+#pragma unroll
+            for (int i = 0; i < kMI; ++i) {
+                const int j = j0 + kt * kK + tid / kAT + kAR * i;
+                r.a[i] = *reinterpret_cast<const u32x4*>(p.A + (size_t)min(j, j1 - 1) * p.lda + acol);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = j0 + kt * kK + (tid >> 5) + 8 * i;
-                const int jc = min(j, j1 - 1);
-                const u32x4 va = *reinterpret_cast<const u32x4*>(p.A + (size_t)jc * p.lda + acol);
-                const u32x4 vb = *reinterpret_cast<const u32x4*>(p.B + (size_t)jc * p.ldb + bcol);
-                const u32x4 z = {0u, 0u, 0u, 0u};
-                r.a[i] = j < j1 ? va : z;
-                r.b[i] = j < j1 ? vb : z;
+                r.b[i] = *reinterpret_cast<const u32x4*>(p.B + (size_t)min(j, j1 - 1) * p.ldb + bcol);
             }
         };
-        const int dst = (tid >> 5) * kN + b_swz(c, tid >> 5) * 8;
-        auto store = [&](int buf, const TnStage& r) {
+        const int adst = (tid / kAT) * TM + b_swz(ca, tid / kAT) * 8;
+        const int bdst = (tid >> 5) * kN + b_swz(cb, tid >> 5) * 8;
+        auto store = [&](int buf, int kt, const TnStage<TM>& r) {
+#pragma unroll
+            for (int i = 0; i < kMI; ++i) {
+                const int j = j0 + kt * kK + tid / kAT + kAR * i;
+                *reinterpret_cast<u32x4*>(sA(buf) + adst + kAR * i * TM) = j < j1 ? r.a[i] : z;
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                *reinterpret_cast<u32x4*>(sA(buf) + dst + 8 * i * kN) = r.a[i];
-                *reinterpret_cast<u32x4*>(sB(buf) + dst + 8 * i * kN) = r.b[i];
+                const int j = j0 + kt * kK + (tid >> 5) + 8 * i;
+                *reinterpret_cast<u32x4*>(sB(buf) + bdst + 8 * i * kN) = j < j1 ? r.b[i] : z;
             }
         };
         // transpose-read fragments: in each 16-lane group g, lane j points at
         // k-row 8 (g/2) + j/4 and columns base + 16 (g%2) + 4 (j%4)..+3
         const int g = lane >> 4, jl = lane & 15;
         const int kr = 8 * (g >> 1) + (jl >> 2);
-        int a_lane[4], b_lane[4];
+        int a_lane[kMI], b_lane[4];
+#pragma unroll
+        for (int mi = 0; mi < kMI; ++mi) {
+            const int m = (TM / 2) * wm + 32 * mi + 16 * (g & 1) + 4 * (jl & 3);
+            a_lane[mi] = kr * TM + b_swz(m >> 3, kr) * 8 + (m & 7);
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int m = 128 * wm + 32 * q + 16 * (g & 1) + 4 * (jl & 3);
             const int n = 128 * wn + 32 * q + 16 * (g & 1) + 4 * (jl & 3);
-            a_lane[q] = kr * kN + b_swz(m >> 3, kr) * 8 + (m & 7);
             b_lane[q] = kr * kN + b_swz(n >> 3, kr) * 8 + (n & 7);
         }
-        auto tr8 = [&](const uint16_t* s) {
+        auto tr8 = [&](const uint16_t* s, int row_elems) {
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(s));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(s + 4 * kN));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(s + 4 * row_elems));
             const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             return __builtin_bit_cast(bf16x8, v);
         };
-        auto compute = [&](int buf) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                bf16x8 fa[4], fb[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    fa[q] = tr8(sA(buf) + a_lane[q] + 16 * ks * kN);
-                    fb[q] = tr8(sB(buf) + b_lane[q] + 16 * ks * kN);
-                }
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        acc[mi][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[q], acc[mi][q], 0, 0, 0);
-            }
+        struct Frags {
+            bf16x8 a[kMI];
+            bf16x8 b[4];
         };
-        auto clampk = [&](int k) { return min(k, KT - 1); };
-        TnStage rs[kSetsB];
+        auto read_frags = [&](int buf, int ks, Frags& fr) {
 #pragma unroll
-        for (int i = 0; i < kSetsB; ++i) load(clampk(i), rs[i]);
-        store(0, rs[0]);
-        load(clampk(3), rs[0]);
-        store(1, rs[1]);
-        load(clampk(4), rs[1]);
+            for (int mi = 0; mi < kMI; ++mi) fr.a[mi] = tr8(sA(buf) + a_lane[mi] + 16 * ks * TM, TM);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) fr.b[q] = tr8(sB(buf) + b_lane[q] + 16 * ks * kN, kN);
+        };
+        auto mfmas = [&](const Frags& fr) {
+#pragma unroll
+            for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[mi][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.a[mi], fr.b[q], acc[mi][q], 0, 0, 0);
+        };
+        // Stage s lives in register set s % kS, then LDS buffer s % 3. Step
+        // kt: the products of stage kt (both k-substeps), store stage kt+2
+        // into the buffer stage kt-1 used (every wavefront passed the barrier
+        // after its last read of it), reload the set with stage kt+2+kS,
+        // barrier. Loads past the last stage re-read it.
+        auto clampk = [&](int k) { return min(k, KT - 1); };
+        TnStage<TM> rs[kS];
+#pragma unroll
+        for (int i = 0; i < kS; ++i) load(clampk(i), rs[i]);
+        store(0, 0, rs[0]);
+        load(clampk(kS), rs[0]);
+        store(1, 1, rs[1]);
+        load(clampk(kS + 1), rs[1]);
         lds_barrier();
-        auto step = [&](int kt, int buf, TnStage& r) {
-            compute(buf);
-            store(buf == 0 ? 2 : buf - 1, r);
-            load(clampk(kt + 5), r);
-            lds_barrier();
-            return buf == kRingB - 1 ? 0 : buf + 1;
+        // TM = 256 (registers to spare) also reads the next stage's first
+        // k-substep ahead, across the barrier, as the data-gradient kernel does
+        Frags f0, f1;
+        if constexpr (TM == 256) read_frags(0, 0, f0);
+        auto step = [&](int kt, int buf, TnStage<TM>& r) {
+            const int nxt = buf == kRingB - 1 ? 0 : buf + 1;
+            const int wr = nxt == kRingB - 1 ? 0 : nxt + 1;
+            if constexpr (TM == 256) {
+                lds_barrier_keep<2 * (kMI + 4)>();
+                read_frags(buf, 1, f1);
+                mfmas(f0);
+                store(wr, kt + 2, r);
+                load(clampk(kt + 2 + kS), r);
+                read_frags(nxt, 0, f0);
+                mfmas(f1);
+            } else {
+                read_frags(buf, 0, f0);
+                mfmas(f0);
+                read_frags(buf, 1, f0);
+                mfmas(f0);
+                store(wr, kt + 2, r);
+                load(clampk(kt + 2 + kS), r);
+                lds_barrier();
+            }
+            return nxt;
         };
         int buf = 0;
-        for (int kt = 0; kt < KT; kt += kSetsB) {
+        for (int kt = 0; kt < KT; kt += kS) {
 #pragma unroll
-            for (int u = 0; u < kSetsB; ++u) buf = step(kt + u, buf, rs[(u + 2) % kSetsB]);
+            for (int u = 0; u < kS; ++u) buf = step(kt + u, buf, rs[(u + 2) % kS]);
         }
     }
 
@@ -408,14 +538,14 @@ __global__ __launch_bounds__(kT, 1) void tn_mfma_kernel(TnArgs p, const int32_t*
     }
     C += (size_t)e * p.M * p.Nc;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int col = cbase + 32 * q + col_l;
             if (col >= p.Nc) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = m0 + 128 * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
+                const int row = m0 + (TM / 2) * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
                 if (row < p.M) C[(size_t)row * p.Nc + col] = p.scale * acc[mi][q][r];
             }
         }
@@ -514,7 +644,7 @@ template <typename XT>
 __global__ __launch_bounds__(256) void tn_generic_kernel(
     const XT* __restrict__ A, int lda, int M, const XT* __restrict__ B, int ldb, int Nc, int pair,
     float* __restrict__ C0, float* __restrict__ C1, float scale,
-    const int32_t* __restrict__ offsets, int rows, int E)
+    const int32_t* __restrict__ offsets, int split, int rows, int E)
 {
     __shared__ float sA[kGK][kGM + 1];
     __shared__ float sB[kGK][kGN + 1];
@@ -531,8 +661,8 @@ __global__ __launch_bounds__(256) void tn_generic_kernel(
     const int nt = rest % nt_n;
     const int m0 = mt * kGM, n0 = nt * kGN;
     const int bcol0 = half ? pair : 0;
-    const int j0 = offsets ? min(max(offsets[e], 0), rows) : 0;
-    const int j1 = offsets ? max(j0, min(offsets[e + 1], rows)) : rows;
+    int j0, j1;
+    group_rows(offsets, split, rows, e, j0, j1);
     const int tid = threadIdx.x;
     const int tx = tid % 16, ty = tid / 16;
     float acc[4][4];
@@ -625,21 +755,29 @@ hipError_t launch_nt(int epi, const void* A, moe_dtype dt, int rows, int K, int 
     return hipGetLastError();
 }
 
+// Weight-gradient tile height (128: two blocks per CU).
+#ifndef MOE_TN_TM
+#define MOE_TN_TM 128
+#endif
+constexpr int kTnTM = MOE_TN_TM;
+
 // C_e[M, Nc] = scale * A_e^T B_e over the rows of each group (offsets NULL:
-// one group of all rows); pair > 0: B columns [0, Nc) -> C0 and
-// [pair, pair + Nc) -> C1.
+// one group of all rows, or with split > 0 groups of `split` consecutive
+// rows); pair > 0: B columns [0, Nc) -> C0 and [pair, pair + Nc) -> C1.
 hipError_t launch_tn(const void* A, int lda, int M, const void* B, int ldb, int Nc, int pair,
                      moe_dtype dt, int rows, int E, const int32_t* offsets, float scale,
-                     float* C0, float* C1, hipStream_t st)
+                     float* C0, float* C1, hipStream_t st, int split)
 {
     const bool mfma = dt == MOE_BF16 && lda % 8 == 0 && ldb % 8 == 0 && M % 8 == 0 &&
                       Nc % 8 == 0 && pair % 8 == 0 && M >= 8 && Nc >= 8 && al16(A) && al16(B);
     if (mfma) {
-        TnArgs p{(const uint16_t*)A, lda, M, (const uint16_t*)B, ldb, Nc, pair, C0, C1, scale};
-        const long long tiles = (long long)E * ((M + kN - 1) / kN) *
+        TnArgs p{(const uint16_t*)A, lda, M, (const uint16_t*)B, ldb, Nc, pair, C0, C1, scale,
+                 split};
+        constexpr int TM = kTnTM;
+        const long long tiles = (long long)E * ((M + TM - 1) / TM) *
                                 ((Nc + (pair > 0 ? 128 : kN) - 1) / (pair > 0 ? 128 : kN));
         const unsigned g = (unsigned)std::max(8LL, (tiles + 7) / 8 * 8);
-        tn_mfma_kernel<<<g, kT, 0, st>>>(p, offsets, rows, E);
+        tn_mfma_kernel<TM><<<g, kT, 0, st>>>(p, offsets, rows, E);
         return hipGetLastError();
     }
     const long long tiles = (long long)E * ((M + kGM - 1) / kGM) * ((Nc + kGN - 1) / kGN) *
@@ -647,10 +785,51 @@ hipError_t launch_tn(const void* A, int lda, int M, const void* B, int ldb, int 
     if (dt == MOE_BF16)
         tn_generic_kernel<uint16_t><<<(unsigned)tiles, 256, 0, st>>>(
             (const uint16_t*)A, lda, M, (const uint16_t*)B, ldb, Nc, pair, C0, C1, scale, offsets,
-            rows, E);
+            split, rows, E);
     else
         tn_generic_kernel<float><<<(unsigned)tiles, 256, 0, st>>>(
-            (const float*)A, lda, M, (const float*)B, ldb, Nc, pair, C0, C1, scale, offsets, rows, E);
+            (const float*)A, lda, M, (const float*)B, ldb, Nc, pair, C0, C1, scale, offsets, split,
+            rows, E);
+    return hipGetLastError();
+}
+
+// out[i] = sum over g ascending of part[g * n + i] (a fixed order: the result
+// does not depend on the launch)
+__global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict__ part, int S,
+                                                        long long n, float* __restrict__ out)
+{
+    const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;
+    if (i + 4 <= n) {
+        f32x4 acc = *reinterpret_cast<const f32x4*>(part + i);
+        for (int g = 1; g < S; ++g) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(part + (size_t)g * n + i);
+            acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
+        }
+        *reinterpret_cast<f32x4*>(out + i) = acc;
+    } else {
+        for (long long q = i; q < n; ++q) {
+            float acc = part[q];
+            for (int g = 1; g < S; ++g) acc += part[(size_t)g * n + q];
+            out[q] = acc;
+        }
+    }
+}
+
+// Row splits of the router's weight gradient (one output reduced over all T
+// tokens): enough groups to fill the machine, each a whole number of the
+// kernel's 96-row loop bodies.
+int router_splits(int T, int& split) {
+    if (T <= 96) { split = 0; return 1; }
+    const int S0 = std::min(64, (T + 95) / 96);
+    split = ((T + S0 - 1) / S0 + 95) / 96 * 96;
+    return (T + split - 1) / split;
+}
+
+hipError_t launch_sum_splits(const float* part, int S, long long n, float* out, hipStream_t st)
+{
+    const long long blocks = (n + 1023) / 1024;
+    sum_splits_kernel<<<(unsigned)blocks, 256, 0, st>>>(part, S, n, out);
     return hipGetLastError();
 }
 

@@ -57,7 +57,7 @@ def lib():
         "moe_ffn_weight_grads": [vp, vp, vp, vp, i, i, i, i, i, vp, ctypes.c_float, vp, vp, vp,
                                  vp],
         "moe_route_backward": [vp, vp, vp, vp, i, i, i, i, vp, vp, vp],
-        "moe_router_backward": [vp, vp, i, vp, i, i, i, vp, i, vp, vp],
+        "moe_router_backward": [vp, vp, i, vp, i, i, i, vp, i, vp, vp, sz, vp],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -65,7 +65,8 @@ def lib():
         fn.restype = i
     for name, args in {"moe_permute_workspace": [i, i, i],
                        "moe_permute_recv_workspace": [i, i, i],
-                       "moe_grouped_ffn_workspace": [i, i, i, i, i]}.items():
+                       "moe_grouped_ffn_workspace": [i, i, i, i, i],
+                       "moe_router_backward_workspace": [i, i, i]}.items():
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = sz
@@ -383,17 +384,24 @@ def route_backward(logits, idx, gates, d_gates, renorm: bool = True, *, lp_dtype
     return d_l, d_lp
 
 
+def router_backward_workspace(T: int, d: int, E: int) -> int:
+    return int(lib().moe_router_backward_workspace(T, d, E))
+
+
 def router_backward(x, w_router, d_logits, *, d_x=None, accumulate=False, want_dw=True,
-                    d_w=None, stream=None):
+                    d_w=None, workspace=None, stream=None):
     """d_x (+)= d_logits W_r^T; dW_r = x^T d_logits (fp32). d_logits in x's dtype."""
     T, d = x.shape
     E = w_router.shape[1]
     dw = d_w
     if dw is None and want_dw:
         dw = torch.empty((d, E), dtype=torch.float32, device=x.device)
+    nbytes = router_backward_workspace(T, d, E) if dw is not None else 0
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
     _check("moe_router_backward", lib().moe_router_backward(
         _p(x), _p(w_router), _dt(x), _p(d_logits), T, d, E, _p(d_x), int(bool(accumulate)),
-        _p(dw), _stream(stream)))
+        _p(dw), _p(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
     return d_x, dw
 
 

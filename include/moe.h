@@ -324,10 +324,16 @@ moe_status moe_route_backward(const float* logits, const int32_t* topk_idx, cons
  *   d_w_router  = x^T . d_logits        [d,E] fp32
  *   x [T,d], W_r [d,E] and d_logits [T,E] in dtype dt (bf16: the copy
  *   moe_route_backward writes). Either output may be NULL.
+ * d_w_router is one [d,E] output reduced over all T tokens: the tokens are
+ * split into row groups whose partial products go to the workspace
+ * (moe_router_backward_workspace bytes; 0 for small T, then ws may be NULL)
+ * and are summed in group order, so the result is the same on every run.
  */
+size_t moe_router_backward_workspace(int T, int d, int E);
 moe_status moe_router_backward(const void* x, const void* w_router, moe_dtype dt,
                                const void* d_logits, int T, int d, int E, float* d_x,
-                               int accumulate, float* d_w_router, void* stream);
+                               int accumulate, float* d_w_router, void* ws, size_t ws_bytes,
+                               void* stream);
 
 #ifdef __cplusplus
 }

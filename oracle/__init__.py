@@ -73,6 +73,7 @@ def lib():
                                      vp, vp, vp, vp]
         i64, i32 = ctypes.c_int64, ctypes.c_int
         L.oracle_route_backward.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, vp]
+        L.oracle_route_stats.argtypes = [vp, vp, i64, i32, i32, vp, vp]
         L.oracle_router_grads.argtypes = [vp, vp, i32, i64, i32, i32, vp, vp, i64, vp, vp]
         L.oracle_combine_backward_gates.argtypes = [vp, i64, i32, i64, vp, vp, vp, vp, vp]
         L.oracle_combine_backward_rows.argtypes = [vp, vp, i64, i32, i64, vp, vp, vp]
@@ -86,7 +87,8 @@ def lib():
                      "oracle_expert_ffn_rows", "oracle_combine",
                      "oracle_route_backward", "oracle_router_grads",
                      "oracle_combine_backward_gates", "oracle_combine_backward_rows",
-                     "oracle_expert_ffn_backward_rows", "oracle_expert_weight_grads"):
+                     "oracle_expert_ffn_backward_rows", "oracle_expert_weight_grads",
+                     "oracle_route_stats"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -560,3 +562,16 @@ def moe_backward(inp: dict, d_out, tokens=None, pairs=None, scale: float = 1.0,
         res["d_w_gate"], res["d_w_val"], res["d_w_out"] = expert_weight_grads(
             xall, offsets, wg, wv, wo, dyall, res["pairs"], scale)
     return res
+
+
+def route_stats(logits, counts, k: int):
+    """(p_mean [E] float64, aux float): mean full-softmax probability per expert
+    and the load-balance statistic E * sum_e (counts_e / (T*k)) * p_mean_e."""
+    logits = _c(logits, np.float32)
+    counts = _c(counts, np.int32)
+    T, E = logits.shape
+    pm = np.empty(E, np.float64)
+    aux = np.empty(1, np.float64)
+    _check(lib().oracle_route_stats(_p(logits), _p(counts), T, E, k, _p(pm), _p(aux)),
+           "oracle_route_stats")
+    return pm, float(aux[0])

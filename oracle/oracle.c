@@ -565,3 +565,28 @@ int oracle_expert_weight_grads(const void* x, int xtype, int64_t N, int d, int f
     }
     return 0;
 }
+
+/* ---------------------------------------------------- load statistics */
+
+int oracle_route_stats(const float* logits, const int32_t* counts, int64_t T, int E, int k,
+                       double* p_mean, double* aux)
+{
+    if (!logits || !counts || !p_mean || !aux || T <= 0 || E <= 0 || k <= 0) return -1;
+    for (int e = 0; e < E; ++e) p_mean[e] = 0.0;
+    /* full-softmax probability of every expert, averaged over the tokens */
+    for (int64_t t = 0; t < T; ++t) {
+        const float* l = logits + (size_t)t * E;
+        double m = (double)l[0];
+        for (int e = 1; e < E; ++e)
+            if ((double)l[e] > m) m = (double)l[e];
+        double z = 0.0;
+        for (int e = 0; e < E; ++e) z += exp((double)l[e] - m);
+        for (int e = 0; e < E; ++e) p_mean[e] += exp((double)l[e] - m) / z;
+    }
+    for (int e = 0; e < E; ++e) p_mean[e] /= (double)T;
+    /* E * sum_e (share of the T*k assignments routed to e) * (mean probability of e) */
+    double s = 0.0;
+    for (int e = 0; e < E; ++e) s += ((double)counts[e] / ((double)T * k)) * p_mean[e];
+    *aux = (double)E * s;
+    return 0;
+}

@@ -103,7 +103,13 @@ def test_host_side_errors_return_before_launch(L):
     # router backward: no output asked for, k > E, NULL inputs with rows
     assert L.moe_route_backward(fake, fake, fake, fake, 4, 8, 2, 1, None, None, None) == 1
     assert L.moe_route_backward(fake, fake, fake, fake, 4, 8, 9, 1, fake, None, None) == 1
-    assert L.moe_router_backward(None, fake, 1, fake, 4, 64, 8, fake, 0, None, None) == 1
+    assert L.moe_router_backward(None, fake, 1, fake, 4, 64, 8, fake, 0, None, None, 0,
+                                 None) == 1
+    # router W_r gradient at large T needs the split workspace
+    need_r = L.moe_router_backward_workspace(4096, 64, 8)
+    assert need_r > 0 and L.moe_router_backward_workspace(64, 64, 8) == 0
+    assert L.moe_router_backward(fake, fake, 1, fake, 4096, 64, 8, None, 0, fake, None, 0,
+                                 None) == 3
 
 
 def test_empty_inputs_are_no_ops(L):

@@ -145,3 +145,43 @@ def test_nonfinite_score_is_rejected():
     w = np.ones((2, 3), np.float32)
     with pytest.raises(oracle.OracleError):
         oracle.route(x, w, None, 1)
+
+
+# ---- load statistics (the load-balance statistic the pages report as a
+# validation metric; switch-style auxiliary-loss reading)
+
+def test_route_stats_uniform_probabilities_give_one():
+    # every logit equal: each probability is 1/E whatever the routing
+    T, E, k = 50, 8, 2
+    logits = np.full((T, E), 0.25, np.float32)
+    rng = np.random.default_rng(0)
+    counts = np.bincount(rng.integers(0, E, size=T * k), minlength=E).astype(np.int32)
+    pm, aux = oracle.route_stats(logits, counts, k)
+    np.testing.assert_allclose(pm, np.full(E, 1.0 / E), rtol=1e-15)
+    assert abs(aux - 1.0) < 1e-14
+
+
+def test_route_stats_collapsed_routing_gives_E():
+    # k = 1, every token's probability and assignment on expert 3
+    T, E = 40, 6
+    logits = np.full((T, E), -200.0, np.float32)
+    logits[:, 3] = 0.0
+    counts = np.zeros(E, np.int32)
+    counts[3] = T
+    pm, aux = oracle.route_stats(logits, counts, 1)
+    assert abs(pm[3] - 1.0) < 1e-12 and abs(aux - E) < 1e-10
+
+
+def test_route_stats_probabilities_average_to_one_and_match_scipy():
+    from scipy.special import softmax
+    rng = np.random.default_rng(3)
+    T, E, k = 33, 7, 3
+    logits = (rng.standard_normal((T, E)) * 2).astype(np.float32)
+    counts = rng.integers(0, 20, size=E).astype(np.int32)
+    pm, aux = oracle.route_stats(logits, counts, k)
+    assert abs(pm.sum() - 1.0) < 1e-14
+    np.testing.assert_allclose(pm, softmax(logits.astype(np.float64), axis=1).mean(0), rtol=1e-13)
+    # aux is linear in the counts: one count on expert e alone gives E p_mean[e] / (T k)
+    c1 = np.zeros(E, np.int32)
+    c1[5] = 1
+    assert abs(oracle.route_stats(logits, c1, k)[1] - E * pm[5] / (T * k)) < 1e-15
