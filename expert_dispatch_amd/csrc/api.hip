@@ -41,6 +41,8 @@ hipError_t launch_tn(const void* A, int lda, int M, const void* B, int ldb, int 
 int router_splits(int T, int& split);
 hipError_t launch_sum_splits(const float* part, int S, long long n, float* out, hipStream_t st);
 enum NtEpi { kNtSwigluBwd = 0, kNtStoreF32 = 1, kNtAccumF32 = 2, kNtStoreBf16 = 3 };
+hipError_t launch_route_stats(const float* logits, const int32_t* counts, int T, int E, int k,
+                              float* p_mean, float* aux, float* mz, hipStream_t st);
 }  // namespace moe
 
 namespace {
@@ -235,6 +237,22 @@ moe_status moe_combine(const void* y_perm, moe_dtype y_dt, const int32_t* dest,
     return hip_status(moe::launch_combine(y_perm, y_dt, dest, gates, T, k, d, y_shared,
                                           y_shared ? sh_dt : MOE_F32, out, out_dt,
                                           as_stream(stream)));
+}
+
+size_t moe_route_stats_workspace(int T)
+{
+    return T > 0 ? moe::align_up((size_t)T * 2 * sizeof(float), 256) : 0;
+}
+
+moe_status moe_route_stats(const float* logits, const int32_t* counts, int T, int E, int k,
+                           float* p_mean, float* aux, void* ws, size_t ws_bytes, void* stream)
+{
+    if (T <= 0 || E <= 0 || k <= 0 || k > E) return MOE_ERR_INVALID_ARG;
+    if ((long long)T * E > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if (!logits || !p_mean || (aux && !counts)) return MOE_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < moe_route_stats_workspace(T)) return MOE_ERR_WORKSPACE;
+    return hip_status(moe::launch_route_stats(logits, counts, T, E, k, p_mean, aux,
+                                              static_cast<float*>(ws), as_stream(stream)));
 }
 
 // ------------------------------------------------------------------ backward

@@ -357,6 +357,74 @@ hipError_t launch_route_bwd(const float* logits, const int32_t* idx, const float
     return hipGetLastError();
 }
 
+// ------------------------------------------------------- load statistics
+//
+// p_mean[e] = (1/T) sum_t softmax(l[t,:])[e] and aux = E sum_e (counts[e] /
+// (T k)) p_mean[e]. Three small launches: per-token max and softmax
+// denominator (one wavefront per token), per-expert column sums (64 experts
+// x 4 token phases per block, fp64 partial sums combined in a fixed order),
+// and the weighted sum over experts (one block). No atomics: the result is
+// the same on every run.
+__global__ __launch_bounds__(256) void route_norm_kernel(const float* __restrict__ logits, int T,
+                                                        int E, float* __restrict__ mz)
+{
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T) return;
+    const int lane = lane_id();
+    const float* l = logits + (size_t)t * E;
+    float m = -__builtin_inff();
+    for (int e = lane; e < E; e += kWave) m = fmaxf(m, l[e]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+    float z = 0.0f;
+    for (int e = lane; e < E; e += kWave) z += expf(l[e] - m);
+    z = wave_sum_f32(z);
+    if (lane == 0) { mz[2 * (size_t)t] = m; mz[2 * (size_t)t + 1] = z; }
+}
+
+__global__ __launch_bounds__(256) void route_pmean_kernel(const float* __restrict__ logits,
+                                                         const float* __restrict__ mz, int T,
+                                                         int E, float* __restrict__ p_mean)
+{
+    __shared__ double part[4][64];
+    const int el = threadIdx.x & 63, g = threadIdx.x >> 6;
+    const int e = blockIdx.x * 64 + el;
+    double acc = 0.0;
+    if (e < E)
+        for (int t = g; t < T; t += 4)
+            acc += (double)(expf(logits[(size_t)t * E + e] - mz[2 * (size_t)t]) / mz[2 * (size_t)t + 1]);
+    part[g][el] = acc;
+    __syncthreads();
+    if (g == 0 && e < E)
+        p_mean[e] = (float)(((part[0][el] + part[1][el]) + (part[2][el] + part[3][el])) / (double)T);
+}
+
+__global__ __launch_bounds__(256) void route_aux_kernel(const float* __restrict__ p_mean,
+                                                       const int32_t* __restrict__ counts, int T,
+                                                       int E, int k, float* __restrict__ aux)
+{
+    __shared__ double part[256];
+    double acc = 0.0;
+    for (int e = threadIdx.x; e < E; e += 256)
+        acc += ((double)counts[e] / ((double)T * k)) * (double)p_mean[e];
+    part[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *aux = (float)((double)E * part[0]);
+}
+
+hipError_t launch_route_stats(const float* logits, const int32_t* counts, int T, int E, int k,
+                              float* p_mean, float* aux, float* mz, hipStream_t st)
+{
+    route_norm_kernel<<<(T + 3) / 4, 256, 0, st>>>(logits, T, E, mz);
+    route_pmean_kernel<<<(E + 63) / 64, 256, 0, st>>>(logits, mz, T, E, p_mean);
+    if (aux) route_aux_kernel<<<1, 256, 0, st>>>(p_mean, counts, T, E, k, aux);
+    return hipGetLastError();
+}
+
 template <typename XT>
 static hipError_t launch_scores_t(const void* x, const void* w, const float* bias, int T, int d,
                                   int E, float* logits, hipStream_t st)

@@ -58,6 +58,7 @@ def lib():
                                  vp],
         "moe_route_backward": [vp, vp, vp, vp, i, i, i, i, vp, vp, vp],
         "moe_router_backward": [vp, vp, i, vp, i, i, i, vp, i, vp, vp, sz, vp],
+        "moe_route_stats": [vp, vp, i, i, i, vp, vp, vp, sz, vp],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -66,7 +67,8 @@ def lib():
     for name, args in {"moe_permute_workspace": [i, i, i],
                        "moe_permute_recv_workspace": [i, i, i],
                        "moe_grouped_ffn_workspace": [i, i, i, i, i],
-                       "moe_router_backward_workspace": [i, i, i]}.items():
+                       "moe_router_backward_workspace": [i, i, i],
+                       "moe_route_stats_workspace": [i]}.items():
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = sz
@@ -120,6 +122,21 @@ def route(x, w_router, bias, k: int, renorm: bool = True, *, out=None, stream=No
                                         int(bool(renorm)), _p(logits), _p(idx), _p(gates),
                                         _stream(stream)))
     return logits, idx, gates
+
+
+def route_stats(logits, counts, k: int, *, stream=None):
+    """(p_mean [E] fp32, aux [1] fp32): the mean full-softmax probability of
+    every expert and the load-balance statistic E * sum_e (counts_e/(T*k)) p_mean_e."""
+    _dev(logits, "logits"); _dev(counts, "counts")
+    T, E = logits.shape
+    p_mean = torch.empty(E, dtype=torch.float32, device=logits.device)
+    aux = torch.empty(1, dtype=torch.float32, device=logits.device)
+    ws = torch.empty(max(1, int(lib().moe_route_stats_workspace(T))), dtype=torch.uint8,
+                     device=logits.device)
+    _check("moe_route_stats", lib().moe_route_stats(
+        _p(logits), _p(counts), T, E, k, _p(p_mean), _p(aux), _p(ws), ws.numel(),
+        _stream(stream)))
+    return p_mean, aux
 
 
 def permute_workspace(T: int, k: int, E: int) -> int:

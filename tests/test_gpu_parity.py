@@ -355,3 +355,28 @@ def test_bf16_outputs():
     ref_rms = float(np.sqrt(np.mean(o["out"] ** 2)))
     assert np.max(np.abs(widen(ob) - o["out"])) / ref_rms <= 4e-2
     assert np.max(np.abs(widen(yb) - o["y"])) / float(np.sqrt(np.mean(o["y"] ** 2))) <= 4e-2
+
+
+@pytest.mark.parametrize("name", ["qwen3_small", "qwen3_30b_a3b", "stress_zipf", "dsv2_small_empty4"])
+def test_route_stats(name):
+    """Per-expert mean probability and the load-balance statistic from the
+    GPU's logits and counts, against the oracle on the same logits and counts
+    (integers bit-exact first, so both sides see the same inputs)."""
+    cfg = W.get(name)
+    say(f"[parity] {name}: load statistics")
+    inp = _inputs(name)
+    dev = _device(inp)
+    logits, idx, gates = ops.route(dev["x"], dev["w_router"], dev.get("bias"), cfg.k)
+    p = ops.permute(idx, dev["x"], cfg.E)
+    p_mean, aux = ops.route_stats(logits, p["counts"], cfg.k)
+    torch.cuda.synchronize()
+    lg = to_numpy(logits)
+    o_logits, o_idx, _ = oracle.route(inp["x"], inp["w_router"], inp.get("bias"), cfg.k)
+    np.testing.assert_array_equal(lg.view(np.uint32), o_logits.view(np.uint32))
+    counts = to_numpy(p["counts"])
+    np.testing.assert_array_equal(counts, np.bincount(o_idx.reshape(-1), minlength=cfg.E))
+    o_pm, o_aux = oracle.route_stats(o_logits, counts, cfg.k)
+    e1 = err_f32(to_numpy(p_mean), o_pm)
+    e2 = abs(float(to_numpy(aux)[0]) - o_aux) / abs(o_aux)
+    assert e1 <= 1e-5 and e2 <= 1e-5, (e1, e2)
+    say(f"[parity] {name}: aux {o_aux:.6f} (1 = balanced) ok p_err={e1:.2e} aux_err={e2:.2e}")
