@@ -26,12 +26,7 @@ namespace moe {
 
 constexpr int kRT = 64;       // tokens per block
 constexpr int kRE = 32;       // experts per block
-constexpr int kRD = 128;      // d-chunk
-constexpr int kRS = kRD + 4;  // x tile row stride (floats)
-constexpr int kXU = kRT * kRD / 1024;  // x groups of 4 per thread per chunk
-constexpr int kWU = kRD * kRE / 1024;  // W_r groups of 4 per thread per chunk
 constexpr int kRG = 8;        // steps per register group
-constexpr int kRBuf = kRT * kRS + kRD * kRE;  // floats per LDS buffer
 
 // VEC: d % 4 == 0, E % 4 == 0 and aligned pointers (4-element vector loads).
 // Block: 64 tokens x 32 experts; thread (eg, tg) = (tid % 8, tid / 8) owns
@@ -46,11 +41,21 @@ constexpr int kRBuf = kRT * kRS + kRD * kRE;  // floats per LDS buffer
 // barrier per chunk). Inside a chunk the LDS reads of the next 8 steps are
 // issued before the 64 FMAs of the current 8 (scheduling barriers keep that
 // order), so one wavefront per SIMD keeps its ALU fed.
-template <typename XT, bool VEC>
+//
+// KRD is the d-chunk: 128 (100 KB of LDS, one block per CU) when the grid
+// has about one block per CU anyway; 64 (50 KB, three blocks per CU, so a
+// CU runs other blocks' FMAs through one block's staging and barriers) when
+// there are many more blocks than CUs.
+template <typename XT, bool VEC, int KRD>
 __global__ __launch_bounds__(256) void route_scores_kernel(
     const XT* __restrict__ x, const XT* __restrict__ w, const float* __restrict__ bias,
     int T, int d, int E, float* __restrict__ logits)
 {
+    constexpr int kRD = KRD;                        // d-chunk
+    constexpr int kRS = kRD + 4;                    // x tile row stride (floats)
+    constexpr int kXU = kRT * kRD / 1024;           // x groups of 4 per thread per chunk
+    constexpr int kWU = kRD * kRE / 1024;           // W_r groups of 4 per thread per chunk
+    constexpr int kRBuf = kRT * kRS + kRD * kRE;    // floats per LDS buffer
     __shared__ __attribute__((aligned(16))) float smem[2 * kRBuf];
 
     const int tid = threadIdx.x;
@@ -432,12 +437,17 @@ static hipError_t launch_scores_t(const void* x, const void* w, const float* bia
     const dim3 grid((T + kRT - 1) / kRT, (E + kRE - 1) / kRE);
     const bool vec = d % 4 == 0 && E % 4 == 0 && (uintptr_t)x % (4 * sizeof(XT)) == 0 &&
                      (uintptr_t)w % (4 * sizeof(XT)) == 0;
-    if (vec)
-        route_scores_kernel<XT, true><<<grid, 256, 0, st>>>((const XT*)x, (const XT*)w, bias, T,
-                                                            d, E, logits);
+    // many more blocks than compute units: the narrower chunk (three blocks per CU)
+    const bool many = (long long)grid.x * grid.y >= 2LL * 256;
+    if (vec && many)
+        route_scores_kernel<XT, true, 64><<<grid, 256, 0, st>>>((const XT*)x, (const XT*)w, bias,
+                                                                T, d, E, logits);
+    else if (vec)
+        route_scores_kernel<XT, true, 128><<<grid, 256, 0, st>>>((const XT*)x, (const XT*)w, bias,
+                                                                 T, d, E, logits);
     else
-        route_scores_kernel<XT, false><<<grid, 256, 0, st>>>((const XT*)x, (const XT*)w, bias, T,
-                                                             d, E, logits);
+        route_scores_kernel<XT, false, 128><<<grid, 256, 0, st>>>((const XT*)x, (const XT*)w,
+                                                                  bias, T, d, E, logits);
     return hipGetLastError();
 }
 
