@@ -28,10 +28,10 @@
 // are the reduction is staged [32][256] with b_swz and read with the gfx950
 // LDS transpose read. Rows of the data-gradient kernel are scheduled by the
 // forward's device-side tile list (256-row tiles, 128-row remainder tiles);
-// the weight-gradient kernel has a fixed E x M/256 x N/256 tile grid, every
-// expert's tiles contiguous on one XCD, and a reduction of ceil(n_e/32)
-// stages (rows past the expert's end load as zeros; an expert with no rows
-// writes zeros). A plain fp32-FMA kernel covers fp32 data and shapes the
+// the weight-gradient kernel walks the E x M/256 x N/256 tile list
+// persistently, every pass giving each XCD a contiguous run, with a
+// reduction of ceil(n_e/32) stages (rows past the expert's end load as
+// zeros; an expert with no rows writes zeros). A plain fp32-FMA kernel covers fp32 data and shapes the
 // matrix-core path does not tile.
 #include "mfma_common.hpp"
 
@@ -206,6 +206,45 @@ __device__ __forceinline__ void nt_tile(const NtArgs& p, const Tile& tile, uint1
         load(clampk(kt + 5), r);
         read_frags(nxt, 0, f0);
         mfmas(f1);
+        // issue order, so that every MFMA has LDS or global-memory work beside it:
+        // the second k-substep's fragment reads over the first MFMAs, the
+        // stage's LDS writes and global loads over the next, the next stage's
+        // first fragment reads over the ones after
+        if constexpr (TM == 256) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 6; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 6; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
         return nxt;
     };
     int kt = 0, buf = 0;
@@ -346,24 +385,23 @@ __device__ __forceinline__ void group_rows(const int32_t* offsets, int split, in
     }
 }
 
-// One output tile of TM (256 or 128) x 256 per block. TM = 256 holds 256
-// fp32 accumulators per lane (one block per CU); TM = 128 holds 128, so two
-// blocks share a CU and one block's epilogue stores overlap the other's
-// loads and products.
-template <int TM>
+// One output tile of 256 x 256 per block iteration, 256 fp32 accumulators per
+// lane (one block per CU). Measured against a 128-row tile with two blocks
+// per CU: 12.6 against 14.8 ms on the stress-shaped backward, and no slower
+// on the Qwen3 shape.
 struct TnStage {
-    u32x4 a[TM / 64];
+    u32x4 a[4];
     u32x4 b[4];
 };
 
-template <int TM>
-__global__ __launch_bounds__(kT, TM == 256 ? 1 : 2) void tn_mfma_kernel(
+__global__ __launch_bounds__(kT, 1) void tn_mfma_kernel(
     TnArgs p, const int32_t* __restrict__ offsets, int rows, int E)
 {
+    constexpr int TM = 256;               // output rows (of M) per tile
     constexpr int kMI = TM / 64;          // 32-row blocks per wavefront (= A chunks per thread)
     constexpr int kAT = TM / 8;           // threads per A k-row (16-byte chunks)
     constexpr int kAR = kT / kAT;         // A k-rows per pass
-    constexpr int kS = TM == 256 ? 3 : 2; // register stages in flight (two blocks per CU: two)
+    constexpr int kS = 3;                 // register stages in flight
     __shared__ __attribute__((aligned(1024))) uint16_t smem[kRingB * kK * (TM + kN)];
     auto sA = [&](int b) { return smem + b * (kK * TM); };
     auto sB = [&](int b) { return smem + kRingB * (kK * TM) + b * (kK * kN); };
@@ -419,7 +457,7 @@ __global__ __launch_bounds__(kT, TM == 256 ? 1 : 2) void tn_mfma_kernel(
         // the stage goes to LDS (a select right after the load would make
         // the wavefront wait for that load there and then).
         const u32x4 z = {0u, 0u, 0u, 0u};
-        auto load = [&](int kt, TnStage<TM>& r) {
+        auto load = [&](int kt, TnStage& r) {
 #pragma unroll
             for (int i = 0; i < kMI; ++i) {
                 const int j = j0 + kt * kK + tid / kAT + kAR * i;
@@ -433,7 +471,7 @@ __global__ __launch_bounds__(kT, TM == 256 ? 1 : 2) void tn_mfma_kernel(
         };
         const int adst = (tid / kAT) * TM + b_swz(ca, tid / kAT) * 8;
         const int bdst = (tid >> 5) * kN + b_swz(cb, tid >> 5) * 8;
-        auto store = [&](int buf, int kt, const TnStage<TM>& r) {
+        auto store = [&](int buf, int kt, const TnStage& r) {
 #pragma unroll
             for (int i = 0; i < kMI; ++i) {
                 const int j = j0 + kt * kK + tid / kAT + kAR * i;
@@ -483,13 +521,15 @@ __global__ __launch_bounds__(kT, TM == 256 ? 1 : 2) void tn_mfma_kernel(
                 for (int q = 0; q < 4; ++q)
                     acc[mi][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.a[mi], fr.b[q], acc[mi][q], 0, 0, 0);
         };
-        // Stage s lives in register set s % kS, then LDS buffer s % 3. Step
-        // kt: the products of stage kt (both k-substeps), store stage kt+2
-        // into the buffer stage kt-1 used (every wavefront passed the barrier
-        // after its last read of it), reload the set with stage kt+2+kS,
-        // barrier. Loads past the last stage re-read it.
+        // The data-gradient kernel's pipeline: stage s lives in register set
+        // s % 3, then LDS buffer s % 3; step kt reads the second k-substep of
+        // stage kt, runs the MFMAs of the first (read in the step before),
+        // stores stage kt+2 into the buffer stage kt-1 used (every wavefront
+        // passed the barrier after its last read of it) and reloads its set
+        // with stage kt+5, reads the first k-substep of stage kt+1, and runs
+        // the MFMAs of the second. Loads past the last stage re-read it.
         auto clampk = [&](int k) { return min(k, KT - 1); };
-        TnStage<TM> rs[kS];
+        TnStage rs[kS];
 #pragma unroll
         for (int i = 0; i < kS; ++i) load(clampk(i), rs[i]);
         store(0, 0, rs[0]);
@@ -497,29 +537,36 @@ __global__ __launch_bounds__(kT, TM == 256 ? 1 : 2) void tn_mfma_kernel(
         store(1, 1, rs[1]);
         load(clampk(kS + 1), rs[1]);
         lds_barrier();
-        // TM = 256 (registers to spare) also reads the next stage's first
-        // k-substep ahead, across the barrier, as the data-gradient kernel does
         Frags f0, f1;
-        if constexpr (TM == 256) read_frags(0, 0, f0);
-        auto step = [&](int kt, int buf, TnStage<TM>& r) {
+        read_frags(0, 0, f0);
+        auto step = [&](int kt, int buf, TnStage& r) {
             const int nxt = buf == kRingB - 1 ? 0 : buf + 1;
             const int wr = nxt == kRingB - 1 ? 0 : nxt + 1;
-            if constexpr (TM == 256) {
-                lds_barrier_keep<2 * (kMI + 4)>();
-                read_frags(buf, 1, f1);
-                mfmas(f0);
-                store(wr, kt + 2, r);
-                load(clampk(kt + 2 + kS), r);
-                read_frags(nxt, 0, f0);
-                mfmas(f1);
-            } else {
-                read_frags(buf, 0, f0);
-                mfmas(f0);
-                read_frags(buf, 1, f0);
-                mfmas(f0);
-                store(wr, kt + 2, r);
-                load(clampk(kt + 2 + kS), r);
-                lds_barrier();
+            lds_barrier_keep<2 * (kMI + 4)>();
+            read_frags(buf, 1, f1);
+            mfmas(f0);
+            store(wr, kt + 2, r);
+            load(clampk(kt + 2 + kS), r);
+            read_frags(nxt, 0, f0);
+            mfmas(f1);
+            // issue order: the 16 transpose reads of the second k-substep over
+            // the first 16 MFMAs, the stage's LDS writes and global loads over
+            // the next 8, the next stage's first 16 reads over the last 8
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
             return nxt;
         };
@@ -760,11 +807,6 @@ hipError_t launch_nt(int epi, const void* A, moe_dtype dt, int rows, int K, int 
     return hipGetLastError();
 }
 
-// Weight-gradient tile height: with the persistent order 256 (one block per
-// CU, every XCD's tiles in step) beat 128 (two blocks per CU): 12.6 against
-// 14.8 ms on the stress-shaped backward, even on the Qwen3 shape.
-constexpr int kTnTM = 256;
-
 // C_e[M, Nc] = scale * A_e^T B_e over the rows of each group (offsets NULL:
 // one group of all rows, or with split > 0 groups of `split` consecutive
 // rows); pair > 0: B columns [0, Nc) -> C0 and [pair, pair + Nc) -> C1.
@@ -777,13 +819,12 @@ hipError_t launch_tn(const void* A, int lda, int M, const void* B, int ldb, int 
     if (mfma) {
         TnArgs p{(const uint16_t*)A, lda, M, (const uint16_t*)B, ldb, Nc, pair, C0, C1, scale,
                  split};
-        constexpr int TM = kTnTM;
-        const long long tiles = (long long)E * ((M + TM - 1) / TM) *
+        const long long tiles = (long long)E * ((M + kN - 1) / kN) *
                                 ((Nc + (pair > 0 ? 128 : kN) - 1) / (pair > 0 ? 128 : kN));
-        // resident blocks: one per CU (TM 256) or two (TM 128), a multiple of 8
-        const long long cap = (long long)mfma_grid(1 << 30, 1, 1) * (TM == 256 ? 1 : 2);
+        // resident blocks: one per CU, a multiple of 8
+        const long long cap = (long long)mfma_grid(1 << 30, 1, 1);
         const unsigned g = (unsigned)std::max(8LL, std::min(cap, (tiles + 7) / 8 * 8));
-        tn_mfma_kernel<TM><<<g, kT, 0, st>>>(p, offsets, rows, E);
+        tn_mfma_kernel<<<g, kT, 0, st>>>(p, offsets, rows, E);
         return hipGetLastError();
     }
     const long long tiles = (long long)E * ((M + kGM - 1) / kGM) * ((Nc + kGN - 1) / kGN) *
