@@ -229,12 +229,13 @@ def backward_work(cfg, counts, es):
                              bytes=rows * (f + d + d + 2 * f) * es + 3 * E * d * f * 4)
     w["gate_up_bwd"] = dict(flops=4.0 * rows * d * f,
                             bytes=rows * 2 * f * es + active * 2 * d * f * es + rows * d * 4)
-    w["unpermute"] = dict(flops=1.0 * rows * d, bytes=rows * d * 4 + T * d * 4 + T * k * 4,
-                          bound="hbm")
+    # every token's rows of d_x_perm plus k rows of W_r^T (L2-resident), d_x written once
+    w["token_grad"] = dict(flops=2.0 * rows * d + 2.0 * T * k * d,
+                           bytes=rows * d * 4 + T * d * 4 + T * k * 16 + d * E * es * 2,
+                           bound="hbm")
     w["route_bwd"] = dict(flops=6.0 * T * E, bytes=T * E * 4 + T * k * 16 + T * E * 6,
                           bound="hbm")
-    w["router_bwd"] = dict(flops=4.0 * T * d * E,
-                           bytes=T * d * es + d * E * es + T * E * es + T * d * 8 + d * E * 4)
+    w["router_bwd"] = dict(flops=2.0 * T * d * E, bytes=T * d * es + T * E * es + d * E * 4)
     for v in w.values():
         if "bound" not in v:
             ai = v["flops"] / max(v["bytes"], 1)
@@ -294,8 +295,9 @@ def main_backward(args):
     ws = torch.empty(max(1, ops.permute_workspace(T, k, E)), dtype=torch.uint8, device=cuda)
     rws = torch.empty(max(1, ops.router_backward_workspace(T, d, E)), dtype=torch.uint8,
                       device=cuda)
+    tws = torch.empty(d * E * es, dtype=torch.uint8, device=cuda)
     stages = ["route", "permute", "gate_up", "down", "combine", "combine_bwd", "down_bwd",
-              "weight_grads", "gate_up_bwd", "unpermute", "route_bwd", "router_bwd"]
+              "weight_grads", "gate_up_bwd", "token_grad", "route_bwd", "router_bwd"]
 
     def step(ev=None):
         def mark(i):
@@ -324,13 +326,13 @@ def main_backward(args):
         ops.ffn_gate_up_backward(b["d_act"], b["offsets"], dev["w_gate"], dev["w_val"],
                                  d_x=b["d_xp"])
         mark(9)
-        ops.combine(b["d_xp"], b["dest"], None, k, out=b["d_x"])
+        ops.token_backward(b["d_xp"], b["dest"], b["idx"], b["gates"], b["d_gates"],
+                           dev["w_router"], d_x=b["d_x"], workspace=tws)
         mark(10)
         ops.route_backward(b["logits"], b["idx"], b["gates"], b["d_gates"], True,
                            d_logits=b["d_l"], d_logits_lp=b["d_lp"])
         mark(11)
-        ops.router_backward(dev["x"], dev["w_router"], b["d_lp"], d_x=b["d_x"], accumulate=True,
-                            d_w=b["d_wr"], workspace=rws)
+        ops.router_backward(dev["x"], dev["w_router"], b["d_lp"], d_w=b["d_wr"], workspace=rws)
         mark(12)
 
     log(f"[bench] warmup {args.warmup}")

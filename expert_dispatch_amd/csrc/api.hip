@@ -43,6 +43,10 @@ hipError_t launch_sum_splits(const float* part, int S, long long n, float* out, 
 enum NtEpi { kNtSwigluBwd = 0, kNtStoreF32 = 1, kNtAccumF32 = 2, kNtStoreBf16 = 3 };
 hipError_t launch_route_stats(const float* logits, const int32_t* counts, int T, int E, int k,
                               float* p_mean, float* aux, float* mz, hipStream_t st);
+hipError_t launch_token_grad(const void* d_xp, moe_dtype p_dt, const int32_t* dest,
+                             const int32_t* idx, const float* gates, const float* d_gates,
+                             const void* w, moe_dtype w_dt, int T, int k, int d, int E,
+                             float* d_x, void* w_t, hipStream_t st);
 }  // namespace moe
 
 namespace {
@@ -334,6 +338,29 @@ moe_status moe_ffn_weight_grads(const void* x_perm, const void* h, const void* d
     // [dW_gate | dW_val][e] [d,f] = x_e^T . d_act_e[:, 0:f | f:2f]
     return hip_status(moe::launch_tn(x_perm, d, d, d_act, 2 * f, f, f, dt, N, E, offsets, scale,
                                      d_w_gate, d_w_val, st, 0));
+}
+
+size_t moe_token_backward_workspace(int d, int E, moe_dtype dt)
+{
+    if (d <= 0 || E <= 0 || !valid_dtype(dt)) return 0;
+    return moe::align_up((size_t)d * E * elem_size(dt), 256);
+}
+
+moe_status moe_token_backward(const void* d_x_perm, moe_dtype dxp_dt, const int32_t* dest,
+                              const int32_t* topk_idx, const float* gates, const float* d_gates,
+                              const void* w_router, moe_dtype dt, int T, int k, int d, int E,
+                              float* d_x, void* ws, size_t ws_bytes, void* stream)
+{
+    if (!valid_dtype(dxp_dt) || !valid_dtype(dt) || T < 0 || k <= 0 || k > E || d <= 0)
+        return MOE_ERR_INVALID_ARG;
+    if (k > kMaxK || (long long)T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!d_x_perm || !dest || !topk_idx || !gates || !d_gates || !w_router || !d_x)
+        return MOE_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < moe_token_backward_workspace(d, E, dt)) return MOE_ERR_WORKSPACE;
+    return hip_status(moe::launch_token_grad(d_x_perm, dxp_dt, dest, topk_idx, gates, d_gates,
+                                             w_router, dt, T, k, d, E, d_x, ws,
+                                             as_stream(stream)));
 }
 
 moe_status moe_route_backward(const float* logits, const int32_t* topk_idx, const float* gates,

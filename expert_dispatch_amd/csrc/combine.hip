@@ -251,6 +251,131 @@ static hipError_t launch_combine_bwd_y(moe_dtype y_dt, moe_dtype dy_dt, const vo
     return launch_combine_bwd_d<GT, float>(dy_dt, d_out, y, dest, gates, T, k, d, d_y, d_gates, st);
 }
 
+// ------------------------------------------------- token input gradient
+//
+// d_x[t] = sum_s d_x_perm[dest[t*k+s]] + sum_s d_l[t,e_s] W_r[:,e_s], the
+// packing's backward (every token sums its rows' input gradients) and the
+// router scores' backward in one pass, for renormalised router weights:
+// there d_l is nonzero only at the k selected experts, d_l[t,e_s] =
+// g_s (dg_s - sum_r g_r dg_r), so the product with W_r^T is a gather of k
+// rows of W_r^T (staged once per call, [E,d], L2-resident). One wavefront
+// per token; lanes 0..k-1 hold the slot's row, expert and d_l, broadcast by
+// shuffles; sums in fp32 in slot order; no atomics.
+template <typename PT, typename WT, bool VEC>
+__global__ __launch_bounds__(256) void token_grad_kernel(
+    const PT* __restrict__ d_xp, const int32_t* __restrict__ dest, const int32_t* __restrict__ idx,
+    const float* __restrict__ gates, const float* __restrict__ d_gates,
+    const WT* __restrict__ w_t, int T, int k, int d, int E, float* __restrict__ d_x)
+{
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T) return;
+    const int lane = lane_id();
+    const long long rows = (long long)T * k;
+    int my_j = -1, my_e = 0;
+    float my_g = 0.0f, my_dg = 0.0f;
+    if (lane < k) {
+        const size_t a = (size_t)t * k + lane;
+        my_j = dest[a];
+        if (my_j < 0 || my_j >= rows) my_j = -1;
+        my_e = min(max(idx[a], 0), E - 1);
+        my_g = gates[a];
+        my_dg = d_gates[a];
+    }
+    const float gdg = wave_sum_f32(my_g * my_dg);
+    const float my_dl = my_g * (my_dg - gdg);
+    float* o = d_x + (size_t)t * d;
+    if constexpr (VEC) {
+        for (int c = lane * 4; c < d; c += kWave * 4) {
+            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int s = 0; s < k; ++s) {
+                const int j = __shfl(my_j, s, kWave);
+                if (j < 0) continue;
+                float v[4];
+                Vec4<PT>::load(d_xp + (size_t)j * d + c, v);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[q] += v[q];
+            }
+            for (int s = 0; s < k; ++s) {
+                const int e = __shfl(my_e, s, kWave);
+                const float dl = __shfl(my_dl, s, kWave);
+                float v[4];
+                Vec4<WT>::load(w_t + (size_t)e * d + c, v);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(dl, v[q], acc[q]);
+            }
+            Vec4<float>::store(o + c, acc);
+        }
+    } else {
+        for (int c = lane; c < d; c += kWave) {
+            float acc = 0.0f;
+            for (int s = 0; s < k; ++s) {
+                const int j = __shfl(my_j, s, kWave);
+                if (j >= 0) acc += Elem<PT>::load(d_xp, (size_t)j * d + c);
+            }
+            for (int s = 0; s < k; ++s) {
+                const int e = __shfl(my_e, s, kWave);
+                const float dl = __shfl(my_dl, s, kWave);
+                acc = __builtin_fmaf(dl, Elem<WT>::load(w_t, (size_t)e * d + c), acc);
+            }
+            d_x[(size_t)t * d + c] = acc;
+        }
+    }
+}
+
+// w_t[e][i] = w[i][e] through 64 x 64 LDS tiles (w: [d, E])
+template <typename WT>
+__global__ __launch_bounds__(256) void transpose_kernel(const WT* __restrict__ w, int d, int E,
+                                                       WT* __restrict__ w_t)
+{
+    __shared__ WT tile[64][65];
+    const int i0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+    for (int q = threadIdx.x; q < 64 * 64; q += 256) {
+        const int r = q / 64, c = q % 64;
+        if (i0 + r < d && e0 + c < E) tile[r][c] = w[(size_t)(i0 + r) * E + e0 + c];
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < 64 * 64; q += 256) {
+        const int r = q / 64, c = q % 64;
+        if (e0 + r < E && i0 + c < d) w_t[(size_t)(e0 + r) * d + i0 + c] = tile[c][r];
+    }
+}
+
+template <typename PT, typename WT>
+static hipError_t launch_token_grad_t(const void* d_xp, const int32_t* dest, const int32_t* idx,
+                                      const float* gates, const float* d_gates, const void* w,
+                                      int T, int k, int d, int E, float* d_x, void* w_t,
+                                      hipStream_t st)
+{
+    const dim3 tg((d + 63) / 64, (E + 63) / 64);
+    transpose_kernel<WT><<<tg, 256, 0, st>>>((const WT*)w, d, E, (WT*)w_t);
+    auto al = [](const void* p, size_t a) { return (uintptr_t)p % a == 0; };
+    const bool vec = d % 4 == 0 && al(d_xp, 4 * sizeof(PT)) && al(w_t, 4 * sizeof(WT)) &&
+                     al(d_x, 16);
+    const dim3 grid((T + 3) / 4);
+    if (vec)
+        token_grad_kernel<PT, WT, true><<<grid, 256, 0, st>>>(
+            (const PT*)d_xp, dest, idx, gates, d_gates, (const WT*)w_t, T, k, d, E, d_x);
+    else
+        token_grad_kernel<PT, WT, false><<<grid, 256, 0, st>>>(
+            (const PT*)d_xp, dest, idx, gates, d_gates, (const WT*)w_t, T, k, d, E, d_x);
+    return hipGetLastError();
+}
+
+hipError_t launch_token_grad(const void* d_xp, moe_dtype p_dt, const int32_t* dest,
+                             const int32_t* idx, const float* gates, const float* d_gates,
+                             const void* w, moe_dtype w_dt, int T, int k, int d, int E,
+                             float* d_x, void* w_t, hipStream_t st)
+{
+    if (p_dt == MOE_BF16) {
+        if (w_dt == MOE_BF16)
+            return launch_token_grad_t<uint16_t, uint16_t>(d_xp, dest, idx, gates, d_gates, w, T, k, d, E, d_x, w_t, st);
+        return launch_token_grad_t<uint16_t, float>(d_xp, dest, idx, gates, d_gates, w, T, k, d, E, d_x, w_t, st);
+    }
+    if (w_dt == MOE_BF16)
+        return launch_token_grad_t<float, uint16_t>(d_xp, dest, idx, gates, d_gates, w, T, k, d, E, d_x, w_t, st);
+    return launch_token_grad_t<float, float>(d_xp, dest, idx, gates, d_gates, w, T, k, d, E, d_x, w_t, st);
+}
+
 hipError_t launch_combine_bwd(const void* d_out, moe_dtype g_dt, const void* y, moe_dtype y_dt,
                               const int32_t* dest, const float* gates, int T, int k, int d,
                               void* d_y, moe_dtype dy_dt, float* d_gates, hipStream_t st)

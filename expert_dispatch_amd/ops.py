@@ -59,6 +59,7 @@ def lib():
         "moe_route_backward": [vp, vp, vp, vp, i, i, i, i, vp, vp, vp],
         "moe_router_backward": [vp, vp, i, vp, i, i, i, vp, i, vp, vp, sz, vp],
         "moe_route_stats": [vp, vp, i, i, i, vp, vp, vp, sz, vp],
+        "moe_token_backward": [vp, i, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, sz, vp],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -68,7 +69,8 @@ def lib():
                        "moe_permute_recv_workspace": [i, i, i],
                        "moe_grouped_ffn_workspace": [i, i, i, i, i],
                        "moe_router_backward_workspace": [i, i, i],
-                       "moe_route_stats_workspace": [i]}.items():
+                       "moe_route_stats_workspace": [i],
+                       "moe_token_backward_workspace": [i, i, i]}.items():
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = sz
@@ -401,6 +403,23 @@ def route_backward(logits, idx, gates, d_gates, renorm: bool = True, *, lp_dtype
     return d_l, d_lp
 
 
+def token_backward(d_x_perm, dest, idx, gates, d_gates, w_router, *, d_x=None, workspace=None,
+                   stream=None):
+    """d_x = sum_s d_x_perm[dest] + sum_s d_l[t,e_s] W_r[:,e_s] for renormalised
+    router weights (d_l formed from gates and d_gates), fp32 [T,d]."""
+    T, k = idx.shape
+    d, E = w_router.shape
+    if d_x is None:
+        d_x = torch.empty((T, d), dtype=torch.float32, device=idx.device)
+    nbytes = int(lib().moe_token_backward_workspace(d, E, _dt(w_router)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=idx.device)
+    _check("moe_token_backward", lib().moe_token_backward(
+        _p(d_x_perm), _dt(d_x_perm), _p(dest), _p(idx), _p(gates), _p(d_gates), _p(w_router),
+        _dt(w_router), T, k, d, E, _p(d_x), _p(workspace), workspace.numel(), _stream(stream)))
+    return d_x
+
+
 def router_backward_workspace(T: int, d: int, E: int) -> int:
     return int(lib().moe_router_backward_workspace(T, d, E))
 
@@ -460,7 +479,13 @@ def moe_layer_backward(sv, d_out, x, w_router, w_gate, w_val, w_out, *, shared=N
         sv["x_perm"], sv["h"], d_y, d_act, sv["offsets"], E, scale=scale, stream=stream)
     d_xp = ffn_gate_up_backward(d_act, sv["offsets"], w_gate, w_val, dx_dtype=dx_perm_dtype,
                                 stream=stream)
-    d_x = combine(d_xp, sv["dest"], None, k, out_dtype=torch.float32, stream=stream)
+    renorm = sv["renorm"]
+    if renorm:
+        # the packing's backward and the router's input term in one pass
+        d_x = token_backward(d_xp, sv["dest"], sv["idx"], sv["gates"], d_gates, w_router,
+                             stream=stream)
+    else:
+        d_x = combine(d_xp, sv["dest"], None, k, out_dtype=torch.float32, stream=stream)
     if shared is not None:
         off = sv["shared_off"]
         d_act_sh = ffn_down_backward(d_out.to(x.dtype), off, shared[2], sv["act_shared"],
@@ -469,9 +494,11 @@ def moe_layer_backward(sv, d_out, x, w_router, w_gate, w_val, w_out, *, shared=N
                                          stream=stream)
         ffn_gate_up_backward(d_act_sh, off, shared[0], shared[1], d_x=d_x, accumulate=True,
                              stream=stream)
-    d_l, d_lp = route_backward(sv["logits"], sv["idx"], sv["gates"], d_gates, sv["renorm"],
+    d_l, d_lp = route_backward(sv["logits"], sv["idx"], sv["gates"], d_gates, renorm,
                                lp_dtype=x.dtype, stream=stream)
+    # full-softmax weights: d_l is dense, the input term is a product with W_r^T
     _, g["d_w_router"] = router_backward(x, w_router, d_lp if d_lp is not None else d_l,
-                                         d_x=d_x, accumulate=True, stream=stream)
+                                         d_x=None if renorm else d_x, accumulate=True,
+                                         stream=stream)
     g.update(d_x=d_x, d_gates=d_gates, d_logits=d_l, d_y=d_y, d_act=d_act, d_x_perm=d_xp)
     return g

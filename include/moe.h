@@ -249,10 +249,12 @@ moe_status moe_route_stats(const float* logits, const int32_t* counts, int T, in
  *   moe_ffn_down_backward     -> d_act [rows,2f]
  *   moe_ffn_weight_grads      -> dW_gate, dW_val, dW_out (x 1/P_EP)
  *   moe_ffn_gate_up_backward  -> d_x_perm [rows,d]
- *   moe_combine(d_x_perm, dest, gates = NULL, k) -> d_x [T,d] (the permutation's
- *                                backward: every token sums its rows' gradients)
  *   moe_route_backward        -> d_logits [T,E]
- *   moe_router_backward       -> d_x += d_logits . W_r^T, dW_r = x^T . d_logits
+ *   moe_token_backward        -> d_x [T,d] (renormalised weights: the packing's
+ *                                backward and the router's input term in one pass)
+ *   or moe_combine(d_x_perm, dest, gates = NULL, k) then moe_router_backward's
+ *                                d_x += d_logits . W_r^T (full-softmax weights)
+ *   moe_router_backward       -> dW_r = x^T . d_logits
  * Products run on the matrix cores in bf16 with fp32 accumulation when dt is
  * MOE_BF16 and the sizes tile (d, f multiples of 32; otherwise, and for fp32,
  * a plain fp32 kernel). Same limits as the forward calls.
@@ -334,6 +336,25 @@ moe_status moe_ffn_weight_grads(const void* x_perm, const void* h, const void* d
 moe_status moe_route_backward(const float* logits, const int32_t* topk_idx, const float* gates,
                               const float* d_gates, int T, int E, int k, int renorm,
                               float* d_logits, void* d_logits_bf16, void* stream);
+
+/*
+ * Input gradient of the tokens for renormalised router weights (moe_route
+ * with renorm != 0), in one pass:
+ *   d_x[t] = sum_s d_x_perm[dest[t*k+s]]                  (the packing's backward)
+ *          + sum_s d_l[t,e_s] * W_r[:,e_s]                (the router scores')
+ * with d_l[t,e_s] = g_s (dg_s - sum_r g_r dg_r) formed from gates and d_gates
+ * (the renormalised softmax's Jacobian; d_l is 0 at unselected experts, so
+ * the product with W_r^T is a gather of k of its rows). Replaces moe_combine
+ * (gates NULL) on d_x_perm plus moe_router_backward's d_x term.
+ *   d_x_perm [*,d] dtype dxp_dt; dest, topk_idx, gates, d_gates [T*k];
+ *   W_r [d,E] dtype dt; d_x [T,d] fp32 (overwritten); workspace
+ *   moe_token_backward_workspace(d, E, dt) bytes (W_r^T, staged per call).
+ */
+size_t moe_token_backward_workspace(int d, int E, moe_dtype dt);
+moe_status moe_token_backward(const void* d_x_perm, moe_dtype dxp_dt, const int32_t* dest,
+                              const int32_t* topk_idx, const float* gates, const float* d_gates,
+                              const void* w_router, moe_dtype dt, int T, int k, int d, int E,
+                              float* d_x, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Backward of the router scores l = x . W_r:

@@ -105,6 +105,9 @@ def test_host_side_errors_return_before_launch(L):
     assert L.moe_route_backward(fake, fake, fake, fake, 4, 8, 9, 1, fake, None, None) == 1
     assert L.moe_router_backward(None, fake, 1, fake, 4, 64, 8, fake, 0, None, None, 0,
                                  None) == 1
+    # token input gradient: too small a workspace
+    assert L.moe_token_backward(fake, 0, fake, fake, fake, fake, fake, 1, 64, 2, 128, 8, fake,
+                                fake, 16, None) == 3
     # load statistics: too small a workspace, k > E
     assert L.moe_route_stats(fake, fake, 64, 8, 2, fake, fake, fake, 16, None) == 3
     assert L.moe_route_stats(fake, fake, 64, 8, 9, fake, fake, fake, 1 << 20, None) == 1
