@@ -285,25 +285,47 @@ __global__ __launch_bounds__(256) void token_grad_kernel(
     const float my_dl = my_g * (my_dg - gdg);
     float* o = d_x + (size_t)t * d;
     if constexpr (VEC) {
-        for (int c = lane * 4; c < d; c += kWave * 4) {
-            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        // two 4-column groups per lane per pass (more loads in flight)
+        constexpr int U = 2;
+        for (int c0 = lane * 4; c0 < d; c0 += kWave * 4 * U) {
+            float acc[U][4];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[u][q] = 0.0f;
             for (int s = 0; s < k; ++s) {
                 const int j = __shfl(my_j, s, kWave);
                 if (j < 0) continue;
-                float v[4];
-                Vec4<PT>::load(d_xp + (size_t)j * d + c, v);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) acc[q] += v[q];
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + u * kWave * 4;
+                    if (c < d) {
+                        float v[4];
+                        Vec4<PT>::load(d_xp + (size_t)j * d + c, v);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[u][q] += v[q];
+                    }
+                }
             }
             for (int s = 0; s < k; ++s) {
                 const int e = __shfl(my_e, s, kWave);
                 const float dl = __shfl(my_dl, s, kWave);
-                float v[4];
-                Vec4<WT>::load(w_t + (size_t)e * d + c, v);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(dl, v[q], acc[q]);
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + u * kWave * 4;
+                    if (c < d) {
+                        float v[4];
+                        Vec4<WT>::load(w_t + (size_t)e * d + c, v);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[u][q] = __builtin_fmaf(dl, v[q], acc[u][q]);
+                    }
+                }
             }
-            Vec4<float>::store(o + c, acc);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * kWave * 4;
+                if (c < d) Vec4<float>::store(o + c, acc[u]);
+            }
         }
     } else {
         for (int c = lane; c < d; c += kWave) {
