@@ -228,10 +228,10 @@ def backward_work(cfg, counts, es):
     w["weight_grads"] = dict(flops=6.0 * rows * d * f,
                              bytes=rows * (f + d + d + 2 * f) * es + 3 * E * d * f * 4)
     w["gate_up_bwd"] = dict(flops=4.0 * rows * d * f,
-                            bytes=rows * 2 * f * es + active * 2 * d * f * es + rows * d * 4)
+                            bytes=rows * 2 * f * es + active * 2 * d * f * es + rows * d * es)
     # every token's rows of d_x_perm plus k rows of W_r^T (L2-resident), d_x written once
     w["token_grad"] = dict(flops=2.0 * rows * d + 2.0 * T * k * d,
-                           bytes=rows * d * 4 + T * d * 4 + T * k * 16 + d * E * es * 2,
+                           bytes=rows * d * es + T * d * 4 + T * k * 16 + d * E * es * 2,
                            bound="hbm")
     w["route_bwd"] = dict(flops=6.0 * T * E, bytes=T * E * 4 + T * k * 16 + T * E * 6,
                           bound="hbm")
@@ -283,7 +283,7 @@ def main_backward(args):
         d_y=torch.empty((rows, d), dtype=bf, device=cuda),
         d_gates=torch.empty((T, k), dtype=f32, device=cuda),
         d_act=torch.empty((rows, 2 * f), dtype=bf, device=cuda),
-        d_xp=torch.empty((rows, d), dtype=f32, device=cuda),
+        d_xp=torch.empty((rows, d), dtype=bf, device=cuda),
         d_x=torch.empty((T, d), dtype=f32, device=cuda),
         dwg=torch.empty((E, d, f), dtype=f32, device=cuda),
         dwv=torch.empty((E, d, f), dtype=f32, device=cuda),
@@ -324,7 +324,7 @@ def main_backward(args):
                              out=(b["dwg"], b["dwv"], b["dwo"]))
         mark(8)
         ops.ffn_gate_up_backward(b["d_act"], b["offsets"], dev["w_gate"], dev["w_val"],
-                                 d_x=b["d_xp"])
+                                 d_x=b["d_xp"])   # bf16, as the training step hands it on
         mark(9)
         ops.token_backward(b["d_xp"], b["dest"], b["idx"], b["gates"], b["d_gates"],
                            dev["w_router"], d_x=b["d_x"], workspace=tws)

@@ -464,10 +464,15 @@ def moe_layer_train(x, w_router, bias, k: int, w_gate, w_val, w_out, *, shared=N
 
 
 def moe_layer_backward(sv, d_out, x, w_router, w_gate, w_val, w_out, *, shared=None,
-                       scale: float = 1.0, dx_perm_dtype=torch.float32, stream=None):
+                       scale: float = 1.0, dx_perm_dtype=None, stream=None):
     """Gradients of sum(out * d_out) through the layer given the saved forward
     ``sv`` of moe_layer_train. Expert weight gradients are multiplied by
-    ``scale`` (1/P for an EP group of P ranks)."""
+    ``scale`` (1/P for an EP group of P ranks). The packed rows' input
+    gradient d_x_perm is kept in the activation type unless ``dx_perm_dtype``
+    says otherwise (bf16 training hands every tensor between kernels over in
+    bf16; the tokens' d_x sums it in fp32)."""
+    if dx_perm_dtype is None:
+        dx_perm_dtype = x.dtype
     k = sv["k"]
     E = w_gate.shape[0]
     T = x.shape[0]

@@ -83,7 +83,7 @@ def _check_backward(name, full, capacity=None, scale=1.0, renorm=True, pairs_per
     e["d_act"] = check_grad(to_numpy(g["d_act"].index_select(0, rows_t)), o["d_act"], dt,
                             f"{name} d_act", stored_bf16=True)
     e["d_x_perm"] = check_grad(to_numpy(g["d_x_perm"].index_select(0, rows_t)), o["d_x_perm"],
-                                dt, f"{name} d_x_perm")
+                               dt, f"{name} d_x_perm", stored_bf16=g["d_x_perm"].dtype == torch.bfloat16)
     e["d_x"] = check_grad(to_numpy(g["d_x"])[tok], o["d_x"], dt, f"{name} d_x")
     pe, pc = pairs[:, 0], pairs[:, 1]
     dwg = to_numpy(g["d_w_gate"])[pe, :, pc]
