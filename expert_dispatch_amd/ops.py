@@ -227,6 +227,9 @@ def grouped_ffn(x_perm, offsets, w_gate, w_val, w_out, *, y_dtype=torch.float32,
 
 
 def ffn_gate_up(x_perm, offsets, w_gate, w_val, *, h=None, stream=None):
+    """h = silu(x_perm W_gate[e]) * (x_perm W_val[e]) per expert segment."""
+    for t, n in ((x_perm, "x_perm"), (offsets, "offsets"), (w_gate, "w_gate"), (w_val, "w_val")):
+        _dev(t, n)
     N, d = x_perm.shape
     E, _, f = w_gate.shape
     if h is None:
@@ -238,6 +241,9 @@ def ffn_gate_up(x_perm, offsets, w_gate, w_val, *, h=None, stream=None):
 
 
 def ffn_down(h, offsets, w_out, *, y_dtype=torch.float32, y=None, stream=None):
+    """y = h W_out[e] per expert segment."""
+    for t, n in ((h, "h"), (offsets, "offsets"), (w_out, "w_out")):
+        _dev(t, n)
     N, f = h.shape
     E, _, d = w_out.shape
     if y is None:
@@ -316,16 +322,6 @@ def ffn_gate_up_train(x_perm, offsets, w_gate, w_val, *, h=None, act=None, strea
         _p(x_perm), _dt(x_perm), N, d, f, E, _p(offsets), _p(w_gate), _p(w_val), _p(h), _p(act),
         _stream(stream)))
     return h, act
-
-
-def ffn_down(h, offsets, w_out, *, y=None, y_dtype=torch.float32, stream=None):
-    N, f = h.shape
-    E, _, d = w_out.shape
-    if y is None:
-        y = torch.empty((N, d), dtype=y_dtype, device=h.device)
-    _check("moe_ffn_down", lib().moe_ffn_down(_p(h), _dt(h), N, f, d, E, _p(offsets), _p(w_out),
-                                              _p(y), _dt(y), _stream(stream)))
-    return y
 
 
 def combine_backward(d_out, y_perm, dest, gates, k: int, *, d_y=None, d_y_dtype=None,
