@@ -274,7 +274,15 @@ __device__ __forceinline__ void nt_tile(const NtArgs& p, const Tile& tile, uint1
         const int rr0 = lane >> 4;           // row within a group of 4
         const int c8 = (lane & 15) * 8;      // 8 columns of the wavefront's 128
         const int col = n0 + 128 * wn + c8;
-        uint16_t* D = static_cast<uint16_t*>(p.C);
+        // act and d_act [rows, 2N] through buffer resources over the tile's
+        // rows inside the segment; a lane whose columns lie past N gets an
+        // offset outside them (its loads read zeros, its stores are dropped)
+        const int nrows = min(TM, seg_last + 1 - m0);
+        const int lim = nrows * 2 * p.N * 2;
+        const __amdgpu_buffer_rsrc_t act_r = tile_rsrc(p.act + (size_t)m0 * 2 * p.N, lim);
+        const __amdgpu_buffer_rsrc_t dact_r =
+            tile_rsrc(static_cast<uint16_t*>(p.C) + (size_t)m0 * 2 * p.N, lim);
+        const int vcol = col < p.N ? (((TM / 2) * wm + rr0) * 2 * p.N + col) * 2 : lim;
 #pragma unroll
         for (int mi = 0; mi < kMI; ++mi) {
 #pragma unroll
@@ -287,13 +295,11 @@ __device__ __forceinline__ void nt_tile(const NtArgs& p, const Tile& tile, uint1
 #pragma unroll 2
             for (int it = 0; it < 8; ++it) {
                 const int rr = rr0 + 4 * it;
-                const int row = m0 + (TM / 2) * wm + 32 * mi + rr;
                 const f32x4 h0 = *reinterpret_cast<const f32x4*>(&sw[rr * SS + c8]);
                 const f32x4 h1 = *reinterpret_cast<const f32x4*>(&sw[rr * SS + c8 + 4]);
-                if (row > seg_last || col >= p.N) continue;
-                const size_t o = (size_t)row * 2 * p.N + col;
-                const u32x4 av = *reinterpret_cast<const u32x4*>(p.act + o);
-                const u32x4 vv = *reinterpret_cast<const u32x4*>(p.act + o + p.N);
+                const int o = vcol + (32 * mi + 4 * it) * 2 * p.N * 2;
+                const u32x4 av = __builtin_amdgcn_raw_buffer_load_b128(act_r, o, 0, 0);
+                const u32x4 vv = __builtin_amdgcn_raw_buffer_load_b128(act_r, o + p.N * 2, 0, 0);
                 const float dh[8] = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
                 u32x4 da_out, dv_out;
 #pragma unroll
@@ -305,29 +311,41 @@ __device__ __forceinline__ void nt_tile(const NtArgs& p, const Tile& tile, uint1
                     da_out[w] = f32x2_to_bf16x2(da0, da1);
                     dv_out[w] = f32x2_to_bf16x2(dv0, dv1);
                 }
-                *reinterpret_cast<u32x4*>(D + o) = da_out;
-                *reinterpret_cast<u32x4*>(D + o + p.N) = dv_out;
+                __builtin_amdgcn_raw_buffer_store_b128(da_out, dact_r, o, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(dv_out, dact_r, o + p.N * 2, 0, 0);
             }
         }
         return;
     }
+    // C [rows, N] through a buffer resource over the tile's rows inside the
+    // segment; columns past N get an offset outside it (dropped, and read as
+    // zero by the accumulating form)
+    constexpr int ES = EPI == kNtStoreBf16 ? 2 : 4;
+    const int nrows = min(TM, seg_last + 1 - m0);
+    const int lim = nrows * p.N * ES;
+    const __amdgpu_buffer_rsrc_t out =
+        tile_rsrc(static_cast<char*>(p.C) + (size_t)m0 * p.N * ES, lim);
+    int vq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int col = n0 + 128 * wn + 32 * q + col_l;
+        vq[q] = col < p.N ? (((TM / 2) * wm + row_l) * p.N + col) * ES : lim;
+    }
 #pragma unroll
     for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int col = n0 + 128 * wn + 32 * q + col_l;
-            if (col >= p.N) continue;
+        for (int r = 0; r < 16; ++r) {
+            const int ro = (32 * mi + 8 * (r >> 2) + (r & 3)) * p.N * ES;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + (TM / 2) * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
-                if (row > seg_last) continue;
+            for (int q = 0; q < 4; ++q) {
                 const float v = acc[mi][q][r];
                 if constexpr (EPI == kNtStoreF32) {
-                    static_cast<float*>(p.C)[(size_t)row * p.N + col] = v;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), out, vq[q] + ro, 0, 0);
                 } else if constexpr (EPI == kNtAccumF32) {
-                    static_cast<float*>(p.C)[(size_t)row * p.N + col] += v;
+                    const float c = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(out, vq[q] + ro, 0, 0));
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(c + v), out, vq[q] + ro, 0, 0);
                 } else {
-                    static_cast<uint16_t*>(p.C)[(size_t)row * p.N + col] = f32_to_bf16(v);
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), out, vq[q] + ro, 0, 0);
                 }
             }
         }
@@ -580,25 +598,33 @@ __global__ __launch_bounds__(kT, 1) void tn_mfma_kernel(
     // Epilogue: 32 lanes write 32 consecutive fp32 of one row per register.
     const int col_l = lane & 31;
     const int row_l = 4 * (lane >> 5);
+    // Stores go through a buffer resource over the tile's rows below M;
+    // columns past Nc get an offset outside it and are dropped.
     float* C = p.C0;
     int cbase = n0 + 128 * wn;
     if (p.pair > 0) {
         // wavefront column half wn: 0 -> first output, 1 -> second
-        C = wn ? p.C1 : p.C0;
+        C = __builtin_amdgcn_readfirstlane(wn) ? p.C1 : p.C0;
         cbase = n0;
     }
-    C += (size_t)e * p.M * p.Nc;
+    const int nrows = min(TM, p.M - m0);
+    const int lim = nrows * p.Nc * 4;
+    const __amdgpu_buffer_rsrc_t out = tile_rsrc(C + ((size_t)e * p.M + m0) * p.Nc, lim);
+    int vq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int col = cbase + 32 * q + col_l;
+        vq[q] = col < p.Nc ? (((TM / 2) * wm + row_l) * p.Nc + col) * 4 : lim;
+    }
 #pragma unroll
     for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int col = cbase + 32 * q + col_l;
-            if (col >= p.Nc) continue;
+        for (int r = 0; r < 16; ++r) {
+            const int ro = (32 * mi + 8 * (r >> 2) + (r & 3)) * p.Nc * 4;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + (TM / 2) * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
-                if (row < p.M) C[(size_t)row * p.Nc + col] = p.scale * acc[mi][q][r];
-            }
+            for (int q = 0; q < 4; ++q)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p.scale * acc[mi][q][r]), out,
+                                                      vq[q] + ro, 0, 0);
         }
     }
 }
@@ -771,8 +797,10 @@ hipError_t launch_nt(int epi, const void* A, moe_dtype dt, int rows, int K, int 
                      const int32_t* offsets, const void* B0, const void* B1, void* C,
                      const void* act, hipStream_t st)
 {
+    // (N < 2^20 keeps a tile's byte offsets in 31 bits)
     const bool mfma = dt == MOE_BF16 && K % kK == 0 && K0 % kK == 0 && K0 > 0 && N % 8 == 0 &&
-                      al16(A) && al16(B0) && al16(B1) && (epi != kNtSwigluBwd || N % 2 == 0);
+                      N < (1 << 20) && al16(A) && al16(B0) && al16(B1) && al16(C) &&
+                      (epi != kNtSwigluBwd || al16(act));
     if (mfma) {
         NtArgs p{(const uint16_t*)A, K, (const uint16_t*)B0, (const uint16_t*)B1, K0, N, C,
                  (const uint16_t*)act};
@@ -814,8 +842,10 @@ hipError_t launch_tn(const void* A, int lda, int M, const void* B, int ldb, int 
                      moe_dtype dt, int rows, int E, const int32_t* offsets, float scale,
                      float* C0, float* C1, hipStream_t st, int split)
 {
+    // (Nc < 2^20 keeps a tile's byte offsets in 31 bits)
     const bool mfma = dt == MOE_BF16 && lda % 8 == 0 && ldb % 8 == 0 && M % 8 == 0 &&
-                      Nc % 8 == 0 && pair % 8 == 0 && M >= 8 && Nc >= 8 && al16(A) && al16(B);
+                      Nc % 8 == 0 && Nc < (1 << 20) && pair % 8 == 0 && M >= 8 && Nc >= 8 &&
+                      al16(A) && al16(B);
     if (mfma) {
         TnArgs p{(const uint16_t*)A, lda, M, (const uint16_t*)B, ldb, Nc, pair, C0, C1, scale,
                  split};

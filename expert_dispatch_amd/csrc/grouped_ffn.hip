@@ -325,7 +325,7 @@ __device__ __forceinline__ void ffn_mfma_tile(
     // rows 8*(r/4) + 4*(lane/32) + r%4 for register r.
     const int col_l = lane & 31;
     const int row_l = 4 * (lane >> 5);
-    const bool full = m0 + TM - 1 <= seg_last;
+    const int nrows = min(TM, seg_last + 1 - m0);   // rows of the tile inside the segment
     if (GATE_UP) {
         // The bf16 h tile is staged row-major through the (now idle) LDS ring
         // and leaves with 16-byte row-contiguous stores instead of one 2-byte
@@ -358,15 +358,17 @@ __device__ __forceinline__ void ffn_mfma_tile(
                         sh[(row + 1) * HS + col] = (uint16_t)(pk >> 16);
                     }
             lds_barrier();
-            // TM rows x 16 chunks of 8 columns; thread -> chunk tid%16, rows tid/16 + 16 i
+            // TM rows x 16 chunks of 8 columns; thread -> chunk tid%16, rows
+            // tid/16 + 16 i; rows past the segment fall outside the resource
+            const __amdgpu_buffer_rsrc_t out =
+                tile_rsrc(dst + (size_t)m0 * ld + col0, nrows * ld * 2);
+            const int c8 = (tid & 15) * 8;
+            const int voff = ((tid >> 4) * ld + c8) * 2;
 #pragma unroll
             for (int i = 0; i < TM / 16; ++i) {
                 const int row = (tid >> 4) + 16 * i;
-                const int c8 = (tid & 15) * 8;
-                if (full || m0 + row <= seg_last) {
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(&sh[row * HS + c8]);
-                    *reinterpret_cast<u32x4*>(&dst[(size_t)(m0 + row) * ld + col0 + c8]) = v;
-                }
+                const u32x4 v = *reinterpret_cast<const u32x4*>(&sh[row * HS + c8]);
+                __builtin_amdgcn_raw_buffer_store_b128(v, out, voff + 16 * i * ld * 2, 0, 0);
             }
         };
         stage_out(0, static_cast<uint16_t*>(C), NC, n0);
@@ -380,38 +382,39 @@ __device__ __forceinline__ void ffn_mfma_tile(
         // pairs (DPP quad_perm [1,0,3,2]) gives every even lane columns c, c+1 of
         // row i and every odd lane columns c-1, c of row i+1: one 4-byte store
         // per two values
-        const bool odd = lane & 1;
-        uint16_t* Y = static_cast<uint16_t*>(C);
+        const int odd = lane & 1;
+        const __amdgpu_buffer_rsrc_t out =
+            tile_rsrc(static_cast<uint16_t*>(C) + (size_t)m0 * NC + n0, nrows * NC * 2);
+        const int voff = (((TM / 2) * wm + row_l + odd) * NC + 128 * wn + col_l - odd) * 2;
 #pragma unroll
         for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int col = n0 + 128 * wn + 32 * q + col_l - (odd ? 1 : 0);
+            for (int r = 0; r < 16; r += 2) {
+                const int roff = voff + (32 * mi + 8 * (r >> 2) + (r & 3)) * NC * 2;
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const int row = m0 + (TM / 2) * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3) + (odd ? 1 : 0);
+                for (int q = 0; q < 4; ++q) {
                     const float x = acc[mi][q][r], y = acc[mi][q][r + 1];
                     const float xs = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
                     const float ys = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0xB1, 0xF, 0xF, false));
                     const unsigned pk = f32x2_to_bf16x2(odd ? ys : x, odd ? y : xs);
-                    if (full || row <= seg_last)
-                        *reinterpret_cast<unsigned*>(&Y[(size_t)row * NC + col]) = pk;
+                    __builtin_amdgcn_raw_buffer_store_b32(pk, out, roff + 64 * q, 0, 0);
                 }
             }
     } else {
         // y in fp32: 32 lanes cover 32 consecutive columns of a row per
         // register, so direct stores already write whole 128-byte row segments
+        const __amdgpu_buffer_rsrc_t out =
+            tile_rsrc(static_cast<float*>(C) + (size_t)m0 * NC + n0, nrows * NC * 4);
+        const int voff = (((TM / 2) * wm + row_l) * NC + 128 * wn + col_l) * 4;
 #pragma unroll
         for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int col = n0 + 128 * wn + 32 * q + col_l;
+            for (int r = 0; r < 16; ++r) {
+                const int roff = voff + (32 * mi + 8 * (r >> 2) + (r & 3)) * NC * 4;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + (TM / 2) * wm + 32 * mi + 8 * (r >> 2) + row_l + (r & 3);
-                    if (full || row <= seg_last)
-                        static_cast<float*>(C)[(size_t)row * NC + col] = acc[mi][q][r];
-                }
+                for (int q = 0; q < 4; ++q)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[mi][q][r]), out,
+                                                          roff + 128 * q, 0, 0);
             }
     }
 }
@@ -540,13 +543,16 @@ __global__ __launch_bounds__(256) void ffn_generic_kernel(
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// (f, d < 2^20 keep a tile's byte offsets in the epilogue's buffer stores in
+// 31 bits)
 bool ffn_gate_up_uses_mfma(moe_dtype dt, int d, int f, const void* x, const void* wg,
                            const void* wv, const void* h) {
-    return dt == MOE_BF16 && d % BK == 0 && f % 128 == 0 && aligned16(x) && aligned16(wg) &&
-           aligned16(wv) && aligned16(h);
+    return dt == MOE_BF16 && d % BK == 0 && f % 128 == 0 && f < (1 << 20) && aligned16(x) &&
+           aligned16(wg) && aligned16(wv) && aligned16(h);
 }
 bool ffn_down_uses_mfma(moe_dtype dt, int f, int d, const void* h, const void* wo) {
-    return dt == MOE_BF16 && f % BK == 0 && d % 256 == 0 && aligned16(h) && aligned16(wo);
+    return dt == MOE_BF16 && f % BK == 0 && d % 256 == 0 && d < (1 << 20) && aligned16(h) &&
+           aligned16(wo);
 }
 
 static unsigned grid_for(long long tiles) {

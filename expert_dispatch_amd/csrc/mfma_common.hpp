@@ -168,6 +168,19 @@ inline long long max_row_tiles(int N, int E, int bm) {
     return ((long long)N + (long long)E * (bm - 1)) / bm;
 }
 
+// Stores of an output tile go through a raw buffer resource (stride 0) that
+// starts at the tile's first element and spans `bytes`: the hardware drops a
+// store whose offset (the lane's VGPR offset plus the instruction's
+// immediate; the scalar offset is kept at 0) is at or past that size. With
+// `bytes` = valid rows x row pitch, the rows of a partial tile past its
+// expert's segment are dropped without a branch per store, and every address
+// is a 32-bit offset from one scalar base instead of a 64-bit lane pointer.
+// The fourth descriptor word is the gfx9 raw-buffer format (32-bit data,
+// no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
 #define LDS_AS __attribute__((address_space(3)))
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
