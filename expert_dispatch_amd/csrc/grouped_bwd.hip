@@ -444,6 +444,9 @@ __global__ __launch_bounds__(kT, 1) void tn_mfma_kernel(
     const int m0 = mt * TM, n0 = nt * ncols;
     int j0, j1;
     group_rows(offsets, p.split, rows, e, j0, j1);
+    // uniform over the block: keep them (and what derives from them) scalar
+    j0 = __builtin_amdgcn_readfirstlane(j0);
+    j1 = __builtin_amdgcn_readfirstlane(j1);
     // stages of 32 rows, rounded up to a whole number of kS-step loop bodies
     // (the rows past the expert's end load as zeros and add nothing)
     const int KT = (j1 - j0 + kS * kK - 1) / (kS * kK) * kS;
@@ -471,35 +474,33 @@ __global__ __launch_bounds__(kT, 1) void tn_mfma_kernel(
         int bcol;
         if (p.pair > 0) bcol = (cb < 16) ? min(n0 + 8 * cb, p.Nc - 8) : p.pair + min(n0 + 8 * (cb - 16), p.Nc - 8);
         else bcol = min(n0 + 8 * cb, p.Nc - 8);
-        // Rows past the expert's end read its last row and are zeroed when
-        // the stage goes to LDS (a select right after the load would make
-        // the wavefront wait for that load there and then).
-        const u32x4 z = {0u, 0u, 0u, 0u};
+        // A stage is read through buffer resources over its own 32 rows,
+        // clipped at the group's end: rows past j1 (the padding of the last
+        // loop body, and every stage past it) load as zeros without a memory
+        // access, and the lane offsets stay small whatever the operand size.
+        const int a_off = ((tid / kAT) * p.lda + acol) * 2;
+        const int b_off = ((tid >> 5) * p.ldb + bcol) * 2;
         auto load = [&](int kt, TnStage& r) {
+            const int j = j0 + kt * kK;
+            const int live = min(max(j1 - j, 0), kK);   // rows of the stage inside the group
+            const __amdgpu_buffer_rsrc_t ar = tile_rsrc(p.A + (size_t)j * p.lda, live * p.lda * 2);
+            const __amdgpu_buffer_rsrc_t br = tile_rsrc(p.B + (size_t)j * p.ldb, live * p.ldb * 2);
 #pragma unroll
-            for (int i = 0; i < kMI; ++i) {
-                const int j = j0 + kt * kK + tid / kAT + kAR * i;
-                r.a[i] = *reinterpret_cast<const u32x4*>(p.A + (size_t)min(j, j1 - 1) * p.lda + acol);
-            }
+            for (int i = 0; i < kMI; ++i)
+                r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ar, a_off + kAR * i * p.lda * 2, 0, 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = j0 + kt * kK + (tid >> 5) + 8 * i;
-                r.b[i] = *reinterpret_cast<const u32x4*>(p.B + (size_t)min(j, j1 - 1) * p.ldb + bcol);
-            }
+            for (int i = 0; i < 4; ++i)
+                r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(br, b_off + 8 * i * p.ldb * 2, 0, 0);
         };
         const int adst = (tid / kAT) * TM + b_swz(ca, tid / kAT) * 8;
         const int bdst = (tid >> 5) * kN + b_swz(cb, tid >> 5) * 8;
-        auto store = [&](int buf, int kt, const TnStage& r) {
+        auto store = [&](int buf, const TnStage& r) {
 #pragma unroll
-            for (int i = 0; i < kMI; ++i) {
-                const int j = j0 + kt * kK + tid / kAT + kAR * i;
-                *reinterpret_cast<u32x4*>(sA(buf) + adst + kAR * i * TM) = j < j1 ? r.a[i] : z;
-            }
+            for (int i = 0; i < kMI; ++i)
+                *reinterpret_cast<u32x4*>(sA(buf) + adst + kAR * i * TM) = r.a[i];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = j0 + kt * kK + (tid >> 5) + 8 * i;
-                *reinterpret_cast<u32x4*>(sB(buf) + bdst + 8 * i * kN) = j < j1 ? r.b[i] : z;
-            }
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<u32x4*>(sB(buf) + bdst + 8 * i * kN) = r.b[i];
         };
         // transpose-read fragments: in each 16-lane group g, lane j points at
         // k-row 8 (g/2) + j/4 and columns base + 16 (g%2) + 4 (j%4)..+3
@@ -545,15 +546,14 @@ __global__ __launch_bounds__(kT, 1) void tn_mfma_kernel(
         // stores stage kt+2 into the buffer stage kt-1 used (every wavefront
         // passed the barrier after its last read of it) and reloads its set
         // with stage kt+5, reads the first k-substep of stage kt+1, and runs
-        // the MFMAs of the second. Loads past the last stage re-read it.
-        auto clampk = [&](int k) { return min(k, KT - 1); };
+        // the MFMAs of the second. Stages past the last one load as zeros.
         TnStage rs[kS];
 #pragma unroll
-        for (int i = 0; i < kS; ++i) load(clampk(i), rs[i]);
-        store(0, 0, rs[0]);
-        load(clampk(kS), rs[0]);
-        store(1, 1, rs[1]);
-        load(clampk(kS + 1), rs[1]);
+        for (int i = 0; i < kS; ++i) load(i, rs[i]);
+        store(0, rs[0]);
+        load(kS, rs[0]);
+        store(1, rs[1]);
+        load(kS + 1, rs[1]);
         lds_barrier();
         Frags f0, f1;
         read_frags(0, 0, f0);
@@ -563,8 +563,8 @@ __global__ __launch_bounds__(kT, 1) void tn_mfma_kernel(
             lds_barrier_keep<2 * (kMI + 4)>();
             read_frags(buf, 1, f1);
             mfmas(f0);
-            store(wr, kt + 2, r);
-            load(clampk(kt + 2 + kS), r);
+            store(wr, r);
+            load(kt + 2 + kS, r);
             read_frags(nxt, 0, f0);
             mfmas(f1);
             // issue order: the 16 transpose reads of the second k-substep over
