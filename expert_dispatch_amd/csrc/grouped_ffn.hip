@@ -6,29 +6,30 @@
 // expert are contiguous the work is E_local independent MLPs.
 //
 // Two launches: gate_up (h = silu(x.W_gate) * (x.W_val), stored bf16) and
-// down (y = h.W_out, stored fp32). Both use one kernel shape:
-//  * a device-side tile scheduler: every block reads offsets[0..E], turns the
-//    per-expert row counts into a prefix of tiles and finds its own
-//    (expert, column tile, row tile) by binary search. Nothing is read back
-//    to the host, empty experts own no tile, the grid is an upper bound and
-//    surplus blocks leave at once;
-//  * XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs,
-//    so block b works on tile (b % 8) * ceil(tiles / 8) + b / 8. Each XCD
-//    then walks a contiguous run of the tile list, ordered expert by expert
-//    and, inside an expert, by groups of 4 row tiles that sweep all column
-//    tiles, so the tiles resident on an XCD share row and weight panels
-//    through its L2;
-//  * block tile 256 rows x 256 B-columns (gate_up: 128 gate + 128 val columns
-//    of the same hidden units), BK = 64, 4 wavefronts of 128 x 128, each a
-//    4 x 4 grid of v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 / lane,
-//    held in AGPRs), so every fragment read from LDS feeds four MFMAs;
-//  * a register-staged pipeline: two stages of global loads in flight in
-//    registers while one LDS buffer (of two, 128 KB) is consumed. A is
-//    K-contiguous in LDS; the weight panel stays N-contiguous as in memory and
-//    the MFMA B fragments come from the gfx950 LDS transpose read. XOR
-//    swizzles keep both fragment reads and the staging writes conflict-free;
-//  * the fused epilogue applies SwiGLU on the two accumulator sets of a lane
-//    (gate and val of the same element sit in the same lane and register).
+// down (y = h.W_out, stored fp32 or bf16). Both use one kernel shape:
+//  * a device-side tile list: every block reads offsets[0..E] and turns the
+//    per-expert row counts into a prefix of tiles in LDS (256-row tiles, and
+//    one 128-row tile for a remainder of at most 128 rows). Nothing is read
+//    back to the host and empty experts own no tile;
+//  * a persistent grid (one block per CU, a multiple of 8) in XCD-aware
+//    order: block b works through tiles i*G + (b % 8) * (G / 8) + b / 8, so in
+//    every pass each XCD takes a contiguous run of the list, which is ordered
+//    expert by expert and, inside an expert, by groups of 4 row tiles that
+//    sweep all column tiles: the tiles resident on an XCD share row and
+//    weight panels through its L2;
+//  * block tile TM rows x 256 B-columns (gate_up: 128 gate + 128 val columns
+//    of the same hidden units), BK = 32, 4 wavefronts of TM/2 x 128, each a
+//    (TM/64) x 4 grid of v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per
+//    lane at TM = 256, held in AGPRs), so every fragment read from LDS feeds
+//    several MFMAs;
+//  * a register-staged pipeline: three stages of global loads in flight in
+//    registers and a three-buffer LDS ring (96 KB). A is K-contiguous in LDS;
+//    the weight panel stays N-contiguous as in memory and the MFMA B
+//    fragments come from the gfx950 LDS transpose read. XOR swizzles keep
+//    both fragment reads and the staging writes conflict-free;
+//  * fused epilogues: SwiGLU on the two accumulator sets of a lane (gate and
+//    val of the same element sit in the same lane and register); outputs
+//    leave through buffer stores bounded by the expert's segment.
 // A plain fp32-FMA kernel covers fp32 data and shapes the matrix-core path
 // does not tile.
 #include <algorithm>
