@@ -15,8 +15,8 @@
 // padding of a chunk past d adds +-0 to a sum that is never -0, so no bit
 // changes. route_topk_kernel then gives each
 // token one wavefront: its E <= 1024 scores spread over the 64 lanes, k
-// rounds of a wave-wide arg-max under (score descending, index ascending),
-// then the softmax weights.
+// rounds of a wave-wide arg-max under (score descending, index ascending)
+// with DPP and ballots, then the softmax weights.
 #include <algorithm>
 #include <type_traits>
 
@@ -241,6 +241,33 @@ __global__ __launch_bounds__(256) void route_scores_kernel(
     }
 }
 
+// Maximum over the wavefront, in every lane: an inclusive max-scan with DPP
+// row shifts (1, 2, 4, 8 lanes inside each row of 16) and row broadcasts
+// (lane 15 into rows 1 and 3, lane 31 into rows 2 and 3) leaves the maximum in
+// lane 63, which is read out. Lanes without a source keep -inf, the identity.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max_step(float v) {
+    const int o = __builtin_amdgcn_update_dpp(__float_as_int(-__builtin_inff()), __float_as_int(v),
+                                              CTRL, ROW_MASK, 0xf, false);
+    return fmaxf(v, __int_as_float(o));
+}
+__device__ __forceinline__ float wave_max_f32_dpp(float x) {
+    x = dpp_max_step<0x111, 0xf>(x);   // row_shr:1
+    x = dpp_max_step<0x112, 0xf>(x);   // row_shr:2
+    x = dpp_max_step<0x114, 0xf>(x);   // row_shr:4
+    x = dpp_max_step<0x118, 0xf>(x);   // row_shr:8
+    x = dpp_max_step<0x142, 0xa>(x);   // row_bcast:15
+    x = dpp_max_step<0x143, 0xc>(x);   // row_bcast:31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kWave - 1));
+}
+
+// One wavefront per token; lane l holds scores l, l + 64, ... (EJ of them,
+// E <= 64 EJ). Each of the k rounds takes the wavefront's maximum m of the
+// scores not taken yet (DPP max-scan, no LDS round trips), then the lowest
+// index holding m (a ballot per register; the indices of register j all lie
+// below those of register j + 1), which is the order (score descending, index
+// ascending). Then the softmax weights.
+template <int EJ>
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ logits, int T, int E, int k, int renorm,
     int32_t* __restrict__ topk_idx, float* __restrict__ gates)
@@ -248,35 +275,32 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     const int t = blockIdx.x * 4 + threadIdx.x / kWave;
     if (t >= T) return;
     const int lane = lane_id();
-    const int EJ = (E + kWave - 1) / kWave;
     const float* l = logits + (size_t)t * E;
-    float v[16];
+    float v[EJ];
+    unsigned avail = 0;   // bit j: score lane + 64 j exists and is not taken yet
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < EJ; ++j) {
         const int e = lane + kWave * j;
-        v[j] = (j < EJ && e < E) ? l[e] : 0.0f;
+        v[j] = e < E ? l[e] : -__builtin_inff();
+        if (e < E) avail |= 1u << j;
     }
-    unsigned used = 0;
     float myv = 0.0f;
     int mye = 0;
     for (int s = 0; s < k; ++s) {
-        float bv = -__builtin_inff();
+        float lv = -__builtin_inff();
+#pragma unroll
+        for (int j = 0; j < EJ; ++j)
+            if ((avail >> j) & 1u) lv = fmaxf(lv, v[j]);
+        const float m = wave_max_f32_dpp(lv);
+        // registers from the last to the first: the lowest one with a hit wins
         int be = 0x7fffffff;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int e = lane + kWave * j;
-            if (j < EJ && e < E && !((used >> j) & 1u)) {
-                if (v[j] > bv || (v[j] == bv && e < be)) { bv = v[j]; be = e; }
-            }
+        for (int j = EJ - 1; j >= 0; --j) {
+            const unsigned long long hit = __ballot(((avail >> j) & 1u) && v[j] == m);
+            if (hit) be = kWave * j + (__ffsll((long long)hit) - 1);
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, kWave);
-            const int oe = __shfl_xor(be, off, kWave);
-            if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-        }
-        if ((be % kWave) == lane) used |= 1u << (be / kWave);
-        if (lane == s) { myv = bv; mye = be; }
+        if (be != 0x7fffffff && (be & (kWave - 1)) == lane) avail &= ~(1u << (be / kWave));
+        if (lane == s) { myv = m; mye = be; }
     }
     const float m = __shfl(myv, 0, kWave);
     const float u = lane < k ? expf(myv - m) : 0.0f;
@@ -286,9 +310,9 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     } else {
         float part = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < EJ; ++j) {
             const int e = lane + kWave * j;
-            if (j < EJ && e < E) part += expf(v[j] - m);
+            if (e < E) part += expf(v[j] - m);
         }
         denom = wave_sum_f32(part);
     }
@@ -458,7 +482,12 @@ hipError_t launch_route(const void* x, moe_dtype dt, const void* w, const float*
     hipError_t e = (dt == MOE_BF16) ? launch_scores_t<uint16_t>(x, w, bias, T, d, E, logits, st)
                                     : launch_scores_t<float>(x, w, bias, T, d, E, logits, st);
     if (e != hipSuccess) return e;
-    route_topk_kernel<<<(T + 3) / 4, 256, 0, st>>>(logits, T, E, k, renorm, idx, gates);
+    const unsigned g = (T + 3) / 4;
+    if (E <= 64) route_topk_kernel<1><<<g, 256, 0, st>>>(logits, T, E, k, renorm, idx, gates);
+    else if (E <= 128) route_topk_kernel<2><<<g, 256, 0, st>>>(logits, T, E, k, renorm, idx, gates);
+    else if (E <= 256) route_topk_kernel<4><<<g, 256, 0, st>>>(logits, T, E, k, renorm, idx, gates);
+    else if (E <= 512) route_topk_kernel<8><<<g, 256, 0, st>>>(logits, T, E, k, renorm, idx, gates);
+    else route_topk_kernel<16><<<g, 256, 0, st>>>(logits, T, E, k, renorm, idx, gates);
     return hipGetLastError();
 }
 
