@@ -79,8 +79,20 @@ __global__ __launch_bounds__(kPermThreads) void perm_rank_kernel(
     const int lane = lane_id();
 
     for (int e = tid; e < E; e += kPermThreads) {
+        // the chunk histograms of expert e, eight loads in flight at a time
         int tot = 0, pre = 0;
-        for (int b = 0; b < nb; ++b) {
+        int b = 0;
+        for (; b + 8 <= nb; b += 8) {
+            int c[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) c[u] = bc[(size_t)(b + u) * E + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                tot += c[u];
+                if (b + u < (int)blockIdx.x) pre += c[u];
+            }
+        }
+        for (; b < nb; ++b) {
             const int c = bc[(size_t)b * E + e];
             tot += c;
             if (b < (int)blockIdx.x) pre += c;
