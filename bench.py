@@ -54,6 +54,12 @@ def parse():
     ap.add_argument("--partial-dtype", choices=("f32", "bf16"), default="bf16",
                     help="gathered-token workload: type of the partial output that the "
                          "reduce-scatter would sum")
+    ap.add_argument("--no-renorm", action="store_true",
+                    help="un-normalised router weights: the full-softmax probabilities of the "
+                         "selected experts instead of a softmax over the k selected logits")
+    ap.add_argument("--route-stats", action="store_true",
+                    help="add the load statistics (mean full-softmax probability per expert and "
+                         "the load-balance statistic) to the step, after the packing")
     ap.add_argument("--backward", action="store_true",
                     help="time a training step instead: the forward keeping what the "
                          "backward needs, then the backward of sum(out * d_out) with a "
@@ -126,6 +132,9 @@ def stage_work(cfg, counts, es, ys=4, kept=None, os_=4, touched=None):
         w["shared_gate_up"] = dict(flops=4.0 * T * d * fs,
                                    bytes=T * d * es + 2 * d * fs * es + T * fs * es)
         w["shared_down"] = dict(flops=2.0 * T * fs * d, bytes=T * fs * es + fs * d * es + T * d * 4)
+    # load statistics: the logits read (once for the normalisers, once for the
+    # probabilities), the counts and the outputs
+    w["route_stats"] = dict(flops=0.0, bytes=2 * T * E * 4 + E * 4 + E * 4 + 4, bound="hbm")
     units = cfg.units
     idx_bytes = T * k * 8 if cfg.kind == "gathered" else rows * 8
     w["combine"] = dict(flops=2.0 * rows * d,
@@ -456,7 +465,19 @@ def main():
                 h=torch.empty((cfg.T, cfg.shared * f), dtype=xdt, device=cuda),
                 y=torch.empty((cfg.T, d), dtype=torch.float32, device=cuda))
 
+    renorm = not args.no_renorm
+    with_stats = args.route_stats and cfg.kind == "routed"
+    if args.route_stats and not with_stats:
+        print("--route-stats applies to the token-routed workloads only", file=sys.stderr)
+        sys.exit(2)
+    if with_stats:
+        stats_out = (torch.empty(E, dtype=torch.float32, device=cuda),
+                     torch.empty(1, dtype=torch.float32, device=cuda))
+        stats_ws = torch.empty(max(1, ops.route_stats_workspace(cfg.T, E)), dtype=torch.uint8,
+                               device=cuda)
+        stats_counts = bufs["routed"] if "routed" in bufs else bufs["counts"]
     stages = (["route", "permute"] if cfg.kind != "recv" else ["permute_recv"]) + \
+        (["route_stats"] if with_stats else []) + \
         ["gate_up", "down"] + (["shared_gate_up", "shared_down"] if shared else []) + ["combine"]
 
     def step(ev=None):
@@ -464,10 +485,15 @@ def main():
         if ev is not None:
             ev[0].record()
         if cfg.kind != "recv":
-            ops.route(dev["x"], dev["w_router"], dev["bias"], cfg.k, out=(logits, idx, gates))
+            ops.route(dev["x"], dev["w_router"], dev["bias"], cfg.k, renorm,
+                      out=(logits, idx, gates))
             if ev is not None: ev[1].record()
             ops.permute(idx, dev["x"], E, capacity=cap, e_first=e_first, out=bufs, workspace=ws)
             i = 2
+            if with_stats:
+                if ev is not None: ev[i].record()
+                ops.route_stats(logits, stats_counts, cfg.k, out=stats_out, workspace=stats_ws)
+                i = 3
         else:
             ops.permute_recv(dev["recv_counts"], dev["x_recv"], out=bufs)
             i = 1
@@ -551,6 +577,8 @@ def main():
         "config": {"workload": cfg.name, "description": cfg.description,
                    "y_perm_dtype": "bf16" if ys == 2 else "f32",
                    "capacity_factor": None if gathered else args.capacity_factor,
+                   "router_weights": "softmax over the selected" if renorm else "full softmax",
+                   "route_stats": with_stats,
                    "kept_rows": kept, "T": cfg.T,
                    "k": cfg.k, "N": cfg.N, "d": d, "f": f, "E": E, "shared": cfg.shared,
                    "rows": rows, "load_max_over_mean": round(float(counts.max() / max(counts.mean(), 1e-9)), 3),

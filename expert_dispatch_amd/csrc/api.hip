@@ -42,7 +42,8 @@ int router_splits(int T, int& split);
 hipError_t launch_sum_splits(const float* part, int S, long long n, float* out, hipStream_t st);
 enum NtEpi { kNtSwigluBwd = 0, kNtStoreF32 = 1, kNtAccumF32 = 2, kNtStoreBf16 = 3 };
 hipError_t launch_route_stats(const float* logits, const int32_t* counts, int T, int E, int k,
-                              float* p_mean, float* aux, float* mz, hipStream_t st);
+                              float* p_mean, float* aux, double* part, hipStream_t st);
+int route_stat_chunks(int T);
 hipError_t launch_token_grad(const void* d_xp, moe_dtype p_dt, const int32_t* dest,
                              const int32_t* idx, const float* gates, const float* d_gates,
                              const void* w, moe_dtype w_dt, int T, int k, int d, int E,
@@ -243,9 +244,11 @@ moe_status moe_combine(const void* y_perm, moe_dtype y_dt, const int32_t* dest,
                                           as_stream(stream)));
 }
 
-size_t moe_route_stats_workspace(int T)
+size_t moe_route_stats_workspace(int T, int E)
 {
-    return T > 0 ? moe::align_up((size_t)T * 2 * sizeof(float), 256) : 0;
+    if (T <= 0 || E <= 0) return 0;
+    // per token-range fp64 partial sums per expert
+    return moe::align_up((size_t)moe::route_stat_chunks(T) * E * sizeof(double), 256);
 }
 
 moe_status moe_route_stats(const float* logits, const int32_t* counts, int T, int E, int k,
@@ -254,9 +257,9 @@ moe_status moe_route_stats(const float* logits, const int32_t* counts, int T, in
     if (T <= 0 || E <= 0 || k <= 0 || k > E) return MOE_ERR_INVALID_ARG;
     if ((long long)T * E > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     if (!logits || !p_mean || (aux && !counts)) return MOE_ERR_INVALID_ARG;
-    if (!ws || ws_bytes < moe_route_stats_workspace(T)) return MOE_ERR_WORKSPACE;
+    if (!ws || ws_bytes < moe_route_stats_workspace(T, E)) return MOE_ERR_WORKSPACE;
     return hip_status(moe::launch_route_stats(logits, counts, T, E, k, p_mean, aux,
-                                              static_cast<float*>(ws), as_stream(stream)));
+                                              static_cast<double*>(ws), as_stream(stream)));
 }
 
 // ------------------------------------------------------------------ backward

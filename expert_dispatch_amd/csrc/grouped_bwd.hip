@@ -878,8 +878,20 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict
     const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= n) return;
     if (i + 4 <= n) {
+        // eight partials in flight at a time, added in ascending g
         f32x4 acc = *reinterpret_cast<const f32x4*>(part + i);
-        for (int g = 1; g < S; ++g) {
+        int g = 1;
+        for (; g + 8 <= S; g += 8) {
+            f32x4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[u] = *reinterpret_cast<const f32x4*>(part + (size_t)(g + u) * n + i);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                acc[0] += v[u][0]; acc[1] += v[u][1]; acc[2] += v[u][2]; acc[3] += v[u][3];
+            }
+        }
+        for (; g < S; ++g) {
             const f32x4 v = *reinterpret_cast<const f32x4*>(part + (size_t)g * n + i);
             acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
         }

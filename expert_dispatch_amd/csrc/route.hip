@@ -389,68 +389,128 @@ hipError_t launch_route_bwd(const float* logits, const int32_t* idx, const float
 // ------------------------------------------------------- load statistics
 //
 // p_mean[e] = (1/T) sum_t softmax(l[t,:])[e] and aux = E sum_e (counts[e] /
-// (T k)) p_mean[e]. Three small launches: per-token max and softmax
-// denominator (one wavefront per token), per-expert column sums (64 experts
-// x 4 token phases per block, fp64 partial sums combined in a fixed order),
-// and the weighted sum over experts (one block). No atomics: the result is
-// the same on every run.
-__global__ __launch_bounds__(256) void route_norm_kernel(const float* __restrict__ logits, int T,
-                                                        int E, float* __restrict__ mz)
+// (T k)) p_mean[e]. Two launches, no atomics (the same result on every run).
+// Pass 1: block c takes the c-th of C equal token ranges in sub-chunks of 16
+// tokens: sixteen threads per token find the maximum and the sum of exp of
+// its logits (into LDS), then every thread adds the softmax probabilities of
+// its experts (e = tid, tid + 256, ...) over the sub-chunk's tokens in
+// ascending order, in fp64, into part[c][e].
+constexpr int kStatSub = 16;
+__global__ __launch_bounds__(256) void route_stats_partial_kernel(
+    const float* __restrict__ logits, int T, int E, int C, double* __restrict__ part)
 {
-    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
-    if (t >= T) return;
-    const int lane = lane_id();
-    const float* l = logits + (size_t)t * E;
-    float m = -__builtin_inff();
-    for (int e = lane; e < E; e += kWave) m = fmaxf(m, l[e]);
+    __shared__ float s_m[kStatSub], s_z[kStatSub];
+    const int tid = threadIdx.x;
+    const int tc = (T + C - 1) / C;
+    const int t0 = blockIdx.x * tc, t1 = min(T, t0 + tc);
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};   // experts tid + 256 j (E <= 1024)
+    for (int s0 = t0; s0 < t1; s0 += kStatSub) {
+        const int n = min(kStatSub, t1 - s0);
+        {
+            // thread (i, p) = (tid / 16, tid % 16) takes logits p, p + 16, ... of
+            // token i; the sixteen combine through lane shuffles
+            const int i = tid >> 4, p = tid & 15;
+            const float* l = logits + (size_t)(s0 + min(i, n - 1)) * E;
+            float m = -__builtin_inff(), z = 0.0f;
+            for (int e = p; e < E; e += 16) m = fmaxf(m, l[e]);
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
-    float z = 0.0f;
-    for (int e = lane; e < E; e += kWave) z += expf(l[e] - m);
-    z = wave_sum_f32(z);
-    if (lane == 0) { mz[2 * (size_t)t] = m; mz[2 * (size_t)t + 1] = z; }
-}
-
-__global__ __launch_bounds__(256) void route_pmean_kernel(const float* __restrict__ logits,
-                                                         const float* __restrict__ mz, int T,
-                                                         int E, float* __restrict__ p_mean)
-{
-    __shared__ double part[4][64];
-    const int el = threadIdx.x & 63, g = threadIdx.x >> 6;
-    const int e = blockIdx.x * 64 + el;
-    double acc = 0.0;
-    if (e < E)
-        for (int t = g; t < T; t += 4)
-            acc += (double)(expf(logits[(size_t)t * E + e] - mz[2 * (size_t)t]) / mz[2 * (size_t)t + 1]);
-    part[g][el] = acc;
-    __syncthreads();
-    if (g == 0 && e < E)
-        p_mean[e] = (float)(((part[0][el] + part[1][el]) + (part[2][el] + part[3][el])) / (double)T);
-}
-
-__global__ __launch_bounds__(256) void route_aux_kernel(const float* __restrict__ p_mean,
-                                                       const int32_t* __restrict__ counts, int T,
-                                                       int E, int k, float* __restrict__ aux)
-{
-    __shared__ double part[256];
-    double acc = 0.0;
-    for (int e = threadIdx.x; e < E; e += 256)
-        acc += ((double)counts[e] / ((double)T * k)) * (double)p_mean[e];
-    part[threadIdx.x] = acc;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+            for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+            for (int e = p; e < E; e += 16) z += expf(l[e] - m);
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, kWave);
+            if (i < n && p == 0) { s_m[i] = m; s_z[i] = z; }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = tid + 256 * j;
+            if (e >= E) continue;
+            const float* l = logits + (size_t)s0 * E + e;
+            double a = acc[j];
+            if (n == kStatSub) {
+                // all sixteen tokens' logits in flight, added in ascending order
+                float v[kStatSub];
+#pragma unroll
+                for (int u = 0; u < kStatSub; ++u) v[u] = l[(size_t)u * E];
+#pragma unroll
+                for (int u = 0; u < kStatSub; ++u) a += (double)(expf(v[u] - s_m[u]) / s_z[u]);
+            } else {
+                for (int i = 0; i < n; ++i) a += (double)(expf(l[(size_t)i * E] - s_m[i]) / s_z[i]);
+            }
+            acc[j] = a;
+        }
         __syncthreads();
     }
-    if (threadIdx.x == 0) *aux = (float)((double)E * part[0]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = tid + 256 * j;
+        if (e < E) part[(size_t)blockIdx.x * E + e] = acc[j];
+    }
 }
 
-hipError_t launch_route_stats(const float* logits, const int32_t* counts, int T, int E, int k,
-                              float* p_mean, float* aux, float* mz, hipStream_t st)
+// Pass 2, one block of 256 threads, experts in passes of 256 / G: G = 256 / E
+// (a power of two, at least 1) threads per expert, thread (e, g) sums
+// part[c][e] over c = g, g + G, ... ascending; the G sums are added pairwise
+// in a fixed tree. p_mean[e] = sum / T; then, if asked, the load-balance
+// statistic E * sum_e (counts_e / (T k)) p_mean_e (per-thread sums over the
+// passes, then a fixed tree).
+__global__ __launch_bounds__(256) void route_aux_kernel(const double* __restrict__ part, int C,
+                                                       const int32_t* __restrict__ counts, int T,
+                                                       int E, int G, int k,
+                                                       float* __restrict__ p_mean,
+                                                       float* __restrict__ aux)
 {
-    route_norm_kernel<<<(T + 3) / 4, 256, 0, st>>>(logits, T, E, mz);
-    route_pmean_kernel<<<(E + 63) / 64, 256, 0, st>>>(logits, mz, T, E, p_mean);
-    if (aux) route_aux_kernel<<<1, 256, 0, st>>>(p_mean, counts, T, E, k, aux);
+    __shared__ double s[256];
+    const int tid = threadIdx.x;
+    const int g = tid % G;
+    double acc = 0.0;
+    for (int e0 = 0; e0 < E; e0 += 256 / G) {
+        const int e = e0 + tid / G;
+        double sum = 0.0;
+        if (e < E) {
+            int c = g;
+            for (; c + 7 * G < C; c += 8 * G) {
+                double v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(c + u * G) * E + e];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) sum += v[u];
+            }
+            for (; c < C; c += G) sum += part[(size_t)c * E + e];
+        }
+        s[tid] = sum;
+        __syncthreads();
+        for (int w = G >> 1; w > 0; w >>= 1) {
+            if (g < w) s[tid] += s[tid + w];
+            __syncthreads();
+        }
+        if (g == 0 && e < E) {
+            const float pm = (float)(s[tid] / (double)T);
+            p_mean[e] = pm;
+            if (aux) acc += ((double)counts[e] / ((double)T * k)) * (double)pm;
+        }
+        __syncthreads();
+    }
+    if (!aux) return;
+    s[tid] = acc;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) s[tid] += s[tid + w];
+        __syncthreads();
+    }
+    if (tid == 0) *aux = (float)((double)E * s[0]);
+}
+
+int route_stat_chunks(int T) { return std::max(1, std::min(256, (T + 15) / 16)); }
+
+hipError_t launch_route_stats(const float* logits, const int32_t* counts, int T, int E, int k,
+                              float* p_mean, float* aux, double* part, hipStream_t st)
+{
+    const int C = route_stat_chunks(T);
+    int G = 1;
+    while (G * 2 * E <= 256) G *= 2;
+    route_stats_partial_kernel<<<C, 256, 0, st>>>(logits, T, E, C, part);
+    route_aux_kernel<<<1, 256, 0, st>>>(part, C, counts, T, E, G, k, p_mean, aux);
     return hipGetLastError();
 }
 

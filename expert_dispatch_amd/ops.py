@@ -69,7 +69,7 @@ def lib():
                        "moe_permute_recv_workspace": [i, i, i],
                        "moe_grouped_ffn_workspace": [i, i, i, i, i],
                        "moe_router_backward_workspace": [i, i, i],
-                       "moe_route_stats_workspace": [i],
+                       "moe_route_stats_workspace": [i, i],
                        "moe_token_backward_workspace": [i, i, i]}.items():
         fn = getattr(L, name)
         fn.argtypes = args
@@ -126,15 +126,23 @@ def route(x, w_router, bias, k: int, renorm: bool = True, *, out=None, stream=No
     return logits, idx, gates
 
 
-def route_stats(logits, counts, k: int, *, stream=None):
+def route_stats_workspace(T: int, E: int) -> int:
+    return int(lib().moe_route_stats_workspace(T, E))
+
+
+def route_stats(logits, counts, k: int, *, out=None, workspace=None, stream=None):
     """(p_mean [E] fp32, aux [1] fp32): the mean full-softmax probability of
     every expert and the load-balance statistic E * sum_e (counts_e/(T*k)) p_mean_e."""
     _dev(logits, "logits"); _dev(counts, "counts")
     T, E = logits.shape
-    p_mean = torch.empty(E, dtype=torch.float32, device=logits.device)
-    aux = torch.empty(1, dtype=torch.float32, device=logits.device)
-    ws = torch.empty(max(1, int(lib().moe_route_stats_workspace(T))), dtype=torch.uint8,
-                     device=logits.device)
+    if out is None:
+        out = (torch.empty(E, dtype=torch.float32, device=logits.device),
+               torch.empty(1, dtype=torch.float32, device=logits.device))
+    p_mean, aux = out
+    ws = workspace
+    if ws is None:
+        ws = torch.empty(max(1, route_stats_workspace(T, E)), dtype=torch.uint8,
+                         device=logits.device)
     _check("moe_route_stats", lib().moe_route_stats(
         _p(logits), _p(counts), T, E, k, _p(p_mean), _p(aux), _p(ws), ws.numel(),
         _stream(stream)))

@@ -227,10 +227,11 @@ moe_status moe_combine(const void* y_perm, moe_dtype y_dt, const int32_t* dest,
  *   aux       = E * sum_e (counts[e] / (T*k)) * p_mean[e]   one fp32 (may be NULL)
  * logits [T,E] as moe_route wrote them; counts [E] the assignments routed to
  * each expert (moe_permute's counts, or moe_permute_capacity's `routed`).
- * Workspace: moe_route_stats_workspace(T) bytes. Sums run in fp64 in a fixed
- * order: the same result on every run.
+ * Workspace: moe_route_stats_workspace(T, E) bytes (fp64 partial sums per
+ * token range and expert). Sums run in fp64 in a fixed order: the same result
+ * on every run.
  */
-size_t moe_route_stats_workspace(int T);
+size_t moe_route_stats_workspace(int T, int E);
 moe_status moe_route_stats(const float* logits, const int32_t* counts, int T, int E, int k,
                            float* p_mean, float* aux, void* ws, size_t ws_bytes, void* stream);
 

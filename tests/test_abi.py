@@ -110,6 +110,9 @@ def test_host_side_errors_return_before_launch(L):
                                 fake, 16, None) == 3
     # load statistics: too small a workspace, k > E
     assert L.moe_route_stats(fake, fake, 64, 8, 2, fake, fake, fake, 16, None) == 3
+    need_s = L.moe_route_stats_workspace(64, 8)
+    assert L.moe_route_stats(fake, fake, 64, 8, 2, fake, fake, fake, need_s - 1, None) == 3
+    assert L.moe_route_stats_workspace(4096, 128) > L.moe_route_stats_workspace(4096, 8)
     assert L.moe_route_stats(fake, fake, 64, 8, 9, fake, fake, fake, 1 << 20, None) == 1
     # router W_r gradient at large T needs the split workspace
     need_r = L.moe_router_backward_workspace(4096, 64, 8)

@@ -380,3 +380,20 @@ def test_route_stats(name):
     e2 = abs(float(to_numpy(aux)[0]) - o_aux) / abs(o_aux)
     assert e1 <= 1e-5 and e2 <= 1e-5, (e1, e2)
     say(f"[parity] {name}: aux {o_aux:.6f} (1 = balanced) ok p_err={e1:.2e} aux_err={e2:.2e}")
+
+
+@pytest.mark.parametrize("T,E,k", [(37, 300, 5), (1000, 1024, 8), (4099, 257, 2), (16, 3, 1)])
+def test_route_stats_shapes(T, E, k):
+    """Load statistics on seeded logits and counts at expert counts past one
+    pass of the final reduction (E > 256, up to the router's limit), token
+    counts with a ragged last range, and a degenerate small case."""
+    say(f"[parity] load statistics T={T} E={E} k={k}")
+    rng = np.random.default_rng(7000 + E + T)
+    logits = (rng.standard_normal((T, E)) * 2.0).astype(np.float32)
+    counts = rng.multinomial(T * k, np.full(E, 1.0 / E)).astype(np.int32)
+    p_mean, aux = ops.route_stats(torch.from_numpy(logits).cuda(), torch.from_numpy(counts).cuda(), k)
+    torch.cuda.synchronize()
+    o_pm, o_aux = oracle.route_stats(logits, counts, k)
+    e1 = err_f32(to_numpy(p_mean), o_pm)
+    e2 = abs(float(to_numpy(aux)[0]) - o_aux) / abs(o_aux)
+    assert e1 <= 1e-5 and e2 <= 1e-5, (e1, e2)
