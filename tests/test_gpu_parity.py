@@ -325,6 +325,33 @@ def test_unnormalised_router_weights():
     assert err_f32(to_numpy(gates), og) <= 1e-5
 
 
+@pytest.mark.parametrize("T,d,E,k,dt,renorm", [
+    (33, 64, 1024, 32, "f32", True),     # the router's largest expert count and k
+    (70, 96, 300, 7, "bf16", True),      # E between 256 and 512
+    (41, 40, 200, 5, "bf16", False),     # E between 128 and 256, full-softmax weights
+    (5, 32, 65, 3, "f32", True),         # E just past one register per lane
+    (9, 8, 32, 32, "f32", False),        # k = E = 32 (the largest k): every expert
+])
+def test_router_expert_counts(T, d, E, k, dt, renorm):
+    """Router scores (bit-exact), ids (exact) and weights (fp32 rule) at expert
+    counts that use 1 to 16 scores per lane in the top-k selection, on seeded
+    inputs with ties made likely by a coarse weight grid."""
+    say(f"[parity] router T={T} d={d} E={E} k={k} {dt} renorm={renorm}")
+    rng = np.random.default_rng(9100 + E + k)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    # weights on a grid of 1/8: many equal scores, so the index order decides
+    w = (np.round(rng.standard_normal((d, E)) * 2.0) / 8.0).astype(np.float32)
+    bias = None if E % 2 else (rng.standard_normal(E) * 0.01).astype(np.float32)
+    if dt == "bf16":
+        x, w = W.f32_to_bf16_bits(x), W.f32_to_bf16_bits(w)
+    logits, idx, gates = ops.route(to_torch(x), to_torch(w), to_torch(bias), k, renorm=renorm)
+    torch.cuda.synchronize()
+    o_logits, o_idx, o_gates = oracle.route(x, w, bias, k, renorm=renorm)
+    np.testing.assert_array_equal(to_numpy(logits).view(np.uint32), o_logits.view(np.uint32))
+    np.testing.assert_array_equal(to_numpy(idx), o_idx)
+    assert err_f32(to_numpy(gates), o_gates) <= 1e-5
+
+
 def test_deterministic_bitwise():
     for name in ("qwen3_small", "qwen3_30b_a3b"):
         inp = _inputs(name)
