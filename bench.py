@@ -371,7 +371,8 @@ def main_backward(args):
     for n in stages:
         r = roofline_entry(work[n], stage_us[n], es)
         rep[n] = dict(us=round(stage_us[n], 2), bound=r["bound"], achieved=round(r["achieved"], 1),
-                      unit=r["unit"], frac=round(r["frac"], 4))
+                      unit=r["unit"], frac=round(r["frac"], 4), alg_flops=work[n]["flops"],
+                      alg_bytes=work[n]["bytes"])
     bwd = stages[5:]
     dominant = max(bwd, key=lambda n: stage_us[n])
     dom = roofline_entry(work[dominant], stage_us[dominant], es)
@@ -389,7 +390,7 @@ def main_backward(args):
                    "kept_rows": int(counts.sum())},
         "roofline": {"kernel": dominant, "bound": dom["bound"], "achieved": round(dom["achieved"], 1),
                      "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4),
-                     "traffic": None},
+                     "traffic": traffic_for(dominant, cfg.name + "/backward")},
         "stages": rep,
         "cpu_baseline": None,
     }
