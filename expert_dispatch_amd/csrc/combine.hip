@@ -108,6 +108,140 @@ __global__ __launch_bounds__(256) void combine_kernel(
     }
 }
 
+// k <= 8 with 16-byte vectors: the k slots' row indices and weights are read
+// out of lanes 0..k-1 once per token into scalar registers and each slot's
+// row gets a buffer descriptor. A token with every slot kept has the loads
+// of all its rows of a column window in flight before the first FMA (slots
+// past k have empty descriptors: zeros without a memory access, weight 0); a
+// token with dropped slots loads its kept rows one slot after the other. The
+// sum runs in slot order as in the general kernel.
+template <typename YT> struct RowLoad;
+template <> struct RowLoad<float> {
+    static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int off, float (&v)[4]) {
+        const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        v[0] = __uint_as_float(u[0]); v[1] = __uint_as_float(u[1]);
+        v[2] = __uint_as_float(u[2]); v[3] = __uint_as_float(u[3]);
+    }
+};
+template <> struct RowLoad<uint16_t> {
+    static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int off, float (&v)[4]) {
+        const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        v[0] = __uint_as_float(u[0] << 16);
+        v[1] = __uint_as_float(u[0] & 0xffff0000u);
+        v[2] = __uint_as_float(u[1] << 16);
+        v[3] = __uint_as_float(u[1] & 0xffff0000u);
+    }
+};
+
+template <typename YT, typename ST, typename OT>
+__global__ __launch_bounds__(256) void combine_k8_kernel(
+    const YT* __restrict__ y, const int32_t* __restrict__ dest, const float* __restrict__ gates,
+    int T, int k, int d, const ST* __restrict__ shared, OT* __restrict__ out)
+{
+    constexpr int KM = 8, U = 2;
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T) return;
+    const int lane = lane_id();
+    const long long rows = (long long)T * k;
+    int my_j = -1;
+    float my_g = 0.0f;
+    if (lane < k) {
+        my_j = dest[(size_t)t * k + lane];
+        if (my_j < 0 || my_j >= rows) my_j = -1;
+        my_g = gates ? gates[(size_t)t * k + lane] : 1.0f;
+    }
+    __amdgpu_buffer_rsrc_t row[KM];
+    float g[KM];
+    unsigned live = 0;   // slots with a kept row (the same in every lane)
+#pragma unroll
+    for (int s = 0; s < KM; ++s) {
+        const int j = __builtin_amdgcn_readlane(my_j, s);
+        g[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_g), s));
+        const bool on = s < k && j >= 0;
+        if (on) live |= 1u << s;
+        row[s] = tile_rsrc(y + (size_t)(on ? j : 0) * d, on ? d * (int)sizeof(YT) : 0);
+    }
+    OT* o = out + (size_t)t * d;
+    if (live != (1u << k) - 1) {
+        // some slot dropped (fixed capacity, or experts of other ranks): load
+        // only the kept rows, one slot after the other, in slot order
+        for (int c0 = lane * 4; c0 < d; c0 += kWave * 4 * U) {
+            float acc[U][4];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[u][q] = 0.0f;
+            for (int s = 0; s < k; ++s) {
+                if (!((live >> s) & 1u)) continue;
+                __amdgpu_buffer_rsrc_t r = row[0];
+                float gs = g[0];
+#pragma unroll
+                for (int q = 1; q < KM; ++q)
+                    if (q == s) { r = row[q]; gs = g[q]; }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    float v[4];
+                    RowLoad<YT>::load(r, (c0 + u * kWave * 4) * (int)sizeof(YT), v);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[u][q] = __builtin_fmaf(gs, v[q], acc[u][q]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * kWave * 4;
+                if (c < d) {
+                    if (shared) {
+                        float w[4];
+                        Vec4<ST>::load(shared + (size_t)t * d + c, w);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[u][q] += w[q];
+                    }
+                    Vec4<OT>::store(o + c, acc[u]);
+                }
+            }
+        }
+        return;
+    }
+    for (int c0 = lane * 4; c0 < d; c0 += kWave * 4 * U) {
+        float v[KM][U][4];
+#pragma unroll
+        for (int s = 0; s < KM; ++s)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                // columns past d fall outside the row's descriptor: zeros
+                const int c = c0 + u * kWave * 4;
+                RowLoad<YT>::load(row[s], c * (int)sizeof(YT), v[s][u]);
+            }
+        float acc[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[u][q] = 0.0f;
+        // slots past k (and dropped ones) have weight 0 or zero rows: they
+        // add +0, so every slot runs and the loads stay ahead of the FMAs
+#pragma unroll
+        for (int s = 0; s < KM; ++s) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[u][q] = __builtin_fmaf(g[s], v[s][u][q], acc[u][q]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u * kWave * 4;
+            if (c < d) {
+                if (shared) {
+                    float w[4];
+                    Vec4<ST>::load(shared + (size_t)t * d + c, w);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[u][q] += w[q];
+                }
+                Vec4<OT>::store(o + c, acc[u]);
+            }
+        }
+    }
+}
+
 template <typename YT, typename ST, typename OT>
 static hipError_t launch_combine_t(const void* y, const int32_t* dest, const float* gates, int T,
                                    int k, int d, const void* sh, void* out, hipStream_t st)
@@ -116,7 +250,10 @@ static hipError_t launch_combine_t(const void* y, const int32_t* dest, const flo
     auto al = [](const void* p, size_t a) { return p == nullptr || (uintptr_t)p % a == 0; };
     const bool vec = d % 4 == 0 && al(y, 4 * sizeof(YT)) && al(sh, 4 * sizeof(ST)) &&
                      al(out, 4 * sizeof(OT));
-    if (vec)
+    if (vec && k <= 8 && (long long)d * sizeof(YT) < (1LL << 31))
+        combine_k8_kernel<YT, ST, OT><<<grid, 256, 0, st>>>(
+            (const YT*)y, dest, gates, T, k, d, (const ST*)sh, (OT*)out);
+    else if (vec)
         combine_kernel<YT, ST, OT, true><<<grid, 256, 0, st>>>(
             (const YT*)y, dest, gates, T, k, d, (const ST*)sh, (OT*)out);
     else

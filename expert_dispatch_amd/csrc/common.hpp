@@ -124,4 +124,25 @@ __device__ __forceinline__ void lds_barrier() {
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Raw buffer resource (stride 0) that starts at `base` and spans `bytes`:
+// the hardware drops a store, and returns zeros for a load without touching
+// memory, whose offset (the lane's VGPR offset plus the instruction's
+// immediate; the scalar offset is kept at 0) is at or past that size. With
+// `bytes` = valid rows x row pitch, the rows of a partial tile past its
+// expert's segment are dropped (or read as zeros) without a branch per
+// access, and every address is a 32-bit offset from one scalar base instead
+// of a 64-bit lane pointer.
+// The fourth descriptor word is the gfx9 raw-buffer format (32-bit data,
+// no swizzle). `base` and `bytes` must be the same in every lane of the
+// wavefront: they pass through readfirstlane, which keeps the descriptor in
+// scalar registers (a descriptor the compiler holds in vector registers
+// becomes a loop over its distinct values around every access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes) {
+    const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+    const unsigned lo = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(a));
+    const unsigned hi = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(a >> 32));
+    void* u = reinterpret_cast<void*>((static_cast<unsigned long long>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(u, 0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
 }  // namespace moe
