@@ -349,6 +349,96 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     }
 }
 
+// 4-element vectors and d <= 4096: the token's d_out row stays in registers
+// (one 4-element vector per lane per 256 columns) and is read once; each
+// kept slot's y row is read through a scalar buffer descriptor with all of
+// the row's loads in flight at once, d_y written through another. The dot
+// product keeps the general kernel's order (per lane ascending columns, then
+// the wavefront sum).
+template <typename T> struct Raw4;
+template <> struct Raw4<float> {
+    typedef u32x4 type;
+    static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, int off) {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    }
+    static __device__ __forceinline__ void unpack(const type& u, float (&v)[4]) {
+        v[0] = __uint_as_float(u[0]); v[1] = __uint_as_float(u[1]);
+        v[2] = __uint_as_float(u[2]); v[3] = __uint_as_float(u[3]);
+    }
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, int off, const float (&v)[4]) {
+        const u32x4 u = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                         __float_as_uint(v[3])};
+        __builtin_amdgcn_raw_buffer_store_b128(u, r, off, 0, 0);
+    }
+};
+template <> struct Raw4<uint16_t> {
+    typedef u32x2 type;
+    static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, int off) {
+        return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    }
+    static __device__ __forceinline__ void unpack(const type& u, float (&v)[4]) {
+        v[0] = __uint_as_float(u[0] << 16);
+        v[1] = __uint_as_float(u[0] & 0xffff0000u);
+        v[2] = __uint_as_float(u[1] << 16);
+        v[3] = __uint_as_float(u[1] & 0xffff0000u);
+    }
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, int off, const float (&v)[4]) {
+        const u32x2 u = {f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(u, r, off, 0, 0);
+    }
+};
+
+// NCH 256-column chunks per row (d <= 256 NCH): every chunk is loaded and
+// stored unconditionally, the ones past d fall outside the row's descriptor.
+template <typename GT, typename YT, typename DT, int NCH>
+__global__ __launch_bounds__(256) void combine_bwd_reg_kernel(
+    const GT* __restrict__ d_out, const YT* __restrict__ y, const int32_t* __restrict__ dest,
+    const float* __restrict__ gates, int T, int k, int d, DT* __restrict__ d_y,
+    float* __restrict__ d_gates)
+{
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T) return;
+    const int lane = lane_id();
+    const long long rows = (long long)T * k;
+    int my_j = -1;
+    float my_g = 0.0f;
+    if (lane < k) {
+        my_j = dest[(size_t)t * k + lane];
+        if (my_j < 0 || my_j >= rows) my_j = -1;
+        my_g = gates[(size_t)t * k + lane];
+    }
+    const __amdgpu_buffer_rsrc_t gr = tile_rsrc(d_out + (size_t)t * d, d * (int)sizeof(GT));
+    typename Raw4<GT>::type o[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) o[i] = Raw4<GT>::load(gr, (lane * 4 + 256 * i) * (int)sizeof(GT));
+    for (int s = 0; s < k; ++s) {
+        const int j = __builtin_amdgcn_readlane(my_j, s);
+        const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_g), s));
+        float dot = 0.0f;
+        if (j >= 0) {
+            const __amdgpu_buffer_rsrc_t yr = tile_rsrc(y + (size_t)j * d, d * (int)sizeof(YT));
+            const __amdgpu_buffer_rsrc_t dr = tile_rsrc(d_y + (size_t)j * d, d * (int)sizeof(DT));
+            typename Raw4<YT>::type v[NCH];
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) v[i] = Raw4<YT>::load(yr, (lane * 4 + 256 * i) * (int)sizeof(YT));
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                float of[4], vf[4], w[4];
+                Raw4<GT>::unpack(o[i], of);
+                Raw4<YT>::unpack(v[i], vf);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    dot = __builtin_fmaf(of[q], vf[q], dot);
+                    w[q] = g * of[q];
+                }
+                Raw4<DT>::store(dr, (lane * 4 + 256 * i) * (int)sizeof(DT), w);
+            }
+        }
+        dot = wave_sum_f32(dot);
+        if (lane == 0) d_gates[(size_t)t * k + s] = dot;
+    }
+}
+
 template <typename GT, typename YT, typename DT>
 static hipError_t launch_combine_bwd_t(const void* d_out, const void* y, const int32_t* dest,
                                        const float* gates, int T, int k, int d, void* d_y,
@@ -358,7 +448,13 @@ static hipError_t launch_combine_bwd_t(const void* d_out, const void* y, const i
     auto al = [](const void* p, size_t a) { return (uintptr_t)p % a == 0; };
     const bool vec = d % 4 == 0 && al(d_out, 4 * sizeof(GT)) && al(y, 4 * sizeof(YT)) &&
                      al(d_y, 4 * sizeof(DT));
-    if (vec)
+    if (vec && d <= 2048)
+        combine_bwd_reg_kernel<GT, YT, DT, 8><<<grid, 256, 0, st>>>(
+            (const GT*)d_out, (const YT*)y, dest, gates, T, k, d, (DT*)d_y, d_gates);
+    else if (vec && d <= 4096)
+        combine_bwd_reg_kernel<GT, YT, DT, 16><<<grid, 256, 0, st>>>(
+            (const GT*)d_out, (const YT*)y, dest, gates, T, k, d, (DT*)d_y, d_gates);
+    else if (vec)
         combine_bwd_kernel<GT, YT, DT, true><<<grid, 256, 0, st>>>(
             (const GT*)d_out, (const YT*)y, dest, gates, T, k, d, (DT*)d_y, d_gates);
     else
