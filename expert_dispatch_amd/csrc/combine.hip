@@ -595,6 +595,83 @@ __global__ __launch_bounds__(256) void transpose_kernel(const WT* __restrict__ w
     }
 }
 
+// k <= 8 with 4-element vectors: the slots' rows, experts and logit
+// gradients read out of lanes 0..k-1 once per token into scalar registers,
+// every row through a buffer descriptor (empty for a dropped slot or a slot
+// past k: zeros without a memory access), and the k rows of d_x_perm and of
+// W_r^T of a column window all in flight before the sums, which keep the
+// general kernel's order (the d_x_perm rows in slot order, then the W_r^T
+// terms in slot order).
+template <typename PT, typename WT>
+__global__ __launch_bounds__(256) void token_grad_k8_kernel(
+    const PT* __restrict__ d_xp, const int32_t* __restrict__ dest, const int32_t* __restrict__ idx,
+    const float* __restrict__ gates, const float* __restrict__ d_gates,
+    const WT* __restrict__ w_t, int T, int k, int d, int E, float* __restrict__ d_x)
+{
+    constexpr int KM = 8, U = 2;
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T) return;
+    const int lane = lane_id();
+    const long long rows = (long long)T * k;
+    int my_j = -1, my_e = 0;
+    float my_g = 0.0f, my_dg = 0.0f;
+    if (lane < k) {
+        const size_t a = (size_t)t * k + lane;
+        my_j = dest[a];
+        if (my_j < 0 || my_j >= rows) my_j = -1;
+        my_e = min(max(idx[a], 0), E - 1);
+        my_g = gates[a];
+        my_dg = d_gates[a];
+    }
+    const float gdg = wave_sum_f32(my_g * my_dg);
+    const float my_dl = my_g * (my_dg - gdg);
+    __amdgpu_buffer_rsrc_t prow[KM], wrow[KM];
+    float dl[KM];
+#pragma unroll
+    for (int s = 0; s < KM; ++s) {
+        const int j = __builtin_amdgcn_readlane(my_j, s);
+        const int e = __builtin_amdgcn_readlane(my_e, s);
+        dl[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_dl), s));
+        const bool pon = s < k && j >= 0, won = s < k;
+        prow[s] = tile_rsrc(d_xp + (size_t)(pon ? j : 0) * d, pon ? d * (int)sizeof(PT) : 0);
+        wrow[s] = tile_rsrc(w_t + (size_t)e * d, won ? d * (int)sizeof(WT) : 0);
+    }
+    float* o = d_x + (size_t)t * d;
+    for (int c0 = lane * 4; c0 < d; c0 += kWave * 4 * U) {
+        float pv[KM][U][4], wv[KM][U][4];
+#pragma unroll
+        for (int s = 0; s < KM; ++s)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * kWave * 4;
+                RowLoad<PT>::load(prow[s], c * (int)sizeof(PT), pv[s][u]);
+                RowLoad<WT>::load(wrow[s], c * (int)sizeof(WT), wv[s][u]);
+            }
+        float acc[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[u][q] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < KM; ++s)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[u][q] += pv[s][u][q];
+#pragma unroll
+        for (int s = 0; s < KM; ++s)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[u][q] = __builtin_fmaf(dl[s], wv[s][u][q], acc[u][q]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u * kWave * 4;
+            if (c < d) Vec4<float>::store(o + c, acc[u]);
+        }
+    }
+}
+
 template <typename PT, typename WT>
 static hipError_t launch_token_grad_t(const void* d_xp, const int32_t* dest, const int32_t* idx,
                                       const float* gates, const float* d_gates, const void* w,
@@ -607,7 +684,10 @@ static hipError_t launch_token_grad_t(const void* d_xp, const int32_t* dest, con
     const bool vec = d % 4 == 0 && al(d_xp, 4 * sizeof(PT)) && al(w_t, 4 * sizeof(WT)) &&
                      al(d_x, 16);
     const dim3 grid((T + 3) / 4);
-    if (vec)
+    if (vec && k <= 8 && d < (1 << 28))
+        token_grad_k8_kernel<PT, WT><<<grid, 256, 0, st>>>(
+            (const PT*)d_xp, dest, idx, gates, d_gates, (const WT*)w_t, T, k, d, E, d_x);
+    else if (vec)
         token_grad_kernel<PT, WT, true><<<grid, 256, 0, st>>>(
             (const PT*)d_xp, dest, idx, gates, d_gates, (const WT*)w_t, T, k, d, E, d_x);
     else
