@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
     }
 }
 
-// k <= 8 with 16-byte vectors: the k slots' row indices and weights are read
+// k <= 8 with 4-element vectors: the k slots' row indices and weights are read
 // out of lanes 0..k-1 once per token into scalar registers and each slot's
 // row gets a buffer descriptor. A token with every slot kept has the loads
 // of all its rows of a column window in flight before the first FMA (slots
@@ -133,12 +133,13 @@ template <> struct RowLoad<uint16_t> {
     }
 };
 
-template <typename YT, typename ST, typename OT>
+// KM: slots held (k <= KM); U: 4-column groups per lane per window (k <= 2
+// takes eight, so that a row's loads are in flight together).
+template <typename YT, typename ST, typename OT, int KM, int U>
 __global__ __launch_bounds__(256) void combine_k8_kernel(
     const YT* __restrict__ y, const int32_t* __restrict__ dest, const float* __restrict__ gates,
     int T, int k, int d, const ST* __restrict__ shared, OT* __restrict__ out)
 {
-    constexpr int KM = 8, U = 2;
     const int t = blockIdx.x * 4 + threadIdx.x / kWave;
     if (t >= T) return;
     const int lane = lane_id();
@@ -202,8 +203,10 @@ __global__ __launch_bounds__(256) void combine_k8_kernel(
         }
         return;
     }
+    const __amdgpu_buffer_rsrc_t srow =
+        tile_rsrc(shared ? shared + (size_t)t * d : nullptr, shared ? d * (int)sizeof(ST) : 0);
     for (int c0 = lane * 4; c0 < d; c0 += kWave * 4 * U) {
-        float v[KM][U][4];
+        float v[KM][U][4], sv[U][4];
 #pragma unroll
         for (int s = 0; s < KM; ++s)
 #pragma unroll
@@ -212,6 +215,11 @@ __global__ __launch_bounds__(256) void combine_k8_kernel(
                 const int c = c0 + u * kWave * 4;
                 RowLoad<YT>::load(row[s], c * (int)sizeof(YT), v[s][u]);
             }
+        if (shared) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                RowLoad<ST>::load(srow, (c0 + u * kWave * 4) * (int)sizeof(ST), sv[u]);
+        }
         float acc[U][4];
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -231,10 +239,8 @@ __global__ __launch_bounds__(256) void combine_k8_kernel(
             const int c = c0 + u * kWave * 4;
             if (c < d) {
                 if (shared) {
-                    float w[4];
-                    Vec4<ST>::load(shared + (size_t)t * d + c, w);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[u][q] += w[q];
+                    for (int q = 0; q < 4; ++q) acc[u][q] += sv[u][q];
                 }
                 Vec4<OT>::store(o + c, acc[u]);
             }
@@ -250,8 +256,12 @@ static hipError_t launch_combine_t(const void* y, const int32_t* dest, const flo
     auto al = [](const void* p, size_t a) { return p == nullptr || (uintptr_t)p % a == 0; };
     const bool vec = d % 4 == 0 && al(y, 4 * sizeof(YT)) && al(sh, 4 * sizeof(ST)) &&
                      al(out, 4 * sizeof(OT));
-    if (vec && k <= 8 && (long long)d * sizeof(YT) < (1LL << 31))
-        combine_k8_kernel<YT, ST, OT><<<grid, 256, 0, st>>>(
+    const bool rows_ok = (long long)d * sizeof(YT) < (1LL << 31) && (long long)d * sizeof(ST) < (1LL << 31);
+    if (vec && k <= 2 && rows_ok)
+        combine_k8_kernel<YT, ST, OT, 2, 8><<<grid, 256, 0, st>>>(
+            (const YT*)y, dest, gates, T, k, d, (const ST*)sh, (OT*)out);
+    else if (vec && k <= 8 && rows_ok)
+        combine_k8_kernel<YT, ST, OT, 8, 2><<<grid, 256, 0, st>>>(
             (const YT*)y, dest, gates, T, k, d, (const ST*)sh, (OT*)out);
     else if (vec)
         combine_kernel<YT, ST, OT, true><<<grid, 256, 0, st>>>(
