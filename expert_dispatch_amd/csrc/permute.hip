@@ -269,7 +269,17 @@ __global__ __launch_bounds__(256) void perm_recv_kernel(
         if (j < 0) continue;
         const V* src = x + (size_t)r * vecs_per_row;
         V* dst = x_perm + (size_t)j * vecs_per_row;
-        for (int c = lane; c < vecs_per_row; c += kWave) dst[c] = src[c];
+        // four vectors per lane in flight before their stores
+        constexpr int U = 4;
+        for (int c0 = lane; c0 < vecs_per_row; c0 += kWave * U) {
+            V v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (c0 + u * kWave < vecs_per_row) v[u] = src[c0 + u * kWave];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (c0 + u * kWave < vecs_per_row) dst[c0 + u * kWave] = v[u];
+        }
     }
 }
 
