@@ -241,6 +241,173 @@ __global__ __launch_bounds__(256) void route_scores_kernel(
     }
 }
 
+// Producer/consumer variant of route_scores_kernel for grids of about one
+// block per CU (where no second block hides one block's staging): eight
+// wavefronts, the first four run the FMA chains with the same thread mapping
+// and order as route_scores_kernel, the last four only stage: global loads
+// of chunk c + 2, conversion to fp32, the LDS writes of chunk c + 1 while
+// chunk c is consumed. One barrier per chunk.
+template <typename XT>
+__global__ __launch_bounds__(512) void route_scores_pc_kernel(
+    const XT* __restrict__ x, const XT* __restrict__ w, const float* __restrict__ bias,
+    int T, int d, int E, float* __restrict__ logits)
+{
+    constexpr int kRD = 128;                        // d-chunk
+    constexpr int kRS = kRD + 4;                    // x tile row stride (floats)
+    constexpr int kXU = kRT * kRD / 1024;           // x groups of 4 per staging thread per chunk
+    constexpr int kWU = kRD * kRE / 1024;           // W_r groups of 4 per staging thread per chunk
+    constexpr int kRBuf = kRT * kRS + kRD * kRE;    // floats per LDS buffer
+    __shared__ __attribute__((aligned(16))) float smem[2 * kRBuf];
+
+    const int t0 = blockIdx.x * kRT;
+    const int e0 = blockIdx.y * kRE;
+    const int nchunks = (d + kRD - 1) / kRD;
+    const bool stager = threadIdx.x >= 256;          // wavefronts 4..7
+
+    using Raw = typename std::conditional<sizeof(XT) == 2, u32x2, f32x4>::type;
+    auto unpack = [&](const Raw& r, bool in, float (&v)[4]) {
+        if constexpr (sizeof(XT) == 2) {
+            v[0] = __uint_as_float(r[0] << 16);
+            v[1] = __uint_as_float(r[0] & 0xffff0000u);
+            v[2] = __uint_as_float(r[1] << 16);
+            v[3] = __uint_as_float(r[1] & 0xffff0000u);
+        } else {
+            v[0] = r[0]; v[1] = r[1]; v[2] = r[2]; v[3] = r[3];
+        }
+        if (!in) v[0] = v[1] = v[2] = v[3] = 0.0f;
+    };
+
+    if (stager) {
+        // x: 64 tokens x 128 values (8 groups of 4 per thread), W_r: 128 rows x
+        // 32 experts (4 groups of 4), raw bits from clamped (always valid)
+        // addresses, out-of-range groups zeroed when written to LDS
+        const int tid = threadIdx.x - 256;
+        Raw rx[kXU], rw[kWU];
+        bool xin[kXU], win[kWU];
+        auto load = [&](int c) {
+            const int i0 = c * kRD;
+#pragma unroll
+            for (int u = 0; u < kXU; ++u) {
+                const int gq = tid + 256 * u;
+                const int tl = gq / (kRD / 4), i4 = (gq % (kRD / 4)) * 4;
+                const int t = t0 + tl, i = i0 + i4;
+                xin[u] = t < T && i < d;
+                rx[u] = *reinterpret_cast<const Raw*>(x + (size_t)min(t, T - 1) * d + min(i, d - 4));
+            }
+#pragma unroll
+            for (int u = 0; u < kWU; ++u) {
+                const int gq = tid + 256 * u;
+                const int il = gq >> 3, e4 = (gq & 7) * 4;
+                const int i = i0 + il, e = e0 + e4;
+                win[u] = i < d && e < E;
+                rw[u] = *reinterpret_cast<const Raw*>(w + (size_t)min(i, d - 1) * E + min(e, E - 4));
+            }
+        };
+        auto store = [&](int c) {
+            float* xs = smem + (c & 1) * kRBuf;
+            float* ws = xs + kRT * kRS;
+#pragma unroll
+            for (int u = 0; u < kXU; ++u) {
+                const int gq = tid + 256 * u;
+                const int tl = gq / (kRD / 4), i4 = (gq % (kRD / 4)) * 4;
+                float v[4];
+                unpack(rx[u], xin[u], v);
+                const f32x4 q = {v[0], v[1], v[2], v[3]};
+                *reinterpret_cast<f32x4*>(&xs[tl * kRS + i4]) = q;
+            }
+#pragma unroll
+            for (int u = 0; u < kWU; ++u) {
+                const int gq = tid + 256 * u;
+                const int il = gq >> 3, e4 = (gq & 7) * 4;
+                float v[4];
+                unpack(rw[u], win[u], v);
+                const f32x4 q = {v[0], v[1], v[2], v[3]};
+                *reinterpret_cast<f32x4*>(&ws[il * kRE + e4]) = q;
+            }
+        };
+        load(0);
+        store(0);
+        load(1);   // past the last chunk: clamped addresses, never stored
+        lds_barrier();
+        for (int c = 0; c < nchunks; ++c) {
+            if (c + 1 < nchunks) store(c + 1);
+            if (c + 2 < nchunks) load(c + 2);
+            lds_barrier();
+        }
+        return;
+    }
+
+    const int tid = threadIdx.x;
+    const int eg = tid & 7;
+    const int tg = tid >> 3;
+    float acc[2][4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) acc[b][a] = 0.0f;
+    struct Group {
+        f32x4 x[2][2];
+        f32x4 w[kRG];
+    };
+    auto read_group = [&](const float* xs, const float* ws, int i, Group& g) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                g.x[b][h] = *reinterpret_cast<const f32x4*>(&xs[(tg + 32 * b) * kRS + i + 4 * h]);
+#pragma unroll
+        for (int q = 0; q < kRG; ++q)
+            g.w[q] = *reinterpret_cast<const f32x4*>(&ws[(i + q) * kRE + 4 * eg]);
+    };
+    auto fma_group = [&](const Group& g) {
+#pragma unroll
+        for (int q = 0; q < kRG; ++q)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+                    acc[b][a] = __builtin_fmaf(g.x[b][q >> 2][q & 3], g.w[q][a], acc[b][a]);
+    };
+    lds_barrier();   // chunk 0 is in LDS
+    for (int c = 0; c < nchunks; ++c) {
+        const float* xs = smem + (c & 1) * kRBuf;
+        const float* ws = xs + kRT * kRS;
+        Group g[2];
+        if ((c + 1) * kRD <= d) {
+            read_group(xs, ws, 0, g[0]);
+#pragma unroll
+            for (int j = 0; j < kRD / kRG; ++j) {
+                if (j + 1 < kRD / kRG) read_group(xs, ws, (j + 1) * kRG, g[(j + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                fma_group(g[j & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            // last, partial chunk: groups up to d rounded up to 8 (zeros past d)
+            const int n = (d - c * kRD + kRG - 1) / kRG;
+            for (int j = 0; j < n; ++j) {
+                read_group(xs, ws, j * kRG, g[0]);
+                fma_group(g[0]);
+            }
+        }
+        lds_barrier();
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int e = e0 + 4 * eg + a;
+        if (e >= E) continue;
+        const float bv = bias ? bias[e] : 0.0f;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int t = t0 + tg + 32 * b;
+            if (t >= T) continue;
+            float l = acc[b][a];
+            if (bias) l = l + bv;
+            logits[(size_t)t * E + e] = l;
+        }
+    }
+}
+
 // Maximum over the wavefront, in every lane: an inclusive max-scan with DPP
 // row shifts (1, 2, 4, 8 lanes inside each row of 16) and row broadcasts
 // (lane 15 into rows 1 and 3, lane 31 into rows 2 and 3) leaves the maximum in
@@ -526,6 +693,9 @@ static hipError_t launch_scores_t(const void* x, const void* w, const float* bia
     if (vec && many)
         route_scores_kernel<XT, true, 64><<<grid, 256, 0, st>>>((const XT*)x, (const XT*)w, bias,
                                                                 T, d, E, logits);
+    else if (vec && d >= 4)
+        route_scores_pc_kernel<XT><<<grid, 512, 0, st>>>((const XT*)x, (const XT*)w, bias, T, d, E,
+                                                         logits);
     else if (vec)
         route_scores_kernel<XT, true, 128><<<grid, 256, 0, st>>>((const XT*)x, (const XT*)w, bias,
                                                                  T, d, E, logits);
