@@ -247,12 +247,12 @@ __global__ __launch_bounds__(256) void route_scores_kernel(
 // and order as route_scores_kernel, the last four only stage: global loads
 // of chunk c + 2, conversion to fp32, the LDS writes of chunk c + 1 while
 // chunk c is consumed. One barrier per chunk.
-template <typename XT>
+template <typename XT, int KRD>
 __global__ __launch_bounds__(512) void route_scores_pc_kernel(
     const XT* __restrict__ x, const XT* __restrict__ w, const float* __restrict__ bias,
     int T, int d, int E, float* __restrict__ logits)
 {
-    constexpr int kRD = 128;                        // d-chunk
+    constexpr int kRD = KRD;                        // d-chunk
     constexpr int kRS = kRD + 4;                    // x tile row stride (floats)
     constexpr int kXU = kRT * kRD / 1024;           // x groups of 4 per staging thread per chunk
     constexpr int kWU = kRD * kRE / 1024;           // W_r groups of 4 per staging thread per chunk
@@ -690,12 +690,12 @@ static hipError_t launch_scores_t(const void* x, const void* w, const float* bia
                      (uintptr_t)w % (4 * sizeof(XT)) == 0;
     // many more blocks than compute units: the narrower chunk (three blocks per CU)
     const bool many = (long long)grid.x * grid.y >= 2LL * 256;
-    if (vec && many)
-        route_scores_kernel<XT, true, 64><<<grid, 256, 0, st>>>((const XT*)x, (const XT*)w, bias,
-                                                                T, d, E, logits);
+    if (vec && many && d >= 4)
+        route_scores_pc_kernel<XT, 64><<<grid, 512, 0, st>>>((const XT*)x, (const XT*)w, bias, T, d,
+                                                             E, logits);
     else if (vec && d >= 4)
-        route_scores_pc_kernel<XT><<<grid, 512, 0, st>>>((const XT*)x, (const XT*)w, bias, T, d, E,
-                                                         logits);
+        route_scores_pc_kernel<XT, 128><<<grid, 512, 0, st>>>((const XT*)x, (const XT*)w, bias, T,
+                                                              d, E, logits);
     else if (vec)
         route_scores_kernel<XT, true, 128><<<grid, 256, 0, st>>>((const XT*)x, (const XT*)w, bias,
                                                                  T, d, E, logits);
