@@ -8,10 +8,12 @@
 // Scores are fixed bit for bit: an fp32 sum in index order, one fused
 // multiply-add per term from +0, then one fp32 bias add. That makes the work
 // T*E independent chains of d dependent FMAs on the vector ALUs (a matrix
-// core would sum in its own order). route_scores_kernel tiles the [T,E]
-// score matrix 64 tokens x 32 experts per block; each thread runs the chains
-// of 2 tokens x 4 experts side by side, reading x and W_r from LDS (staged
-// in 128-wide d-chunks, double-buffered, loaded into registers ahead). Zero
+// core would sum in its own order). route_scores_pc_kernel tiles the [T,E]
+// score matrix 64 tokens x 32 experts per block; each of four wavefronts'
+// threads runs the chains of 2 tokens x 4 experts side by side, reading x and
+// W_r from LDS (d-chunks double-buffered in LDS), while four more wavefronts
+// stage the chunks. route_scores_kernel_any does the same without the
+// staging wavefronts for shapes and pointers vector loads do not fit. Zero
 // padding of a chunk past d adds +-0 to a sum that is never -0, so no bit
 // changes. route_topk_kernel then gives each
 // token one wavefront: its E <= 1024 scores spread over the 64 lanes, k
@@ -28,30 +30,19 @@ constexpr int kRT = 64;       // tokens per block
 constexpr int kRE = 32;       // experts per block
 constexpr int kRG = 8;        // steps per register group
 
-// VEC: d % 4 == 0, E % 4 == 0 and aligned pointers (4-element vector loads).
-// Block: 64 tokens x 32 experts; thread (eg, tg) = (tid % 8, tid / 8) owns
-// experts 4eg..4eg+3 and tokens tg, tg+32: eight FMA chains. x is staged
-// [token][i] (rows padded to 132 floats: the 8 token rows a wavefront reads
-// at once fall in distinct banks) and W_r as it is laid out, [i][expert], so
-// one 16-byte LDS read gives four steps of a token or one step of four
-// experts, and the staging writes are plain 16-byte stores.
-//
-// Pipeline: chunk c + 3 is loaded into registers while chunk c + 1 is written
-// to the second LDS buffer and chunk c is consumed from the first (one
-// barrier per chunk). Inside a chunk the LDS reads of the next 8 steps are
-// issued before the 64 FMAs of the current 8 (scheduling barriers keep that
-// order), so one wavefront per SIMD keeps its ALU fed.
-//
-// KRD is the d-chunk: 128 (100 KB of LDS, one block per CU) when the grid
-// has about one block per CU anyway; 64 (50 KB, three blocks per CU, so a
-// CU runs other blocks' FMAs through one block's staging and barriers) when
-// there are many more blocks than CUs.
-template <typename XT, bool VEC, int KRD>
-__global__ __launch_bounds__(256) void route_scores_kernel(
-    const XT* __restrict__ x, const XT* __restrict__ w, const float* __restrict__ bias,
-    int T, int d, int E, float* __restrict__ logits)
+// Any d, E and alignment (element loads). Block: 64 tokens x 32 experts;
+// thread (eg, tg) = (tid % 8, tid / 8) owns experts 4eg..4eg+3 and tokens tg,
+// tg+32: eight FMA chains. x is staged [token][i] (rows padded to 132 floats:
+// the 8 token rows a wavefront reads at once fall in distinct banks) and W_r
+// as it is laid out, [i][expert], so one 16-byte LDS read gives four steps of
+// a token or one step of four experts. d is walked in chunks of 128, double-
+// buffered in LDS with one barrier per chunk; inside a chunk the LDS reads of
+// the next 8 steps are issued before the 64 FMAs of the current 8.
+__global__ __launch_bounds__(256) void route_scores_kernel_any(
+    const void* __restrict__ xv, const void* __restrict__ wv, bool bf16,
+    const float* __restrict__ bias, int T, int d, int E, float* __restrict__ logits)
 {
-    constexpr int kRD = KRD;                        // d-chunk
+    constexpr int kRD = 128;                        // d-chunk
     constexpr int kRS = kRD + 4;                    // x tile row stride (floats)
     constexpr int kXU = kRT * kRD / 1024;           // x groups of 4 per thread per chunk
     constexpr int kWU = kRD * kRE / 1024;           // W_r groups of 4 per thread per chunk
@@ -64,82 +55,33 @@ __global__ __launch_bounds__(256) void route_scores_kernel(
     const int t0 = blockIdx.x * kRT;
     const int e0 = blockIdx.y * kRE;
     const int nchunks = (d + kRD - 1) / kRD;
-
-    // staging: x 64 tokens x 128 values (8 groups of 4 per thread) and W_r
-    // 128 rows x 32 experts (4 groups of 4 per thread). The vector path loads raw
-    // bits from clamped (always valid) addresses with no branch and converts /
-    // zeroes out-of-range groups when writing to LDS.
-    using Raw = typename std::conditional<sizeof(XT) == 2, u32x2, f32x4>::type;
-    struct Chunk {
-        Raw x[kXU], w[kWU];
-        bool xin[kXU], win[kWU];
+    auto ld = [&](const void* p, size_t i) {
+        return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
     };
-    Chunk ch[2];
-    float xr[kXU][4], wr[kWU][4];
-    auto load_chunk = [&](int c, Chunk& cr) {
+
+    // staging of chunk c into LDS buffer c % 2 (zeros past T, d and E)
+    auto stage = [&](int c) {
         const int i0 = c * kRD;
+        float* xs = smem + (c & 1) * kRBuf;
+        float* ws = xs + kRT * kRS;
 #pragma unroll
         for (int u = 0; u < kXU; ++u) {
             const int gq = tid + 256 * u;
             const int tl = gq / (kRD / 4), i4 = (gq % (kRD / 4)) * 4;
             const int t = t0 + tl, i = i0 + i4;
-            if (VEC) {
-                cr.xin[u] = t < T && i < d;
-                cr.x[u] = *reinterpret_cast<const Raw*>(x + (size_t)min(t, T - 1) * d + min(i, d - 4));
-            } else {
+            f32x4 v;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    xr[u][q] = (t < T && i + q < d) ? Elem<XT>::load(x, (size_t)t * d + i + q) : 0.0f;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kWU; ++u) {
-            const int gq = tid + 256 * u;
-            const int il = gq >> 3, e4 = (gq & 7) * 4;
-            const int i = i0 + il, e = e0 + e4;
-            if (VEC) {
-                cr.win[u] = i < d && e < E;
-                cr.w[u] = *reinterpret_cast<const Raw*>(w + (size_t)min(i, d - 1) * E + min(e, E - 4));
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    wr[u][q] = (i < d && e + q < E) ? Elem<XT>::load(w, (size_t)i * E + e + q) : 0.0f;
-            }
-        }
-    };
-    auto unpack = [&](const Raw& r, bool in, float (&v)[4]) {
-        if constexpr (sizeof(XT) == 2) {
-            v[0] = __uint_as_float(r[0] << 16);
-            v[1] = __uint_as_float(r[0] & 0xffff0000u);
-            v[2] = __uint_as_float(r[1] << 16);
-            v[3] = __uint_as_float(r[1] & 0xffff0000u);
-        } else {
-            v[0] = r[0]; v[1] = r[1]; v[2] = r[2]; v[3] = r[3];
-        }
-        if (!in) v[0] = v[1] = v[2] = v[3] = 0.0f;
-    };
-    auto store_chunk = [&](int c, const Chunk& cr) {
-        if (!VEC) load_chunk(c, ch[0]);
-        float* xs = smem + (c & 1) * kRBuf;
-        float* ws = xs + kRT * kRS;
-        if (VEC) {
-#pragma unroll
-            for (int u = 0; u < kXU; ++u) unpack(cr.x[u], cr.xin[u], xr[u]);
-#pragma unroll
-            for (int u = 0; u < kWU; ++u) unpack(cr.w[u], cr.win[u], wr[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < kXU; ++u) {
-            const int gq = tid + 256 * u;
-            const int tl = gq / (kRD / 4), i4 = (gq % (kRD / 4)) * 4;
-            f32x4 v = {xr[u][0], xr[u][1], xr[u][2], xr[u][3]};
+            for (int q = 0; q < 4; ++q) v[q] = (t < T && i + q < d) ? ld(xv, (size_t)t * d + i + q) : 0.0f;
             *reinterpret_cast<f32x4*>(&xs[tl * kRS + i4]) = v;
         }
 #pragma unroll
         for (int u = 0; u < kWU; ++u) {
             const int gq = tid + 256 * u;
             const int il = gq >> 3, e4 = (gq & 7) * 4;
-            f32x4 v = {wr[u][0], wr[u][1], wr[u][2], wr[u][3]};
+            const int i = i0 + il, e = e0 + e4;
+            f32x4 v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = (i < d && e + q < E) ? ld(wv, (size_t)i * E + e + q) : 0.0f;
             *reinterpret_cast<f32x4*>(&ws[il * kRE + e4]) = v;
         }
     };
@@ -174,56 +116,22 @@ __global__ __launch_bounds__(256) void route_scores_kernel(
                 for (int a = 0; a < 4; ++a)
                     acc[b][a] = __builtin_fmaf(g.x[b][q >> 2][q & 3], g.w[q][a], acc[b][a]);
     };
-    auto compute_chunk = [&](int c) {
+
+    stage(0);
+    lds_barrier();
+    for (int c = 0; c < nchunks; ++c) {
+        if (c + 1 < nchunks) stage(c + 1);
         const float* xs = smem + (c & 1) * kRBuf;
         const float* ws = xs + kRT * kRS;
-        Group g[2];
-        if ((c + 1) * kRD <= d) {
-            // full chunk: 8 groups, reads one group ahead
-            read_group(xs, ws, 0, g[0]);
-#pragma unroll
-            for (int j = 0; j < kRD / kRG; ++j) {
-                if (j + 1 < kRD / kRG) read_group(xs, ws, (j + 1) * kRG, g[(j + 1) & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-                fma_group(g[j & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        } else {
-            // last, partial chunk: groups up to d rounded up to 8 (the tile
-            // holds zeros past d)
-            const int n = (d - c * kRD + kRG - 1) / kRG;
-            for (int j = 0; j < n; ++j) {
-                read_group(xs, ws, j * kRG, g[0]);
-                fma_group(g[0]);
-            }
+        // groups up to d rounded up to 8 (the tile holds zeros past d)
+        const int n = min(kRD, d - c * kRD + kRG - 1) / kRG;
+        Group g;
+        for (int j = 0; j < n; ++j) {
+            read_group(xs, ws, j * kRG, g);
+            fma_group(g);
         }
-    };
-
-    if (VEC) {
-        load_chunk(0, ch[0]);
-        load_chunk(1, ch[1]);
-    }
-    store_chunk(0, ch[0]);
-    if (VEC) load_chunk(2, ch[0]);
-    lds_barrier();
-    // chunk c: store c + 1 (register set (c + 1) % 2), load c + 3 into the
-    // same set, consume c, barrier. Unrolled by two so the sets are fixed and
-    // with no exit in between (an exit there would merge into the loop head
-    // and make the compiler wait for every load in flight). Loads and stores
-    // are unconditional: past the last chunk the loads read clamped, valid
-    // addresses and the zeros stored go to a buffer nobody reads.
-    int c = 0;
-    for (; c + 1 < nchunks; c += 2) {
-        store_chunk(c + 1, ch[1]);
-        if (VEC) load_chunk(c + 3, ch[1]);
-        compute_chunk(c);
-        lds_barrier();
-        store_chunk(c + 2, ch[0]);
-        if (VEC) load_chunk(c + 4, ch[0]);
-        compute_chunk(c + 1);
         lds_barrier();
     }
-    if (c < nchunks) compute_chunk(c);  // odd count: the last chunk is already stored
 
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -241,12 +149,13 @@ __global__ __launch_bounds__(256) void route_scores_kernel(
     }
 }
 
-// Producer/consumer variant of route_scores_kernel for grids of about one
-// block per CU (where no second block hides one block's staging): eight
+// 4-element vector loads (d % 4 == 0, E % 4 == 0, aligned pointers): eight
 // wavefronts, the first four run the FMA chains with the same thread mapping
-// and order as route_scores_kernel, the last four only stage: global loads
-// of chunk c + 2, conversion to fp32, the LDS writes of chunk c + 1 while
-// chunk c is consumed. One barrier per chunk.
+// and order as route_scores_kernel_any, the last four only stage: global
+// loads of chunk c + 2, conversion to fp32, the LDS writes of chunk c + 1
+// while chunk c is consumed. One barrier per chunk. KRD is the d-chunk: 128
+// (100 KB of LDS, one block per CU) when the grid has about one block per CU;
+// 64 (50 KB, more blocks per CU) when there are many more blocks than CUs.
 template <typename XT, int KRD>
 __global__ __launch_bounds__(512) void route_scores_pc_kernel(
     const XT* __restrict__ x, const XT* __restrict__ w, const float* __restrict__ bias,
@@ -688,20 +597,16 @@ static hipError_t launch_scores_t(const void* x, const void* w, const float* bia
     const dim3 grid((T + kRT - 1) / kRT, (E + kRE - 1) / kRE);
     const bool vec = d % 4 == 0 && E % 4 == 0 && (uintptr_t)x % (4 * sizeof(XT)) == 0 &&
                      (uintptr_t)w % (4 * sizeof(XT)) == 0;
-    // many more blocks than compute units: the narrower chunk (three blocks per CU)
+    // many more blocks than compute units: the narrower chunk (more blocks per CU)
     const bool many = (long long)grid.x * grid.y >= 2LL * 256;
-    if (vec && many && d >= 4)
+    if (vec && many)
         route_scores_pc_kernel<XT, 64><<<grid, 512, 0, st>>>((const XT*)x, (const XT*)w, bias, T, d,
                                                              E, logits);
-    else if (vec && d >= 4)
+    else if (vec)
         route_scores_pc_kernel<XT, 128><<<grid, 512, 0, st>>>((const XT*)x, (const XT*)w, bias, T,
                                                               d, E, logits);
-    else if (vec)
-        route_scores_kernel<XT, true, 128><<<grid, 256, 0, st>>>((const XT*)x, (const XT*)w, bias,
-                                                                 T, d, E, logits);
     else
-        route_scores_kernel<XT, false, 128><<<grid, 256, 0, st>>>((const XT*)x, (const XT*)w,
-                                                                  bias, T, d, E, logits);
+        route_scores_kernel_any<<<grid, 256, 0, st>>>(x, w, sizeof(XT) == 2, bias, T, d, E, logits);
     return hipGetLastError();
 }
 
