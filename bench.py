@@ -284,7 +284,7 @@ def main_backward(args):
         offsets=torch.empty(E + 1, dtype=torch.int32, device=cuda),
         perm_src=torch.empty(rows, dtype=torch.int32, device=cuda),
         dest=torch.empty(rows, dtype=torch.int32, device=cuda),
-        x_perm=torch.empty((rows, d), dtype=bf, device=cuda),
+        x_perm=ops.empty_rows(rows, d, bf, cuda),
         h=torch.empty((rows, f), dtype=bf, device=cuda),
         act=torch.empty((rows, 2 * f), dtype=bf, device=cuda),
         y=torch.empty((rows, d), dtype=f32, device=cuda),
@@ -435,7 +435,7 @@ def main():
         offsets=torch.empty(E + 1, dtype=torch.int32, device=cuda),
         perm_src=torch.empty(rows, dtype=torch.int32, device=cuda),
         dest=torch.empty(rows, dtype=torch.int32, device=cuda),
-        x_perm=torch.empty((rows, d), dtype=xdt, device=cuda),
+        x_perm=ops.empty_rows(rows, d, xdt, cuda),   # the padded packed-row stride
     )
     h = torch.empty((rows, f), dtype=xdt, device=cuda)
     ys = 2 if (args.y_dtype == "bf16" and es == 2) else 4

@@ -13,11 +13,11 @@ size_t permute_ws_bytes(int T, int k, int E);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int e_base, int E, int cap,
                           const void* x, int es, int d, int32_t* routed,
                           int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* dest,
-                          void* x_perm, void* ws, hipStream_t st);
+                          void* x_perm, int ld, void* ws, hipStream_t st);
 hipError_t launch_permute_recv(const int32_t* recv, int S, int E, int N, const void* x, int es,
                                int d, int32_t* counts, int32_t* offsets, int32_t* perm_src,
-                               int32_t* dest, void* x_perm, hipStream_t st);
-hipError_t launch_gate_up(const void* x, moe_dtype dt, int N, int d, int f, int E,
+                               int32_t* dest, void* x_perm, int ld, hipStream_t st);
+hipError_t launch_gate_up(const void* x, int ldx, moe_dtype dt, int N, int d, int f, int E,
                           const int32_t* offsets, const void* wg, const void* wv, void* h,
                           void* act, hipStream_t st);
 hipError_t launch_down(const void* h, moe_dtype dt, int N, int f, int d, int E,
@@ -58,6 +58,13 @@ constexpr int kMaxFfnE = 4096;
 constexpr int kMaxRecvCells = 4096;
 
 bool valid_dtype(moe_dtype t) { return t == MOE_F32 || t == MOE_BF16; }
+
+// Row stride of a packed-row buffer: 0 selects dense rows (d); anything
+// below d is rejected (returns -1).
+int resolve_ld(int ld, int d) {
+    if (ld == 0) return d;
+    return ld >= d ? ld : -1;
+}
 int elem_size(moe_dtype t) { return t == MOE_BF16 ? 2 : 4; }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
@@ -83,7 +90,14 @@ const char* moe_status_string(moe_status s) {
     return "unknown status";
 }
 
-int moe_version(void) { return 100; }
+int moe_version(void) { return 101; }
+
+int moe_x_perm_ld(int d, moe_dtype dt) {
+    if (d <= 0 || !valid_dtype(dt)) return 0;
+    // one 128-byte line past the row: rows of a power-of-two byte length
+    // would otherwise start on the same memory channel
+    return d + 128 / (int)elem_size(dt);
+}
 
 moe_status moe_route(const void* x, moe_dtype dt, const void* w_router, const float* bias,
                      int T, int d, int E, int k, int renorm, float* logits, int32_t* topk_idx,
@@ -107,49 +121,56 @@ size_t moe_permute_workspace(int T, int k, int E) {
 
 moe_status moe_permute(const int32_t* topk_idx, int T, int k, int E, const void* x,
                        moe_dtype dt, int d, int32_t* counts, int32_t* offsets, int32_t* perm_src,
-                       int32_t* dest, void* x_perm, void* ws, size_t ws_bytes, void* stream)
+                       int32_t* dest, void* x_perm, int ld_x_perm, void* ws, size_t ws_bytes,
+                       void* stream)
 {
     if (!valid_dtype(dt) || T < 0 || k <= 0 || E <= 0 || d <= 0) return MOE_ERR_INVALID_ARG;
+    const int ld = resolve_ld(ld_x_perm, d);
+    if (ld < 0) return MOE_ERR_INVALID_ARG;
     if (E > kMaxRouteE || k > kMaxK || (long long)T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
     if (T > 0 && (!topk_idx || !x || !perm_src || !dest || !x_perm)) return MOE_ERR_INVALID_ARG;
     if (!ws || ws_bytes < moe::permute_ws_bytes(T, k, E)) return MOE_ERR_WORKSPACE;
     return hip_status(moe::launch_permute(topk_idx, T, k, 0, E, INT32_MAX, x, elem_size(dt), d,
-                                          nullptr, counts, offsets, perm_src, dest, x_perm, ws,
-                                          as_stream(stream)));
+                                          nullptr, counts, offsets, perm_src, dest, x_perm, ld,
+                                          ws, as_stream(stream)));
 }
 
 moe_status moe_permute_capacity(const int32_t* topk_idx, int T, int k, int E, int capacity,
                                 const void* x, moe_dtype dt, int d, int32_t* routed,
                                 int32_t* counts, int32_t* offsets, int32_t* perm_src,
-                                int32_t* dest, void* x_perm, void* ws, size_t ws_bytes,
-                                void* stream)
+                                int32_t* dest, void* x_perm, int ld_x_perm, void* ws,
+                                size_t ws_bytes, void* stream)
 {
     if (!valid_dtype(dt) || T < 0 || k <= 0 || E <= 0 || d <= 0 || capacity < 0)
         return MOE_ERR_INVALID_ARG;
+    const int ld = resolve_ld(ld_x_perm, d);
+    if (ld < 0) return MOE_ERR_INVALID_ARG;
     if (E > kMaxRouteE || k > kMaxK || (long long)T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
     if (T > 0 && (!topk_idx || !x || !perm_src || !dest || !x_perm)) return MOE_ERR_INVALID_ARG;
     if (!ws || ws_bytes < moe::permute_ws_bytes(T, k, E)) return MOE_ERR_WORKSPACE;
     return hip_status(moe::launch_permute(topk_idx, T, k, 0, E, capacity, x, elem_size(dt), d,
-                                          routed, counts, offsets, perm_src, dest, x_perm, ws,
-                                          as_stream(stream)));
+                                          routed, counts, offsets, perm_src, dest, x_perm, ld,
+                                          ws, as_stream(stream)));
 }
 
 moe_status moe_permute_range(const int32_t* topk_idx, int T, int k, int e_first, int E_loc,
                              const void* x, moe_dtype dt, int d, int32_t* counts,
                              int32_t* offsets, int32_t* perm_src, int32_t* dest, void* x_perm,
-                             void* ws, size_t ws_bytes, void* stream)
+                             int ld_x_perm, void* ws, size_t ws_bytes, void* stream)
 {
     if (!valid_dtype(dt) || T < 0 || k <= 0 || E_loc <= 0 || e_first < 0 || d <= 0)
         return MOE_ERR_INVALID_ARG;
+    const int ld = resolve_ld(ld_x_perm, d);
+    if (ld < 0) return MOE_ERR_INVALID_ARG;
     if (E_loc > kMaxRouteE || k > kMaxK || (long long)T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
     if (T > 0 && (!topk_idx || !x || !perm_src || !dest || !x_perm)) return MOE_ERR_INVALID_ARG;
     if (!ws || ws_bytes < moe::permute_ws_bytes(T, k, E_loc)) return MOE_ERR_WORKSPACE;
     return hip_status(moe::launch_permute(topk_idx, T, k, e_first, E_loc, INT32_MAX, x,
                                           elem_size(dt), d, nullptr, counts, offsets, perm_src,
-                                          dest, x_perm, ws, as_stream(stream)));
+                                          dest, x_perm, ld, ws, as_stream(stream)));
 }
 
 size_t moe_permute_recv_workspace(int S, int E_loc, int N) {
@@ -160,15 +181,17 @@ size_t moe_permute_recv_workspace(int S, int E_loc, int N) {
 moe_status moe_permute_recv(const int32_t* recv_counts, int S, int E_loc, int N,
                             const void* x_recv, moe_dtype dt, int d, int32_t* counts,
                             int32_t* offsets, int32_t* perm_src, int32_t* dest, void* x_perm,
-                            void* ws, size_t ws_bytes, void* stream)
+                            int ld_x_perm, void* ws, size_t ws_bytes, void* stream)
 {
     (void)ws; (void)ws_bytes;
     if (!valid_dtype(dt) || S <= 0 || E_loc <= 0 || N < 0 || d <= 0) return MOE_ERR_INVALID_ARG;
+    const int ld = resolve_ld(ld_x_perm, d);
+    if (ld < 0) return MOE_ERR_INVALID_ARG;
     if ((long long)S * E_loc > kMaxRecvCells || E_loc > kMaxRouteE) return MOE_ERR_UNSUPPORTED;
     if (!recv_counts || !counts || !offsets) return MOE_ERR_INVALID_ARG;
     if (N > 0 && (!x_recv || !perm_src || !dest || !x_perm)) return MOE_ERR_INVALID_ARG;
     return hip_status(moe::launch_permute_recv(recv_counts, S, E_loc, N, x_recv, elem_size(dt), d,
-                                               counts, offsets, perm_src, dest, x_perm,
+                                               counts, offsets, perm_src, dest, x_perm, ld,
                                                as_stream(stream)));
 }
 
@@ -186,15 +209,17 @@ static moe_status check_ffn(moe_dtype dt, int N, int d, int f, int E, const int3
     return MOE_OK;
 }
 
-moe_status moe_ffn_gate_up(const void* x_perm, moe_dtype dt, int N, int d, int f, int E,
-                           const int32_t* offsets, const void* w_gate, const void* w_val,
+moe_status moe_ffn_gate_up(const void* x_perm, int ld_x_perm, moe_dtype dt, int N, int d, int f,
+                           int E, const int32_t* offsets, const void* w_gate, const void* w_val,
                            void* h, void* stream)
 {
     moe_status s = check_ffn(dt, N, d, f, E, offsets);
     if (s != MOE_OK) return s;
+    const int ldx = resolve_ld(ld_x_perm, d);
+    if (ldx < 0) return MOE_ERR_INVALID_ARG;
     if (N == 0) return MOE_OK;
     if (!x_perm || !w_gate || !w_val || !h) return MOE_ERR_INVALID_ARG;
-    return hip_status(moe::launch_gate_up(x_perm, dt, N, d, f, E, offsets, w_gate, w_val, h,
+    return hip_status(moe::launch_gate_up(x_perm, ldx, dt, N, d, f, E, offsets, w_gate, w_val, h,
                                           nullptr, as_stream(stream)));
 }
 
@@ -211,19 +236,21 @@ moe_status moe_ffn_down(const void* h, moe_dtype dt, int N, int f, int d, int E,
                                        as_stream(stream)));
 }
 
-moe_status moe_grouped_ffn(const void* x_perm, moe_dtype dt, int N, int d, int f, int E,
-                           const int32_t* offsets, const void* w_gate, const void* w_val,
+moe_status moe_grouped_ffn(const void* x_perm, int ld_x_perm, moe_dtype dt, int N, int d, int f,
+                           int E, const int32_t* offsets, const void* w_gate, const void* w_val,
                            const void* w_out, void* y, moe_dtype y_dt, void* ws, size_t ws_bytes,
                            void* stream)
 {
     moe_status s = check_ffn(dt, N, d, f, E, offsets);
     if (s != MOE_OK) return s;
+    const int ldx = resolve_ld(ld_x_perm, d);
+    if (ldx < 0) return MOE_ERR_INVALID_ARG;
     if (!valid_dtype(y_dt)) return MOE_ERR_INVALID_ARG;
     if (N == 0) return MOE_OK;
     if (!x_perm || !w_gate || !w_val || !w_out || !y) return MOE_ERR_INVALID_ARG;
     if (!ws || ws_bytes < h_bytes(N, f, dt)) return MOE_ERR_WORKSPACE;
     hipStream_t st = as_stream(stream);
-    hipError_t e = moe::launch_gate_up(x_perm, dt, N, d, f, E, offsets, w_gate, w_val, ws,
+    hipError_t e = moe::launch_gate_up(x_perm, ldx, dt, N, d, f, E, offsets, w_gate, w_val, ws,
                                        nullptr, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
     return hip_status(moe::launch_down(ws, dt, N, f, d, E, offsets, w_out, y, y_dt, st));
@@ -264,16 +291,18 @@ moe_status moe_route_stats(const float* logits, const int32_t* counts, int T, in
 
 // ------------------------------------------------------------------ backward
 
-moe_status moe_ffn_gate_up_train(const void* x_perm, moe_dtype dt, int N, int d, int f, int E,
-                                 const int32_t* offsets, const void* w_gate, const void* w_val,
-                                 void* h, void* act, void* stream)
+moe_status moe_ffn_gate_up_train(const void* x_perm, int ld_x_perm, moe_dtype dt, int N, int d,
+                                 int f, int E, const int32_t* offsets, const void* w_gate,
+                                 const void* w_val, void* h, void* act, void* stream)
 {
     moe_status s = check_ffn(dt, N, d, f, E, offsets);
     if (s != MOE_OK) return s;
+    const int ldx = resolve_ld(ld_x_perm, d);
+    if (ldx < 0) return MOE_ERR_INVALID_ARG;
     if (N == 0) return MOE_OK;
     if (!x_perm || !w_gate || !w_val || !h || !act) return MOE_ERR_INVALID_ARG;
-    return hip_status(moe::launch_gate_up(x_perm, dt, N, d, f, E, offsets, w_gate, w_val, h, act,
-                                          as_stream(stream)));
+    return hip_status(moe::launch_gate_up(x_perm, ldx, dt, N, d, f, E, offsets, w_gate, w_val, h,
+                                          act, as_stream(stream)));
 }
 
 moe_status moe_combine_backward(const void* d_out, moe_dtype d_out_dt, const void* y_perm,
@@ -324,13 +353,15 @@ moe_status moe_ffn_gate_up_backward(const void* d_act, moe_dtype dt, int N, int 
                                      d_x_perm, nullptr, as_stream(stream)));
 }
 
-moe_status moe_ffn_weight_grads(const void* x_perm, const void* h, const void* d_y,
+moe_status moe_ffn_weight_grads(const void* x_perm, int ld_x_perm, const void* h, const void* d_y,
                                 const void* d_act, moe_dtype dt, int N, int d, int f, int E,
                                 const int32_t* offsets, float scale, float* d_w_gate,
                                 float* d_w_val, float* d_w_out, void* stream)
 {
     moe_status s = check_ffn(dt, N, d, f, E, offsets);
     if (s != MOE_OK) return s;
+    const int ldx = resolve_ld(ld_x_perm, d);
+    if (ldx < 0) return MOE_ERR_INVALID_ARG;
     if (!d_w_gate || !d_w_val || !d_w_out) return MOE_ERR_INVALID_ARG;
     if (N > 0 && (!x_perm || !h || !d_y || !d_act)) return MOE_ERR_INVALID_ARG;
     hipStream_t st = as_stream(stream);
@@ -339,7 +370,7 @@ moe_status moe_ffn_weight_grads(const void* x_perm, const void* h, const void* d
                                   nullptr, st, 0);
     if (e != hipSuccess) return MOE_ERR_HIP;
     // [dW_gate | dW_val][e] [d,f] = x_e^T . d_act_e[:, 0:f | f:2f]
-    return hip_status(moe::launch_tn(x_perm, d, d, d_act, 2 * f, f, f, dt, N, E, offsets, scale,
+    return hip_status(moe::launch_tn(x_perm, ldx, d, d_act, 2 * f, f, f, dt, N, E, offsets, scale,
                                      d_w_gate, d_w_val, st, 0));
 }
 

@@ -75,7 +75,7 @@ struct Stage {
     u32x4 b[kBChunks];
 };
 
-// Per-thread global sources of one tile. A: chunk q = tid + 256 i -> row
+// Per-thread global sources of one tile (A rows lda elements apart). A: chunk q = tid + 256 i -> row
 // tid/4 + 64 i, chunk tid%4 (4 lanes per 64-byte row); rows past the expert's
 // segment re-read its last row (never stored). B: chunk q = tid + 256 i ->
 // k-row tid/32 + 8 i, chunk tid%32 (32 lanes per 512-byte row; gate_up: 16
@@ -86,14 +86,14 @@ struct TileSrc {
     const uint16_t* a[kAChunks];
     const uint16_t* b;
 
-    __device__ __forceinline__ TileSrc(const uint16_t* A, int K, int NC, const uint16_t* B0,
-                                       const uint16_t* B1, const Tile& tile) {
+    __device__ __forceinline__ TileSrc(const uint16_t* A, int lda, int K, int NC,
+                                       const uint16_t* B0, const uint16_t* B1, const Tile& tile) {
         const int tid = threadIdx.x;
         const int seg_last = tile.seg_end - 1;
 #pragma unroll
         for (int i = 0; i < kAChunks; ++i) {
             const int r = (tid >> 2) + 64 * i;
-            a[i] = A + (size_t)min(tile.m0 + r, seg_last) * K + (tid & 3) * 8;
+            a[i] = A + (size_t)min(tile.m0 + r, seg_last) * lda + (tid & 3) * 8;
         }
         const size_t wbase = (size_t)tile.e * (size_t)K * (size_t)NC;
         const int c = tid & 31;
@@ -125,7 +125,7 @@ struct TileSrc {
 // v_mfma_f32_32x32x16_bf16 accumulators held in AGPRs.
 template <bool GATE_UP, bool Y_BF16, int TM, bool STREAM, bool SAVE>
 __device__ __forceinline__ void ffn_mfma_tile(
-    const uint16_t* __restrict__ A, int K, int NC, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ A, int lda, int K, int NC, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, void* __restrict__ C, uint16_t* __restrict__ act,
     const Tile& tile, uint16_t* smem)
 {
@@ -150,7 +150,7 @@ __device__ __forceinline__ void ffn_mfma_tile(
     const int m0 = tile.m0;
     const int seg_last = tile.seg_end - 1;
     const int n0 = tile.n_tile * BNT;
-    const TileSrc<GATE_UP, TM, STREAM> src(A, K, NC, B0, B1, tile);
+    const TileSrc<GATE_UP, TM, STREAM> src(A, lda, K, NC, B0, B1, tile);
 
     // LDS destinations of this thread's chunks: A + 64 i rows, B + 8 i k-rows
     // (the swizzle terms do not depend on i)
@@ -427,8 +427,8 @@ __device__ __forceinline__ void ffn_mfma_tile(
 // on one XCD and share its L2.
 template <bool GATE_UP, bool Y_BF16, bool SAVE>
 __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
-    const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int N, int K, int NC,
-    int E, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
+    const uint16_t* __restrict__ A, int lda, const int32_t* __restrict__ offsets, int N, int K,
+    int NC, int E, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
     void* __restrict__ C, uint16_t* __restrict__ act)
 {
     constexpr int BNT = GATE_UP ? 128 : 256;
@@ -443,11 +443,11 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
     for (int t = base; t < total; t += G) {
         const Tile tile = decode_tile(L, t);
         if (tile.bm == 128)
-            ffn_mfma_tile<GATE_UP, Y_BF16, 128, true, SAVE>(A, K, NC, B0, B1, C, act, tile, smem);
+            ffn_mfma_tile<GATE_UP, Y_BF16, 128, true, SAVE>(A, lda, K, NC, B0, B1, C, act, tile, smem);
         else if (tile.stream)
-            ffn_mfma_tile<GATE_UP, Y_BF16, 256, true, SAVE>(A, K, NC, B0, B1, C, act, tile, smem);
+            ffn_mfma_tile<GATE_UP, Y_BF16, 256, true, SAVE>(A, lda, K, NC, B0, B1, C, act, tile, smem);
         else
-            ffn_mfma_tile<GATE_UP, Y_BF16, 256, false, SAVE>(A, K, NC, B0, B1, C, act, tile, smem);
+            ffn_mfma_tile<GATE_UP, Y_BF16, 256, false, SAVE>(A, lda, K, NC, B0, B1, C, act, tile, smem);
     }
 }
 
@@ -457,8 +457,8 @@ constexpr int GBM = 64, GBN = 64, GBK = 16;
 
 template <typename XT, typename OT, bool GATE_UP>
 __global__ __launch_bounds__(256) void ffn_generic_kernel(
-    const XT* __restrict__ A, const int32_t* __restrict__ offsets, int N, int K, int NC, int E,
-    const XT* __restrict__ B0, const XT* __restrict__ B1, OT* __restrict__ C,
+    const XT* __restrict__ A, int lda, const int32_t* __restrict__ offsets, int N, int K, int NC,
+    int E, const XT* __restrict__ B0, const XT* __restrict__ B1, OT* __restrict__ C,
     OT* __restrict__ act)
 {
     __shared__ float sAg[GBM][GBK + 1];
@@ -488,7 +488,7 @@ __global__ __launch_bounds__(256) void ffn_generic_kernel(
             const int r = q / GBK, kk = q % GBK;
             const int row = min(m0 + r, seg_last);
             const int kx = k0 + kk;
-            sAg[r][kk] = kx < K ? Elem<XT>::load(A, (size_t)row * K + kx) : 0.f;
+            sAg[r][kk] = kx < K ? Elem<XT>::load(A, (size_t)row * lda + kx) : 0.f;
         }
         for (int q = tid; q < GBK * GBN; q += 256) {
             const int kk = q / GBN, c = q % GBN;
@@ -546,9 +546,10 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // (f, d < 2^20 keep a tile's byte offsets in the epilogue's buffer stores in
 // 31 bits)
-bool ffn_gate_up_uses_mfma(moe_dtype dt, int d, int f, const void* x, const void* wg,
+bool ffn_gate_up_uses_mfma(moe_dtype dt, int d, int ldx, int f, const void* x, const void* wg,
                            const void* wv, const void* h) {
-    return dt == MOE_BF16 && d % BK == 0 && f % 128 == 0 && f < (1 << 20) && aligned16(x) &&
+    return dt == MOE_BF16 && d % BK == 0 && ldx % 8 == 0 && f % 128 == 0 && f < (1 << 20) &&
+           aligned16(x) &&
            aligned16(wg) && aligned16(wv) && aligned16(h);
 }
 bool ffn_down_uses_mfma(moe_dtype dt, int f, int d, const void* h, const void* wo) {
@@ -561,29 +562,29 @@ static unsigned grid_for(long long tiles) {
     return (unsigned)std::max(8LL, g);
 }
 
-hipError_t launch_gate_up(const void* x, moe_dtype dt, int N, int d, int f, int E,
+hipError_t launch_gate_up(const void* x, int ldx, moe_dtype dt, int N, int d, int f, int E,
                           const int32_t* offsets, const void* wg, const void* wv, void* h,
                           void* act, hipStream_t st)
 {
-    if (ffn_gate_up_uses_mfma(dt, d, f, x, wg, wv, h) && aligned16(act)) {
+    if (ffn_gate_up_uses_mfma(dt, d, ldx, f, x, wg, wv, h) && aligned16(act)) {
         const unsigned g = mfma_grid(N, E, f / 128);
         if (act)
             ffn_mfma_kernel<true, false, true><<<g, kMfmaThreads, 0, st>>>(
-                (const uint16_t*)x, offsets, N, d, f, E, (const uint16_t*)wg, (const uint16_t*)wv,
-                h, (uint16_t*)act);
+                (const uint16_t*)x, ldx, offsets, N, d, f, E, (const uint16_t*)wg,
+                (const uint16_t*)wv, h, (uint16_t*)act);
         else
             ffn_mfma_kernel<true, false, false><<<g, kMfmaThreads, 0, st>>>(
-                (const uint16_t*)x, offsets, N, d, f, E, (const uint16_t*)wg, (const uint16_t*)wv,
-                h, nullptr);
+                (const uint16_t*)x, ldx, offsets, N, d, f, E, (const uint16_t*)wg,
+                (const uint16_t*)wv, h, nullptr);
     } else {
         const long long tiles = max_row_tiles(N, E, GBM) * ((f + GBN - 1) / GBN);
         if (dt == MOE_BF16)
             ffn_generic_kernel<uint16_t, uint16_t, true><<<grid_for(tiles), 256, 0, st>>>(
-                (const uint16_t*)x, offsets, N, d, f, E, (const uint16_t*)wg,
+                (const uint16_t*)x, ldx, offsets, N, d, f, E, (const uint16_t*)wg,
                 (const uint16_t*)wv, (uint16_t*)h, (uint16_t*)act);
         else
             ffn_generic_kernel<float, float, true><<<grid_for(tiles), 256, 0, st>>>(
-                (const float*)x, offsets, N, d, f, E, (const float*)wg, (const float*)wv,
+                (const float*)x, ldx, offsets, N, d, f, E, (const float*)wg, (const float*)wv,
                 (float*)h, (float*)act);
     }
     return hipGetLastError();
@@ -597,30 +598,32 @@ hipError_t launch_down(const void* h, moe_dtype dt, int N, int f, int d, int E,
         const unsigned grid = mfma_grid(N, E, d / 256);
         if (y_dt == MOE_BF16)
             ffn_mfma_kernel<false, true, false><<<grid, kMfmaThreads, 0, st>>>(
-                (const uint16_t*)h, offsets, N, f, d, E, (const uint16_t*)wo, nullptr, y, nullptr);
+                (const uint16_t*)h, f, offsets, N, f, d, E, (const uint16_t*)wo, nullptr, y,
+                nullptr);
         else
             ffn_mfma_kernel<false, false, false><<<grid, kMfmaThreads, 0, st>>>(
-                (const uint16_t*)h, offsets, N, f, d, E, (const uint16_t*)wo, nullptr, y, nullptr);
+                (const uint16_t*)h, f, offsets, N, f, d, E, (const uint16_t*)wo, nullptr, y,
+                nullptr);
     } else {
         const long long tiles = max_row_tiles(N, E, GBM) * ((d + GBN - 1) / GBN);
         const unsigned g = grid_for(tiles);
         if (dt == MOE_BF16) {
             if (y_dt == MOE_BF16)
                 ffn_generic_kernel<uint16_t, uint16_t, false><<<g, 256, 0, st>>>(
-                    (const uint16_t*)h, offsets, N, f, d, E, (const uint16_t*)wo, nullptr,
+                    (const uint16_t*)h, f, offsets, N, f, d, E, (const uint16_t*)wo, nullptr,
                     (uint16_t*)y, nullptr);
             else
                 ffn_generic_kernel<uint16_t, float, false><<<g, 256, 0, st>>>(
-                    (const uint16_t*)h, offsets, N, f, d, E, (const uint16_t*)wo, nullptr,
+                    (const uint16_t*)h, f, offsets, N, f, d, E, (const uint16_t*)wo, nullptr,
                     (float*)y, nullptr);
         } else {
             if (y_dt == MOE_BF16)
                 ffn_generic_kernel<float, uint16_t, false><<<g, 256, 0, st>>>(
-                    (const float*)h, offsets, N, f, d, E, (const float*)wo, nullptr, (uint16_t*)y,
+                    (const float*)h, f, offsets, N, f, d, E, (const float*)wo, nullptr, (uint16_t*)y,
                     nullptr);
             else
                 ffn_generic_kernel<float, float, false><<<g, 256, 0, st>>>(
-                    (const float*)h, offsets, N, f, d, E, (const float*)wo, nullptr, (float*)y,
+                    (const float*)h, f, offsets, N, f, d, E, (const float*)wo, nullptr, (float*)y,
                     nullptr);
         }
     }

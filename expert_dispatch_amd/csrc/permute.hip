@@ -168,11 +168,12 @@ __global__ __launch_bounds__(kPermThreads) void perm_rank_kernel(
     }
 }
 
-// x_perm[dest[t*k+s]] = x[t]: one wavefront per token, V-byte vectors.
+// x_perm[dest[t*k+s]] = x[t]: one wavefront per token, V-byte vectors;
+// packed rows are out_stride vectors apart.
 template <typename V>
 __global__ __launch_bounds__(256) void perm_gather_kernel(
     const V* __restrict__ x, int vecs_per_row, int T, int k, const int32_t* __restrict__ dest,
-    int rows_out, V* __restrict__ x_perm)
+    int rows_out, V* __restrict__ x_perm, int out_stride)
 {
     const int t = blockIdx.x * 4 + threadIdx.x / kWave;
     if (t >= T) return;
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(256) void perm_gather_kernel(
         for (int s = 0; s < k; ++s) {
             const int j = __shfl(my_dest, s, kWave);
             if ((unsigned)j >= (unsigned)rows_out) continue;
-            V* dst = x_perm + (size_t)j * vecs_per_row;
+            V* dst = x_perm + (size_t)j * out_stride;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int c = c0 + u * kWave + lane;
@@ -208,7 +209,8 @@ __global__ __launch_bounds__(256) void perm_recv_kernel(
     const int32_t* __restrict__ recv, int S, int E, int N,
     const V* __restrict__ x, int vecs_per_row,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm_src, int32_t* __restrict__ dest, V* __restrict__ x_perm)
+    int32_t* __restrict__ perm_src, int32_t* __restrict__ dest, V* __restrict__ x_perm,
+    int out_stride)
 {
     __shared__ int s_start[kRecvMaxCells];   // first received row of cell (i,j)
     __shared__ int s_dbase[kRecvMaxCells];   // first packed row of cell (i,j)
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(256) void perm_recv_kernel(
         }
         if (j < 0) continue;
         const V* src = x + (size_t)r * vecs_per_row;
-        V* dst = x_perm + (size_t)j * vecs_per_row;
+        V* dst = x_perm + (size_t)j * out_stride;
         // four vectors per lane in flight before their stores
         constexpr int U = 4;
         for (int c0 = lane; c0 < vecs_per_row; c0 += kWave * U) {
@@ -299,7 +301,7 @@ size_t permute_ws_bytes(int T, int k, int E) {
 hipError_t launch_permute(const int32_t* idx, int T, int k, int e_base, int E, int cap,
                           const void* x, int es, int d, int32_t* routed, int32_t* counts,
                           int32_t* offsets, int32_t* perm_src, int32_t* dest, void* x_perm,
-                          void* ws, hipStream_t st)
+                          int ld, void* ws, hipStream_t st)
 {
     const int TK = T * k;
     const int chunk = perm_chunk(TK);
@@ -318,31 +320,39 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int e_base, int E, i
     }
     if (T > 0) {
         const size_t row_bytes = (size_t)d * es;
+        const size_t ld_bytes = (size_t)ld * es;
         const dim3 grid((T + 3) / 4);
-        if (row_bytes % 16 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)x_perm % 16 == 0)
+        if (row_bytes % 16 == 0 && ld_bytes % 16 == 0 && (uintptr_t)x % 16 == 0 &&
+            (uintptr_t)x_perm % 16 == 0)
             perm_gather_kernel<u32x4><<<grid, 256, 0, st>>>(
-                (const u32x4*)x, (int)(row_bytes / 16), T, k, dest, TK, (u32x4*)x_perm);
+                (const u32x4*)x, (int)(row_bytes / 16), T, k, dest, TK, (u32x4*)x_perm,
+                (int)(ld_bytes / 16));
         else
             perm_gather_kernel<uint16_t><<<grid, 256, 0, st>>>(
-                (const uint16_t*)x, (int)(row_bytes / 2), T, k, dest, TK, (uint16_t*)x_perm);
+                (const uint16_t*)x, (int)(row_bytes / 2), T, k, dest, TK, (uint16_t*)x_perm,
+                (int)(ld_bytes / 2));
     }
     return hipGetLastError();
 }
 
 hipError_t launch_permute_recv(const int32_t* recv, int S, int E, int N, const void* x, int es,
                                int d, int32_t* counts, int32_t* offsets, int32_t* perm_src,
-                               int32_t* dest, void* x_perm, hipStream_t st)
+                               int32_t* dest, void* x_perm, int ld, hipStream_t st)
 {
     const int nblk = std::max(1, (N + kRecvRowsPerBlock - 1) / kRecvRowsPerBlock);
     const size_t row_bytes = (size_t)d * es;
-    if (row_bytes % 16 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)x_perm % 16 == 0)
+    const size_t ld_bytes = (size_t)ld * es;
+    if (row_bytes % 16 == 0 && ld_bytes % 16 == 0 && (uintptr_t)x % 16 == 0 &&
+        (uintptr_t)x_perm % 16 == 0)
         perm_recv_kernel<u32x4><<<nblk, 256, 0, st>>>(recv, S, E, N, (const u32x4*)x,
                                                       (int)(row_bytes / 16), counts, offsets,
-                                                      perm_src, dest, (u32x4*)x_perm);
+                                                      perm_src, dest, (u32x4*)x_perm,
+                                                      (int)(ld_bytes / 16));
     else
         perm_recv_kernel<uint16_t><<<nblk, 256, 0, st>>>(recv, S, E, N, (const uint16_t*)x,
                                                          (int)(row_bytes / 2), counts, offsets,
-                                                         perm_src, dest, (uint16_t*)x_perm);
+                                                         perm_src, dest, (uint16_t*)x_perm,
+                                                         (int)(ld_bytes / 2));
     return hipGetLastError();
 }
 

@@ -40,22 +40,25 @@ def lib():
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_status_string.argtypes = [i]
     L.moe_version.restype = i
+    L.moe_x_perm_ld.restype = i
+    L.moe_x_perm_ld.argtypes = [i, i]
     sigs = {
         "moe_route": [vp, i, vp, vp, i, i, i, i, i, vp, vp, vp, vp],
-        "moe_permute": [vp, i, i, i, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp],
-        "moe_permute_capacity": [vp, i, i, i, i, vp, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp],
-        "moe_permute_range": [vp, i, i, i, i, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp],
-        "moe_permute_recv": [vp, i, i, i, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp],
-        "moe_grouped_ffn": [vp, i, i, i, i, i, vp, vp, vp, vp, vp, i, vp, sz, vp],
-        "moe_ffn_gate_up": [vp, i, i, i, i, i, vp, vp, vp, vp, vp],
+        "moe_permute": [vp, i, i, i, vp, i, i, vp, vp, vp, vp, vp, i, vp, sz, vp],
+        "moe_permute_capacity": [vp, i, i, i, i, vp, i, i, vp, vp, vp, vp, vp, vp, i, vp, sz,
+                                 vp],
+        "moe_permute_range": [vp, i, i, i, i, vp, i, i, vp, vp, vp, vp, vp, i, vp, sz, vp],
+        "moe_permute_recv": [vp, i, i, i, vp, i, i, vp, vp, vp, vp, vp, i, vp, sz, vp],
+        "moe_grouped_ffn": [vp, i, i, i, i, i, i, vp, vp, vp, vp, vp, i, vp, sz, vp],
+        "moe_ffn_gate_up": [vp, i, i, i, i, i, i, vp, vp, vp, vp, vp],
         "moe_ffn_down": [vp, i, i, i, i, i, vp, vp, vp, i, vp],
         "moe_combine": [vp, i, vp, vp, i, i, i, vp, i, vp, i, vp],
-        "moe_ffn_gate_up_train": [vp, i, i, i, i, i, vp, vp, vp, vp, vp, vp],
+        "moe_ffn_gate_up_train": [vp, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp],
         "moe_combine_backward": [vp, i, vp, i, vp, vp, i, i, i, vp, i, vp, vp],
         "moe_ffn_down_backward": [vp, i, i, i, i, i, vp, vp, vp, vp, vp],
         "moe_ffn_gate_up_backward": [vp, i, i, i, i, i, vp, vp, vp, vp, i, i, vp],
-        "moe_ffn_weight_grads": [vp, vp, vp, vp, i, i, i, i, i, vp, ctypes.c_float, vp, vp, vp,
-                                 vp],
+        "moe_ffn_weight_grads": [vp, i, vp, vp, vp, i, i, i, i, i, vp, ctypes.c_float, vp, vp,
+                                 vp, vp],
         "moe_route_backward": [vp, vp, vp, vp, i, i, i, i, vp, vp, vp],
         "moe_router_backward": [vp, vp, i, vp, i, i, i, vp, i, vp, vp, sz, vp],
         "moe_route_stats": [vp, vp, i, i, i, vp, vp, vp, sz, vp],
@@ -102,6 +105,27 @@ def _p(t):
 def _dev(t: torch.Tensor, name: str):
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    """Row stride (elements) of a 2-D device tensor whose rows are contiguous
+    (packed rows may sit in a wider buffer: x_perm = buf[:, :d])."""
+    if not t.is_cuda or t.dim() != 2 or (t.stride(1) != 1 and t.shape[1] > 1) \
+            or t.stride(0) < t.shape[1]:
+        raise ValueError(f"{name} must be a 2-D device tensor with contiguous rows")
+    return int(t.stride(0))
+
+
+def x_perm_ld(d: int, dtype) -> int:
+    """The library's recommended row stride for packed rows of width d."""
+    return int(lib().moe_x_perm_ld(d, _dt_of(dtype)))
+
+
+def empty_rows(rows: int, d: int, dtype, device) -> torch.Tensor:
+    """[rows, d] view of a [rows, x_perm_ld(d)] buffer: packed rows laid out
+    with the recommended padded stride."""
+    ld = x_perm_ld(d, dtype)
+    return torch.empty((rows, ld), dtype=dtype, device=device)[:, :d]
 
 
 def _stream(stream=None):
@@ -168,27 +192,28 @@ def permute(topk_idx, x, E: int, *, capacity=None, e_first=None, out=None, works
                    offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
                    perm_src=torch.empty(T * k, dtype=torch.int32, device=dev),
                    dest=torch.empty(T * k, dtype=torch.int32, device=dev),
-                   x_perm=torch.empty((T * k, d), dtype=x.dtype, device=dev))
+                   x_perm=empty_rows(T * k, d, x.dtype, dev))
         if capacity is not None:
             out["routed"] = torch.empty(E, dtype=torch.int32, device=dev)
+    ldx = _rows(out["x_perm"], "x_perm")
     nbytes = permute_workspace(T, k, E)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     if e_first is not None:
         _check("moe_permute_range", lib().moe_permute_range(
             _p(topk_idx), T, k, int(e_first), E, _p(x), _dt(x), d, _p(out["counts"]),
-            _p(out["offsets"]), _p(out["perm_src"]), _p(out["dest"]), _p(out["x_perm"]),
+            _p(out["offsets"]), _p(out["perm_src"]), _p(out["dest"]), _p(out["x_perm"]), ldx,
             _p(workspace), workspace.numel(), _stream(stream)))
     elif capacity is None:
         _check("moe_permute", lib().moe_permute(
             _p(topk_idx), T, k, E, _p(x), _dt(x), d, _p(out["counts"]), _p(out["offsets"]),
-            _p(out["perm_src"]), _p(out["dest"]), _p(out["x_perm"]), _p(workspace),
+            _p(out["perm_src"]), _p(out["dest"]), _p(out["x_perm"]), ldx, _p(workspace),
             workspace.numel(), _stream(stream)))
     else:
         _check("moe_permute_capacity", lib().moe_permute_capacity(
             _p(topk_idx), T, k, E, int(capacity), _p(x), _dt(x), d, _p(out.get("routed")),
             _p(out["counts"]), _p(out["offsets"]), _p(out["perm_src"]), _p(out["dest"]),
-            _p(out["x_perm"]), _p(workspace), workspace.numel(), _stream(stream)))
+            _p(out["x_perm"]), ldx, _p(workspace), workspace.numel(), _stream(stream)))
     return out
 
 
@@ -203,11 +228,12 @@ def permute_recv(recv_counts, x_recv, *, out=None, stream=None):
                    offsets=torch.empty(E_loc + 1, dtype=torch.int32, device=dev),
                    perm_src=torch.empty(N, dtype=torch.int32, device=dev),
                    dest=torch.empty(N, dtype=torch.int32, device=dev),
-                   x_perm=torch.empty((N, d), dtype=x_recv.dtype, device=dev))
+                   x_perm=empty_rows(N, d, x_recv.dtype, dev))
+    ldx = _rows(out["x_perm"], "x_perm")
     _check("moe_permute_recv", lib().moe_permute_recv(
         _p(recv_counts), S, E_loc, N, _p(x_recv), _dt(x_recv), d, _p(out["counts"]),
-        _p(out["offsets"]), _p(out["perm_src"]), _p(out["dest"]), _p(out["x_perm"]), None, 0,
-        _stream(stream)))
+        _p(out["offsets"]), _p(out["perm_src"]), _p(out["dest"]), _p(out["x_perm"]), ldx, None,
+        0, _stream(stream)))
     return out
 
 
@@ -218,9 +244,9 @@ def grouped_ffn_workspace(N: int, d: int, f: int, E: int, dtype) -> int:
 def grouped_ffn(x_perm, offsets, w_gate, w_val, w_out, *, y_dtype=torch.float32, y=None,
                 workspace=None, stream=None):
     """y[j] = (silu(x_perm[j] W_gate[e]) * (x_perm[j] W_val[e])) W_out[e] per expert segment."""
-    for t, n in ((x_perm, "x_perm"), (offsets, "offsets"), (w_gate, "w_gate"),
-                 (w_val, "w_val"), (w_out, "w_out")):
+    for t, n in ((offsets, "offsets"), (w_gate, "w_gate"), (w_val, "w_val"), (w_out, "w_out")):
         _dev(t, n)
+    ldx = _rows(x_perm, "x_perm")
     N, d = x_perm.shape
     E, _, f = w_gate.shape
     if y is None:
@@ -229,21 +255,22 @@ def grouped_ffn(x_perm, offsets, w_gate, w_val, w_out, *, y_dtype=torch.float32,
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x_perm.device)
     _check("moe_grouped_ffn", lib().moe_grouped_ffn(
-        _p(x_perm), _dt(x_perm), N, d, f, E, _p(offsets), _p(w_gate), _p(w_val), _p(w_out),
+        _p(x_perm), ldx, _dt(x_perm), N, d, f, E, _p(offsets), _p(w_gate), _p(w_val), _p(w_out),
         _p(y), _dt(y), _p(workspace), workspace.numel(), _stream(stream)))
     return y
 
 
 def ffn_gate_up(x_perm, offsets, w_gate, w_val, *, h=None, stream=None):
     """h = silu(x_perm W_gate[e]) * (x_perm W_val[e]) per expert segment."""
-    for t, n in ((x_perm, "x_perm"), (offsets, "offsets"), (w_gate, "w_gate"), (w_val, "w_val")):
+    for t, n in ((offsets, "offsets"), (w_gate, "w_gate"), (w_val, "w_val")):
         _dev(t, n)
+    ldx = _rows(x_perm, "x_perm")
     N, d = x_perm.shape
     E, _, f = w_gate.shape
     if h is None:
         h = torch.empty((N, f), dtype=x_perm.dtype, device=x_perm.device)
     _check("moe_ffn_gate_up", lib().moe_ffn_gate_up(
-        _p(x_perm), _dt(x_perm), N, d, f, E, _p(offsets), _p(w_gate), _p(w_val), _p(h),
+        _p(x_perm), ldx, _dt(x_perm), N, d, f, E, _p(offsets), _p(w_gate), _p(w_val), _p(h),
         _stream(stream)))
     return h
 
@@ -318,8 +345,9 @@ def moe_layer(x, w_router, bias, k: int, w_gate, w_val, w_out, *, shared=None, c
 def ffn_gate_up_train(x_perm, offsets, w_gate, w_val, *, h=None, act=None, stream=None):
     """h = silu(x W_gate[e]) * (x W_val[e]) and the pre-activations act = [a | v]
     [N,2f] that the backward needs."""
-    for t, n in ((x_perm, "x_perm"), (offsets, "offsets"), (w_gate, "w_gate"), (w_val, "w_val")):
+    for t, n in ((offsets, "offsets"), (w_gate, "w_gate"), (w_val, "w_val")):
         _dev(t, n)
+    ldx = _rows(x_perm, "x_perm")
     N, d = x_perm.shape
     E, _, f = w_gate.shape
     if h is None:
@@ -327,7 +355,8 @@ def ffn_gate_up_train(x_perm, offsets, w_gate, w_val, *, h=None, act=None, strea
     if act is None:
         act = torch.empty((N, 2 * f), dtype=x_perm.dtype, device=x_perm.device)
     _check("moe_ffn_gate_up_train", lib().moe_ffn_gate_up_train(
-        _p(x_perm), _dt(x_perm), N, d, f, E, _p(offsets), _p(w_gate), _p(w_val), _p(h), _p(act),
+        _p(x_perm), ldx, _dt(x_perm), N, d, f, E, _p(offsets), _p(w_gate), _p(w_val), _p(h),
+        _p(act),
         _stream(stream)))
     return h, act
 
@@ -376,6 +405,7 @@ def ffn_gate_up_backward(d_act, offsets, w_gate, w_val, *, d_x=None, dx_dtype=to
 def ffn_weight_grads(x_perm, h, d_y, d_act, offsets, E: int, *, scale: float = 1.0, out=None,
                      stream=None):
     """(dW_gate [E,d,f], dW_val [E,d,f], dW_out [E,f,d]) in fp32, times ``scale``."""
+    ldx = _rows(x_perm, "x_perm")
     N, d = x_perm.shape
     f = h.shape[1]
     dev = x_perm.device
@@ -385,7 +415,7 @@ def ffn_weight_grads(x_perm, h, d_y, d_act, offsets, E: int, *, scale: float = 1
                torch.empty((E, f, d), dtype=torch.float32, device=dev))
     dwg, dwv, dwo = out
     _check("moe_ffn_weight_grads", lib().moe_ffn_weight_grads(
-        _p(x_perm), _p(h), _p(d_y), _p(d_act), _dt(x_perm), N, d, f, E, _p(offsets),
+        _p(x_perm), ldx, _p(h), _p(d_y), _p(d_act), _dt(x_perm), N, d, f, E, _p(offsets),
         float(scale), _p(dwg), _p(dwv), _p(dwo), _stream(stream)))
     return dwg, dwv, dwo
 

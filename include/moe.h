@@ -18,7 +18,10 @@
  *    tensors) unless stated otherwise. The library never allocates or frees
  *    device memory on these calls and keeps no state between calls; calls
  *    on different streams are independent.
- *  - Every tensor is row-major and contiguous. bf16 data are raw 16-bit
+ *  - Every tensor is row-major and contiguous, except the packed rows x_perm:
+ *    those are ld_x_perm elements apart (an argument of every call that
+ *    reads or writes them; 0 = d, dense), so that a caller can lay them out
+ *    with moe_x_perm_ld's padded stride. bf16 data are raw 16-bit
  *    patterns (the upper half of an IEEE binary32). Expert weights use the
  *    x.W orientation: W_gate, W_val [E,d,f], W_out [E,f,d].
  *  - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
@@ -58,6 +61,17 @@ const char* moe_status_string(moe_status s);
 int moe_version(void);
 
 /*
+ * Recommended row stride, in elements, for the packed rows x_perm [rows,d]
+ * of dtype dt: d plus one 128-byte line (0 for d <= 0 or an unknown dtype).
+ * Rows whose byte length is a multiple of 4 KiB all start on the same memory
+ * channel; the matrix-core gate/up product reads 64 bytes of 256 such rows
+ * per step, and at d = 2048 bf16 runs about 12 % faster per flop on the
+ * padded rows. Any stride >= d works; the caller owns the padding bytes,
+ * which no call reads or writes.
+ */
+int moe_x_perm_ld(int d, moe_dtype dt);
+
+/*
  * Router ("Three axes of Parallelism", Expert Parallel (EP) -> Producing
  * assignments: scores [T,E], top-K expert ids and router weights [T,K]).
  *   x        [T,d] dtype dt        token activations
@@ -89,7 +103,9 @@ moe_status moe_route(const void* x, moe_dtype dt, const void* w_router, const fl
  *   offsets  [E+1] int32 out       offsets[0] = 0, offsets[E] = T*k
  *   perm_src [T*k] int32 out       packed row -> assignment a
  *   dest     [T*k] int32 out       assignment a -> packed row
- *   x_perm   [T*k,d] dtype dt out  x_perm[dest[a]] = x[a / k]
+ *   x_perm   [T*k,d] dtype dt out  x_perm[dest[a]] = x[a / k], rows ld_x_perm
+ *                                  elements apart (0 = d; smaller than d ->
+ *                                  MOE_ERR_INVALID_ARG)
  *   ws       device workspace of at least moe_permute_workspace(T,k,E) bytes
  * Inside an expert's region the assignments keep ascending a (stable), which
  * is the order the pages' per-expert argwhere produces. An id outside [0,E)
@@ -100,7 +116,7 @@ size_t moe_permute_workspace(int T, int k, int E);
 moe_status moe_permute(const int32_t* topk_idx, int T, int k, int E,
                        const void* x, moe_dtype dt, int d,
                        int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* dest,
-                       void* x_perm, void* ws, size_t ws_bytes, void* stream);
+                       void* x_perm, int ld_x_perm, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Fixed-capacity packing, a routing variant the pages name but do not define
@@ -120,8 +136,8 @@ moe_status moe_permute(const int32_t* topk_idx, int T, int k, int E,
 moe_status moe_permute_capacity(const int32_t* topk_idx, int T, int k, int E, int capacity,
                                 const void* x, moe_dtype dt, int d, int32_t* routed,
                                 int32_t* counts, int32_t* offsets, int32_t* perm_src,
-                                int32_t* dest, void* x_perm, void* ws, size_t ws_bytes,
-                                void* stream);
+                                int32_t* dest, void* x_perm, int ld_x_perm, void* ws,
+                                size_t ws_bytes, void* stream);
 
 /*
  * Packing of one rank's expert range in the all-gather / reduce-scatter
@@ -140,7 +156,7 @@ moe_status moe_permute_capacity(const int32_t* topk_idx, int T, int k, int E, in
 moe_status moe_permute_range(const int32_t* topk_idx, int T, int k, int e_first, int E_loc,
                              const void* x, moe_dtype dt, int d, int32_t* counts,
                              int32_t* offsets, int32_t* perm_src, int32_t* dest, void* x_perm,
-                             void* ws, size_t ws_bytes, void* stream);
+                             int ld_x_perm, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Receive-side reorder ("Three axes of Parallelism", Dispatch, expert
@@ -152,7 +168,8 @@ moe_status moe_permute_range(const int32_t* topk_idx, int T, int k, int e_first,
  *   x_recv      [N,d] dtype dt     rows sender-major, inside a sender grouped
  *                                  by local expert ascending
  *   counts [E_loc], offsets [E_loc+1], perm_src [N], dest [N] int32 out,
- *   x_perm [N,d] out               x_perm[dest[r]] = x_recv[r]
+ *   x_perm [N,d] out               x_perm[dest[r]] = x_recv[r], rows ld_x_perm
+ *                                  elements apart (0 = d)
  * Rows of one expert keep their arrival (sender) order. N is a host integer
  * the caller already holds (the one split-count copy of the exchange).
  * Precondition: sum(recv_counts) == N. Limits: S*E_loc <= 4096.
@@ -161,8 +178,8 @@ size_t moe_permute_recv_workspace(int S, int E_loc, int N);
 moe_status moe_permute_recv(const int32_t* recv_counts, int S, int E_loc, int N,
                             const void* x_recv, moe_dtype dt, int d,
                             int32_t* counts, int32_t* offsets, int32_t* perm_src,
-                            int32_t* dest, void* x_perm, void* ws, size_t ws_bytes,
-                            void* stream);
+                            int32_t* dest, void* x_perm, int ld_x_perm, void* ws,
+                            size_t ws_bytes, void* stream);
 
 /*
  * Grouped SwiGLU expert MLPs ("Three axes of Parallelism", Mapping experts to
@@ -171,19 +188,21 @@ moe_status moe_permute_recv(const int32_t* recv_counts, int S, int E_loc, int N,
  * For every packed row j of expert e (offsets[e] <= j < offsets[e+1]):
  *   h = silu(x_perm[j] . W_gate[e]) * (x_perm[j] . W_val[e]),  silu(z) = z*sigmoid(z)
  *   y[j] = h . W_out[e]
- *   x_perm [N,d] dtype dt, offsets [E+1] int32 (device, read on the device),
+ *   x_perm [N,d] dtype dt, rows ld_x_perm elements apart (0 = d),
+ *   offsets [E+1] int32 (device, read on the device),
  *   y      [N,d] dtype y_dt out
  * Products accumulate in fp32. With dt = MOE_BF16 the hidden activation h is
  * stored as bf16 (round to nearest even) between the two products; with
  * MOE_F32 it stays fp32. y is rounded once to y_dt: MOE_BF16 halves the bytes
  * the down product writes and the combine reads, MOE_F32 keeps the fp32 sums.
  * Experts with no rows cost nothing.
- * Limits: E <= 4096, N < 2^31. Any d, f >= 1 work; bf16 with d % 256 == 0 and
- * f % 128 == 0 (and 16-byte aligned pointers) takes the matrix-core path.
+ * Limits: E <= 4096, N < 2^31. Any d, f >= 1 work; bf16 with d % 256 == 0,
+ * f % 128 == 0, ld_x_perm % 8 == 0 and 16-byte aligned pointers takes the
+ * matrix-core path.
  */
 size_t moe_grouped_ffn_workspace(int N, int d, int f, int E, moe_dtype dt);
-moe_status moe_grouped_ffn(const void* x_perm, moe_dtype dt, int N, int d, int f, int E,
-                           const int32_t* offsets, const void* w_gate, const void* w_val,
+moe_status moe_grouped_ffn(const void* x_perm, int ld_x_perm, moe_dtype dt, int N, int d, int f,
+                           int E, const int32_t* offsets, const void* w_gate, const void* w_val,
                            const void* w_out, void* y, moe_dtype y_dt,
                            void* ws, size_t ws_bytes, void* stream);
 
@@ -193,8 +212,8 @@ moe_status moe_grouped_ffn(const void* x_perm, moe_dtype dt, int N, int d, int f
  *   moe_ffn_down:    y [N,d] (dtype y_dt) = h . W_out[e]
  * Same layouts, limits and row-to-expert mapping as moe_grouped_ffn.
  */
-moe_status moe_ffn_gate_up(const void* x_perm, moe_dtype dt, int N, int d, int f, int E,
-                           const int32_t* offsets, const void* w_gate, const void* w_val,
+moe_status moe_ffn_gate_up(const void* x_perm, int ld_x_perm, moe_dtype dt, int N, int d, int f,
+                           int E, const int32_t* offsets, const void* w_gate, const void* w_val,
                            void* h, void* stream);
 moe_status moe_ffn_down(const void* h, moe_dtype dt, int N, int f, int d, int E,
                         const int32_t* offsets, const void* w_out, void* y, moe_dtype y_dt,
@@ -267,9 +286,9 @@ moe_status moe_route_stats(const float* logits, const int32_t* counts, int T, in
  * act[j,f:2f] = x_perm[j] . W_val[e] (rounded once to dt), which the backward
  * of the SwiGLU needs.
  */
-moe_status moe_ffn_gate_up_train(const void* x_perm, moe_dtype dt, int N, int d, int f, int E,
-                                 const int32_t* offsets, const void* w_gate, const void* w_val,
-                                 void* h, void* act, void* stream);
+moe_status moe_ffn_gate_up_train(const void* x_perm, int ld_x_perm, moe_dtype dt, int N, int d,
+                                 int f, int E, const int32_t* offsets, const void* w_gate,
+                                 const void* w_val, void* h, void* act, void* stream);
 
 /*
  * Backward of moe_combine (weights given):
@@ -315,10 +334,11 @@ moe_status moe_ffn_gate_up_backward(const void* d_act, moe_dtype dt, int N, int 
  *   dW_out[e]  = scale * h_e^T . d_y_e          [E,f,d]
  *   dW_gate[e] = scale * x_e^T . d_act_e[:,0:f]  [E,d,f]
  *   dW_val[e]  = scale * x_e^T . d_act_e[:,f:2f] [E,d,f]
- *   x_perm [N,d], h [N,f], d_y [N,d], d_act [N,2f] dtype dt; outputs fp32.
+ *   x_perm [N,d] (rows ld_x_perm elements apart, 0 = d), h [N,f], d_y [N,d],
+ *   d_act [N,2f] dtype dt; outputs fp32.
  * Every expert's gradients are written, zeros for an expert with no rows.
  */
-moe_status moe_ffn_weight_grads(const void* x_perm, const void* h, const void* d_y,
+moe_status moe_ffn_weight_grads(const void* x_perm, int ld_x_perm, const void* h, const void* d_y,
                                 const void* d_act, moe_dtype dt, int N, int d, int f, int E,
                                 const int32_t* offsets, float scale, float* d_w_gate,
                                 float* d_w_val, float* d_w_out, void* stream);

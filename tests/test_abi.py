@@ -39,7 +39,12 @@ def test_library_exports_every_declared_symbol(L):
 def test_status_strings_and_version(L):
     assert L.moe_status_string(0) == b"ok"
     assert L.moe_status_string(3) == b"workspace too small"
-    assert L.moe_version() >= 100
+    assert L.moe_version() >= 101
+    # recommended packed-row stride: one 128-byte line past the row
+    assert L.moe_x_perm_ld(2048, 1) == 2112
+    assert L.moe_x_perm_ld(64, 0) == 96
+    assert L.moe_x_perm_ld(0, 1) == 0
+    assert L.moe_x_perm_ld(64, 7) == 0
 
 
 def test_workspace_queries(L):
@@ -60,30 +65,41 @@ def test_host_side_errors_return_before_launch(L):
     assert L.moe_route(fake, 1, fake, None, 16, 64, 8, 2, 1, fake, None, fake, None) == 1
     # permute: too small a workspace, NULL workspace
     need = L.moe_permute_workspace(100, 2, 8)
-    assert L.moe_permute(fake, 100, 2, 8, fake, 1, 64, fake, fake, fake, fake, fake, fake,
+    assert L.moe_permute(fake, 100, 2, 8, fake, 1, 64, fake, fake, fake, fake, fake, 0, fake,
                          need - 1, None) == 3
-    assert L.moe_permute(fake, 100, 2, 8, fake, 1, 64, fake, fake, fake, fake, fake, None,
+    assert L.moe_permute(fake, 100, 2, 8, fake, 1, 64, fake, fake, fake, fake, fake, 0, None,
                          0, None) == 3
+    # packed-row stride below the row width
+    assert L.moe_permute(fake, 100, 2, 8, fake, 1, 64, fake, fake, fake, fake, fake, 63, fake,
+                         need, None) == 1
     # capacity packing: negative capacity, small workspace
     assert L.moe_permute_capacity(fake, 100, 2, 8, -1, fake, 1, 64, None, fake, fake, fake,
-                                  fake, fake, fake, need, None) == 1
+                                  fake, fake, 0, fake, need, None) == 1
     assert L.moe_permute_capacity(fake, 100, 2, 8, 10, fake, 1, 64, None, fake, fake, fake,
-                                  fake, fake, fake, need - 1, None) == 3
+                                  fake, fake, 0, fake, need - 1, None) == 3
     # range packing: negative first expert, E_loc too large
     assert L.moe_permute_range(fake, 100, 2, -1, 8, fake, 1, 64, fake, fake, fake, fake, fake,
-                               fake, need, None) == 1
+                               0, fake, need, None) == 1
     assert L.moe_permute_range(fake, 100, 2, 0, 2048, fake, 1, 64, fake, fake, fake, fake, fake,
-                               fake, need, None) == 2
+                               0, fake, need, None) == 2
     # permute_recv: too many cells
     assert L.moe_permute_recv(fake, 64, 128, 10, fake, 1, 64, fake, fake, fake, fake, fake,
-                              None, 0, None) == 2
+                              0, None, 0, None) == 2
+    assert L.moe_permute_recv(fake, 4, 16, 10, fake, 1, 64, fake, fake, fake, fake, fake,
+                              32, None, 0, None) == 1
     # grouped ffn: NULL offsets, small workspace, bad y dtype
-    assert L.moe_grouped_ffn(fake, 1, 10, 64, 64, 2, None, fake, fake, fake, fake, 0, fake,
+    assert L.moe_grouped_ffn(fake, 0, 1, 10, 64, 64, 2, None, fake, fake, fake, fake, 0, fake,
                              1 << 20, None) == 1
-    assert L.moe_grouped_ffn(fake, 1, 10, 64, 64, 2, fake, fake, fake, fake, fake, 0, fake,
+    assert L.moe_grouped_ffn(fake, 0, 1, 10, 64, 64, 2, fake, fake, fake, fake, fake, 0, fake,
                              16, None) == 3
-    assert L.moe_grouped_ffn(fake, 1, 10, 64, 64, 2, fake, fake, fake, fake, fake, 9, fake,
+    assert L.moe_grouped_ffn(fake, 0, 1, 10, 64, 64, 2, fake, fake, fake, fake, fake, 9, fake,
                              1 << 20, None) == 1
+    # packed-row stride below d, for the readers of x_perm
+    assert L.moe_grouped_ffn(fake, 32, 1, 10, 64, 64, 2, fake, fake, fake, fake, fake, 0, fake,
+                             1 << 20, None) == 1
+    assert L.moe_ffn_gate_up(fake, 60, 1, 10, 64, 64, 2, fake, fake, fake, fake, None) == 1
+    assert L.moe_ffn_weight_grads(fake, 8, fake, fake, fake, 1, 10, 64, 64, 2, fake, 1.0,
+                                  fake, fake, fake, None) == 1
     # combine: k too large
     assert L.moe_combine(fake, 0, fake, None, 4, 33, 64, None, 0, fake, 0, None) == 2
     # backward: combine without weights, k = 0
@@ -98,7 +114,7 @@ def test_host_side_errors_return_before_launch(L):
                                       None) == 1
     # down backward: NULL saved pre-activations; training forward: NULL act
     assert L.moe_ffn_down_backward(fake, 1, 10, 64, 64, 2, fake, fake, None, fake, None) == 1
-    assert L.moe_ffn_gate_up_train(fake, 1, 10, 64, 64, 2, fake, fake, fake, fake, None,
+    assert L.moe_ffn_gate_up_train(fake, 0, 1, 10, 64, 64, 2, fake, fake, fake, fake, None,
                                    None) == 1
     # router backward: no output asked for, k > E, NULL inputs with rows
     assert L.moe_route_backward(fake, fake, fake, fake, 4, 8, 2, 1, None, None, None) == 1
@@ -124,8 +140,8 @@ def test_host_side_errors_return_before_launch(L):
 def test_empty_inputs_are_no_ops(L):
     # T = 0 / N = 0 enqueue nothing and succeed
     assert L.moe_route(None, 1, None, None, 0, 64, 8, 2, 1, None, None, None, None) == 0
-    assert L.moe_grouped_ffn(None, 1, 0, 64, 64, 2, ctypes.c_void_p(0x1000), None, None, None,
-                             None, 0, None, 0, None) == 0
+    assert L.moe_grouped_ffn(None, 0, 1, 0, 64, 64, 2, ctypes.c_void_p(0x1000), None, None,
+                             None, None, 0, None, 0, None) == 0
     assert L.moe_combine(None, 0, None, None, 0, 2, 64, None, 0, None, 0, None) == 0
     assert L.moe_combine_backward(None, 1, None, 0, None, None, 0, 2, 64, None, 1, None,
                                   None) == 0

@@ -304,6 +304,48 @@ def test_one_token_and_ragged_tiles():
     _small_layer(W.generate(cfg), "T=257 E=3")
 
 
+def _strided_rows(rows, d, ld, dtype):
+    return torch.empty((rows, ld), dtype=dtype, device="cuda")[:, :d]
+
+
+@pytest.mark.parametrize("name", ["qwen3_small", "odd_f32"])
+def test_packed_row_strides(name):
+    """Packed rows at any stride >= d: the dense layout, the library's padded
+    one and an odd one (off the 16-byte vector paths) pack the same bits,
+    and the expert products read them to the same bits."""
+    inp = _inputs(name)
+    dev = _device(inp)
+    k, E = inp["k"], inp["w_gate"].shape[0]
+    o = oracle.moe_layer(inp)
+    logits, idx, gates = ops.route(dev["x"], dev["w_router"], dev.get("bias"), k)
+    T, d = dev["x"].shape
+    dt = dev["x"].dtype
+    ref = None
+    for ld in (0, ops.x_perm_ld(d, dt), d + 3):
+        out = dict(counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+                   offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+                   perm_src=torch.empty(T * k, dtype=torch.int32, device="cuda"),
+                   dest=torch.empty(T * k, dtype=torch.int32, device="cuda"),
+                   x_perm=(torch.empty((T * k, d), dtype=dt, device="cuda") if ld == 0
+                           else _strided_rows(T * k, d, ld, dt)))
+        p = ops.permute(idx, dev["x"], E, out=out)
+        h = ops.ffn_gate_up(p["x_perm"], p["offsets"], dev["w_gate"], dev["w_val"])
+        y = ops.grouped_ffn(p["x_perm"], p["offsets"], dev["w_gate"], dev["w_val"],
+                            dev["w_out"])
+        torch.cuda.synchronize()
+        say(f"{name}: x_perm row stride {p['x_perm'].stride(0)} (d = {d})")
+        np.testing.assert_array_equal(to_numpy(p["x_perm"]), o["x_perm"])
+        got = (to_numpy(h), to_numpy(y))
+        check_float(got[1], o["y"], W.get(name).dtype, f"{name} y_perm (ld {ld})")
+        if ld == d + 3:
+            continue   # a row stride off 16 bytes takes the plain fp32 kernel
+        if ref is None:
+            ref = got
+        else:
+            np.testing.assert_array_equal(got[0], ref[0])
+            np.testing.assert_array_equal(got[1], ref[1])
+
+
 def test_empty_batch():
     inp = _inputs("qwen3_small")
     dev = _device(inp)
