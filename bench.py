@@ -11,8 +11,13 @@ un-permutes back to sender-major order; the gathered-token workload routes every
 gathered token over the whole expert set, packs only the rank's own experts and
 combines into the rank's partial output). Inputs are seeded synthetic tensors
 already resident in HBM; every buffer is allocated before timing, so the timed
-region is kernel launches only. Per-stage times come from HIP events recorded
-on the stream the kernels are launched on. Prints one JSON line on stdout.
+region is kernel launches only. After the timed steps the same K steps run
+once more (the A/A repeat, reported as the run-to-run noise floor), then K
+steps with HIP events recorded between the stages on the stream the kernels
+are launched on (the per-stage times; the events slow a step down, so they
+stay out of the timed region), and each stage is timed cold: right after a
+1 GiB write that evicts its inputs from the L2s and the Infinity Cache.
+Prints one JSON line on stdout.
 """
 from __future__ import annotations
 
@@ -42,8 +47,8 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="qwen3_30b_a3b")
     ap.add_argument("--capacity-factor", type=float, default=None,
                     help="fixed-capacity packing: each expert keeps at most "
@@ -64,6 +69,9 @@ def parse():
                     help="time a training step instead: the forward keeping what the "
                          "backward needs, then the backward of sum(out * d_out) with a "
                          "seeded d_out (token-routed workloads)")
+    ap.add_argument("--cold-reps", type=int, default=3,
+                    help="reps of the per-stage cold timing (each stage right after a 1 GiB "
+                         "write that evicts the caches); 0 skips it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU work of the oracle baseline sample")
@@ -356,10 +364,15 @@ def main_backward(args):
     torch.cuda.synchronize()
     t0.record()
     for s_ in range(args.steps):
-        step(evs[s_])
+        step()
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
+    # per-stage times from K more steps with events between the stages (kept
+    # out of the timed steps, which they would slow down)
+    for s_ in range(args.steps):
+        step(evs[s_])
+    torch.cuda.synchronize()
     stage_us = {n: float(np.mean([evs[s_][j].elapsed_time(evs[s_][j + 1])
                                   for s_ in range(args.steps)]) * 1e3)
                 for j, n in enumerate(stages)}
@@ -481,42 +494,46 @@ def main():
         (["route_stats"] if with_stats else []) + \
         ["gate_up", "down"] + (["shared_gate_up", "shared_down"] if shared else []) + ["combine"]
 
-    def step(ev=None):
-        i = 0
-        if ev is not None:
-            ev[0].record()
+    # the step as its stages' launches, in order
+    def _route():
+        ops.route(dev["x"], dev["w_router"], dev["bias"], cfg.k, renorm, out=(logits, idx, gates))
+
+    def _permute():
+        ops.permute(idx, dev["x"], E, capacity=cap, e_first=e_first, out=bufs, workspace=ws)
+
+    def _shared_up():
+        ops.ffn_gate_up(dev["x"], shared["off"], shared["wg"], shared["wv"], h=shared["h"])
+
+    def _combine():
         if cfg.kind != "recv":
-            ops.route(dev["x"], dev["w_router"], dev["bias"], cfg.k, renorm,
-                      out=(logits, idx, gates))
-            if ev is not None: ev[1].record()
-            ops.permute(idx, dev["x"], E, capacity=cap, e_first=e_first, out=bufs, workspace=ws)
-            i = 2
-            if with_stats:
-                if ev is not None: ev[i].record()
-                ops.route_stats(logits, stats_counts, cfg.k, out=stats_out, workspace=stats_ws)
-                i = 3
-        else:
-            ops.permute_recv(dev["recv_counts"], dev["x_recv"], out=bufs)
-            i = 1
-        if ev is not None: ev[i].record()
-        ops.ffn_gate_up(bufs["x_perm"], bufs["offsets"], dev["w_gate"], dev["w_val"], h=h)
-        if ev is not None: ev[i + 1].record()
-        ops.ffn_down(h, bufs["offsets"], dev["w_out"], y=y)
-        if ev is not None: ev[i + 2].record()
-        i += 3
-        y_sh = None
-        if shared:
-            ops.ffn_gate_up(dev["x"], shared["off"], shared["wg"], shared["wv"], h=shared["h"])
-            if ev is not None: ev[i].record()
-            ops.ffn_down(shared["h"], shared["off"], shared["wo"], y=shared["y"])
-            if ev is not None: ev[i + 1].record()
-            i += 2
-            y_sh = shared["y"]
-        if cfg.kind != "recv":
-            ops.combine(y, bufs["dest"], gates, cfg.k, y_shared=y_sh, out=out)
+            ops.combine(y, bufs["dest"], gates, cfg.k, y_shared=shared["y"] if shared else None,
+                        out=out)
         else:
             ops.combine(y, bufs["dest"], None, 1, out=out)
-        if ev is not None: ev[i].record()
+
+    fns = {
+        "route": _route,
+        "permute": _permute,
+        "route_stats": lambda: ops.route_stats(logits, stats_counts, cfg.k, out=stats_out,
+                                               workspace=stats_ws),
+        "permute_recv": lambda: ops.permute_recv(dev["recv_counts"], dev["x_recv"], out=bufs),
+        "gate_up": lambda: ops.ffn_gate_up(bufs["x_perm"], bufs["offsets"], dev["w_gate"],
+                                           dev["w_val"], h=h),
+        "down": lambda: ops.ffn_down(h, bufs["offsets"], dev["w_out"], y=y),
+        "shared_gate_up": _shared_up,
+        "shared_down": lambda: ops.ffn_down(shared["h"], shared["off"], shared["wo"],
+                                            y=shared["y"]),
+        "combine": _combine,
+    }
+    stage_fns = [fns[n] for n in stages]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        for j, fn in enumerate(stage_fns):
+            fn()
+            if ev is not None:
+                ev[j + 1].record()
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -528,17 +545,50 @@ def main():
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t_start.record()
+
+    def timed():
+        torch.cuda.synchronize()
+        t_start.record()
+        for _ in range(args.steps):
+            step()
+        t_end.record()
+        torch.cuda.synchronize()
+        return t_start.elapsed_time(t_end) / args.steps
+
+    ms = timed()
+    # A/A: the same K timed steps once more, back to back: the run-to-run noise floor
+    ms_repeat = timed()
+    # per-stage times: K more steps with an event between stages (kept out of
+    # the timed steps: an event between two launches makes the second wait for
+    # the first to drain completely)
     for s in range(args.steps):
         step(evs[s])
-    t_end.record()
     torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_end) / args.steps
     stage_us = {}
     for j, name in enumerate(stages):
         stage_us[name] = float(np.mean([evs[s][j].elapsed_time(evs[s][j + 1])
                                         for s in range(args.steps)]) * 1e3)
+    events_ms = float(np.mean([evs[s][0].elapsed_time(evs[s][-1]) for s in range(args.steps)]))
+
+    # cold stages: before each stage a 1 GiB write evicts its inputs from the
+    # L2s and the 256 MB Infinity Cache, so the stage reads them from HBM
+    cold_us = {}
+    if args.cold_reps > 0:
+        log(f"[bench] cold stages, {args.cold_reps} rep(s)")
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=cuda)
+        cev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in stages] for _ in range(args.cold_reps)]
+        for r in range(args.cold_reps):
+            for j, fn in enumerate(stage_fns):
+                flush.fill_(r & 0xff)
+                cev[r][j][0].record()
+                fn()
+                cev[r][j][1].record()
+        torch.cuda.synchronize()
+        for j, name in enumerate(stages):
+            cold_us[name] = float(np.mean([cev[r][j][0].elapsed_time(cev[r][j][1])
+                                           for r in range(args.cold_reps)]) * 1e3)
+        del flush
 
     counts = bufs["counts"].cpu().numpy()
     kept = int(counts.sum())
@@ -553,6 +603,10 @@ def main():
                                achieved=round(r["achieved"], 1), unit=r["unit"],
                                frac=round(r["frac"], 4), alg_flops=work[name]["flops"],
                                alg_bytes=work[name]["bytes"])
+        if name in cold_us:
+            rc = roofline_entry(work[name], cold_us[name], es)
+            stage_rep[name].update(cold_us=round(cold_us[name], 2),
+                                   cold_frac=round(rc["frac"], 4))
     gemm = [n for n in stages if n in ("gate_up", "down", "shared_gate_up", "shared_down")]
     dominant = max(stages, key=lambda n: stage_us[n])
     dom = roofline_entry(work[dominant], stage_us[dominant], es)
@@ -590,6 +644,9 @@ def main():
         "roofline": {"kernel": dominant, "bound": dom["bound"], "achieved": round(dom["achieved"], 1),
                      "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4),
                      "traffic": traffic},
+        "aa": {"ms_per_step_repeat": round(ms_repeat, 5),
+               "rel_delta": round(abs(ms_repeat - ms) / ms, 4)},
+        "ms_per_step_with_stage_events": round(events_ms, 5),
         "gemm_mfma_frac": round(gemm_flops / (gemm_us * 1e-6) / 1e12 / (PEAK_MFMA_BF16_TFS if es == 2 else PEAK_MFMA_F32_TFS), 4),
         "stages": stage_rep,
     }
