@@ -30,6 +30,25 @@ constexpr int kRT = 64;       // tokens per block
 constexpr int kRE = 32;       // experts per block
 constexpr int kRG = 8;        // steps per register group
 
+// Score tile of this block in a 1-D grid of score_blocks(T, E) blocks: the
+// expert tiles of one token tile go to blocks b, b + 8, b + 16, ..., which
+// the hardware places on one XCD (blocks are dealt to the 8 XCDs round
+// robin), so the token rows are read from HBM once and from that XCD's L2
+// by the other expert tiles. Returns false for a block past the last token
+// tile.
+__device__ __forceinline__ bool score_tile(int T, int E, int& t0, int& e0) {
+    const int et = (E + kRE - 1) / kRE;
+    const int slot = blockIdx.x / 8;
+    const int tt = (slot / et) * 8 + blockIdx.x % 8;
+    t0 = tt * kRT;
+    e0 = (slot % et) * kRE;
+    return t0 < T;
+}
+inline unsigned score_blocks(int T, int E) {
+    const long long tt = (T + kRT - 1) / kRT, et = (E + kRE - 1) / kRE;
+    return (unsigned)((tt + 7) / 8 * 8 * et);
+}
+
 // Any d, E and alignment (element loads). Block: 64 tokens x 32 experts;
 // thread (eg, tg) = (tid % 8, tid / 8) owns experts 4eg..4eg+3 and tokens tg,
 // tg+32: eight FMA chains. x is staged [token][i] (rows padded to 132 floats:
@@ -52,8 +71,8 @@ __global__ __launch_bounds__(256) void route_scores_kernel_any(
     const int tid = threadIdx.x;
     const int eg = tid & 7;
     const int tg = tid >> 3;
-    const int t0 = blockIdx.x * kRT;
-    const int e0 = blockIdx.y * kRE;
+    int t0, e0;
+    if (!score_tile(T, E, t0, e0)) return;
     const int nchunks = (d + kRD - 1) / kRD;
     auto ld = [&](const void* p, size_t i) {
         return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
@@ -168,8 +187,8 @@ __global__ __launch_bounds__(512) void route_scores_pc_kernel(
     constexpr int kRBuf = kRT * kRS + kRD * kRE;    // floats per LDS buffer
     __shared__ __attribute__((aligned(16))) float smem[2 * kRBuf];
 
-    const int t0 = blockIdx.x * kRT;
-    const int e0 = blockIdx.y * kRE;
+    int t0, e0;
+    if (!score_tile(T, E, t0, e0)) return;
     const int nchunks = (d + kRD - 1) / kRD;
     const bool stager = threadIdx.x >= 256;          // wavefronts 4..7
 
@@ -594,11 +613,11 @@ template <typename XT>
 static hipError_t launch_scores_t(const void* x, const void* w, const float* bias, int T, int d,
                                   int E, float* logits, hipStream_t st)
 {
-    const dim3 grid((T + kRT - 1) / kRT, (E + kRE - 1) / kRE);
+    const unsigned grid = score_blocks(T, E);
     const bool vec = d % 4 == 0 && E % 4 == 0 && (uintptr_t)x % (4 * sizeof(XT)) == 0 &&
                      (uintptr_t)w % (4 * sizeof(XT)) == 0;
     // many more blocks than compute units: the narrower chunk (more blocks per CU)
-    const bool many = (long long)grid.x * grid.y >= 2LL * 256;
+    const bool many = (long long)((T + kRT - 1) / kRT) * ((E + kRE - 1) / kRE) >= 2LL * 256;
     if (vec && many)
         route_scores_pc_kernel<XT, 64><<<grid, 512, 0, st>>>((const XT*)x, (const XT*)w, bias, T, d,
                                                              E, logits);
