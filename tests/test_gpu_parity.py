@@ -346,6 +346,38 @@ def test_packed_row_strides(name):
             np.testing.assert_array_equal(got[1], ref[1])
 
 
+def test_grouped_ffn_largest_expert_count():
+    """The expert MLPs at the largest expert count the call takes (E = 4096):
+    most experts empty, one with several 256-row tiles and a 128-row
+    remainder, the rest a few rows each; matrix-core shapes (d = 256,
+    f = 128), checked row by row against the oracle."""
+    E, d, f = 4096, 256, 128
+    rng = np.random.default_rng(41)
+    counts = np.zeros(E, np.int64)
+    counts[E - 1] = 700                                   # 2 x 256 + a 188-row tile
+    busy = rng.choice(E - 1, size=500, replace=False)
+    counts[busy] = rng.integers(1, 9, size=busy.size)
+    counts[0] = 129                                        # 256-row tile, 1 padded past half
+    N = int(counts.sum())
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    bf = W.f32_to_bf16_bits
+    x_perm = bf(rng.standard_normal((N, d), dtype=np.float32))
+    # weights drawn for the experts with rows; no call reads the others (zeros)
+    live = np.flatnonzero(counts)
+    wg = np.zeros((E, d, f), np.uint16)
+    wv = np.zeros((E, d, f), np.uint16)
+    wo = np.zeros((E, f, d), np.uint16)
+    wg[live] = bf(rng.standard_normal((live.size, d, f), dtype=np.float32) / np.float32(np.sqrt(d)))
+    wv[live] = bf(rng.standard_normal((live.size, d, f), dtype=np.float32) / np.float32(np.sqrt(d)))
+    wo[live] = bf(rng.standard_normal((live.size, f, d), dtype=np.float32) / np.float32(np.sqrt(f)))
+    say(f"E = {E}: {int((counts > 0).sum())} experts with rows, N = {N}")
+    y = ops.grouped_ffn(to_torch(x_perm), to_torch(offsets), to_torch(wg), to_torch(wv),
+                        to_torch(wo))
+    torch.cuda.synchronize()
+    ref = oracle.expert_ffn_rows(x_perm, offsets, wg, wv, wo)
+    check_float(to_numpy(y), ref, "bf16", "E=4096 y_perm")
+
+
 def test_empty_batch():
     inp = _inputs("qwen3_small")
     dev = _device(inp)
