@@ -16,7 +16,7 @@ once more (the A/A repeat, reported as the run-to-run noise floor), then K
 steps with HIP events recorded between the stages on the stream the kernels
 are launched on (the per-stage times; the events slow a step down, so they
 stay out of the timed region), and each stage is timed cold: right after a
-1 GiB write that evicts its inputs from the L2s and the Infinity Cache.
+1 GiB read that evicts its inputs from the L2s and the Infinity Cache.
 Prints one JSON line on stdout.
 """
 from __future__ import annotations
@@ -71,7 +71,7 @@ def parse():
                          "seeded d_out (token-routed workloads)")
     ap.add_argument("--cold-reps", type=int, default=3,
                     help="reps of the per-stage cold timing (each stage right after a 1 GiB "
-                         "write that evicts the caches); 0 skips it")
+                         "read that evicts the caches); 0 skips it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU work of the oracle baseline sample")
@@ -570,17 +570,20 @@ def main():
                                         for s in range(args.steps)]) * 1e3)
     events_ms = float(np.mean([evs[s][0].elapsed_time(evs[s][-1]) for s in range(args.steps)]))
 
-    # cold stages: before each stage a 1 GiB write evicts its inputs from the
-    # L2s and the 256 MB Infinity Cache, so the stage reads them from HBM
+    # cold stages: before each stage a 1 GiB read evicts its inputs from the
+    # L2s and the 256 MB Infinity Cache, so the stage reads them from HBM (a
+    # read, not a write: evicting dirty lines would put write-backs to HBM
+    # under the timed stage)
     cold_us = {}
     if args.cold_reps > 0:
         log(f"[bench] cold stages, {args.cold_reps} rep(s)")
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=cuda)
+        flush = torch.ones(1 << 28, dtype=torch.int32, device=cuda)
+        flush_sum = torch.empty((), dtype=torch.int64, device=cuda)
         cev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 for _ in stages] for _ in range(args.cold_reps)]
         for r in range(args.cold_reps):
             for j, fn in enumerate(stage_fns):
-                flush.fill_(r & 0xff)
+                torch.sum(flush, dim=0, out=flush_sum)
                 cev[r][j][0].record()
                 fn()
                 cev[r][j][1].record()
@@ -588,7 +591,7 @@ def main():
         for j, name in enumerate(stages):
             cold_us[name] = float(np.mean([cev[r][j][0].elapsed_time(cev[r][j][1])
                                            for r in range(args.cold_reps)]) * 1e3)
-        del flush
+        del flush, flush_sum
 
     counts = bufs["counts"].cpu().numpy()
     kept = int(counts.sum())
