@@ -418,6 +418,103 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     }
 }
 
+// Top-k with 16 lanes (one DPP row) per token, four tokens per wavefront, for
+// k <= 16 and E <= 16 EJ: lane r of a row holds scores r, r + 16, ...; each
+// round takes the row's maximum m of the scores not taken yet (DPP max-scan
+// inside the row, lane 15 read back), then the lowest index holding m (a
+// DPP min-scan of each lane's lowest candidate index), which is the order
+// (score descending, index ascending). A quarter of the wavefronts of the
+// one-token-per-wavefront kernel, for the same result.
+template <int CTRL>
+__device__ __forceinline__ float row_max_step(float v) {
+    const int o = __builtin_amdgcn_update_dpp(__float_as_int(-__builtin_inff()), __float_as_int(v),
+                                              CTRL, 0xf, 0xf, false);
+    return fmaxf(v, __int_as_float(o));
+}
+template <int CTRL>
+__device__ __forceinline__ int row_min_step(int v) {
+    const int o = __builtin_amdgcn_update_dpp(0x7fffffff, v, CTRL, 0xf, 0xf, false);
+    return min(v, o);
+}
+// value of lane 15 of the calling lane's row, in every lane of the row
+__device__ __forceinline__ float row_last_f32(float v) {
+    return __int_as_float(__shfl(__float_as_int(v), lane_id() | 15, kWave));
+}
+__device__ __forceinline__ float row_max_f32(float v) {
+    v = row_max_step<0x111>(v);   // row_shr:1
+    v = row_max_step<0x112>(v);   // row_shr:2
+    v = row_max_step<0x114>(v);   // row_shr:4
+    v = row_max_step<0x118>(v);   // row_shr:8
+    return row_last_f32(v);
+}
+__device__ __forceinline__ int row_min_i32(int v) {
+    v = row_min_step<0x111>(v);
+    v = row_min_step<0x112>(v);
+    v = row_min_step<0x114>(v);
+    v = row_min_step<0x118>(v);
+    return __shfl(v, lane_id() | 15, kWave);
+}
+__device__ __forceinline__ float row_sum_f32(float v) {
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+template <int EJ>
+__global__ __launch_bounds__(256) void route_topk_row_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int renorm,
+    int32_t* __restrict__ topk_idx, float* __restrict__ gates)
+{
+    // every lane runs every round (rows past T hold -inf and write nothing),
+    // so the DPP row operations always read active lanes
+    const int t = blockIdx.x * 16 + threadIdx.x / 16;
+    const int r = threadIdx.x & 15;
+    const bool live = t < T;
+    const float* l = logits + (size_t)(live ? t : 0) * E;
+    float v[EJ];
+    unsigned avail = 0;   // bit j: score r + 16 j exists and is not taken yet
+#pragma unroll
+    for (int j = 0; j < EJ; ++j) {
+        const int e = r + 16 * j;
+        const bool in = live && e < E;
+        v[j] = in ? l[e] : -__builtin_inff();
+        if (in) avail |= 1u << j;
+    }
+    float myv = 0.0f;
+    int mye = 0;
+    for (int s = 0; s < k; ++s) {
+        float lv = -__builtin_inff();
+#pragma unroll
+        for (int j = 0; j < EJ; ++j)
+            if ((avail >> j) & 1u) lv = fmaxf(lv, v[j]);
+        const float m = row_max_f32(lv);
+        int cand = 0x7fffffff;
+#pragma unroll
+        for (int j = EJ - 1; j >= 0; --j)
+            if (((avail >> j) & 1u) && v[j] == m) cand = r + 16 * j;
+        const int be = row_min_i32(cand);
+        if (be != 0x7fffffff && (be & 15) == r) avail &= ~(1u << (be >> 4));
+        if (r == s) { myv = m; mye = be; }
+    }
+    const float m0 = __shfl(myv, threadIdx.x & ~15 & (kWave - 1), kWave);
+    const float u = r < k ? expf(myv - m0) : 0.0f;
+    float denom;
+    if (renorm) {
+        denom = row_sum_f32(u);
+    } else {
+        float part = 0.0f;
+#pragma unroll
+        for (int j = 0; j < EJ; ++j)
+            if (live && r + 16 * j < E) part += expf(v[j] - m0);
+        denom = row_sum_f32(part);
+    }
+    if (live && r < k) {
+        const size_t o = (size_t)t * k + r;
+        topk_idx[o] = mye;
+        gates[o] = u / denom;
+    }
+}
+
 // Backward of the router weights, one wavefront per token. With g the
 // weights of the k selected experts and dg their gradients, gdg = sum_s g_s dg_s:
 //  renorm:    g = softmax over the selected logits, so
@@ -636,6 +733,16 @@ hipError_t launch_route(const void* x, moe_dtype dt, const void* w, const float*
     hipError_t e = (dt == MOE_BF16) ? launch_scores_t<uint16_t>(x, w, bias, T, d, E, logits, st)
                                     : launch_scores_t<float>(x, w, bias, T, d, E, logits, st);
     if (e != hipSuccess) return e;
+    if (k <= 16 && E <= 256) {
+        const unsigned g16 = (T + 15) / 16;
+        if (E <= 64)
+            route_topk_row_kernel<4><<<g16, 256, 0, st>>>(logits, T, E, k, renorm, idx, gates);
+        else if (E <= 128)
+            route_topk_row_kernel<8><<<g16, 256, 0, st>>>(logits, T, E, k, renorm, idx, gates);
+        else
+            route_topk_row_kernel<16><<<g16, 256, 0, st>>>(logits, T, E, k, renorm, idx, gates);
+        return hipGetLastError();
+    }
     const unsigned g = (T + 3) / 4;
     if (E <= 64) route_topk_kernel<1><<<g, 256, 0, st>>>(logits, T, E, k, renorm, idx, gates);
     else if (E <= 128) route_topk_kernel<2><<<g, 256, 0, st>>>(logits, T, E, k, renorm, idx, gates);
