@@ -9,9 +9,9 @@
 // page (Design) builds those indices on the device with no readback.
 //
 // Token-routed packing, three launches and no host synchronisation:
-//  1. perm_hist:  per-chunk expert histogram in LDS (1024 or 4096 assignments
-//                 per block: small batches get more blocks, large ones fewer
-//                 chunk histograms for every ranking block to sum);
+//  1. perm_hist:  per-chunk expert histogram in LDS (512, 1024 or 4096
+//                 assignments per block: small batches get more blocks, large
+//                 ones fewer chunk histograms for every ranking block to sum);
 //  2. perm_rank:  every block re-derives the global offsets and its own base
 //                 per expert from the chunk histograms, then ranks its
 //                 assignments stably with wave ballots (a bit-sliced match of
@@ -32,9 +32,12 @@ namespace moe {
 constexpr int kPermThreads = 256;
 constexpr int kPermMaxE = 1024;
 constexpr int kPermSmallTK = 65536;   // up to this many assignments: 1024-chunks
+constexpr int kPermTinyTK = 32768;    // up to this many: 512-chunks
 
 // assignments per ranking block
-static int perm_chunk(long long TK) { return TK <= kPermSmallTK ? 1024 : 4096; }
+static int perm_chunk(long long TK) {
+    return TK <= kPermTinyTK ? 512 : (TK <= kPermSmallTK ? 1024 : 4096);
+}
 
 // e_base: the packing covers global expert ids [e_base, e_base + E) (an
 // expert-parallel rank's range); any other id is dropped.
@@ -307,7 +310,12 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int e_base, int E, i
     const int chunk = perm_chunk(TK);
     const int nb = std::max(1, (TK + chunk - 1) / chunk);
     int32_t* bc = static_cast<int32_t*>(ws);
-    if (chunk == 1024) {
+    if (chunk == 512) {
+        perm_hist_kernel<512><<<nb, kPermThreads, 0, st>>>(idx, TK, e_base, E, bc);
+        perm_rank_kernel<512><<<nb, kPermThreads, 0, st>>>(idx, TK, e_base, E, ceil_log2(E), cap, bc,
+                                                           nb, routed, counts, offsets,
+                                                           perm_src, dest);
+    } else if (chunk == 1024) {
         perm_hist_kernel<1024><<<nb, kPermThreads, 0, st>>>(idx, TK, e_base, E, bc);
         perm_rank_kernel<1024><<<nb, kPermThreads, 0, st>>>(idx, TK, e_base, E, ceil_log2(E), cap, bc,
                                                             nb, routed, counts, offsets,
