@@ -842,10 +842,10 @@ hipError_t launch_tn(const void* A, int lda, int M, const void* B, int ldb, int 
                      moe_dtype dt, int rows, int E, const int32_t* offsets, float scale,
                      float* C0, float* C1, hipStream_t st, int split)
 {
-    // (Nc < 2^20 keeps a tile's byte offsets in 31 bits)
+    // (Nc, lda, ldb < 2^20 keep a tile's byte offsets in 31 bits)
     const bool mfma = dt == MOE_BF16 && lda % 8 == 0 && ldb % 8 == 0 && M % 8 == 0 &&
-                      Nc % 8 == 0 && Nc < (1 << 20) && pair % 8 == 0 && M >= 8 && Nc >= 8 &&
-                      al16(A) && al16(B);
+                      Nc % 8 == 0 && Nc < (1 << 20) && lda < (1 << 20) && ldb < (1 << 20) &&
+                      pair % 8 == 0 && M >= 8 && Nc >= 8 && al16(A) && al16(B);
     if (mfma) {
         TnArgs p{(const uint16_t*)A, lda, M, (const uint16_t*)B, ldb, Nc, pair, C0, C1, scale,
                  split};
