@@ -378,6 +378,56 @@ def test_grouped_ffn_largest_expert_count():
     check_float(to_numpy(y), ref, "bf16", "E=4096 y_perm")
 
 
+@pytest.mark.parametrize("variant", ["recv", "capacity", "range"])
+def test_packed_row_strides_other_packings(variant):
+    """The receive-side reorder and the capacity and expert-range packings
+    write the same packed rows, bit for bit, at the dense row stride, the
+    library's padded one and an odd one (off the 16-byte vector paths); the
+    dense rows match the oracle's."""
+    name = "ep_share_small" if variant == "recv" else "qwen3_small"
+    inp = _inputs(name)
+    dev = _device(inp)
+    if variant == "recv":
+        N, d = dev["x_recv"].shape
+        counts, offsets, perm_src, dest = oracle.permute_recv(inp["recv_counts"], N)
+        ref = oracle.gather(inp["x_recv"], perm_src, 1)
+    else:
+        k, E = inp["k"], inp["w_gate"].shape[0]
+        T, d = dev["x"].shape
+        N = T * k
+        logits, idx, gates = ops.route(dev["x"], dev["w_router"], dev.get("bias"), k)
+        _, oidx, _ = oracle.route(inp["x"], inp["w_router"], inp.get("bias"), k)
+        if variant == "capacity":
+            cap = int(np.ceil(1.0 * T * k / E))
+            _, counts, offsets, perm_src, dest = oracle.permute_capacity(oidx, E, cap)
+        else:
+            e_first, E = E // 2, E // 4
+            counts, offsets, perm_src, dest = oracle.permute_range(oidx, e_first, E)
+        kept = int(offsets[-1])
+        ref = oracle.gather(inp["x"], perm_src[:kept], k)
+    dt = (dev["x_recv"] if variant == "recv" else dev["x"]).dtype
+    kept = int(offsets[-1])
+    for ld in (0, ops.x_perm_ld(d, dt), d + 3):
+        xp = (torch.empty((N, d), dtype=dt, device="cuda") if ld == 0
+              else _strided_rows(N, d, ld, dt))
+        out = dict(counts=torch.empty(len(counts), dtype=torch.int32, device="cuda"),
+                   offsets=torch.empty(len(counts) + 1, dtype=torch.int32, device="cuda"),
+                   perm_src=torch.empty(N, dtype=torch.int32, device="cuda"),
+                   dest=torch.empty(N, dtype=torch.int32, device="cuda"), x_perm=xp)
+        if variant == "recv":
+            p = ops.permute_recv(dev["recv_counts"], dev["x_recv"], out=out)
+        elif variant == "capacity":
+            out["routed"] = torch.empty(len(counts), dtype=torch.int32, device="cuda")
+            p = ops.permute(idx, dev["x"], len(counts), capacity=cap, out=out)
+        else:
+            p = ops.permute(idx, dev["x"], E, e_first=e_first, out=out)
+        torch.cuda.synchronize()
+        say(f"{variant}: x_perm row stride {p['x_perm'].stride(0)} (d = {d}), {kept} rows")
+        np.testing.assert_array_equal(to_numpy(p["offsets"]), offsets)
+        np.testing.assert_array_equal(to_numpy(p["dest"]), dest)
+        np.testing.assert_array_equal(to_numpy(p["x_perm"])[:kept], ref)
+
+
 def test_empty_batch():
     inp = _inputs("qwen3_small")
     dev = _device(inp)
