@@ -37,7 +37,11 @@ METRIC = "MoE-layer tokens/sec at 1 GPU; % bf16 MFMA peak (GEMM), % HBM BW (perm
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_MFMA_BF16_TFS = 2500.0    # dense bf16 matrix peak
 PEAK_MFMA_F32_TFS = 157.3      # used for the fp32 path (vector fp32 peak)
-PEAK_VALU_F32_TFS = 157.3      # fp32 vector peak: 256 CUs x 2.4 GHz x 256 flop/clk
+# fp32 vector peak without packed-fp32 instructions (the library is built
+# without them): 256 CUs x 4 SIMDs x 16 lanes x 2 flop (one FMA) x 2.4 GHz =
+# 78.6 TFLOP/s; the 157.3 TFLOP/s figure counts packed FMAs (two per lane and
+# clock)
+PEAK_VALU_F32_TFS = 78.6
 
 
 def log(*a):
@@ -49,7 +53,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="qwen3_30b_a3b")
+    ap.add_argument("--config", default="stress_zipf",
+                    help="workload (default: the largest one-GPU workload, the T=32768, "
+                         "d=4096 Zipf stress layer)")
     ap.add_argument("--capacity-factor", type=float, default=None,
                     help="fixed-capacity packing: each expert keeps at most "
                          "ceil(factor * T * k / E) assignments (token-routed workloads)")
@@ -73,6 +79,8 @@ def parse():
                     help="reps of the per-stage cold timing (each stage right after a 1 GiB "
                          "read that evicts the caches); 0 skips it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the matrix-core-loop and streaming-copy ceilings")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU work of the oracle baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -131,15 +139,19 @@ def stage_work(cfg, counts, es, ys=4, kept=None, os_=4, touched=None):
                             bound="hbm")
     else:
         w["permute_recv"] = dict(flops=0.0, bytes=2 * rows * d * es + 2 * rows * 4, bound="hbm")
+    # the expert MLPs' algorithmic bytes: the weights once, x_perm in (gate_up)
+    # and y_perm out (down); the hidden activations h between the two launches
+    # are implementation traffic, listed apart (impl_bytes)
     w["gate_up"] = dict(flops=4.0 * rows * d * f,
-                        bytes=rows * d * es + active * 2 * d * f * es + rows * f * es)
+                        bytes=rows * d * es + active * 2 * d * f * es, impl_bytes=rows * f * es)
     w["down"] = dict(flops=2.0 * rows * f * d,
-                     bytes=rows * f * es + active * f * d * es + rows * d * ys)
+                     bytes=active * f * d * es + rows * d * ys, impl_bytes=rows * f * es)
     if cfg.shared:
         fs = cfg.shared * f
-        w["shared_gate_up"] = dict(flops=4.0 * T * d * fs,
-                                   bytes=T * d * es + 2 * d * fs * es + T * fs * es)
-        w["shared_down"] = dict(flops=2.0 * T * fs * d, bytes=T * fs * es + fs * d * es + T * d * 4)
+        w["shared_gate_up"] = dict(flops=4.0 * T * d * fs, bytes=T * d * es + 2 * d * fs * es,
+                                   impl_bytes=T * fs * es)
+        w["shared_down"] = dict(flops=2.0 * T * fs * d, bytes=fs * d * es + T * d * ys,
+                                impl_bytes=T * fs * es)
     # load statistics: the logits read (once for the normalisers, once for the
     # probabilities), the counts and the outputs
     w["route_stats"] = dict(flops=0.0, bytes=2 * T * E * 4 + E * 4 + E * 4 + 4, bound="hbm")
@@ -151,7 +163,8 @@ def stage_work(cfg, counts, es, ys=4, kept=None, os_=4, touched=None):
     mfma_peak = PEAK_MFMA_BF16_TFS if es == 2 else PEAK_MFMA_F32_TFS
     for name, v in w.items():
         if "bound" not in v:
-            ai = v["flops"] / max(v["bytes"], 1)
+            # the bound follows from all bytes the kernel must move (h included)
+            ai = v["flops"] / max(v["bytes"] + v.get("impl_bytes", 0), 1)
             v["bound"] = "mfma" if ai * PEAK_HBM_GBS * 1e9 > mfma_peak * 1e12 else "hbm"
     return w
 
@@ -191,26 +204,46 @@ def traffic_for(stage: str, workload: str):
         return None
 
 
+def host_info() -> dict:
+    """CPU model and thread settings of the host the oracle runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return dict(cpu_model=model, os_cpu_count=os.cpu_count(),
+                omp_num_threads=os.environ.get("OMP_NUM_THREADS"))
+
+
 def cpu_baseline(cfg, inp, target_s: float):
+    """Time the oracle on the first n tokens (rows) of the same workload, n
+    calibrated to about target_s seconds of CPU work. Returns the report and
+    the oracle's results of the last run (the parity reference for those
+    tokens)."""
     import oracle
+    last = {}
     if cfg.kind == "routed":
         def run(n):
             sub = dict(inp, x=inp["x"][:n])
             t = time.perf_counter()
-            oracle.moe_layer(sub)
+            last["o"] = oracle.moe_layer(sub)
             return time.perf_counter() - t
         total = cfg.T
     elif cfg.kind == "gathered":
         def run(n):
             sub = dict(inp, x=inp["x"][:n])
             t = time.perf_counter()
-            oracle.moe_partial_layer(sub, cfg.e_first)
+            last["o"] = oracle.moe_partial_layer(sub, cfg.e_first)
             return time.perf_counter() - t
         total = cfg.T
     else:
         def run(n):
             t = time.perf_counter()
-            oracle.moe_recv_layer(inp, rows=np.arange(n, dtype=np.int32))
+            last["o"] = oracle.moe_recv_layer(inp, rows=np.arange(n, dtype=np.int32))
             return time.perf_counter() - t
         total = cfg.N
     n0 = min(total, 16)
@@ -224,9 +257,87 @@ def cpu_baseline(cfg, inp, target_s: float):
         reps += 1
     unit_name = {"routed": "tokens", "gathered": "gathered tokens"}.get(cfg.kind, "rows")
     what = (f"all {total}" if n == total else f"first {n} of {total}")
-    return dict(value=reps * n / t, unit=f"{unit_name}/s", cores=oracle.num_threads(), kind="oracle",
-                sample=f"{what} {unit_name} of the same workload (same weights), whole layer "
-                       f"in the oracle, {reps} run(s), {t:.1f} s")
+    rep = dict(value=reps * n / t, unit=f"{unit_name}/s", cores=oracle.num_threads(),
+               kind="oracle",
+               sample=f"{what} {unit_name} of the same workload (same weights), whole layer "
+                      f"in the oracle, {reps} run(s), {t:.1f} s", **host_info())
+    return rep, last["o"], n
+
+
+def sample_parity(cfg, o, n, g):
+    """Parity of the timed GPU run's outputs against the oracle's on the
+    cpu_baseline sample (the first n tokens or received rows): integer
+    mismatches of the router ids, the fp32 rule on the router weights, and
+    the layer output's max error / RMS (the bf16 bar) and normwise error."""
+    def num(t):
+        t = t.detach().cpu()
+        if t.dtype == torch_bf16():
+            t = t.float()
+        return t.numpy().astype(np.float64) if t.is_floating_point() else t.numpy()
+
+    res = {"sample": n}
+    if cfg.kind != "recv":
+        idx = g["idx"][:n].cpu().numpy()
+        res["idx_mismatches"] = int((idx != o["idx"]).sum())
+        gg = num(g["gates"][:n])
+        ref = np.asarray(o["gates"], np.float64)
+        rms = float(np.sqrt(np.mean(ref * ref)))
+        res["gates_max_rel_err"] = float(np.max(np.abs(gg - ref) / np.maximum(np.abs(ref), rms)))
+        out = num(g["out"][:n])
+    else:
+        out = num(g["out"][o["rows"]])
+    ref = o["out"]
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    res["out_max_err_over_rms"] = float(np.max(np.abs(out - ref)) / rms)
+    res["out_rel_l2"] = float(np.sqrt(np.sum((out - ref) ** 2) / np.sum(ref * ref)))
+    return res
+
+
+def torch_bf16():
+    import torch
+    return torch.bfloat16
+
+
+def ceilings(torch, ops):
+    """What the chip reaches on this machine in the plainest kernels: the
+    matrix-core loop (bf16 TFLOP/s) and a 2 GiB streaming copy and read
+    (GB/s), each the median of 5 event-timed launches."""
+    cuda = torch.device("cuda")
+    res = {}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn, reps=5):
+        fn()
+        ts = []
+        for _ in range(reps):
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+        return float(np.median(ts))
+
+    blocks = 256 * 4
+    sink = torch.empty(blocks, dtype=torch.float32, device=cuda)
+    flops = {}
+
+    def mfma():
+        flops["n"] = ops.ceiling_mfma(blocks, 4096, sink)
+    t = timed(mfma)
+    res["mfma_bf16_tflops"] = round(flops["n"] / t / 1e12, 1)
+    nbytes = 2 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device=cuda)
+    dst = torch.empty_like(src)
+    usink = torch.empty(4096, dtype=torch.int32, device=cuda)
+    t = timed(lambda: ops.ceiling_copy(src, dst, nbytes, 4096))
+    res["copy_gbs"] = round(2 * nbytes / t / 1e9, 1)
+    t = timed(lambda: ops.ceiling_read(src, nbytes, usink, 4096))
+    res["read_gbs"] = round(nbytes / t / 1e9, 1)
+    res["how"] = ("matrix-core loop: 1024 blocks x 4 wavefronts x 4096 x 8 "
+                  "v_mfma_f32_32x32x16_bf16 on registers; copy and read: 2 GiB, 16-byte "
+                  "non-temporal accesses, 4096 blocks; median of 5 launches")
+    del src, dst
+    return res
 
 
 def backward_work(cfg, counts, es):
@@ -458,6 +569,7 @@ def main():
     os_ = 2 if (gathered and args.partial_dtype == "bf16") else 4
     out = torch.empty((units, d), dtype=torch.bfloat16 if os_ == 2 else torch.float32, device=cuda)
     shared = None
+    cap = None
     e_first = cfg.e_first if gathered else None
     if cfg.kind in ("routed", "gathered"):
         Er = cfg.E_global if gathered else E   # experts the router scores
@@ -466,7 +578,6 @@ def main():
         gates = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=cuda)
         ws = torch.empty(max(1, ops.permute_workspace(cfg.T, cfg.k, E)), dtype=torch.uint8,
                          device=cuda)
-        cap = None
         if args.capacity_factor is not None and not gathered:
             cap = int(np.ceil(args.capacity_factor * cfg.T * cfg.k / E))
             bufs["routed"] = torch.empty(E, dtype=torch.int32, device=cuda)
@@ -475,7 +586,7 @@ def main():
                 wg=to_dev(np.concatenate(list(inp["shared_w_gate"]), axis=1)[None], torch),
                 wv=to_dev(np.concatenate(list(inp["shared_w_val"]), axis=1)[None], torch),
                 wo=to_dev(np.concatenate(list(inp["shared_w_out"]), axis=0)[None], torch),
-                off=torch.tensor([0, cfg.T], dtype=torch.int32, device=cuda),
+                off=None,   # one group of all T tokens
                 h=torch.empty((cfg.T, cfg.shared * f), dtype=xdt, device=cuda),
                 y=torch.empty((cfg.T, d), dtype=torch.float32, device=cuda))
 
@@ -558,6 +669,16 @@ def main():
     ms = timed()
     # A/A: the same K timed steps once more, back to back: the run-to-run noise floor
     ms_repeat = timed()
+    # the distribution of single steps: K more steps with an event between
+    # consecutive steps (none inside a step)
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    sev[0].record()
+    for s in range(args.steps):
+        step()
+        sev[s + 1].record()
+    torch.cuda.synchronize()
+    step_ms = np.array([sev[s].elapsed_time(sev[s + 1]) for s in range(args.steps)])
     # per-stage times: K more steps with an event between stages (kept out of
     # the timed steps: an event between two launches makes the second wait for
     # the first to drain completely)
@@ -606,6 +727,8 @@ def main():
                                achieved=round(r["achieved"], 1), unit=r["unit"],
                                frac=round(r["frac"], 4), alg_flops=work[name]["flops"],
                                alg_bytes=work[name]["bytes"])
+        if "impl_bytes" in work[name]:
+            stage_rep[name]["impl_bytes"] = work[name]["impl_bytes"]
         if name in cold_us:
             rc = roofline_entry(work[name], cold_us[name], es)
             stage_rep[name].update(cold_us=round(cold_us[name], 2),
@@ -647,15 +770,32 @@ def main():
         "roofline": {"kernel": dominant, "bound": dom["bound"], "achieved": round(dom["achieved"], 1),
                      "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4),
                      "traffic": traffic},
-        "aa": {"ms_per_step_repeat": round(ms_repeat, 5),
+        "aa": {"ms_per_step": round(ms, 5), "ms_per_step_repeat": round(ms_repeat, 5),
                "rel_delta": round(abs(ms_repeat - ms) / ms, 4)},
+        "step_ms": {"median": round(float(np.median(step_ms)), 5),
+                    "p10": round(float(np.percentile(step_ms, 10)), 5),
+                    "p90": round(float(np.percentile(step_ms, 90)), 5),
+                    "how": "K single steps, an event between consecutive steps"},
         "ms_per_step_with_stage_events": round(events_ms, 5),
         "gemm_mfma_frac": round(gemm_flops / (gemm_us * 1e-6) / 1e12 / (PEAK_MFMA_BF16_TFS if es == 2 else PEAK_MFMA_F32_TFS), 4),
         "stages": stage_rep,
     }
+    res["ceilings"] = None
+    if not args.no_ceilings:
+        log("[bench] ceilings")
+        res["ceilings"] = ceilings(torch, ops)
+    res["parity"] = None
     if not args.no_cpu_baseline:
         log("[bench] oracle CPU baseline")
-        res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+        res["cpu_baseline"], o_sample, n_sample = cpu_baseline(cfg, inp, args.cpu_seconds)
+        if cap is None and renorm and cfg.kind in ("routed", "recv"):
+            g = dict(out=out)
+            if cfg.kind == "routed":
+                g.update(idx=idx, gates=gates)
+            res["parity"] = sample_parity(cfg, o_sample, n_sample, g)
+            res["parity"]["note"] = ("the timed run's outputs on the oracle sample: router ids "
+                                     "(mismatches), router weights (fp32 rule), layer output "
+                                     "(max error / RMS against the 2e-2 bf16 bar)")
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

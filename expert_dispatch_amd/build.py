@@ -1,6 +1,6 @@
 """Build libmoe.so (the HIP library behind include/moe.h) for gfx950.
 
-    python -m expert_dispatch_amd.build
+    python -m expert_dispatch_amd.build [--debug]
 
 Each source is compiled to an object in ``_build/`` (in parallel), then
 linked in-tree as ``expert_dispatch_amd/libmoe.so``. Packed fp32 VALU
@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["api.hip", "route.hip", "permute.hip", "grouped_ffn.hip", "grouped_bwd.hip",
-           "combine.hip"]
+           "combine.hip", "ceiling.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 CFLAGS = [
@@ -29,14 +29,23 @@ CFLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+LIB_DEBUG = os.path.join(PKG, "libmoe_debug.so")
+
+
+def build(verbose: bool = False, debug: bool = False) -> str:
+    """Build libmoe.so, or with ``debug`` libmoe_debug.so: the same sources
+    compiled with MOE_DEBUG, whose kernels record broken device-side
+    preconditions for moe_debug_status (test-only)."""
+    bdir = os.path.join(BUILD, "debug") if debug else BUILD
+    out_lib = LIB_DEBUG if debug else LIB
+    os.makedirs(bdir, exist_ok=True)
     procs = []
     objs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(bdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *CFLAGS, *(["-DMOE_DEBUG"] if debug else []), "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -52,12 +61,14 @@ def build(verbose: bool = False) -> str:
             failed.append(src)
     if failed:
         raise RuntimeError(f"hipcc failed on {failed}")
-    tmp = LIB + ".tmp"
-    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
-                   check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = out_lib + ".tmp"
+    # -Bsymbolic: the library's own calls bind inside it, so the release and
+    # the debug library can be open in one process side by side
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-Bsymbolic", *objs,
+                    "-o", tmp], check=True)
+    os.replace(tmp, out_lib)
+    return out_lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, debug="--debug" in sys.argv))

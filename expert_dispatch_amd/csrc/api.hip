@@ -10,7 +10,7 @@ hipError_t launch_route(const void* x, moe_dtype dt, const void* w, const float*
                         int d, int E, int k, int renorm, float* logits, int32_t* idx,
                         float* gates, hipStream_t st);
 size_t permute_ws_bytes(int T, int k, int E);
-hipError_t launch_permute(const int32_t* idx, int T, int k, int e_base, int E, int cap,
+hipError_t launch_permute(const int32_t* idx, int T, int k, int e_base, int E, int id_hi, int cap,
                           const void* x, int es, int d, int32_t* routed,
                           int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* dest,
                           void* x_perm, int ld, void* ws, hipStream_t st);
@@ -41,6 +41,10 @@ hipError_t launch_tn(const void* A, int lda, int M, const void* B, int ldb, int 
 int router_splits(int T, int& split);
 hipError_t launch_sum_splits(const float* part, int S, long long n, float* out, hipStream_t st);
 enum NtEpi { kNtSwigluBwd = 0, kNtStoreF32 = 1, kNtAccumF32 = 2, kNtStoreBf16 = 3 };
+unsigned debug_read_route(int reset);
+unsigned debug_read_permute(int reset);
+unsigned debug_read_ffn(int reset);
+unsigned debug_read_bwd(int reset);
 hipError_t launch_route_stats(const float* logits, const int32_t* counts, int T, int E, int k,
                               float* p_mean, float* aux, double* part, hipStream_t st);
 int route_stat_chunks(int T);
@@ -90,7 +94,25 @@ const char* moe_status_string(moe_status s) {
     return "unknown status";
 }
 
-int moe_version(void) { return 101; }
+int moe_version(void) { return 102; }
+
+moe_status moe_debug_status(unsigned* flags, int reset)
+{
+    if (!flags) return MOE_ERR_INVALID_ARG;
+    *flags = 0;
+#ifdef MOE_DEBUG
+    // test-only: waits for the device so that every enqueued kernel has run
+    if (hipDeviceSynchronize() != hipSuccess) return MOE_ERR_HIP;
+    const unsigned v = moe::debug_read_route(reset) | moe::debug_read_permute(reset) |
+                       moe::debug_read_ffn(reset) | moe::debug_read_bwd(reset);
+    if (v & 0x80000000u) return MOE_ERR_HIP;
+    *flags = v;
+    return MOE_OK;
+#else
+    (void)reset;
+    return MOE_ERR_UNSUPPORTED;
+#endif
+}
 
 int moe_x_perm_ld(int d, moe_dtype dt) {
     if (d <= 0 || !valid_dtype(dt)) return 0;
@@ -131,7 +153,7 @@ moe_status moe_permute(const int32_t* topk_idx, int T, int k, int E, const void*
     if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
     if (T > 0 && (!topk_idx || !x || !perm_src || !dest || !x_perm)) return MOE_ERR_INVALID_ARG;
     if (!ws || ws_bytes < moe::permute_ws_bytes(T, k, E)) return MOE_ERR_WORKSPACE;
-    return hip_status(moe::launch_permute(topk_idx, T, k, 0, E, INT32_MAX, x, elem_size(dt), d,
+    return hip_status(moe::launch_permute(topk_idx, T, k, 0, E, E, INT32_MAX, x, elem_size(dt), d,
                                           nullptr, counts, offsets, perm_src, dest, x_perm, ld,
                                           ws, as_stream(stream)));
 }
@@ -150,7 +172,7 @@ moe_status moe_permute_capacity(const int32_t* topk_idx, int T, int k, int E, in
     if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
     if (T > 0 && (!topk_idx || !x || !perm_src || !dest || !x_perm)) return MOE_ERR_INVALID_ARG;
     if (!ws || ws_bytes < moe::permute_ws_bytes(T, k, E)) return MOE_ERR_WORKSPACE;
-    return hip_status(moe::launch_permute(topk_idx, T, k, 0, E, capacity, x, elem_size(dt), d,
+    return hip_status(moe::launch_permute(topk_idx, T, k, 0, E, E, capacity, x, elem_size(dt), d,
                                           routed, counts, offsets, perm_src, dest, x_perm, ld,
                                           ws, as_stream(stream)));
 }
@@ -168,7 +190,8 @@ moe_status moe_permute_range(const int32_t* topk_idx, int T, int k, int e_first,
     if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
     if (T > 0 && (!topk_idx || !x || !perm_src || !dest || !x_perm)) return MOE_ERR_INVALID_ARG;
     if (!ws || ws_bytes < moe::permute_ws_bytes(T, k, E_loc)) return MOE_ERR_WORKSPACE;
-    return hip_status(moe::launch_permute(topk_idx, T, k, e_first, E_loc, INT32_MAX, x,
+    // (global ids: only their sign is known to be wrong here)
+    return hip_status(moe::launch_permute(topk_idx, T, k, e_first, E_loc, INT32_MAX, INT32_MAX, x,
                                           elem_size(dt), d, nullptr, counts, offsets, perm_src,
                                           dest, x_perm, ld, ws, as_stream(stream)));
 }
@@ -205,7 +228,8 @@ static moe_status check_ffn(moe_dtype dt, int N, int d, int f, int E, const int3
     if (!valid_dtype(dt) || N < 0 || d <= 0 || f <= 0 || E <= 0) return MOE_ERR_INVALID_ARG;
     if (E > kMaxFfnE) return MOE_ERR_UNSUPPORTED;
     if ((long long)N * std::max(d, f) > (1LL << 40)) return MOE_ERR_UNSUPPORTED;
-    if (!offsets) return MOE_ERR_INVALID_ARG;
+    // offsets NULL: one group of all N rows (E must be 1), e.g. shared experts
+    if (!offsets && E != 1) return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 

@@ -124,6 +124,44 @@ __device__ __forceinline__ void lds_barrier() {
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// ------------------------------------------------------------ debug checks
+// Device-side preconditions the release build leaves unchecked (the kernels
+// only keep every access inside its buffer when they are broken). A build
+// with MOE_DEBUG records each broken one as a bit in a device word of the
+// source file that checks it; moe_debug_status() ORs and clears them.
+enum DebugFlag : unsigned {
+    kDbgIdRange = 1u,      // a router id outside [0, E) reached a packing
+    kDbgRecvSum = 2u,      // receive counts negative or not summing to N
+    kDbgNonFinite = 4u,    // a router score is not finite
+    kDbgOffsets = 8u,      // expert offsets: offsets[0] != 0, decreasing or past N
+};
+#ifdef MOE_DEBUG
+static __device__ unsigned g_debug_flags = 0;   // one word per source file
+__device__ __forceinline__ void debug_flag(unsigned bit) { atomicOr(&g_debug_flags, bit); }
+#define MOE_DBG_CHECK(cond, bit)            \
+    do {                                     \
+        if (!(cond)) ::moe::debug_flag(bit); \
+    } while (0)
+// Host side: the flags of this source file (then cleared when `reset`).
+#define MOE_DBG_READER(name)                                                          \
+    unsigned debug_read_##name(int reset) {                                           \
+        unsigned v = 0;                                                               \
+        if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_debug_flags), sizeof v) != hipSuccess) \
+            return 0x80000000u;                                                       \
+        if (reset) {                                                                  \
+            const unsigned z = 0;                                                     \
+            (void)hipMemcpyToSymbol(HIP_SYMBOL(g_debug_flags), &z, sizeof z);         \
+        }                                                                             \
+        return v;                                                                     \
+    }
+#else
+#define MOE_DBG_CHECK(cond, bit) \
+    do {                         \
+    } while (0)
+#define MOE_DBG_READER(name) \
+    unsigned debug_read_##name(int) { return 0; }
+#endif
+
 // Raw buffer resource (stride 0) that starts at `base` and spans `bytes`:
 // the hardware drops a store, and returns zeros for a load without touching
 // memory, whose offset (the lane's VGPR offset plus the instruction's

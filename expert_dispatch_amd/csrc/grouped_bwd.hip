@@ -925,4 +925,6 @@ hipError_t launch_sum_splits(const float* part, int S, long long n, float* out, 
     return hipGetLastError();
 }
 
+MOE_DBG_READER(bwd)
+
 }  // namespace moe

@@ -630,4 +630,6 @@ hipError_t launch_down(const void* h, moe_dtype dt, int N, int f, int d, int E,
     return hipGetLastError();
 }
 
+MOE_DBG_READER(ffn)
+
 }  // namespace moe

@@ -28,6 +28,13 @@ __device__ bool schedule_tile(const int32_t* __restrict__ offsets, int N, int E,
     // offsets NULL: one group of all N rows
     for (int e = tid; e <= E; e += blockDim.x)
         s_off[e] = offsets ? min(max(offsets[e], 0), N) : (e == 0 ? 0 : N);
+#ifdef MOE_DEBUG
+    if (offsets && blockIdx.x == 0)
+        for (int e = tid; e <= E; e += blockDim.x)
+            MOE_DBG_CHECK(offsets[e] >= 0 && offsets[e] <= N && (e > 0 || offsets[0] == 0) &&
+                              (e == 0 || offsets[e] >= offsets[e - 1]),
+                          kDbgOffsets);
+#endif
     __syncthreads();
     for (int e = tid; e < E; e += blockDim.x) {
         const int lo = s_off[e];
@@ -90,6 +97,13 @@ __device__ TileList build_tile_list(const int32_t* __restrict__ offsets, int N, 
     // offsets NULL: one group of all N rows
     for (int e = tid; e <= E; e += blockDim.x)
         s_off[e] = offsets ? min(max(offsets[e], 0), N) : (e == 0 ? 0 : N);
+#ifdef MOE_DEBUG
+    if (offsets && blockIdx.x == 0)
+        for (int e = tid; e <= E; e += blockDim.x)
+            MOE_DBG_CHECK(offsets[e] >= 0 && offsets[e] <= N && (e > 0 || offsets[0] == 0) &&
+                              (e == 0 || offsets[e] >= offsets[e - 1]),
+                          kDbgOffsets);
+#endif
     __syncthreads();
     for (int e = tid; e < E; e += blockDim.x) {
         const int n = max(0, s_off[e + 1] - s_off[e]);

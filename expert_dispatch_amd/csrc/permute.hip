@@ -41,9 +41,11 @@ static int perm_chunk(long long TK) {
 
 // e_base: the packing covers global expert ids [e_base, e_base + E) (an
 // expert-parallel rank's range); any other id is dropped.
+// id_hi: router ids are expected in [0, id_hi) (checked in debug builds only)
 template <int CHUNK>
 __global__ __launch_bounds__(kPermThreads) void perm_hist_kernel(
-    const int32_t* __restrict__ idx, int TK, int e_base, int E, int32_t* __restrict__ bc)
+    const int32_t* __restrict__ idx, int TK, int e_base, int E, int id_hi,
+    int32_t* __restrict__ bc)
 {
     constexpr int kPermIters = CHUNK / kPermThreads;
     __shared__ int h[kPermMaxE];
@@ -54,7 +56,10 @@ __global__ __launch_bounds__(kPermThreads) void perm_hist_kernel(
     for (int q = 0; q < kPermIters; ++q) {
         const int a = base + threadIdx.x + q * kPermThreads;
         if (a < TK) {
-            const int e = idx[a] - e_base;
+            const int id = idx[a];
+            MOE_DBG_CHECK(id >= 0 && id < id_hi, kDbgIdRange);
+            (void)id_hi;
+            const int e = id - e_base;
             if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
         }
     }
@@ -75,7 +80,7 @@ __global__ __launch_bounds__(kPermThreads) void perm_rank_kernel(
     __shared__ int s_off[kPermMaxE];       // offsets of the kept assignments
     __shared__ int s_base[kPermMaxE];      // assignments of earlier blocks (rank base)
     __shared__ int s_wcnt[4][kPermMaxE];   // per-wave running counts, then wave bases
-    __shared__ int scratch[kPermThreads / kWave + 1];
+    __shared__ int s_scan[kPermThreads / kWave + 1];
 
     const int tid = threadIdx.x;
     const int w = tid / kWave;
@@ -111,7 +116,7 @@ __global__ __launch_bounds__(kPermThreads) void perm_rank_kernel(
         for (int q = 0; q < 4; ++q) s_wcnt[q][e] = 0;
     }
     __syncthreads();
-    const int total = block_exclusive_scan_lds(s_off, E, scratch);
+    const int total = block_exclusive_scan_lds(s_off, E, s_scan);
     if (blockIdx.x == 0) {
         for (int e = tid; e < E; e += kPermThreads) offsets[e] = s_off[e];
         if (tid == 0) offsets[E] = total;
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(256) void perm_recv_kernel(
     __shared__ int s_start[kRecvMaxCells];   // first received row of cell (i,j)
     __shared__ int s_dbase[kRecvMaxCells];   // first packed row of cell (i,j)
     __shared__ int s_off[kPermMaxE + 1];
-    __shared__ int scratch[256 / kWave + 1];
+    __shared__ int s_scan[256 / kWave + 1];
     const int tid = threadIdx.x;
     const int C = S * E;
     for (int c = tid; c < C; c += blockDim.x) {
@@ -238,8 +243,14 @@ __global__ __launch_bounds__(256) void perm_recv_kernel(
         s_off[j] = run;
     }
     __syncthreads();
-    const int total_rows = block_exclusive_scan_lds(s_start, C, scratch);
-    const int total_e = block_exclusive_scan_lds(s_off, E, scratch);
+    const int total_rows = block_exclusive_scan_lds(s_start, C, s_scan);
+    const int total_e = block_exclusive_scan_lds(s_off, E, s_scan);
+#ifdef MOE_DEBUG
+    if (blockIdx.x == 0) {
+        for (int c = tid; c < C; c += blockDim.x) MOE_DBG_CHECK(recv[c] >= 0, kDbgRecvSum);
+        if (tid == 0) MOE_DBG_CHECK(total_rows == N, kDbgRecvSum);
+    }
+#endif
     for (int c = tid; c < C; c += blockDim.x) s_dbase[c] += s_off[c % E];
     if (blockIdx.x == 0) {
         for (int j = tid; j < E; j += blockDim.x) {
@@ -301,7 +312,7 @@ size_t permute_ws_bytes(int T, int k, int E) {
     return align_up((size_t)(nb * E) * sizeof(int32_t), 256);
 }
 
-hipError_t launch_permute(const int32_t* idx, int T, int k, int e_base, int E, int cap,
+hipError_t launch_permute(const int32_t* idx, int T, int k, int e_base, int E, int id_hi, int cap,
                           const void* x, int es, int d, int32_t* routed, int32_t* counts,
                           int32_t* offsets, int32_t* perm_src, int32_t* dest, void* x_perm,
                           int ld, void* ws, hipStream_t st)
@@ -311,17 +322,17 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int e_base, int E, i
     const int nb = std::max(1, (TK + chunk - 1) / chunk);
     int32_t* bc = static_cast<int32_t*>(ws);
     if (chunk == 512) {
-        perm_hist_kernel<512><<<nb, kPermThreads, 0, st>>>(idx, TK, e_base, E, bc);
+        perm_hist_kernel<512><<<nb, kPermThreads, 0, st>>>(idx, TK, e_base, E, id_hi, bc);
         perm_rank_kernel<512><<<nb, kPermThreads, 0, st>>>(idx, TK, e_base, E, ceil_log2(E), cap, bc,
                                                            nb, routed, counts, offsets,
                                                            perm_src, dest);
     } else if (chunk == 1024) {
-        perm_hist_kernel<1024><<<nb, kPermThreads, 0, st>>>(idx, TK, e_base, E, bc);
+        perm_hist_kernel<1024><<<nb, kPermThreads, 0, st>>>(idx, TK, e_base, E, id_hi, bc);
         perm_rank_kernel<1024><<<nb, kPermThreads, 0, st>>>(idx, TK, e_base, E, ceil_log2(E), cap, bc,
                                                             nb, routed, counts, offsets,
                                                             perm_src, dest);
     } else {
-        perm_hist_kernel<4096><<<nb, kPermThreads, 0, st>>>(idx, TK, e_base, E, bc);
+        perm_hist_kernel<4096><<<nb, kPermThreads, 0, st>>>(idx, TK, e_base, E, id_hi, bc);
         perm_rank_kernel<4096><<<nb, kPermThreads, 0, st>>>(idx, TK, e_base, E, ceil_log2(E), cap, bc,
                                                             nb, routed, counts, offsets,
                                                             perm_src, dest);
@@ -363,5 +374,7 @@ hipError_t launch_permute_recv(const int32_t* recv, int S, int E, int N, const v
                                                          (int)(ld_bytes / 2));
     return hipGetLastError();
 }
+
+MOE_DBG_READER(permute)
 
 }  // namespace moe

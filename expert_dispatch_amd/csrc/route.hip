@@ -378,6 +378,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
         const int e = lane + kWave * j;
         v[j] = e < E ? l[e] : -__builtin_inff();
         if (e < E) avail |= 1u << j;
+        MOE_DBG_CHECK(e >= E || __builtin_isfinite(v[j]), kDbgNonFinite);
     }
     float myv = 0.0f;
     int mye = 0;
@@ -479,6 +480,7 @@ __global__ __launch_bounds__(256) void route_topk_row_kernel(
         const bool in = live && e < E;
         v[j] = in ? l[e] : -__builtin_inff();
         if (in) avail |= 1u << j;
+        MOE_DBG_CHECK(!in || __builtin_isfinite(v[j]), kDbgNonFinite);
     }
     float myv = 0.0f;
     int mye = 0;
@@ -751,5 +753,7 @@ hipError_t launch_route(const void* x, moe_dtype dt, const void* w, const float*
     else route_topk_kernel<16><<<g, 256, 0, st>>>(logits, T, E, k, renorm, idx, gates);
     return hipGetLastError();
 }
+
+MOE_DBG_READER(route)
 
 }  // namespace moe

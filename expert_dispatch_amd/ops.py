@@ -27,15 +27,25 @@ def lib_path() -> str:
     return _LIB_PATH
 
 
+def debug_lib_path() -> str:
+    """The MOE_DEBUG build (device precondition checks; tests only)."""
+    return os.path.join(os.path.dirname(_LIB_PATH), "libmoe_debug.so")
+
+
 def lib():
     """Open libmoe.so (raises if it has not been built)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(_LIB_PATH):
-        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+    if _lib is None:
+        _lib = bind(_LIB_PATH)
+    return _lib
+
+
+def bind(path: str):
+    """Open a build of libmoe at `path` and declare its entry points."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m expert_dispatch_amd.build`")
-    L = ctypes.CDLL(_LIB_PATH)
+    L = ctypes.CDLL(path)
     vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_status_string.argtypes = [i]
@@ -68,6 +78,13 @@ def lib():
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = i
+    # measurement helpers (include/moe_ceiling.h)
+    L.moe_ceiling_mfma.argtypes = [i, i, vp, vp]
+    L.moe_ceiling_mfma.restype = ctypes.c_longlong
+    L.moe_ceiling_copy.argtypes = [vp, vp, ctypes.c_longlong, i, vp]
+    L.moe_ceiling_copy.restype = i
+    L.moe_ceiling_read.argtypes = [vp, ctypes.c_longlong, vp, i, vp]
+    L.moe_ceiling_read.restype = i
     for name, args in {"moe_permute_workspace": [i, i, i],
                        "moe_permute_recv_workspace": [i, i, i],
                        "moe_grouped_ffn_workspace": [i, i, i, i, i],
@@ -77,7 +94,8 @@ def lib():
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = sz
-    _lib = L
+    L.moe_debug_status.argtypes = [vp, i]
+    L.moe_debug_status.restype = i
     return L
 
 
@@ -241,11 +259,22 @@ def grouped_ffn_workspace(N: int, d: int, f: int, E: int, dtype) -> int:
     return int(lib().moe_grouped_ffn_workspace(N, d, f, E, _dt_of(dtype)))
 
 
+def _offsets(offsets, E: int):
+    """Device offsets [E+1], or None: one group of all rows (E must be 1)."""
+    if offsets is None:
+        if E != 1:
+            raise ValueError("offsets may be None only for a single expert (E = 1)")
+        return
+    _dev(offsets, "offsets")
+
+
 def grouped_ffn(x_perm, offsets, w_gate, w_val, w_out, *, y_dtype=torch.float32, y=None,
                 workspace=None, stream=None):
-    """y[j] = (silu(x_perm[j] W_gate[e]) * (x_perm[j] W_val[e])) W_out[e] per expert segment."""
-    for t, n in ((offsets, "offsets"), (w_gate, "w_gate"), (w_val, "w_val"), (w_out, "w_out")):
+    """y[j] = (silu(x_perm[j] W_gate[e]) * (x_perm[j] W_val[e])) W_out[e] per expert segment
+    (offsets None: one expert over all rows)."""
+    for t, n in ((w_gate, "w_gate"), (w_val, "w_val"), (w_out, "w_out")):
         _dev(t, n)
+    _offsets(offsets, w_gate.shape[0])
     ldx = _rows(x_perm, "x_perm")
     N, d = x_perm.shape
     E, _, f = w_gate.shape
@@ -262,8 +291,9 @@ def grouped_ffn(x_perm, offsets, w_gate, w_val, w_out, *, y_dtype=torch.float32,
 
 def ffn_gate_up(x_perm, offsets, w_gate, w_val, *, h=None, stream=None):
     """h = silu(x_perm W_gate[e]) * (x_perm W_val[e]) per expert segment."""
-    for t, n in ((offsets, "offsets"), (w_gate, "w_gate"), (w_val, "w_val")):
+    for t, n in ((w_gate, "w_gate"), (w_val, "w_val")):
         _dev(t, n)
+    _offsets(offsets, w_gate.shape[0])
     ldx = _rows(x_perm, "x_perm")
     N, d = x_perm.shape
     E, _, f = w_gate.shape
@@ -277,8 +307,9 @@ def ffn_gate_up(x_perm, offsets, w_gate, w_val, *, h=None, stream=None):
 
 def ffn_down(h, offsets, w_out, *, y_dtype=torch.float32, y=None, stream=None):
     """y = h W_out[e] per expert segment."""
-    for t, n in ((h, "h"), (offsets, "offsets"), (w_out, "w_out")):
+    for t, n in ((h, "h"), (w_out, "w_out")):
         _dev(t, n)
+    _offsets(offsets, w_out.shape[0])
     N, f = h.shape
     E, _, d = w_out.shape
     if y is None:
@@ -318,26 +349,73 @@ def moe_partial_layer(x, w_router, bias, k: int, e_first: int, w_gate, w_val, w_
     return dict(logits=logits, idx=idx, gates=gates, y=y, out=out, **p)
 
 
+def layer_buffers(T: int, k: int, d: int, f: int, E: int, dtype, device, *, shared_f: int = 0,
+                  capacity: bool = False, y_dtype=torch.float32, out_dtype=torch.float32) -> dict:
+    """Every output and workspace of one moe_layer pass, allocated once, so
+    that later passes allocate nothing (a caller that captures the layer in
+    a HIP graph passes them as ``bufs``). ``shared_f``: width of the fused
+    shared-expert SwiGLU (0: none)."""
+    rows = T * k
+    i32 = torch.int32
+    b = dict(
+        logits=torch.empty((T, E), dtype=torch.float32, device=device),
+        idx=torch.empty((T, k), dtype=i32, device=device),
+        gates=torch.empty((T, k), dtype=torch.float32, device=device),
+        counts=torch.empty(E, dtype=i32, device=device),
+        offsets=torch.empty(E + 1, dtype=i32, device=device),
+        perm_src=torch.empty(rows, dtype=i32, device=device),
+        dest=torch.empty(rows, dtype=i32, device=device),
+        x_perm=empty_rows(rows, d, dtype, device),
+        permute_ws=torch.empty(max(1, permute_workspace(T, k, E)), dtype=torch.uint8,
+                               device=device),
+        ffn_ws=torch.empty(max(1, grouped_ffn_workspace(rows, d, f, E, dtype)),
+                           dtype=torch.uint8, device=device),
+        y=torch.empty((rows, d), dtype=y_dtype, device=device),
+        out=torch.empty((T, d), dtype=out_dtype, device=device),
+    )
+    if capacity:
+        b["routed"] = torch.empty(E, dtype=i32, device=device)
+    if shared_f:
+        b["shared_ws"] = torch.empty(max(1, grouped_ffn_workspace(T, d, shared_f, 1, dtype)),
+                                     dtype=torch.uint8, device=device)
+        b["y_shared"] = torch.empty((T, d), dtype=y_dtype, device=device)
+    return b
+
+
 def moe_layer(x, w_router, bias, k: int, w_gate, w_val, w_out, *, shared=None, capacity=None,
-              y_dtype=torch.float32, out_dtype=torch.float32, stream=None):
+              y_dtype=torch.float32, out_dtype=torch.float32, bufs=None, stream=None):
     """The whole token-routed layer: route -> permute -> grouped FFN -> combine.
     ``shared`` = (w_gate, w_val, w_out) of the always-on shared experts
     concatenated along f (one SwiGLU of width q*f equals the sum of q).
     ``y_dtype`` is the storage type of the expert outputs between the down
     GEMM and the combine. ``capacity``: fixed-capacity packing (at most that
-    many rows per expert; dropped assignments add nothing to their token)."""
+    many rows per expert; dropped assignments add nothing to their token).
+    ``bufs``: outputs and workspaces from layer_buffers (then nothing is
+    allocated and the dtypes are the buffers'); every call only enqueues
+    work on the stream, none waits for the device."""
     E = w_gate.shape[0]
-    logits, idx, gates = route(x, w_router, bias, k, stream=stream)
-    p = permute(idx, x, E, capacity=capacity, stream=stream)
-    y = grouped_ffn(p["x_perm"], p["offsets"], w_gate, w_val, w_out, y_dtype=y_dtype,
-                    stream=stream)
+    if bufs is None:
+        T, d = x.shape
+        bufs = layer_buffers(T, k, d, w_gate.shape[2], E, x.dtype, x.device,
+                             shared_f=0 if shared is None else shared[0].shape[2],
+                             capacity=capacity is not None, y_dtype=y_dtype,
+                             out_dtype=out_dtype)
+    b = bufs
+    logits, idx, gates = route(x, w_router, bias, k, out=(b["logits"], b["idx"], b["gates"]),
+                               stream=stream)
+    p = permute(idx, x, E, capacity=capacity, out=b, workspace=b["permute_ws"], stream=stream)
+    y = grouped_ffn(p["x_perm"], p["offsets"], w_gate, w_val, w_out, y=b["y"],
+                    workspace=b["ffn_ws"], stream=stream)
     y_sh = None
     if shared is not None:
-        T = x.shape[0]
-        off = torch.tensor([0, T], dtype=torch.int32, device=x.device)
-        y_sh = grouped_ffn(x, off, *shared, y_dtype=y_dtype, stream=stream)
-    out = combine(y, p["dest"], gates, k, y_shared=y_sh, out_dtype=out_dtype, stream=stream)
-    return dict(logits=logits, idx=idx, gates=gates, y=y, y_shared=y_sh, out=out, **p)
+        # one group of all T tokens: offsets NULL
+        y_sh = grouped_ffn(x, None, *shared, y=b["y_shared"], workspace=b["shared_ws"],
+                           stream=stream)
+    out = combine(y, p["dest"], gates, k, y_shared=y_sh, out=b["out"], stream=stream)
+    res = {key: b[key] for key in ("counts", "offsets", "perm_src", "dest", "x_perm")}
+    if "routed" in b:
+        res["routed"] = b["routed"]
+    return dict(logits=logits, idx=idx, gates=gates, y=y, y_shared=y_sh, out=out, **res)
 
 
 # ------------------------------------------------------------------ backward
@@ -345,8 +423,9 @@ def moe_layer(x, w_router, bias, k: int, w_gate, w_val, w_out, *, shared=None, c
 def ffn_gate_up_train(x_perm, offsets, w_gate, w_val, *, h=None, act=None, stream=None):
     """h = silu(x W_gate[e]) * (x W_val[e]) and the pre-activations act = [a | v]
     [N,2f] that the backward needs."""
-    for t, n in ((offsets, "offsets"), (w_gate, "w_gate"), (w_val, "w_val")):
+    for t, n in ((w_gate, "w_gate"), (w_val, "w_val")):
         _dev(t, n)
+    _offsets(offsets, w_gate.shape[0])
     ldx = _rows(x_perm, "x_perm")
     N, d = x_perm.shape
     E, _, f = w_gate.shape
@@ -488,11 +567,10 @@ def moe_layer_train(x, w_router, bias, k: int, w_gate, w_val, w_out, *, shared=N
     sv = dict(logits=logits, idx=idx, gates=gates, h=h, act=act, y=y, renorm=renorm, k=k, **p)
     y_sh = None
     if shared is not None:
-        T = x.shape[0]
-        off = torch.tensor([0, T], dtype=torch.int32, device=x.device)
-        h_sh, act_sh = ffn_gate_up_train(x, off, shared[0], shared[1], stream=stream)
-        y_sh = ffn_down(h_sh, off, shared[2], y_dtype=y_dtype, stream=stream)
-        sv.update(shared_off=off, h_shared=h_sh, act_shared=act_sh, y_shared=y_sh)
+        # one group of all T tokens: offsets NULL
+        h_sh, act_sh = ffn_gate_up_train(x, None, shared[0], shared[1], stream=stream)
+        y_sh = ffn_down(h_sh, None, shared[2], y_dtype=y_dtype, stream=stream)
+        sv.update(shared_off=None, h_shared=h_sh, act_shared=act_sh, y_shared=y_sh)
     sv["out"] = combine(y, p["dest"], gates, k, y_shared=y_sh, stream=stream)
     return sv
 
@@ -541,3 +619,23 @@ def moe_layer_backward(sv, d_out, x, w_router, w_gate, w_val, w_out, *, shared=N
                                          stream=stream)
     g.update(d_x=d_x, d_gates=d_gates, d_logits=d_l, d_y=d_y, d_act=d_act, d_x_perm=d_xp)
     return g
+
+
+# ------------------------------------------------------- measurement helpers
+
+def ceiling_mfma(blocks: int, iters: int, sink, stream=None) -> int:
+    """Enqueue the matrix-core loop (include/moe_ceiling.h); returns its flops."""
+    n = int(lib().moe_ceiling_mfma(blocks, iters, _p(sink), _stream(stream)))
+    if n < 0:
+        raise MoeError("moe_ceiling_mfma", n, "bad argument or launch")
+    return n
+
+
+def ceiling_copy(src, dst, nbytes: int, blocks: int, stream=None):
+    if lib().moe_ceiling_copy(_p(src), _p(dst), nbytes, blocks, _stream(stream)) != 0:
+        raise MoeError("moe_ceiling_copy", -1, "bad argument or launch")
+
+
+def ceiling_read(src, nbytes: int, sink, blocks: int, stream=None):
+    if lib().moe_ceiling_read(_p(src), nbytes, _p(sink), blocks, _stream(stream)) != 0:
+        raise MoeError("moe_ceiling_read", -1, "bad argument or launch")

@@ -30,9 +30,12 @@
  *    non-positive or too large sizes, k > E, too small a workspace) return an
  *    error code before anything is enqueued. A failed launch returns
  *    MOE_ERR_HIP. Device-side preconditions (ids in [0,E), counts summing to
- *    the row total, finite scores) are not checked; when broken the results
- *    are unspecified, but no kernel reads or writes outside the buffers
- *    described here.
+ *    the row total, finite scores, monotone expert offsets) are not checked
+ *    in the release library; when broken the results are unspecified, but no
+ *    kernel reads or writes outside the buffers described here (moe_combine
+ *    excepted: dest must index rows of y_perm). The debug library
+ *    (libmoe_debug.so, built with MOE_DEBUG) records each broken one, see
+ *    moe_debug_status.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -59,6 +62,27 @@ const char* moe_status_string(moe_status s);
 
 /* Library version as major*10000 + minor*100 + patch. */
 int moe_version(void);
+
+/*
+ * Device-side precondition checks (test-only; the debug library). The
+ * kernels of a MOE_DEBUG build record every broken precondition they meet
+ * as a bit of a device flag word:
+ *   MOE_DBG_ID_RANGE  1  a router id outside [0,E) reached moe_permute or
+ *                        moe_permute_capacity (a negative id moe_permute_range)
+ *   MOE_DBG_RECV_SUM  2  moe_permute_recv: a negative count, or counts not
+ *                        summing to N
+ *   MOE_DBG_NONFINITE 4  moe_route: a router score (with its bias) is not finite
+ *   MOE_DBG_OFFSETS   8  expert offsets given to the grouped products:
+ *                        offsets[0] != 0, decreasing, or past N
+ * moe_debug_status waits for the device (it is not for the layer's path),
+ * ORs the flags of every kernel into *flags and clears them when reset != 0.
+ * The release library returns MOE_ERR_UNSUPPORTED with *flags = 0.
+ */
+#define MOE_DBG_ID_RANGE 1u
+#define MOE_DBG_RECV_SUM 2u
+#define MOE_DBG_NONFINITE 4u
+#define MOE_DBG_OFFSETS 8u
+moe_status moe_debug_status(unsigned* flags, int reset);
 
 /*
  * Recommended row stride, in elements, for the packed rows x_perm [rows,d]
@@ -195,10 +219,20 @@ moe_status moe_permute_recv(const int32_t* recv_counts, int S, int E_loc, int N,
  * stored as bf16 (round to nearest even) between the two products; with
  * MOE_F32 it stays fp32. y is rounded once to y_dt: MOE_BF16 halves the bytes
  * the down product writes and the combine reads, MOE_F32 keeps the fp32 sums.
+ * Accuracy of a bf16 y: that one rounding (up to 2^-9 of an element) alone
+ * reaches 2.0-2.6e-2 of the RMS at the largest SwiGLU outputs of the
+ * measured workloads, so a bf16-stored y (and a bf16 moe_combine output)
+ * misses the 2e-2-of-RMS max-error bar stated for bf16 data with fp32
+ * accumulation; it meets that bar once its own storage rounding is taken
+ * off each element. The fp32 y meets the bar as is.
  * Experts with no rows cost nothing.
- * Limits: E <= 4096, N < 2^31. Any d, f >= 1 work; bf16 with d % 256 == 0,
- * f % 128 == 0, ld_x_perm % 8 == 0 and 16-byte aligned pointers takes the
- * matrix-core path.
+ * offsets may be NULL when E == 1: one expert over all N rows (the shared
+ * experts of a layer).
+ * Limits: E <= 4096, N < 2^31. Any d, f >= 1 work. bf16 takes the
+ * matrix-core path where the sizes tile and every pointer is 16-byte
+ * aligned: the gate/up product when d % 32 == 0, f % 128 == 0 and
+ * ld_x_perm % 8 == 0; the down product when f % 32 == 0 and d % 256 == 0
+ * (and f, d < 2^20). Otherwise, and for fp32, a plain fp32-FMA kernel runs.
  */
 size_t moe_grouped_ffn_workspace(int N, int d, int f, int E, moe_dtype dt);
 moe_status moe_grouped_ffn(const void* x_perm, int ld_x_perm, moe_dtype dt, int N, int d, int f,

@@ -1,4 +1,4 @@
-"""The C ABI library loads, exports every entry point include/moe.h declares,
+"""The C ABI library loads, exports every entry point include/*.h declares,
 and rejects bad host-side arguments before touching the device (no compute
 call is made here, so these run without a GPU)."""
 import ctypes
@@ -9,12 +9,17 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
+HEADERS = sorted(os.path.join(ROOT, "include", h) for h in os.listdir(os.path.join(ROOT, "include"))
+                 if h.endswith(".h"))
 
 
-def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+def _declared(headers=(HEADER,)):
+    names = set()
+    for h in headers:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +37,9 @@ def test_header_declares_the_path():
 
 
 def test_library_exports_every_declared_symbol(L):
-    for n in _declared():
+    names = _declared(HEADERS)
+    assert "moe_ceiling_mfma" in names
+    for n in names:
         assert hasattr(L, n), n
 
 
@@ -146,3 +153,19 @@ def test_empty_inputs_are_no_ops(L):
     assert L.moe_combine_backward(None, 1, None, 0, None, None, 0, 2, 64, None, 1, None,
                                   None) == 0
     assert L.moe_route_backward(None, None, None, None, 0, 8, 2, 1, None, None, None) == 0
+
+
+def test_debug_status_release_and_debug_builds(L):
+    """The release library reports that it checks no device preconditions;
+    the debug build (MOE_DEBUG) loads beside it and exports the same calls."""
+    from expert_dispatch_amd import ops
+    f = ctypes.c_uint(7)
+    assert L.moe_debug_status(ctypes.byref(f), 0) == 2   # MOE_ERR_UNSUPPORTED
+    assert f.value == 0
+    assert L.moe_debug_status(None, 0) == 1              # MOE_ERR_INVALID_ARG
+    if not os.path.exists(ops.debug_lib_path()):
+        pytest.skip("libmoe_debug.so not built")
+    D = ops.bind(ops.debug_lib_path())
+    for n in _declared(HEADERS):
+        assert hasattr(D, n), n
+    assert D.moe_version() == L.moe_version()

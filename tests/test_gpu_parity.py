@@ -4,9 +4,16 @@ Integer results (router ids, counts, offsets, permutation, packed rows) must
 match bit for bit, and so must the router scores, whose definition fixes
 every bit. Floating-point results must meet the gate: fp32 max relative
 error 1e-5; bf16 max error 2e-2 of the reference output's RMS (fp32
-accumulation). Reduced configs are compared element by element; the full
-workload shapes are compared on every integer output and on sampled rows of
-the floating-point ones, in the same launch configuration as the benchmark.
+accumulation). Every workload, the full shapes included, is compared
+element by element on every output (the large ones in row chunks), in the
+same launch configuration as the benchmark.
+
+Outputs the caller asks to store in bf16 (expert outputs y_perm, the layer
+output) carry one more rounding than the fp32 sums the bar is stated for,
+up to 2^-9 of each element; on the heavy-tailed SwiGLU outputs that alone
+reaches 2.0-2.6e-2 of the RMS at the largest elements, so they miss the
+strict bar by their own storage rounding. They are held to the bar after
+that rounding is taken off each element (check_rows with an allowance).
 """
 import functools
 import sys
@@ -18,8 +25,8 @@ import torch
 import oracle
 from expert_dispatch_amd import ops
 from expert_dispatch_amd import workloads as W
-from util import (check_bf16_stored, check_float, err_bf16, err_f32, sample_rows, to_numpy,
-                  to_torch, widen)
+from util import (U_BF16, assert_rows_equal, check_bf16_stored, check_float, check_rows,
+                  err_f32, stored_bf16_allowance, to_numpy, to_torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +45,13 @@ def _inputs(name):
     return W.generate(W.get(name))
 
 
+@functools.lru_cache(maxsize=1)
+def _oracle_layer(name, capacity):
+    """The oracle's whole layer (every token, every packed row), kept for the
+    next test of the same workload."""
+    return oracle.moe_layer(_inputs(name), capacity=capacity)
+
+
 def _device(inp):
     dev = {}
     for key in ("x", "w_router", "bias", "w_gate", "w_val", "w_out", "x_recv", "recv_counts"):
@@ -51,82 +65,94 @@ def _device(inp):
     return dev
 
 
-def _gpu_routed(dev, k, y_dtype=torch.float32, capacity=None):
+def _gpu_routed(dev, k, y_dtype=torch.float32, capacity=None, out_dtype=torch.float32):
     r = ops.moe_layer(dev["x"], dev["w_router"], dev.get("bias"), k, dev["w_gate"], dev["w_val"],
-                      dev["w_out"], shared=dev.get("shared"), y_dtype=y_dtype, capacity=capacity)
+                      dev["w_out"], shared=dev.get("shared"), y_dtype=y_dtype, capacity=capacity,
+                      out_dtype=out_dtype)
     torch.cuda.synchronize()
     return r
 
 
-def _check_routed(name, full, y_dtype=torch.float32, capacity=None):
+def _combine_allowance(o, k):
+    """Per-element bound of what bf16-stored expert outputs add to the layer
+    output: sum_s g[t,s] * U * |y[dest[t,s]]| (y, g the oracle's)."""
+    dest = o["dest"].reshape(-1, k)
+    g = np.asarray(o["gates"], np.float64).reshape(-1, k)
+    y = o["y"]
+
+    def allow(r0, r1, rb):
+        acc = np.zeros_like(rb)
+        for s_ in range(k):
+            rows = dest[r0:r1, s_]
+            ok = rows >= 0
+            acc[ok] += g[r0:r1, s_][ok, None] * np.abs(y[rows[ok]])
+        return U_BF16 * acc
+    return allow
+
+
+def _check_routed(name, y_dtypes=(torch.float32,), capacity=None):
+    """The whole layer on the GPU against the oracle, every output compared
+    element by element: once per storage type of the expert outputs."""
     cfg = W.get(name)
     say(f"[parity] {name}: generate")
     inp = _inputs(name)
     dev = _device(inp)
-    say(f"[parity] {name}: gpu layer (y {y_dtype}, capacity {capacity})")
-    g = _gpu_routed(dev, cfg.k, y_dtype, capacity)
-    rng = np.random.default_rng(0)
     T, k = cfg.T, cfg.k
-    tokens = None
-    if full:
-        tokens = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, size=96)])).astype(np.int32)
-    say(f"[parity] {name}: oracle")
-    o = oracle.moe_layer(inp, tokens=tokens, capacity=capacity)
-    kept = int(o["offsets"][-1])
-
-    # router: scores fixed bit for bit, ids bit-exact, weights at fp32 tolerance
-    np.testing.assert_array_equal(to_numpy(g["logits"]).view(np.uint32), o["logits"].view(np.uint32))
-    np.testing.assert_array_equal(to_numpy(g["idx"]), o["idx"])
-    e = err_f32(to_numpy(g["gates"]), o["gates"])
-    assert e <= 1e-5, f"gates rel err {e:.3e}"
-    # packing: bit-exact
-    for key in ("counts", "offsets", "dest"):
-        np.testing.assert_array_equal(to_numpy(g[key]), o[key], err_msg=key)
-    np.testing.assert_array_equal(to_numpy(g["perm_src"])[:kept], o["perm_src"][:kept])
-    if capacity is not None:
-        np.testing.assert_array_equal(to_numpy(g["routed"]), o["routed"], err_msg="routed")
-        say(f"[parity] {name}: capacity {capacity} keeps {kept} of {T * k} assignments")
-    # packed rows: bitwise copies
-    if full:
-        rows_t = torch.from_numpy(o["y_rows"]).to("cuda")
-        xp = to_numpy(g["x_perm"].index_select(0, rows_t))
-        y = to_numpy(g["y"].index_select(0, rows_t))
-    else:
-        xp = to_numpy(g["x_perm"])[:kept]
-        y = to_numpy(g["y"])[:kept]
-    np.testing.assert_array_equal(xp, o["x_perm"])
-    if y_dtype == torch.bfloat16:
-        # y_perm stored as bf16 (the narrow-output option): rounding the fp32
-        # sums to bf16 adds up to half an ulp (2^-9 of the element, about 1e-2
-        # of the RMS at the largest elements) on top of the product's error;
-        # the layer output below is held to the full bar
-        ey = err_bf16(widen(y), o["y"])
-        assert ey <= 4e-2, f"{name} y_perm (bf16 storage): max err / rms {ey:.3e} > 4e-2"
-    else:
-        ey = check_float(y, o["y"], cfg.dtype, f"{name} y_perm")
-    # shared experts (one fused SwiGLU of width 2f vs the sum of two)
-    if o["shared"] is not None:
-        sh = to_numpy(g["y_shared"])[o["tokens"]]
-        check_float(sh, o["shared"], cfg.dtype, f"{name} y_shared")
-    out = to_numpy(g["out"])[o["tokens"]]
-    eo = check_float(out, o["out"], cfg.dtype, f"{name} out")
-    say(f"[parity] {name}: ok  y_err={ey:.3e} out_err={eo:.3e}")
+    o = None
+    for y_dtype in y_dtypes:
+        say(f"[parity] {name}: gpu layer (y {y_dtype}, capacity {capacity})")
+        g = _gpu_routed(dev, k, y_dtype, capacity)
+        if o is None:
+            say(f"[parity] {name}: oracle")
+            o = _oracle_layer(name, capacity)
+        kept = int(o["offsets"][-1])
+        # router: scores fixed bit for bit, ids bit-exact, weights at fp32 tolerance
+        np.testing.assert_array_equal(to_numpy(g["logits"]).view(np.uint32),
+                                      o["logits"].view(np.uint32))
+        np.testing.assert_array_equal(to_numpy(g["idx"]), o["idx"])
+        e = err_f32(to_numpy(g["gates"]), o["gates"])
+        assert e <= 1e-5, f"gates rel err {e:.3e}"
+        # packing: bit-exact
+        for key in ("counts", "offsets", "dest"):
+            np.testing.assert_array_equal(to_numpy(g[key]), o[key], err_msg=key)
+        np.testing.assert_array_equal(to_numpy(g["perm_src"])[:kept], o["perm_src"][:kept])
+        if capacity is not None:
+            np.testing.assert_array_equal(to_numpy(g["routed"]), o["routed"], err_msg="routed")
+            say(f"[parity] {name}: capacity {capacity} keeps {kept} of {T * k} assignments")
+        # packed rows: bitwise copies, every row
+        assert_rows_equal(g["x_perm"], o["x_perm"], f"{name} x_perm")
+        if y_dtype == torch.bfloat16:
+            ey = check_rows(g["y"], o["y"], cfg.dtype, f"{name} y_perm (bf16-stored)",
+                            allowance=stored_bf16_allowance)
+            allow = _combine_allowance(o, k)
+        else:
+            ey = check_rows(g["y"], o["y"], cfg.dtype, f"{name} y_perm")
+            allow = None
+        # shared experts (one fused SwiGLU of width 2f vs the sum of two)
+        if o["shared"] is not None:
+            sh_allow = stored_bf16_allowance if y_dtype == torch.bfloat16 else None
+            check_rows(g["y_shared"], o["shared"], cfg.dtype, f"{name} y_shared",
+                       allowance=sh_allow)
+            if allow is not None:
+                base = allow
+                allow = lambda r0, r1, rb: base(r0, r1, rb) + U_BF16 * np.abs(o["shared"][r0:r1])
+        eo = check_rows(g["out"], o["out"], cfg.dtype, f"{name} out", allowance=allow)
+        say(f"[parity] {name}: ok  y {y_dtype}: y_err={ey:.3e} out_err={eo:.3e} "
+            f"({kept} packed rows, {T} tokens, all compared)")
+        del g
 
 
 @pytest.mark.parametrize("name", SMALL_ROUTED)
 def test_routed_layer_small(name):
-    _check_routed(name, full=False)
+    _check_routed(name)
 
 
 @pytest.mark.parametrize("name", FULL_ROUTED)
 def test_routed_layer_full(name):
-    _check_routed(name, full=True)
-
-
-@pytest.mark.parametrize("name", ["qwen3_30b_a3b", "dsv2_lite", "stress_zipf"])
-def test_routed_layer_full_bf16_expert_outputs(name):
-    """Expert outputs stored as bf16 (bench.py --y-dtype bf16)."""
-    _check_routed(name, full=True, y_dtype=torch.bfloat16)
+    """Full workload shapes, every element; the expert outputs stored fp32
+    (the measured path) and, where the bench offers it, bf16."""
+    ys = (torch.float32,) if name == "dsv2_lite_empty4" else (torch.float32, torch.bfloat16)
+    _check_routed(name, ys)
 
 
 def _capacity(name, factor):
@@ -138,21 +164,22 @@ def _capacity(name, factor):
                                          ("tiny_f32", 0.5), ("stress_small", 1.0)])
 def test_capacity_layer_small(name, factor):
     """Fixed-capacity packing (each expert keeps its first C assignments)."""
-    _check_routed(name, full=False, capacity=_capacity(name, factor))
+    _check_routed(name, capacity=_capacity(name, factor))
 
 
 def test_capacity_zero_drops_everything():
-    _check_routed("qwen3_small", full=False, capacity=0)
+    _check_routed("qwen3_small", capacity=0)
 
 
 @pytest.mark.parametrize("name,factor", [("qwen3_30b_a3b", 1.0), ("stress_zipf", 1.25)])
 def test_capacity_layer_full(name, factor):
-    _check_routed(name, full=True, capacity=_capacity(name, factor))
+    _check_routed(name, capacity=_capacity(name, factor))
 
 
-def _check_partial(name, full, out_dtype):
-    """One rank of the all-gather / reduce-scatter layout against the oracle;
-    the partial output in fp32 or bf16 (the reduce-scatter's wire format)."""
+def _check_partial(name, out_dtype):
+    """One rank of the all-gather / reduce-scatter layout against the oracle,
+    every element; the partial output in fp32 or bf16 (the reduce-scatter's
+    wire format, held to the bar after its own storage rounding)."""
     cfg = W.get(name)
     say(f"[parity] {name}: generate")
     inp = _inputs(name)
@@ -163,97 +190,70 @@ def _check_partial(name, full, out_dtype):
                               dev["w_gate"], dev["w_val"], dev["w_out"], out_dtype=out_dtype)
     torch.cuda.synchronize()
     T, k = cfg.T, cfg.k
-    tokens = None
-    if full:
-        rng = np.random.default_rng(0)
-        tokens = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, size=96)])).astype(np.int32)
     say(f"[parity] {name}: oracle")
-    o = oracle.moe_partial_layer(inp, cfg.e_first, tokens=tokens)
+    o = oracle.moe_partial_layer(inp, cfg.e_first)
     kept = int(o["offsets"][-1])
     np.testing.assert_array_equal(to_numpy(g["logits"]).view(np.uint32), o["logits"].view(np.uint32))
     np.testing.assert_array_equal(to_numpy(g["idx"]), o["idx"])
     for key in ("counts", "offsets", "dest"):
         np.testing.assert_array_equal(to_numpy(g[key]), o[key], err_msg=key)
     np.testing.assert_array_equal(to_numpy(g["perm_src"])[:kept], o["perm_src"][:kept])
-    if full:
-        rows_t = torch.from_numpy(o["y_rows"]).to("cuda")
-        xp = to_numpy(g["x_perm"].index_select(0, rows_t))
-        y = to_numpy(g["y"].index_select(0, rows_t))
-    else:
-        xp = to_numpy(g["x_perm"])[:kept]
-        y = to_numpy(g["y"])[:kept]
-    np.testing.assert_array_equal(xp, o["x_perm"])
-    ey = check_float(y, o["y"], cfg.dtype, f"{name} y_perm")
-    out = to_numpy(g["out"])[o["tokens"]]
-    if out_dtype == torch.bfloat16:
-        eo = check_bf16_stored(out, o["out"], f"{name} partial out (bf16)")
-    else:
-        eo = check_float(out, o["out"], cfg.dtype, f"{name} partial out")
+    assert_rows_equal(g["x_perm"], o["x_perm"], f"{name} x_perm")
+    ey = check_rows(g["y"], o["y"], cfg.dtype, f"{name} y_perm")
+    allow = stored_bf16_allowance if out_dtype == torch.bfloat16 else None
+    eo = check_rows(g["out"], o["out"], cfg.dtype, f"{name} partial out", allowance=allow)
     say(f"[parity] {name}: keeps {kept} of {T * k} assignments; ok y_err={ey:.3e} out_err={eo:.3e}")
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_partial_layer_small(out_dtype):
-    _check_partial("ag_rs_small", full=False, out_dtype=out_dtype)
+    _check_partial("ag_rs_small", out_dtype=out_dtype)
 
 
 def test_partial_layer_full():
-    _check_partial("ag_rs_rank", full=True, out_dtype=torch.bfloat16)
+    _check_partial("ag_rs_rank", out_dtype=torch.bfloat16)
 
 
-def _check_recv(name, full, zero_col=None):
+def _check_recv(name, zero_col=None):
+    """Receive side (reorder, expert MLPs, un-permute) against the oracle,
+    every element."""
     cfg = W.get(name)
     say(f"[parity] {name} recv: generate")
     inp = _inputs(name)
     if zero_col is not None:
         inp = W.zero_expert_column(inp, zero_col)
     dev = _device(inp)
-    N = cfg.N
     say(f"[parity] {name} recv: gpu")
     p = ops.permute_recv(dev["recv_counts"], dev["x_recv"])
     y = ops.grouped_ffn(p["x_perm"], p["offsets"], dev["w_gate"], dev["w_val"], dev["w_out"])
     out = ops.combine(y, p["dest"], None, 1)
     torch.cuda.synchronize()
-    rows = None
-    if full:
-        rng = np.random.default_rng(1)
-        rows = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, size=128)])).astype(np.int32)
     say(f"[parity] {name} recv: oracle")
-    o = oracle.moe_recv_layer(inp, rows=rows)
+    o = oracle.moe_recv_layer(inp)
     for key in ("counts", "offsets", "perm_src", "dest"):
         np.testing.assert_array_equal(to_numpy(p[key]), o[key], err_msg=key)
     if zero_col is not None:
         assert int(to_numpy(p["counts"])[zero_col]) == 0
-    if full:
-        rt = torch.from_numpy(o["y_rows"]).to("cuda")
-        xp = to_numpy(p["x_perm"].index_select(0, rt))
-        yy = to_numpy(y.index_select(0, rt))
-        # the packed buffer is a permutation of the received one: check it whole on the device
-        src = dev["x_recv"].index_select(0, p["perm_src"].long())
-        assert torch.equal(src.view(torch.int16), p["x_perm"].view(torch.int16))
-    else:
-        xp = to_numpy(p["x_perm"])
-        yy = to_numpy(y)
-    np.testing.assert_array_equal(xp, o["x_perm"])
-    check_float(yy, o["y"], cfg.dtype, f"{name} y_perm")
-    check_float(to_numpy(out)[o["rows"]], o["out"], cfg.dtype, f"{name} out")
-    say(f"[parity] {name} recv: ok")
+    assert_rows_equal(p["x_perm"], o["x_perm"], f"{name} x_perm")
+    check_rows(y, o["y"], cfg.dtype, f"{name} y_perm")
+    check_rows(out, o["out"], cfg.dtype, f"{name} out")
+    say(f"[parity] {name} recv: ok ({cfg.N} rows, all compared)")
 
 
 def test_recv_small():
-    _check_recv("ep_share_small", full=False)
+    _check_recv("ep_share_small")
 
 
 def test_recv_small_with_empty_expert():
-    _check_recv("ep_share_small", full=False, zero_col=2)
+    _check_recv("ep_share_small", zero_col=2)
 
 
 def test_recv_full():
-    _check_recv("ep_rank_share", full=True)
+    _check_recv("ep_rank_share")
 
 
 def test_recv_full_with_empty_expert():
-    _check_recv("ep_rank_share", full=True, zero_col=5)
+    _check_recv("ep_rank_share", zero_col=5)
 
 
 # ------------------------------------------------------------------- edges
@@ -489,7 +489,10 @@ def test_deterministic_bitwise():
 
 
 def test_bf16_outputs():
-    """y_perm and out stored as bf16 (the narrow-output variant) stay in tolerance."""
+    """y_perm and out both stored as bf16 (the narrow-output variant). Each
+    carries its own storage rounding (up to 2^-9 of the element) beyond the
+    fp32 sums the bar is stated for; with that rounding (and, for out, the
+    rounding of the y rows it sums) taken off, they meet 2e-2 of the RMS."""
     inp = _inputs("qwen3_small")
     dev = _device(inp)
     k = inp["k"]
@@ -500,12 +503,10 @@ def test_bf16_outputs():
     out = ops.combine(y, p["dest"], gates, k, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     o = oracle.moe_layer(inp)
-    yb = to_numpy(y)
-    ob = to_numpy(out)
-    # bf16 storage adds at most half an ulp (2^-9 relative) on top of the fp32 result
-    ref_rms = float(np.sqrt(np.mean(o["out"] ** 2)))
-    assert np.max(np.abs(widen(ob) - o["out"])) / ref_rms <= 4e-2
-    assert np.max(np.abs(widen(yb) - o["y"])) / float(np.sqrt(np.mean(o["y"] ** 2))) <= 4e-2
+    check_rows(y, o["y"], "bf16", "y_perm (bf16-stored)", allowance=stored_bf16_allowance)
+    y_allow = _combine_allowance(o, k)
+    check_rows(out, o["out"], "bf16", "out (bf16-stored, from bf16 y)",
+               allowance=lambda r0, r1, rb: y_allow(r0, r1, rb) + U_BF16 * np.abs(rb))
 
 
 @pytest.mark.parametrize("name", ["qwen3_small", "qwen3_30b_a3b", "stress_zipf", "dsv2_small_empty4"])

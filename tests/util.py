@@ -122,6 +122,75 @@ def check_grad(got, ref, dtype: str, what: str, stored_bf16: bool = False):
     return l2
 
 
+def _rms(ref: np.ndarray, chunk: int) -> float:
+    """RMS of a large float array, accumulated in float64 over row chunks."""
+    n = ref.shape[0]
+    tot = 0.0
+    for r0 in range(0, n, chunk):
+        blk = np.asarray(ref[r0:r0 + chunk], np.float64)
+        tot += float(np.sum(blk * blk))
+    return float(np.sqrt(tot / max(ref.size, 1)))
+
+
+def _host_rows(got, r0: int, r1: int) -> np.ndarray:
+    """Rows [r0, r1) of a device tensor or host array, widened to float64."""
+    if isinstance(got, torch.Tensor):
+        got = to_numpy(got[r0:r1])
+    else:
+        got = got[r0:r1]
+    return widen(got) if got.dtype == np.uint16 else np.asarray(got, np.float64)
+
+
+def check_rows(got, ref: np.ndarray, dtype: str, what: str, allowance=None,
+               chunk: int = 4096) -> float:
+    """Parity gate of a large 2-D float output, compared element by element in
+    row chunks (bounded host memory): ``got`` is a device tensor (or host
+    array) whose first len(ref) rows are compared with ``ref`` (float64).
+    fp32: max_i |d_i| / max(|ref_i|, rms(ref)) <= TOL_F32; bf16:
+    max_i |d_i| / rms(ref) <= TOL_BF16. ``allowance`` (bf16 only): a function
+    of (r0, r1, ref block) giving the per-element storage-rounding bound that
+    is taken off each error first (see check_bf16_stored)."""
+    n = ref.shape[0]
+    if n == 0:
+        return 0.0
+    rms = _rms(ref, chunk)
+    worst = 0.0
+    for r0 in range(0, n, chunk):
+        r1 = min(n, r0 + chunk)
+        g = _host_rows(got, r0, r1)
+        rb = np.asarray(ref[r0:r1], np.float64)
+        diff = np.abs(g - rb)
+        if dtype == "f32":
+            e = float(np.max(diff / np.maximum(np.abs(rb), rms if rms > 0 else 1.0)))
+        else:
+            if allowance is not None:
+                diff = np.maximum(diff - allowance(r0, r1, rb), 0.0) / (1 + U_BF16)
+            e = float(diff.max()) / (rms if rms > 0 else 1.0)
+        worst = max(worst, e)
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    assert worst <= tol, f"{what}: error {worst:.3e} > {tol} ({dtype} rule)"
+    return worst
+
+
+def stored_bf16_allowance(r0, r1, rb):
+    """Storage rounding of an output stored in bf16: at most U_BF16 of the
+    element's magnitude (twice the round-to-nearest bound, for the
+    difference between the computed and the exact value)."""
+    return U_BF16 * np.abs(rb)
+
+
+def assert_rows_equal(got, ref: np.ndarray, what: str, chunk: int = 8192):
+    """Bitwise equality of a device tensor's first len(ref) rows with ``ref``,
+    in row chunks."""
+    n = ref.shape[0]
+    for r0 in range(0, n, chunk):
+        r1 = min(n, r0 + chunk)
+        g = to_numpy(got[r0:r1]) if isinstance(got, torch.Tensor) else got[r0:r1]
+        if not np.array_equal(g, ref[r0:r1]):
+            bad = np.flatnonzero(np.any(g != ref[r0:r1], axis=tuple(range(1, ref.ndim))))
+            raise AssertionError(f"{what}: rows differ, first at {r0 + int(bad[0])}")
+
+
 def sample_rows(offsets: np.ndarray, per_expert: int, rng) -> np.ndarray:
     """First and last packed row of every non-empty expert plus random rows."""
     rows = []
