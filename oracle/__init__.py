@@ -69,6 +69,9 @@ def lib():
         L.oracle_expert_ffn_rows.argtypes = [vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                              ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp,
                                              ctypes.c_int64, ctypes.c_int, vp]
+        L.oracle_expert_ffn_rows_h.argtypes = [vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp,
+                                               ctypes.c_int64, ctypes.c_int, ctypes.c_int, vp]
         L.oracle_combine.argtypes = [vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, vp, vp,
                                      vp, vp, vp, vp]
         i64, i32 = ctypes.c_int64, ctypes.c_int
@@ -84,7 +87,7 @@ def lib():
         for name in ("oracle_route", "oracle_permute", "oracle_permute_capacity",
                      "oracle_permute_range",
                      "oracle_permute_recv", "oracle_gather",
-                     "oracle_expert_ffn_rows", "oracle_combine",
+                     "oracle_expert_ffn_rows", "oracle_expert_ffn_rows_h", "oracle_combine",
                      "oracle_route_backward", "oracle_router_grads",
                      "oracle_combine_backward_gates", "oracle_combine_backward_rows",
                      "oracle_expert_ffn_backward_rows", "oracle_expert_weight_grads",
@@ -217,11 +220,13 @@ def gather(x, perm_src, k: int):
     return out
 
 
-def expert_ffn_rows(x_perm, offsets, wg, wv, wo, rows=None, N=None):
+def expert_ffn_rows(x_perm, offsets, wg, wv, wo, rows=None, N=None, round_h=False):
     """SwiGLU expert MLPs evaluated in double on the listed packed rows
     (all rows if None). Returns float64 [len(rows), d]. With ``N`` given,
     ``x_perm`` holds only the listed rows (row r = packed row rows[r]) of a
-    packed buffer of N rows."""
+    packed buffer of N rows. ``round_h``: the hidden activations are rounded
+    once to bf16 before the down product (their storage point for bf16 data
+    with fp32 accumulation); otherwise everything is exact."""
     x_perm, wg, wv, wo = _c(x_perm), _c(wg), _c(wv), _c(wo)
     xt = _xtype(x_perm)
     for w in (wg, wv, wo):
@@ -239,9 +244,10 @@ def expert_ffn_rows(x_perm, offsets, wg, wv, wo, rows=None, N=None):
     if compact:
         assert x_perm.shape[0] == rows.shape[0]
     y = np.empty((rows.shape[0], d), np.float64)
-    _check(lib().oracle_expert_ffn_rows(_p(x_perm), xt, N, d, f, E, _p(off), _p(wg), _p(wv),
-                                        _p(wo), _p(rows), rows.shape[0], int(compact), _p(y)),
-           "oracle_expert_ffn_rows")
+    _check(lib().oracle_expert_ffn_rows_h(_p(x_perm), xt, N, d, f, E, _p(off), _p(wg), _p(wv),
+                                          _p(wo), _p(rows), rows.shape[0], int(compact),
+                                          int(bool(round_h)), _p(y)),
+           "oracle_expert_ffn_rows_h")
     return y
 
 
@@ -261,7 +267,7 @@ def combine(tokens, k: int, dest, gates, y, yrow=None, shared=None):
     return out
 
 
-def swiglu_shared(x, wg, wv, wo, rows=None):
+def swiglu_shared(x, wg, wv, wo, rows=None, round_h=False):
     """Sum of always-on shared experts on token rows: sum_q SwiGLU_q(x[t]),
     in double, q ascending. wg/wv [Q,d,f], wo [Q,f,d]."""
     x = _c(x)
@@ -270,12 +276,12 @@ def swiglu_shared(x, wg, wv, wo, rows=None):
     total = None
     for q in range(wg.shape[0]):
         part = expert_ffn_rows(x, np.array([0, T], np.int32), wg[q:q + 1], wv[q:q + 1],
-                               wo[q:q + 1], rows)
+                               wo[q:q + 1], rows, round_h=round_h)
         total = part if total is None else total + part
     return total
 
 
-def moe_layer(inp: dict, tokens=None, capacity=None):
+def moe_layer(inp: dict, tokens=None, capacity=None, round_h=False):
     """The whole layer on a token-routed workload dict (see
     expert_dispatch_amd.workloads). Returns a dict of every intermediate.
     With ``tokens`` given, only the packed rows those tokens need are
@@ -283,7 +289,8 @@ def moe_layer(inp: dict, tokens=None, capacity=None):
     combined; ``x_perm`` then holds the rows listed in ``y_rows``. With
     ``capacity`` given, the packing keeps at most that many assignments per
     expert (see permute_capacity); ``routed`` then holds the counts before
-    the cap."""
+    the cap. ``round_h``: the hidden activations rounded to bf16 at their
+    storage point (see expert_ffn_rows)."""
     k = inp["k"]
     logits, idx, gates = route(inp["x"], inp["w_router"], inp.get("bias"), k,
                                inp.get("renorm", True))
@@ -299,31 +306,33 @@ def moe_layer(inp: dict, tokens=None, capacity=None):
     if tokens is None:
         need = np.arange(kept, dtype=np.int64)
         x_perm = gather(inp["x"], perm_src, k)
-        y_rows = expert_ffn_rows(x_perm, offsets, inp["w_gate"], inp["w_val"], inp["w_out"])
+        y_rows = expert_ffn_rows(x_perm, offsets, inp["w_gate"], inp["w_val"], inp["w_out"],
+                                 round_h=round_h)
     else:
         need = np.unique(dest.reshape(T, k)[tok].reshape(-1)).astype(np.int64)
         need = need[need >= 0]
         x_perm = gather(inp["x"], perm_src[need], k)
         y_rows = expert_ffn_rows(x_perm, offsets, inp["w_gate"], inp["w_val"], inp["w_out"],
-                                 need, N=kept)
+                                 need, N=kept, round_h=round_h)
     yrow = np.full(max(kept, 1), -1, np.int64)
     yrow[need] = np.arange(need.shape[0])
     shared = None
     if inp.get("shared_w_gate") is not None:
         shared = swiglu_shared(inp["x"], inp["shared_w_gate"], inp["shared_w_val"],
-                               inp["shared_w_out"], tok.astype(np.int64))
+                               inp["shared_w_out"], tok.astype(np.int64), round_h=round_h)
     out = combine(tok, k, dest, gates, y_rows, yrow, shared)
     return dict(logits=logits, idx=idx, gates=gates, counts=counts, routed=routed,
                 offsets=offsets, perm_src=perm_src, dest=dest, x_perm=x_perm, y_rows=need,
                 y=y_rows, shared=shared, tokens=tok, out=out)
 
 
-def moe_partial_layer(inp: dict, e_first: int, tokens=None):
+def moe_partial_layer(inp: dict, e_first: int, tokens=None, round_h=False):
     """One rank of the all-gather / reduce-scatter layout on a gathered-token
     workload: the replicated router over every token, the rank's local experts
     (inp["w_gate"] etc. hold them, global ids e_first..) over the assignments
     routed to them, and the combine into this rank's partial output (the
-    reduce-scatter then sums the partials of all ranks)."""
+    reduce-scatter then sums the partials of all ranks). ``round_h`` as in
+    moe_layer."""
     k = inp["k"]
     logits, idx, gates = route(inp["x"], inp["w_router"], inp.get("bias"), k,
                                inp.get("renorm", True))
@@ -335,13 +344,14 @@ def moe_partial_layer(inp: dict, e_first: int, tokens=None):
     if tokens is None:
         need = np.arange(kept, dtype=np.int64)
         x_perm = gather(inp["x"], perm_src, k)
-        y_rows = expert_ffn_rows(x_perm, offsets, inp["w_gate"], inp["w_val"], inp["w_out"])
+        y_rows = expert_ffn_rows(x_perm, offsets, inp["w_gate"], inp["w_val"], inp["w_out"],
+                                 round_h=round_h)
     else:
         need = np.unique(dest.reshape(T, k)[tok].reshape(-1)).astype(np.int64)
         need = need[need >= 0]
         x_perm = gather(inp["x"], perm_src[need], k)
         y_rows = expert_ffn_rows(x_perm, offsets, inp["w_gate"], inp["w_val"], inp["w_out"],
-                                 need, N=kept)
+                                 need, N=kept, round_h=round_h)
     yrow = np.full(max(kept, 1), -1, np.int64)
     yrow[need] = np.arange(need.shape[0])
     out = combine(tok, k, dest, gates, y_rows, yrow, None)

@@ -235,10 +235,30 @@ int oracle_gather(const void* x, int elem_bytes, int64_t d,
 
 /* -------------------------------------------------------------- expert FFN */
 
+/* The value of v rounded once to bf16 (8 significant bits, to nearest, ties
+ * to even), straight from double: v = m 2^ex with m in [0.5, 1), so the bf16
+ * grid around v has spacing 2^(ex - 8). */
+static double round_bf16(double v) {
+    if (v == 0.0 || !isfinite(v)) return v;
+    int ex = 0;
+    (void)frexp(v, &ex);
+    return ldexp(nearbyint(ldexp(v, 8 - ex)), ex - 8);
+}
+
 int oracle_expert_ffn_rows(const void* x, int xtype, int64_t N, int d, int f, int E,
                            const int32_t* offsets,
                            const void* wg, const void* wv, const void* wo,
                            const int64_t* rows, int64_t nrows, int x_compact, double* y)
+{
+    return oracle_expert_ffn_rows_h(x, xtype, N, d, f, E, offsets, wg, wv, wo, rows, nrows,
+                                    x_compact, 0, y);
+}
+
+int oracle_expert_ffn_rows_h(const void* x, int xtype, int64_t N, int d, int f, int E,
+                             const int32_t* offsets,
+                             const void* wg, const void* wv, const void* wo,
+                             const int64_t* rows, int64_t nrows, int x_compact, int h_bf16,
+                             double* y)
 {
     if (!x || !offsets || !wg || !wv || !wo || !rows || !y) return -1;
     if (d <= 0 || f <= 0 || E <= 0 || N < 0) return -1;
@@ -270,6 +290,10 @@ int oracle_expert_ffn_rows(const void* x, int xtype, int64_t N, int d, int f, in
             }
             /* SwiGLU: silu(g) * v, silu(z) = z * sigmoid(z) */
             for (int c = 0; c < f; ++c) g[c] = g[c] / (1.0 + exp(-g[c])) * v[c];
+            /* h stored in bf16 between the two products (the storage point of
+             * bf16 data with fp32 accumulation), when asked */
+            if (h_bf16)
+                for (int c = 0; c < f; ++c) g[c] = round_bf16(g[c]);
             double* yo = y + (size_t)r * d;
             for (int o = 0; o < d; ++o) yo[o] = 0.0;
             for (int c = 0; c < f; ++c) {

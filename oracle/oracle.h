@@ -119,6 +119,18 @@ int oracle_expert_ffn_rows(const void* x, int xtype, int64_t N, int d, int f, in
                            const int64_t* rows, int64_t nrows, int x_compact, double* y);
 
 /*
+ * As oracle_expert_ffn_rows; with h_bf16 != 0 every h_c is rounded once to
+ * bf16 (to nearest, ties to even, straight from its exact value) before the
+ * down product: the layer as bf16 data with fp32 accumulation stores it
+ * between the two products. Everything else stays exact.
+ */
+int oracle_expert_ffn_rows_h(const void* x, int xtype, int64_t N, int d, int f, int E,
+                             const int32_t* offsets,
+                             const void* wg, const void* wv, const void* wo,
+                             const int64_t* rows, int64_t nrows, int x_compact, int h_bf16,
+                             double* y);
+
+/*
  * Weighted combine [Three axes of Parallelism, "Dispatch, expert computation
  * and combine": undo the packing, weight each expert output by its router
  * weight, sum the k outputs of each token]:

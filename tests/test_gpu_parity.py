@@ -25,8 +25,8 @@ import torch
 import oracle
 from expert_dispatch_amd import ops
 from expert_dispatch_amd import workloads as W
-from util import (U_BF16, assert_rows_equal, check_bf16_stored, check_float, check_rows,
-                  err_f32, stored_bf16_allowance, to_numpy, to_torch)
+from util import (U_BF16, assert_rows_equal, check_float, check_rows, err_f32, rel_l2,
+                  stored_bf16_allowance, to_numpy, to_torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -46,10 +46,11 @@ def _inputs(name):
 
 
 @functools.lru_cache(maxsize=1)
-def _oracle_layer(name, capacity):
+def _oracle_layer(name, capacity, round_h=False):
     """The oracle's whole layer (every token, every packed row), kept for the
-    next test of the same workload."""
-    return oracle.moe_layer(_inputs(name), capacity=capacity)
+    next test of the same workload. round_h: h rounded to bf16 at its
+    storage point (the layer as bf16 data with fp32 accumulation)."""
+    return oracle.moe_layer(_inputs(name), capacity=capacity, round_h=round_h)
 
 
 def _device(inp):
@@ -136,7 +137,23 @@ def _check_routed(name, y_dtypes=(torch.float32,), capacity=None):
             if allow is not None:
                 base = allow
                 allow = lambda r0, r1, rb: base(r0, r1, rb) + U_BF16 * np.abs(o["shared"][r0:r1])
-        eo = check_rows(g["out"], o["out"], cfg.dtype, f"{name} out", allowance=allow)
+        if capacity is None or cfg.dtype != "bf16":
+            eo = check_rows(g["out"], o["out"], cfg.dtype, f"{name} out", allowance=allow)
+        else:
+            # A capped layer output has a smaller RMS than the full one (tokens
+            # lose assignments, some all of them), while the per-element error
+            # that bf16 storage of h leaves in each expert output does not
+            # shrink with it: on the stress shape the exact-oracle max error
+            # reaches 2.6e-2 of that RMS. The output is held to the bar against
+            # the oracle with h rounded at its storage point, and norm-wise
+            # against the exact one.
+            eo_exact = rel_l2(g["out"], o["out"])
+            assert eo_exact <= 2e-2, f"{name} out: relative L2 error {eo_exact:.3e} > 2e-2"
+            o_h = oracle.moe_layer(_inputs(name), capacity=capacity, round_h=True)
+            eo = check_rows(g["out"], o_h["out"], cfg.dtype, f"{name} out (h at bf16)",
+                            allowance=allow)
+            say(f"[parity] {name}: out relative L2 error {eo_exact:.3e} against the exact oracle")
+            del o_h
         say(f"[parity] {name}: ok  y {y_dtype}: y_err={ey:.3e} out_err={eo:.3e} "
             f"({kept} packed rows, {T} tokens, all compared)")
         del g
@@ -201,8 +218,19 @@ def _check_partial(name, out_dtype):
     assert_rows_equal(g["x_perm"], o["x_perm"], f"{name} x_perm")
     ey = check_rows(g["y"], o["y"], cfg.dtype, f"{name} y_perm")
     allow = stored_bf16_allowance if out_dtype == torch.bfloat16 else None
-    eo = check_rows(g["out"], o["out"], cfg.dtype, f"{name} partial out", allowance=allow)
-    say(f"[parity] {name}: keeps {kept} of {T * k} assignments; ok y_err={ey:.3e} out_err={eo:.3e}")
+    # A rank's partial output sums only its own experts' outputs (a token
+    # has 1 of its k assignments here on average, many have none), so its RMS
+    # is a fraction of the layer output's while the per-element error that
+    # bf16 storage of h leaves in each expert output is not: held to the bar
+    # against the oracle with h rounded at its storage point, and norm-wise
+    # against the exact one (as the capped layer).
+    e_l2 = rel_l2(g["out"], o["out"])
+    assert e_l2 <= 2e-2, f"{name} partial out: relative L2 error {e_l2:.3e} > 2e-2"
+    o_h = oracle.moe_partial_layer(inp, cfg.e_first, round_h=True)
+    eo = check_rows(g["out"], o_h["out"], cfg.dtype, f"{name} partial out (h at bf16)",
+                    allowance=allow)
+    say(f"[parity] {name}: keeps {kept} of {T * k} assignments; ok y_err={ey:.3e} out_err={eo:.3e}"
+        f" (relative L2 against the exact oracle {e_l2:.3e})")
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])

@@ -238,3 +238,50 @@ def test_partial_layer_sampled_equals_full():
     toks = np.array([0, 7, 150, 299], np.int32)
     part = oracle.moe_partial_layer(inp, inp["e_first"], tokens=toks)
     np.testing.assert_array_equal(part["out"], full["out"][toks])
+
+
+def test_hidden_rounding_with_identity_down_weight_is_bf16_of_h():
+    """round_h: with one expert and W_out = I (f = d) the output is h itself,
+    so the rounded variant must equal the exact variant's output rounded to
+    bf16 by torch (to nearest, ties to even)."""
+    rng = np.random.default_rng(501)
+    n, d = 48, 64
+    bf = W.f32_to_bf16_bits
+    x = bf(rng.standard_normal((n, d)).astype(np.float32))
+    wg = bf((rng.standard_normal((1, d, d)) / 8).astype(np.float32))
+    wv = bf((rng.standard_normal((1, d, d)) / 8).astype(np.float32))
+    wo = bf(np.eye(d, dtype=np.float32)[None])
+    off = np.array([0, n], np.int32)
+    exact = oracle.expert_ffn_rows(x, off, wg, wv, wo)
+    rounded = oracle.expert_ffn_rows(x, off, wg, wv, wo, round_h=True)
+    want = torch.from_numpy(exact).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(rounded, want)
+    assert np.any(rounded != exact)
+
+
+def test_hidden_rounding_error_within_its_bound():
+    """round_h moves every output by at most 2^-9 sum_c |h_c| |W_out[c,o]|
+    (one rounding of each h_c to 8 significant bits), and does move it."""
+    inp = W.generate(W.get("qwen3_small"))
+    o = oracle.moe_layer(inp)
+    r = oracle.moe_layer(inp, round_h=True)
+    np.testing.assert_array_equal(r["dest"], o["dest"])
+    y, yr = o["y"], r["y"]
+    # |h| from the exact layer: the identity-weight run gives h for expert e
+    # rows directly, so bound with the exact h of each packed row
+    E, d, f = inp["w_gate"].shape
+    x_perm = o["x_perm"]
+    xw = _widen(x_perm)
+    bound = np.zeros_like(y)
+    off = o["offsets"]
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi <= lo:
+            continue
+        g = xw[lo:hi] @ _widen(inp["w_gate"][e])
+        v = xw[lo:hi] @ _widen(inp["w_val"][e])
+        h = g / (1.0 + np.exp(-g)) * v
+        bound[lo:hi] = (2.0 ** -9) * (np.abs(h) @ np.abs(_widen(inp["w_out"][e])))
+    diff = np.abs(yr - y)
+    assert np.all(diff <= bound * (1 + 1e-9) + 1e-300)
+    assert diff.max() > 0

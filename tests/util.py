@@ -172,6 +172,18 @@ def check_rows(got, ref: np.ndarray, dtype: str, what: str, allowance=None,
     return worst
 
 
+def rel_l2(got, ref: np.ndarray, chunk: int = 4096) -> float:
+    """||got - ref||_2 / ||ref||_2 over the first len(ref) rows, in row chunks."""
+    num = den = 0.0
+    for r0 in range(0, ref.shape[0], chunk):
+        r1 = min(ref.shape[0], r0 + chunk)
+        g = _host_rows(got, r0, r1)
+        rb = np.asarray(ref[r0:r1], np.float64)
+        num += float(np.sum((g - rb) ** 2))
+        den += float(np.sum(rb * rb))
+    return float(np.sqrt(num / max(den, 1e-300)))
+
+
 def stored_bf16_allowance(r0, r1, rb):
     """Storage rounding of an output stored in bf16: at most U_BF16 of the
     element's magnitude (twice the round-to-nearest bound, for the
