@@ -10,6 +10,8 @@ hipError_t launch_route(const void* x, moe_dtype dt, const void* w, const float*
                         int d, int E, int k, int renorm, float* logits, int32_t* idx,
                         float* gates, hipStream_t st);
 size_t permute_ws_bytes(int T, int k, int E);
+size_t static_permute_bytes();
+void* static_permute_scratch(hipError_t* err);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int e_base, int E, int id_hi, int cap,
                           const void* x, int es, int d, int32_t* routed,
                           int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* dest,
@@ -153,6 +155,27 @@ moe_status moe_permute(const int32_t* topk_idx, int T, int k, int E, const void*
     if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
     if (T > 0 && (!topk_idx || !x || !perm_src || !dest || !x_perm)) return MOE_ERR_INVALID_ARG;
     if (!ws || ws_bytes < moe::permute_ws_bytes(T, k, E)) return MOE_ERR_WORKSPACE;
+    return hip_status(moe::launch_permute(topk_idx, T, k, 0, E, E, INT32_MAX, x, elem_size(dt), d,
+                                          nullptr, counts, offsets, perm_src, dest, x_perm, ld,
+                                          ws, as_stream(stream)));
+}
+
+moe_status moe_permute_noalloc(const int32_t* topk_idx, int T, int k, int E, const void* x,
+                               moe_dtype dt, int d, int32_t* counts, int32_t* offsets,
+                               int32_t* perm_src, int32_t* dest, void* x_perm, int ld_x_perm,
+                               void* stream)
+{
+    if (!valid_dtype(dt) || T < 0 || k <= 0 || E <= 0 || d <= 0) return MOE_ERR_INVALID_ARG;
+    const int ld = resolve_ld(ld_x_perm, d);
+    if (ld < 0) return MOE_ERR_INVALID_ARG;
+    if (E > kMaxRouteE || k > kMaxK || (long long)T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
+    if (T > 0 && (!topk_idx || !x || !perm_src || !dest || !x_perm)) return MOE_ERR_INVALID_ARG;
+    // the chunk histograms must fit the library's static per-GPU array
+    if (moe::permute_ws_bytes(T, k, E) > moe::static_permute_bytes()) return MOE_ERR_WORKSPACE;
+    hipError_t err = hipSuccess;
+    void* ws = moe::static_permute_scratch(&err);
+    if (!ws) return MOE_ERR_HIP;
     return hip_status(moe::launch_permute(topk_idx, T, k, 0, E, E, INT32_MAX, x, elem_size(dt), d,
                                           nullptr, counts, offsets, perm_src, dest, x_perm, ld,
                                           ws, as_stream(stream)));

@@ -24,6 +24,7 @@
 // expert) block starts from the count matrix in LDS, then each wavefront maps
 // its rows and copies them.
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 
@@ -373,6 +374,45 @@ hipError_t launch_permute_recv(const int32_t* recv, int S, int E, int N, const v
                                                          perm_src, dest, (uint16_t*)x_perm,
                                                          (int)(ld_bytes / 2));
     return hipGetLastError();
+}
+
+// ------------------------------------------------ packing without allocation
+// Callers that cannot allocate (code under HIP graph capture, tight serving
+// loops) take the chunk histograms in this file-scope device array instead
+// of a workspace: kStaticPermuteBytes per GPU, held until the process ends.
+// In host code the array's name is a stand-in, not a device address: the
+// address each device uses comes from hipGetSymbolAddress, once per device,
+// with that device current.
+constexpr size_t kStaticPermuteBytes = size_t(1) << 20;
+static __device__ __align__(256) int32_t scratch[kStaticPermuteBytes / sizeof(int32_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // per device, filled on first use
+}  // namespace
+
+size_t static_permute_bytes() { return kStaticPermuteBytes; }
+
+// The current device's address of `scratch`, or nullptr (with the HIP error
+// in *err) if it cannot be had.
+void* static_permute_scratch(hipError_t* err) {
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    *err = hipSuccess;
+    return g_scratch_ptr[dev];
 }
 
 MOE_DBG_READER(permute)

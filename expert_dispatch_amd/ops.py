@@ -55,6 +55,7 @@ def bind(path: str):
     sigs = {
         "moe_route": [vp, i, vp, vp, i, i, i, i, i, vp, vp, vp, vp],
         "moe_permute": [vp, i, i, i, vp, i, i, vp, vp, vp, vp, vp, i, vp, sz, vp],
+        "moe_permute_noalloc": [vp, i, i, i, vp, i, i, vp, vp, vp, vp, vp, i, vp],
         "moe_permute_capacity": [vp, i, i, i, i, vp, i, i, vp, vp, vp, vp, vp, vp, i, vp, sz,
                                  vp],
         "moe_permute_range": [vp, i, i, i, i, vp, i, i, vp, vp, vp, vp, vp, i, vp, sz, vp],

@@ -143,6 +143,24 @@ moe_status moe_permute(const int32_t* topk_idx, int T, int k, int E,
                        void* x_perm, int ld_x_perm, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_permute without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments, results and limits as
+ * moe_permute, minus ws / ws_bytes: the chunk histograms live in a static
+ * device array of the library, 1 MiB per GPU (held until the process ends),
+ * so moe_permute_workspace(T, k, E) must be at most 1 MiB, else
+ * MOE_ERR_WORKSPACE (at E = 1024 that is up to about 10^6 assignments). The
+ * array's address on the current device is looked up once (MOE_ERR_HIP if
+ * that fails). Nothing is allocated and nothing needs clearing: every call
+ * writes the part it reads. Calls that overlap on one GPU (on different
+ * streams) share the array and race; serialise them.
+ */
+moe_status moe_permute_noalloc(const int32_t* topk_idx, int T, int k, int E,
+                               const void* x, moe_dtype dt, int d,
+                               int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                               int32_t* dest, void* x_perm, int ld_x_perm, void* stream);
+
+/*
  * Fixed-capacity packing, a routing variant the pages name but do not define
  * (Modalities EP PR, "Not done yet / follow-ups": fixed-capacity dispatchers;
  * "Three axes of Parallelism", "Discussion, Future work": capacity load

@@ -169,3 +169,17 @@ def test_debug_status_release_and_debug_builds(L):
     for n in _declared(HEADERS):
         assert hasattr(D, n), n
     assert D.moe_version() == L.moe_version()
+
+
+def test_noalloc_packing_rejects_sizes_past_its_static_array(L):
+    """moe_permute_noalloc keeps its chunk histograms in a 1 MiB static
+    array per GPU: a request that needs more returns MOE_ERR_WORKSPACE
+    before anything is enqueued (the pointers here are never dereferenced)."""
+    fake = ctypes.c_void_p(0x1000)
+    assert L.moe_permute_workspace(1 << 20, 2, 1024) > (1 << 20)
+    assert L.moe_permute_noalloc(fake, 1 << 20, 2, 1024, fake, 1, 64, fake, fake, fake, fake, fake,
+                                 0, None) == 3
+    assert L.moe_permute_noalloc(fake, 16, 2, 1025, fake, 1, 64, fake, fake, fake, fake, fake,
+                                 0, None) == 2   # E past the packing's limit
+    assert L.moe_permute_noalloc(fake, 16, 0, 8, fake, 1, 64, fake, fake, fake, fake, fake,
+                                 0, None) == 1   # k <= 0
