@@ -124,6 +124,10 @@ __device__ __forceinline__ void lds_barrier() {
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Buffers streamed once and far larger than the 256 MB Infinity Cache are
+// read or written with non-temporal accesses past this size.
+constexpr long long kStreamBytes = 1LL << 30;
+
 // ------------------------------------------------------------ debug checks
 // Device-side preconditions the release build leaves unchecked (the kernels
 // only keep every access inside its buffer when they are broken). A build

@@ -178,8 +178,8 @@ __global__ __launch_bounds__(kPermThreads) void perm_rank_kernel(
 }
 
 // x_perm[dest[t*k+s]] = x[t]: one wavefront per token, V-byte vectors;
-// packed rows are out_stride vectors apart.
-template <typename V>
+// packed rows are out_stride vectors apart. NTS: non-temporal stores.
+template <typename V, bool NTS>
 __global__ __launch_bounds__(256) void perm_gather_kernel(
     const V* __restrict__ x, int vecs_per_row, int T, int k, const int32_t* __restrict__ dest,
     int rows_out, V* __restrict__ x_perm, int out_stride)
@@ -204,7 +204,10 @@ __global__ __launch_bounds__(256) void perm_gather_kernel(
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int c = c0 + u * kWave + lane;
-                if (c < vecs_per_row) dst[c] = v[u];
+                if (c < vecs_per_row) {
+                    if constexpr (NTS) __builtin_nontemporal_store(v[u], dst + c);
+                    else dst[c] = v[u];
+                }
             }
         }
     }
@@ -342,13 +345,16 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int e_base, int E, i
         const size_t row_bytes = (size_t)d * es;
         const size_t ld_bytes = (size_t)ld * es;
         const dim3 grid((T + 3) / 4);
+        // (non-temporal stores of the packed rows measured no faster on the
+        // stress layer's routing, whose rows land in ascending order inside
+        // each expert's region; plain stores everywhere)
         if (row_bytes % 16 == 0 && ld_bytes % 16 == 0 && (uintptr_t)x % 16 == 0 &&
             (uintptr_t)x_perm % 16 == 0)
-            perm_gather_kernel<u32x4><<<grid, 256, 0, st>>>(
+            perm_gather_kernel<u32x4, false><<<grid, 256, 0, st>>>(
                 (const u32x4*)x, (int)(row_bytes / 16), T, k, dest, TK, (u32x4*)x_perm,
                 (int)(ld_bytes / 16));
         else
-            perm_gather_kernel<uint16_t><<<grid, 256, 0, st>>>(
+            perm_gather_kernel<uint16_t, false><<<grid, 256, 0, st>>>(
                 (const uint16_t*)x, (int)(row_bytes / 2), T, k, dest, TK, (uint16_t*)x_perm,
                 (int)(ld_bytes / 2));
     }
