@@ -84,6 +84,12 @@ def lib():
                                                       vp, vp, i64, i32, vp, vp, vp, vp]
         L.oracle_expert_weight_grads.argtypes = [vp, i32, i64, i32, i32, i32, vp, vp, vp, vp,
                                                  vp, vp, vp, i64, ctypes.c_double, vp, vp, vp]
+        L.oracle_expert_ffn_backward_rows_h.argtypes = [vp, i32, i64, i32, i32, i32, vp, vp, vp,
+                                                        vp, vp, i64, i32, i32, vp, vp, vp, vp]
+        L.oracle_expert_weight_grads_h.argtypes = [vp, i32, i64, i32, i32, i32, vp, vp, vp, vp,
+                                                   vp, vp, vp, i64, ctypes.c_double, i32, vp, vp,
+                                                   vp]
+        L.oracle_round_bf16.argtypes = [vp, i64]
         for name in ("oracle_route", "oracle_permute", "oracle_permute_capacity",
                      "oracle_permute_range",
                      "oracle_permute_recv", "oracle_gather",
@@ -91,6 +97,8 @@ def lib():
                      "oracle_route_backward", "oracle_router_grads",
                      "oracle_combine_backward_gates", "oracle_combine_backward_rows",
                      "oracle_expert_ffn_backward_rows", "oracle_expert_weight_grads",
+                     "oracle_expert_ffn_backward_rows_h", "oracle_expert_weight_grads_h",
+                     "oracle_round_bf16",
                      "oracle_route_stats"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -450,10 +458,23 @@ def combine_backward_rows(perm_src, rows, k: int, gates, d_out):
     return out
 
 
-def expert_ffn_backward_rows(x_perm, offsets, wg, wv, wo, d_y, rows=None, N=None):
+# storage points of bf16 training (oracle.h ORACLE_STORE_*)
+STORE_DY, STORE_ACT, STORE_DACT, STORE_DX = 1, 2, 4, 8
+
+
+def round_bf16(a) -> np.ndarray:
+    """float64 copy of ``a`` with every value rounded once to bf16 (to
+    nearest, ties to even)."""
+    out = np.array(a, dtype=np.float64, copy=True, order="C")
+    _check(lib().oracle_round_bf16(_p(out), out.size), "oracle_round_bf16")
+    return out
+
+
+def expert_ffn_backward_rows(x_perm, offsets, wg, wv, wo, d_y, rows=None, N=None, store=0):
     """(act, d_act, d_x) of the listed packed rows, float64: act = [a | v]
     [n,2f], d_act = [da | dv] [n,2f], d_x [n,d]. ``rows`` and ``N`` as in
-    expert_ffn_rows; d_y [n,d] the rows' output gradients."""
+    expert_ffn_rows; d_y [n,d] the rows' output gradients. ``store``: an OR
+    of STORE_* (the values rounded to bf16 at those storage points)."""
     x_perm, wg, wv, wo = _c(x_perm), _c(wg), _c(wv), _c(wo)
     xt = _xtype(x_perm)
     compact = N is not None
@@ -468,14 +489,15 @@ def expert_ffn_backward_rows(x_perm, offsets, wg, wv, wo, d_y, rows=None, N=None
     act = np.empty((n, 2 * f), np.float64)
     dact = np.empty((n, 2 * f), np.float64)
     dx = np.empty((n, d), np.float64)
-    _check(lib().oracle_expert_ffn_backward_rows(_p(x_perm), xt, N, d, f, E, _p(off), _p(wg),
-                                                 _p(wv), _p(wo), _p(rows), n, int(compact),
-                                                 _p(dy), _p(act), _p(dact), _p(dx)),
-           "oracle_expert_ffn_backward_rows")
+    _check(lib().oracle_expert_ffn_backward_rows_h(_p(x_perm), xt, N, d, f, E, _p(off), _p(wg),
+                                                   _p(wv), _p(wo), _p(rows), n, int(compact),
+                                                   int(store), _p(dy), _p(act), _p(dact),
+                                                   _p(dx)),
+           "oracle_expert_ffn_backward_rows_h")
     return act, dact, dx
 
 
-def expert_weight_grads(x_perm, offsets, wg, wv, wo, d_y, pairs, scale: float = 1.0):
+def expert_weight_grads(x_perm, offsets, wg, wv, wo, d_y, pairs, scale: float = 1.0, store=0):
     """Weight gradients of the listed (expert, hidden column) pairs:
     (dWg[e][:,c], dWv[e][:,c], dWo[e][c,:]), each float64 [P,d]. x_perm and
     d_y hold every packed row."""
@@ -491,10 +513,10 @@ def expert_weight_grads(x_perm, offsets, wg, wv, wo, d_y, pairs, scale: float = 
     dy = _c(d_y, np.float64)
     assert dy.shape == (N, d)
     outs = [np.empty((P, d), np.float64) for _ in range(3)]
-    _check(lib().oracle_expert_weight_grads(_p(x_perm), xt, N, d, f, E, _p(off), _p(wg),
-                                            _p(wv), _p(wo), _p(dy), _p(pe), _p(pc), P,
-                                            float(scale), *(_p(o) for o in outs)),
-           "oracle_expert_weight_grads")
+    _check(lib().oracle_expert_weight_grads_h(_p(x_perm), xt, N, d, f, E, _p(off), _p(wg),
+                                              _p(wv), _p(wo), _p(dy), _p(pe), _p(pc), P,
+                                              float(scale), int(store), *(_p(o) for o in outs)),
+           "oracle_expert_weight_grads_h")
     return tuple(outs)
 
 
@@ -505,7 +527,7 @@ def all_pairs(E: int, f: int) -> np.ndarray:
 
 
 def moe_backward(inp: dict, d_out, tokens=None, pairs=None, scale: float = 1.0,
-                 capacity=None, e_first=None):
+                 capacity=None, e_first=None, store_bf16=False):
     """Gradients of the loss L = sum(out * d_out) through the layer (or, with
     ``e_first``, through one rank's partial output), in double.
 
@@ -517,7 +539,14 @@ def moe_backward(inp: dict, d_out, tokens=None, pairs=None, scale: float = 1.0,
     gradients are formed over all packed rows (all_pairs(E, f) for all of
     them), multiplied by ``scale``. Shared experts, where the workload has
     them, add their input gradient to d_x; their weight gradients are the
-    same functions on the token rows (expert_weight_grads with offsets [0,T])."""
+    same functions on the token rows (expert_weight_grads with offsets [0,T]).
+
+    ``store_bf16``: the chain as bf16 training hands values between its
+    kernels, every value rounded once to bf16 at those storage points (the
+    forward's h; the backward's d_y, the kept pre-activations a and v, their
+    gradients da and dv, the packed rows' input gradients, and the logit
+    gradients that the router weight gradient's product reads); all sums
+    exact. Otherwise every value is exact."""
     k = inp["k"]
     renorm = inp.get("renorm", True)
     x = inp["x"]
@@ -547,19 +576,29 @@ def moe_backward(inp: dict, d_out, tokens=None, pairs=None, scale: float = 1.0,
     # combine: out[t] = sum_s g[t,s] y[dest[t,s]]
     d_gates = combine_backward_gates(tok, k, dest, y, yrow, dout[tok])
     d_y = combine_backward_rows(perm_src, need, k, gates, dout)
-    act, d_act, d_xp = expert_ffn_backward_rows(xp, offsets, wg, wv, wo, d_y, need, N=kept)
+    routed_store = (STORE_DY | STORE_ACT | STORE_DACT | STORE_DX) if store_bf16 else 0
+    act, d_act, d_xp = expert_ffn_backward_rows(xp, offsets, wg, wv, wo, d_y, need, N=kept,
+                                                store=routed_store)
+    if store_bf16:
+        d_y = round_bf16(d_y)
     # the packing's backward: each token sums the input gradients of its rows
     d_x = combine(tok, k, dest, None, d_xp, yrow)
     # router
     d_logits = route_backward(logits[tok], idx[tok], gates[tok], d_gates, renorm)
-    dxr, dwr = router_grads(x[tok], inp["w_router"], d_logits, True, full)
+    dxr, _ = router_grads(x[tok], inp["w_router"], d_logits, True, False)
+    dwr = None
+    if full:
+        _, dwr = router_grads(x[tok], inp["w_router"],
+                              round_bf16(d_logits) if store_bf16 else d_logits, False, True)
     d_x += dxr
     if inp.get("shared_w_gate") is not None:
         sg, sv, so = inp["shared_w_gate"], inp["shared_w_val"], inp["shared_w_out"]
         for q in range(sg.shape[0]):
             _, _, dxs = expert_ffn_backward_rows(x, np.array([0, T], np.int32), sg[q:q + 1],
                                                  sv[q:q + 1], so[q:q + 1], dout[tok],
-                                                 tok.astype(np.int64))
+                                                 tok.astype(np.int64),
+                                                 store=(STORE_DY | STORE_ACT | STORE_DACT)
+                                                 if store_bf16 else 0)
             d_x += dxs
     res = dict(logits=logits, idx=idx, gates=gates, counts=counts, offsets=offsets,
                perm_src=perm_src, dest=dest, tokens=tok, y_rows=need, y=y, d_y=d_y, act=act,
@@ -570,7 +609,8 @@ def moe_backward(inp: dict, d_out, tokens=None, pairs=None, scale: float = 1.0,
         dyall = combine_backward_rows(perm_src, np.arange(kept, dtype=np.int64), k, gates, dout)
         res["pairs"] = np.asarray(pairs, np.int64).reshape(-1, 2)
         res["d_w_gate"], res["d_w_val"], res["d_w_out"] = expert_weight_grads(
-            xall, offsets, wg, wv, wo, dyall, res["pairs"], scale)
+            xall, offsets, wg, wv, wo, dyall, res["pairs"], scale,
+            store=(STORE_DY | STORE_ACT | STORE_DACT) if store_bf16 else 0)
     return res
 
 

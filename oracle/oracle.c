@@ -245,6 +245,13 @@ static double round_bf16(double v) {
     return ldexp(nearbyint(ldexp(v, 8 - ex)), ex - 8);
 }
 
+int oracle_round_bf16(double* a, int64_t n)
+{
+    if (!a || n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) a[i] = round_bf16(a[i]);
+    return 0;
+}
+
 int oracle_expert_ffn_rows(const void* x, int xtype, int64_t N, int d, int f, int E,
                            const int32_t* offsets,
                            const void* wg, const void* wv, const void* wo,
@@ -470,6 +477,17 @@ int oracle_expert_ffn_backward_rows(const void* x, int xtype, int64_t N, int d, 
                                     const int64_t* rows, int64_t nrows, int x_compact,
                                     const double* d_y, double* act, double* d_act, double* d_x)
 {
+    return oracle_expert_ffn_backward_rows_h(x, xtype, N, d, f, E, offsets, wg, wv, wo, rows,
+                                             nrows, x_compact, 0, d_y, act, d_act, d_x);
+}
+
+int oracle_expert_ffn_backward_rows_h(const void* x, int xtype, int64_t N, int d, int f, int E,
+                                      const int32_t* offsets,
+                                      const void* wg, const void* wv, const void* wo,
+                                      const int64_t* rows, int64_t nrows, int x_compact,
+                                      int store_bf16, const double* d_y, double* act,
+                                      double* d_act, double* d_x)
+{
     if (!x || !offsets || !wg || !wv || !wo || !rows || !d_y) return -1;
     if (d <= 0 || f <= 0 || E <= 0 || N < 0) return -1;
     if (offsets[0] != 0 || offsets[E] != N) return -2;
@@ -497,14 +515,18 @@ int oracle_expert_ffn_backward_rows(const void* x, int xtype, int64_t N, int d, 
                     v[c] += xi * (double)load_f(wv, xtype, wrow + c);
                 }
             }
-            /* y = h Wo  ->  dh_c = sum_o dy_o Wo[c,o] */
+            /* y = h Wo  ->  dh_c = sum_o dy_o Wo[c,o] (dy as stored) */
             const double* dy = d_y + (size_t)r * d;
+            const int rdy = store_bf16 & ORACLE_STORE_DY;
             for (int c = 0; c < f; ++c) {
                 size_t wrow = wbase + (size_t)c * d;
                 double acc = 0.0;
-                for (int o = 0; o < d; ++o) acc += dy[o] * (double)load_f(wo, xtype, wrow + o);
+                for (int o = 0; o < d; ++o)
+                    acc += (rdy ? round_bf16(dy[o]) : dy[o]) * (double)load_f(wo, xtype, wrow + o);
                 dh[c] = acc;
             }
+            if (store_bf16 & ORACLE_STORE_ACT)
+                for (int c = 0; c < f; ++c) { a[c] = round_bf16(a[c]); v[c] = round_bf16(v[c]); }
             if (act)
                 for (int c = 0; c < f; ++c) {
                     act[(size_t)r * 2 * f + c] = a[c];
@@ -516,8 +538,8 @@ int oracle_expert_ffn_backward_rows(const void* x, int xtype, int64_t N, int d, 
                 double s = 1.0 / (1.0 + exp(-a[c]));
                 double da = dh[c] * v[c] * (s * (1.0 + a[c] * (1.0 - s)));
                 double dv = dh[c] * (a[c] * s);
-                a[c] = da;
-                v[c] = dv;
+                a[c] = (store_bf16 & ORACLE_STORE_DACT) ? round_bf16(da) : da;
+                v[c] = (store_bf16 & ORACLE_STORE_DACT) ? round_bf16(dv) : dv;
             }
             if (d_act)
                 for (int c = 0; c < f; ++c) {
@@ -532,7 +554,7 @@ int oracle_expert_ffn_backward_rows(const void* x, int xtype, int64_t N, int d, 
                     for (int c = 0; c < f; ++c)
                         acc += a[c] * (double)load_f(wg, xtype, wrow + c)
                              + v[c] * (double)load_f(wv, xtype, wrow + c);
-                    d_x[(size_t)r * d + i] = acc;
+                    d_x[(size_t)r * d + i] = (store_bf16 & ORACLE_STORE_DX) ? round_bf16(acc) : acc;
                 }
         }
         free(a);
@@ -548,6 +570,17 @@ int oracle_expert_weight_grads(const void* x, int xtype, int64_t N, int d, int f
                                const double* d_y, const int32_t* pair_e, const int32_t* pair_c,
                                int64_t npairs, double scale,
                                double* dwg, double* dwv, double* dwo)
+{
+    return oracle_expert_weight_grads_h(x, xtype, N, d, f, E, offsets, wg, wv, wo, d_y, pair_e,
+                                        pair_c, npairs, scale, 0, dwg, dwv, dwo);
+}
+
+int oracle_expert_weight_grads_h(const void* x, int xtype, int64_t N, int d, int f, int E,
+                                 const int32_t* offsets,
+                                 const void* wg, const void* wv, const void* wo,
+                                 const double* d_y, const int32_t* pair_e, const int32_t* pair_c,
+                                 int64_t npairs, double scale, int store_bf16,
+                                 double* dwg, double* dwv, double* dwo)
 {
     if (!x || !offsets || !wg || !wv || !wo || !d_y || !pair_e || !pair_c) return -1;
     if (!dwg || !dwv || !dwo || d <= 0 || f <= 0 || E <= 0 || N < 0) return -1;
@@ -572,18 +605,27 @@ int oracle_expert_weight_grads(const void* x, int xtype, int64_t N, int d, int f
                 v += xi * (double)load_f(wv, xtype, wbase + (size_t)i * f + c);
             }
             const double* dy = d_y + (size_t)j * d;
-            for (int o = 0; o < d; ++o) dh += dy[o] * (double)load_f(wo, xtype, wbase + (size_t)c * d + o);
+            const int rdy = store_bf16 & ORACLE_STORE_DY;
+            for (int o = 0; o < d; ++o)
+                dh += (rdy ? round_bf16(dy[o]) : dy[o]) * (double)load_f(wo, xtype, wbase + (size_t)c * d + o);
+            /* h as the forward stored it (from the exact a and v) */
+            double h = a * (1.0 / (1.0 + exp(-a))) * v;
+            if (store_bf16 & ORACLE_STORE_ACT) {
+                h = round_bf16(h);
+                a = round_bf16(a);
+                v = round_bf16(v);
+            }
             double s = 1.0 / (1.0 + exp(-a));
-            double h = a * s * v;
             double da = dh * v * (s * (1.0 + a * (1.0 - s)));
             double dv = dh * (a * s);
+            if (store_bf16 & ORACLE_STORE_DACT) { da = round_bf16(da); dv = round_bf16(dv); }
             /* a = x Wg[:,c]: dWg[i,c] += x_i da; likewise Wv; y = h Wo: dWo[c,o] += h dy_o */
             for (int i = 0; i < d; ++i) {
                 double xi = (double)load_f(x, xtype, (size_t)j * d + i);
                 og[i] += xi * da;
                 ov[i] += xi * dv;
             }
-            for (int o = 0; o < d; ++o) oo[o] += h * dy[o];
+            for (int o = 0; o < d; ++o) oo[o] += h * (rdy ? round_bf16(dy[o]) : dy[o]);
         }
         for (int i = 0; i < d; ++i) { og[i] *= scale; ov[i] *= scale; oo[i] *= scale; }
     }

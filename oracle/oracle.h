@@ -212,6 +212,29 @@ int oracle_expert_ffn_backward_rows(const void* x, int xtype, int64_t N, int d, 
                                     const double* d_y, double* act, double* d_act, double* d_x);
 
 /*
+ * Storage points of bf16 training (each value rounded once to bf16, to
+ * nearest even, where the layer hands it from one kernel to the next):
+ * ORACLE_STORE_DY the expert-output gradients d_y, ORACLE_STORE_ACT the
+ * pre-activations a, v (and h, from the exact a and v), ORACLE_STORE_DACT
+ * their gradients da, dv, ORACLE_STORE_DX the packed rows' input gradients.
+ * oracle_expert_ffn_backward_rows_h and oracle_expert_weight_grads_h take an
+ * OR of them (0: everything exact, as the plain functions).
+ */
+#define ORACLE_STORE_DY 1
+#define ORACLE_STORE_ACT 2
+#define ORACLE_STORE_DACT 4
+#define ORACLE_STORE_DX 8
+int oracle_expert_ffn_backward_rows_h(const void* x, int xtype, int64_t N, int d, int f, int E,
+                                      const int32_t* offsets,
+                                      const void* wg, const void* wv, const void* wo,
+                                      const int64_t* rows, int64_t nrows, int x_compact,
+                                      int store_bf16, const double* d_y, double* act,
+                                      double* d_act, double* d_x);
+
+/* a[i] rounded once to bf16 (to nearest, ties to even), in place. */
+int oracle_round_bf16(double* a, int64_t n);
+
+/*
  * Expert weight gradients of the listed (expert e, hidden column c) pairs,
  * summed over every packed row j of expert e and multiplied by `scale` (1/P
  * for an EP group of P ranks):
@@ -226,6 +249,12 @@ int oracle_expert_weight_grads(const void* x, int xtype, int64_t N, int d, int f
                                const double* d_y, const int32_t* pair_e, const int32_t* pair_c,
                                int64_t npairs, double scale,
                                double* dwg, double* dwv, double* dwo);
+int oracle_expert_weight_grads_h(const void* x, int xtype, int64_t N, int d, int f, int E,
+                                 const int32_t* offsets,
+                                 const void* wg, const void* wv, const void* wo,
+                                 const double* d_y, const int32_t* pair_e, const int32_t* pair_c,
+                                 int64_t npairs, double scale, int store_bf16,
+                                 double* dwg, double* dwv, double* dwo);
 
 /*
  * Per-expert load statistics (a routing variant's by-product). The PithTrain

@@ -118,6 +118,13 @@ static void layer(int xtype, int T, int d, int f, int E, int k, int renorm, floa
     double* dwo = malloc(3 * (size_t)d * sizeof(double));
     EXPECT(oracle_expert_weight_grads(xp, xtype, TK, d, f, E, offsets, wg, wv, wo, dy, pe, pc, 3,
                                       0.25, dwg, dwv, dwo), 0);
+    /* the storage-point variants (bf16 rounding where training stores values) */
+    EXPECT(oracle_expert_ffn_rows_h(xp, xtype, TK, d, f, E, offsets, wg, wv, wo, rows, TK, 0, 1, y), 0);
+    EXPECT(oracle_expert_ffn_backward_rows_h(xp, xtype, TK, d, f, E, offsets, wg, wv, wo, rows, TK,
+                                             0, 15, dy, act, dact, dxp), 0);
+    EXPECT(oracle_expert_weight_grads_h(xp, xtype, TK, d, f, E, offsets, wg, wv, wo, dy, pe, pc, 3,
+                                        0.25, 7, dwg, dwv, dwo), 0);
+    EXPECT(oracle_round_bf16(dy, (int64_t)TK * d), 0);
     double* dl = malloc((size_t)T * E * sizeof(double));
     EXPECT(oracle_route_backward(logits, idx, gates, dg, T, E, k, renorm, dl), 0);
     double* dx = malloc((size_t)T * d * sizeof(double));

@@ -19,6 +19,7 @@ import pytest
 import torch
 
 import oracle
+from expert_dispatch_amd import workloads as W
 
 
 def _layer(seed, T=14, d=10, f=6, E=5, k=2, dtype="f32", shared=0, router_scale=1.5):
@@ -220,3 +221,55 @@ def test_sampled_tokens_equal_full():
     np.testing.assert_array_equal(part["d_x"], full["d_x"][tok])
     np.testing.assert_array_equal(part["d_gates"], full["d_gates"][tok])
     np.testing.assert_array_equal(part["d_logits"], full["d_logits"][tok])
+
+
+def _is_bf16(a):
+    a = np.asarray(a, np.float64)
+    f = a.astype(np.float32)
+    return np.array_equal(f.astype(np.float64), a) and \
+        np.all((f.view(np.uint32) & np.uint32(0xFFFF)) == 0)
+
+
+def test_storage_point_chain_rounds_where_stated_and_stays_close():
+    """store_bf16: the values handed between kernels are bf16 numbers (d_y,
+    a and v, da and dv, the packed rows' input gradients), every gradient
+    stays within a few bf16 roundings of the exact chain (relative L2 below
+    1e-2) and differs from it (the roundings happened)."""
+    inp = W.generate(W.get("qwen3_small"))
+    d_out = W.output_gradient(W.get("qwen3_small"))
+    E, f = inp["w_gate"].shape[0], inp["w_gate"].shape[2]
+    pairs = oracle.all_pairs(E, f)[:: 7]
+    ex = oracle.moe_backward(inp, d_out, pairs=pairs)
+    st = oracle.moe_backward(inp, d_out, pairs=pairs, store_bf16=True)
+    for key in ("d_y", "act", "d_act", "d_x_perm"):
+        assert _is_bf16(st[key]), key
+    for key in ("d_y", "d_act", "d_x_perm", "d_x", "d_gates", "d_logits", "d_w_gate", "d_w_val",
+                "d_w_out", "d_w_router"):
+        a, b = st[key], ex[key]
+        l2 = float(np.sqrt(np.sum((a - b) ** 2) / np.sum(b * b)))
+        assert 0 < l2 < 1e-2 or key in ("d_gates", "d_logits"), (key, l2)
+    # the router weights' gradients come from the fp32 expert outputs: no storage point
+    np.testing.assert_array_equal(st["d_gates"], ex["d_gates"])
+    np.testing.assert_array_equal(st["d_logits"], ex["d_logits"])
+
+
+def test_storage_point_rounding_of_bf16_exact_values_changes_nothing():
+    """With one expert, top-1 routing (weight 1) and a bf16 upstream gradient,
+    d_y = d_out is already a bf16 number: rounding it at its storage point
+    leaves the input-side chain (ORACLE_STORE_DY alone) unchanged."""
+    inp = dict(W.generate(W.get("qwen3_small")))
+    inp.update(k=1, w_router=inp["w_router"][:, :1], bias=None, w_gate=inp["w_gate"][:1],
+               w_val=inp["w_val"][:1], w_out=inp["w_out"][:1])
+    d_out = W.output_gradient(W.get("qwen3_small"))
+    T = inp["x"].shape[0]
+    off = np.array([0, T], np.int32)
+    dy = oracle.widen(d_out)
+    base = oracle.expert_ffn_backward_rows(inp["x"], off, inp["w_gate"], inp["w_val"],
+                                           inp["w_out"], dy)
+    rd = oracle.expert_ffn_backward_rows(inp["x"], off, inp["w_gate"], inp["w_val"],
+                                         inp["w_out"], dy, store=oracle.STORE_DY)
+    for a, b in zip(base, rd):
+        np.testing.assert_array_equal(a, b)
+    ra = oracle.expert_ffn_backward_rows(inp["x"], off, inp["w_gate"], inp["w_val"],
+                                         inp["w_out"], dy, store=oracle.STORE_ACT)
+    assert not np.array_equal(ra[1], base[1])
