@@ -246,9 +246,13 @@ def cpu_baseline(cfg, inp, target_s: float):
             last["o"] = oracle.moe_recv_layer(inp, rows=np.arange(n, dtype=np.int32))
             return time.perf_counter() - t
         total = cfg.N
+    # calibrate in two steps: a 16-token run overstates the cost per token (the
+    # per-expert setup of a tiny batch), so size a ~2 s run from it first
     n0 = min(total, 16)
     t0 = run(n0)
-    n = int(min(total, max(n0, n0 * target_s / max(t0, 1e-3))))
+    n1 = int(min(total, max(n0, n0 * 2.0 / max(t0, 1e-3))))
+    t1 = run(n1) if n1 > n0 else t0
+    n = int(min(total, max(n1, n1 * target_s / max(t1, 1e-3))))
     t = run(n)
     reps = 1
     # the whole workload in less than the target time: repeat it
