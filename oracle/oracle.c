@@ -237,11 +237,14 @@ int oracle_gather(const void* x, int elem_bytes, int64_t d,
 
 /* The value of v rounded once to bf16 (8 significant bits, to nearest, ties
  * to even), straight from double: v = m 2^ex with m in [0.5, 1), so the bf16
- * grid around v has spacing 2^(ex - 8). */
+ * grid around v has spacing 2^(ex - 8). bf16 shares float32's exponent range:
+ * below its smallest normal 2^-126 (ex < -125) the grid is the subnormal one,
+ * of fixed spacing 2^-133. */
 static double round_bf16(double v) {
     if (v == 0.0 || !isfinite(v)) return v;
     int ex = 0;
     (void)frexp(v, &ex);
+    if (ex < -125) ex = -125;
     return ldexp(nearbyint(ldexp(v, 8 - ex)), ex - 8);
 }
 

@@ -273,3 +273,42 @@ def test_storage_point_rounding_of_bf16_exact_values_changes_nothing():
     ra = oracle.expert_ffn_backward_rows(inp["x"], off, inp["w_gate"], inp["w_val"],
                                          inp["w_out"], dy, store=oracle.STORE_ACT)
     assert not np.array_equal(ra[1], base[1])
+
+
+def test_round_bf16_matches_torch_cast_on_fp32_values():
+    """The oracle's bf16 rounding (to nearest, ties to even) equals torch's
+    float32 -> bfloat16 conversion on float32 inputs, ties and subnormals
+    included."""
+    rng = np.random.default_rng(11)
+    bits = rng.integers(0, 2**32, size=20000, dtype=np.uint64).astype(np.uint32)
+    bits = bits[(bits & 0x7F800000) != 0x7F800000]                 # finite only
+    ties = (bits & np.uint32(0xFFFF0000)) | np.uint32(0x8000)       # exactly half-way
+    vals = np.concatenate([bits, ties]).view(np.float32)
+    vals = vals[np.abs(vals) < 3.0e38]                              # no overflow to inf
+    want = torch.from_numpy(vals.copy()).to(torch.bfloat16).float().numpy().astype(np.float64)
+    np.testing.assert_array_equal(oracle.round_bf16(vals), want)
+
+
+def test_each_storage_point_rounds_only_its_own_stage():
+    """ACT rounds only the stored activations, DACT only their gradients,
+    DX only the packed rows' input gradients: each result equals the exact
+    chain's value rounded once to bf16, and the stages before it are left
+    exactly as the exact chain has them."""
+    inp = W.generate(W.get("qwen3_small"))
+    d_out = W.output_gradient(W.get("qwen3_small"))
+    k = inp["k"]
+    idx, gates = oracle.route(inp["x"], inp["w_router"], inp["bias"], k)[1:3]
+    _, offsets, perm_src, _ = oracle.permute(idx, inp["w_gate"].shape[0])
+    x_perm = oracle.gather(inp["x"], perm_src, k)
+    dy = oracle.widen(d_out)[perm_src // k] * gates.reshape(-1)[perm_src][:, None]
+    args = (x_perm, offsets, inp["w_gate"], inp["w_val"], inp["w_out"], dy)
+    act, dact, dx = oracle.expert_ffn_backward_rows(*args)
+    a1, d1, x1 = oracle.expert_ffn_backward_rows(*args, store=oracle.STORE_DX)
+    np.testing.assert_array_equal(a1, act)
+    np.testing.assert_array_equal(d1, dact)
+    np.testing.assert_array_equal(x1, oracle.round_bf16(dx))
+    a2, d2, _ = oracle.expert_ffn_backward_rows(*args, store=oracle.STORE_DACT)
+    np.testing.assert_array_equal(a2, act)
+    np.testing.assert_array_equal(d2, oracle.round_bf16(dact))
+    a3, _, _ = oracle.expert_ffn_backward_rows(*args, store=oracle.STORE_ACT)
+    np.testing.assert_array_equal(a3, oracle.round_bf16(act))
