@@ -20,6 +20,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["api.hip", "route.hip", "permute.hip", "grouped_ffn.hip", "grouped_bwd.hip",
            "combine.hip", "ceiling.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ROCM_LIB = "/opt/rocm/lib"
 
 CFLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -65,6 +66,7 @@ def build(verbose: bool = False, debug: bool = False) -> str:
     # -Bsymbolic: the library's own calls bind inside it, so the release and
     # the debug library can be open in one process side by side
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-Bsymbolic", *objs,
+                    "-L", ROCM_LIB, "-Wl,-rpath," + ROCM_LIB, "-lrocprofiler-sdk-roctx",
                     "-o", tmp], check=True)
     os.replace(tmp, out_lib)
     return out_lib

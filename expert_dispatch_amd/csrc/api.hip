@@ -3,6 +3,8 @@
 // device or copies device -> host.
 #include <algorithm>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "common.hpp"
 
 namespace moe {
@@ -77,6 +79,18 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// A roctx range named after the entry point, open while the call checks its
+// arguments and enqueues its kernels: a marker trace (rocprofv3
+// --marker-trace) shows each call on the host timeline beside the kernels it
+// launched. Without a profiler attached a push/pop is a cheap no-op.
+struct Range {
+    explicit Range(const char* name) { roctxRangePushA(name); }
+    ~Range() { roctxRangePop(); }
+    Range(const Range&) = delete;
+    Range& operator=(const Range&) = delete;
+};
+#define MOE_RANGE() Range moe_range_(__func__)
+
 size_t h_bytes(int N, int f, moe_dtype dt) {
     return moe::align_up((size_t)N * (size_t)f * (size_t)elem_size(dt), 256);
 }
@@ -127,6 +141,7 @@ moe_status moe_route(const void* x, moe_dtype dt, const void* w_router, const fl
                      int T, int d, int E, int k, int renorm, float* logits, int32_t* topk_idx,
                      float* gates, void* stream)
 {
+    MOE_RANGE();
     if (!valid_dtype(dt) || T < 0 || d <= 0 || E <= 0 || k <= 0 || k > E)
         return MOE_ERR_INVALID_ARG;
     if (E > kMaxRouteE || k > kMaxK) return MOE_ERR_UNSUPPORTED;
@@ -148,6 +163,7 @@ moe_status moe_permute(const int32_t* topk_idx, int T, int k, int E, const void*
                        int32_t* dest, void* x_perm, int ld_x_perm, void* ws, size_t ws_bytes,
                        void* stream)
 {
+    MOE_RANGE();
     if (!valid_dtype(dt) || T < 0 || k <= 0 || E <= 0 || d <= 0) return MOE_ERR_INVALID_ARG;
     const int ld = resolve_ld(ld_x_perm, d);
     if (ld < 0) return MOE_ERR_INVALID_ARG;
@@ -165,6 +181,7 @@ moe_status moe_permute_noalloc(const int32_t* topk_idx, int T, int k, int E, con
                                int32_t* perm_src, int32_t* dest, void* x_perm, int ld_x_perm,
                                void* stream)
 {
+    MOE_RANGE();
     if (!valid_dtype(dt) || T < 0 || k <= 0 || E <= 0 || d <= 0) return MOE_ERR_INVALID_ARG;
     const int ld = resolve_ld(ld_x_perm, d);
     if (ld < 0) return MOE_ERR_INVALID_ARG;
@@ -187,6 +204,7 @@ moe_status moe_permute_capacity(const int32_t* topk_idx, int T, int k, int E, in
                                 int32_t* dest, void* x_perm, int ld_x_perm, void* ws,
                                 size_t ws_bytes, void* stream)
 {
+    MOE_RANGE();
     if (!valid_dtype(dt) || T < 0 || k <= 0 || E <= 0 || d <= 0 || capacity < 0)
         return MOE_ERR_INVALID_ARG;
     const int ld = resolve_ld(ld_x_perm, d);
@@ -205,6 +223,7 @@ moe_status moe_permute_range(const int32_t* topk_idx, int T, int k, int e_first,
                              int32_t* offsets, int32_t* perm_src, int32_t* dest, void* x_perm,
                              int ld_x_perm, void* ws, size_t ws_bytes, void* stream)
 {
+    MOE_RANGE();
     if (!valid_dtype(dt) || T < 0 || k <= 0 || E_loc <= 0 || e_first < 0 || d <= 0)
         return MOE_ERR_INVALID_ARG;
     const int ld = resolve_ld(ld_x_perm, d);
@@ -229,6 +248,7 @@ moe_status moe_permute_recv(const int32_t* recv_counts, int S, int E_loc, int N,
                             int32_t* offsets, int32_t* perm_src, int32_t* dest, void* x_perm,
                             int ld_x_perm, void* ws, size_t ws_bytes, void* stream)
 {
+    MOE_RANGE();
     (void)ws; (void)ws_bytes;
     if (!valid_dtype(dt) || S <= 0 || E_loc <= 0 || N < 0 || d <= 0) return MOE_ERR_INVALID_ARG;
     const int ld = resolve_ld(ld_x_perm, d);
@@ -260,6 +280,7 @@ moe_status moe_ffn_gate_up(const void* x_perm, int ld_x_perm, moe_dtype dt, int 
                            int E, const int32_t* offsets, const void* w_gate, const void* w_val,
                            void* h, void* stream)
 {
+    MOE_RANGE();
     moe_status s = check_ffn(dt, N, d, f, E, offsets);
     if (s != MOE_OK) return s;
     const int ldx = resolve_ld(ld_x_perm, d);
@@ -274,6 +295,7 @@ moe_status moe_ffn_down(const void* h, moe_dtype dt, int N, int f, int d, int E,
                         const int32_t* offsets, const void* w_out, void* y, moe_dtype y_dt,
                         void* stream)
 {
+    MOE_RANGE();
     moe_status s = check_ffn(dt, N, d, f, E, offsets);
     if (s != MOE_OK) return s;
     if (!valid_dtype(y_dt)) return MOE_ERR_INVALID_ARG;
@@ -288,6 +310,7 @@ moe_status moe_grouped_ffn(const void* x_perm, int ld_x_perm, moe_dtype dt, int 
                            const void* w_out, void* y, moe_dtype y_dt, void* ws, size_t ws_bytes,
                            void* stream)
 {
+    MOE_RANGE();
     moe_status s = check_ffn(dt, N, d, f, E, offsets);
     if (s != MOE_OK) return s;
     const int ldx = resolve_ld(ld_x_perm, d);
@@ -307,6 +330,7 @@ moe_status moe_combine(const void* y_perm, moe_dtype y_dt, const int32_t* dest,
                        const float* gates, int T, int k, int d, const void* y_shared,
                        moe_dtype sh_dt, void* out, moe_dtype out_dt, void* stream)
 {
+    MOE_RANGE();
     if (!valid_dtype(y_dt) || !valid_dtype(out_dt) || T < 0 || k <= 0 || d <= 0)
         return MOE_ERR_INVALID_ARG;
     if (y_shared && !valid_dtype(sh_dt)) return MOE_ERR_INVALID_ARG;
@@ -328,6 +352,7 @@ size_t moe_route_stats_workspace(int T, int E)
 moe_status moe_route_stats(const float* logits, const int32_t* counts, int T, int E, int k,
                            float* p_mean, float* aux, void* ws, size_t ws_bytes, void* stream)
 {
+    MOE_RANGE();
     if (T <= 0 || E <= 0 || k <= 0 || k > E) return MOE_ERR_INVALID_ARG;
     if ((long long)T * E > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     if (!logits || !p_mean || (aux && !counts)) return MOE_ERR_INVALID_ARG;
@@ -342,6 +367,7 @@ moe_status moe_ffn_gate_up_train(const void* x_perm, int ld_x_perm, moe_dtype dt
                                  int f, int E, const int32_t* offsets, const void* w_gate,
                                  const void* w_val, void* h, void* act, void* stream)
 {
+    MOE_RANGE();
     moe_status s = check_ffn(dt, N, d, f, E, offsets);
     if (s != MOE_OK) return s;
     const int ldx = resolve_ld(ld_x_perm, d);
@@ -357,6 +383,7 @@ moe_status moe_combine_backward(const void* d_out, moe_dtype d_out_dt, const voi
                                 int T, int k, int d, void* d_y, moe_dtype d_y_dt,
                                 float* d_gates, void* stream)
 {
+    MOE_RANGE();
     if (!valid_dtype(d_out_dt) || !valid_dtype(y_dt) || !valid_dtype(d_y_dt) || T < 0 ||
         k <= 0 || d <= 0)
         return MOE_ERR_INVALID_ARG;
@@ -371,6 +398,7 @@ moe_status moe_ffn_down_backward(const void* d_y, moe_dtype dt, int N, int d, in
                                  const int32_t* offsets, const void* w_out, const void* act,
                                  void* d_act, void* stream)
 {
+    MOE_RANGE();
     moe_status s = check_ffn(dt, N, d, f, E, offsets);
     if (s != MOE_OK) return s;
     if (N == 0) return MOE_OK;
@@ -385,6 +413,7 @@ moe_status moe_ffn_gate_up_backward(const void* d_act, moe_dtype dt, int N, int 
                                     const void* w_val, void* d_x_perm, moe_dtype dx_dt,
                                     int accumulate, void* stream)
 {
+    MOE_RANGE();
     moe_status s = check_ffn(dt, N, d, f, E, offsets);
     if (s != MOE_OK) return s;
     if (!valid_dtype(dx_dt)) return MOE_ERR_INVALID_ARG;
@@ -405,6 +434,7 @@ moe_status moe_ffn_weight_grads(const void* x_perm, int ld_x_perm, const void* h
                                 const int32_t* offsets, float scale, float* d_w_gate,
                                 float* d_w_val, float* d_w_out, void* stream)
 {
+    MOE_RANGE();
     moe_status s = check_ffn(dt, N, d, f, E, offsets);
     if (s != MOE_OK) return s;
     const int ldx = resolve_ld(ld_x_perm, d);
@@ -432,6 +462,7 @@ moe_status moe_token_backward(const void* d_x_perm, moe_dtype dxp_dt, const int3
                               const void* w_router, moe_dtype dt, int T, int k, int d, int E,
                               float* d_x, void* ws, size_t ws_bytes, void* stream)
 {
+    MOE_RANGE();
     if (!valid_dtype(dxp_dt) || !valid_dtype(dt) || T < 0 || k <= 0 || k > E || d <= 0)
         return MOE_ERR_INVALID_ARG;
     if (k > kMaxK || (long long)T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
@@ -448,6 +479,7 @@ moe_status moe_route_backward(const float* logits, const int32_t* topk_idx, cons
                               const float* d_gates, int T, int E, int k, int renorm,
                               float* d_logits, void* d_logits_bf16, void* stream)
 {
+    MOE_RANGE();
     if (T < 0 || E <= 0 || k <= 0 || k > E) return MOE_ERR_INVALID_ARG;
     if (k > kMaxK || (long long)T * E > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     if (T == 0) return MOE_OK;
@@ -471,6 +503,7 @@ moe_status moe_router_backward(const void* x, const void* w_router, moe_dtype dt
                                int accumulate, float* d_w_router, void* ws, size_t ws_bytes,
                                void* stream)
 {
+    MOE_RANGE();
     if (!valid_dtype(dt) || T < 0 || d <= 0 || E <= 0) return MOE_ERR_INVALID_ARG;
     if ((long long)T * std::max(d, E) > (1LL << 40) || (long long)T * E > INT32_MAX)
         return MOE_ERR_UNSUPPORTED;

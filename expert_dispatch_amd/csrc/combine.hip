@@ -1,8 +1,9 @@
 // Weighted combine / un-permute.
 //
-// "Three axes of Parallelism", Dispatch, expert computation and combine: undo
-// the original packing, multiply each expert output by its router weight and
-// sum the K outputs of each token, restoring [T,D]. Written as a gather per
+// "Three axes of Parallelism", Dispatch, expert computation and combine: each
+// packed expert output goes back to its token, scaled by that slot's router
+// weight, and a token's k contributions are added, giving the [T,D] layout
+// again. Written as a gather per
 // token (the deterministic form of the scatter-add, no atomics): one
 // wavefront per token reads its k packed rows (indices and weights held in
 // lanes 0..k-1 and broadcast by shuffles), sums them in fp32 in slot order,

@@ -184,9 +184,10 @@ moe_status moe_permute_capacity(const int32_t* topk_idx, int T, int k, int E, in
 /*
  * Packing of one rank's expert range in the all-gather / reduce-scatter
  * layout (SpecForge PR "expert parallelism for MoE drafters on the FSDP2
- * backend", What this adds: all-gather the group's tokens, run the
- * replicated router on them, compute only the locally owned experts for all
- * of them, reduce-scatter the partial outputs). The rank owns global experts
+ * backend", What this adds: every rank of the group receives all of the
+ * group's tokens by an all-gather, routes them with the same router weights,
+ * evaluates only the experts it owns, and a reduce-scatter sums the partial
+ * outputs back to the ranks that own the tokens). The rank owns global experts
  * [e_first, e_first + E_loc): an assignment with an id in that range goes to
  * local expert id - e_first; any other is dropped (dest = -1, no packed row;
  * moe_combine skips it, so its output is this rank's partial sum).

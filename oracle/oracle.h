@@ -74,9 +74,9 @@ int oracle_permute_capacity(const int32_t* idx, int64_t TK, int E, int64_t capac
 /*
  * Packing of one rank's expert range in the all-gather / reduce-scatter
  * layout [SpecForge PR "expert parallelism for MoE drafters on the FSDP2
- * backend", "What this adds": all-gather the group's tokens, run the
- * replicated router on them, compute only the locally owned experts for all
- * of them, reduce-scatter the partial outputs]: the rank owns global experts
+ * backend", What this adds: each rank gets all of the group's tokens by an
+ * all-gather, routes them with the same router, evaluates only its own
+ * experts, and a reduce-scatter sums the partial outputs per token owner]: the rank owns global experts
  * [e_first, e_first + E_loc). An assignment whose id lies in that range goes
  * to local expert idx - e_first, packed as in oracle_permute; any other is
  * dropped (dest = -1). Fails (-1) on a bad range.
