@@ -570,7 +570,7 @@ def moe_backward(inp: dict, d_out, tokens=None, pairs=None, scale: float = 1.0,
         need = need[need >= 0]
     wg, wv, wo = inp["w_gate"], inp["w_val"], inp["w_out"]
     xp = gather(x, perm_src[need], k)
-    y = expert_ffn_rows(xp, offsets, wg, wv, wo, need, N=kept)
+    y = expert_ffn_rows(xp, offsets, wg, wv, wo, need, N=kept, round_h=store_bf16)
     yrow = np.full(max(kept, 1), -1, np.int64)
     yrow[need] = np.arange(need.shape[0])
     # combine: out[t] = sum_s g[t,s] y[dest[t,s]]

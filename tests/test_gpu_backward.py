@@ -10,15 +10,14 @@ pre-activation and packed-input gradients per packed row, and the expert and
 router weight gradients. Reduced workloads are compared in full; the full
 Qwen3-30B-A3B-shaped workload in full as well (every token, every packed row
 and every hidden column of every expert); the d = 4096 stress workload on
-sampled tokens and a few hidden columns of every expert. Floating-point bar (tests/util.py check_grad): fp32 data as in
-the forward, max relative error <= 1e-5; bf16 data, relative L2 error <=
-2e-2 and max error <= 0.1 of the reference's RMS (a bf16-stored gradient
-after its own storage rounding) against the oracle's chain with every value
-rounded to bf16 at the storage points where training hands it between
-kernels, and relative L2 error <= 2e-2 against the exact chain. (Against the
-exact chain alone the largest of the 5 x 10^7 d_act elements of the full
-Qwen3-shaped layer is 0.13 of the RMS off: the bf16 d_y feeding dh, and the
-stored pre-activations, in the tails of the distribution.)"""
+sampled tokens and a few hidden columns of every expert. Floating-point bar
+(tests/util.py check_grad): fp32 data as in the forward, max relative error
+<= 1e-5; bf16 data, against the oracle's chain with every value rounded to
+bf16 at the storage points where training hands it between kernels: the
+forward's max error <= 2e-2 of the reference's RMS beyond two bf16 ulps of
+each element (room for rounding flips at its own storage point and at one
+of its inputs), and relative L2 error <= 2e-2; against the exact chain,
+relative L2 error <= 2e-2."""
 import numpy as np
 import pytest
 import torch
@@ -92,12 +91,11 @@ def _check_backward(name, full, capacity=None, scale=1.0, renorm=True, pairs_per
     e = {}
     e["d_gates"] = check_grad(to_numpy(g["d_gates"])[tok], o["d_gates"], dt, f"{name} d_gates")
     e["d_logits"] = check_grad(to_numpy(g["d_logits"])[tok], o["d_logits"], dt, f"{name} d_logits")
-    e["d_y"] = check_grad(to_numpy(g["d_y"].index_select(0, rows_t)), o["d_y"], dt, f"{name} d_y",
-                          stored_bf16=True)
+    e["d_y"] = check_grad(to_numpy(g["d_y"].index_select(0, rows_t)), o["d_y"], dt, f"{name} d_y")
     e["d_act"] = check_grad(to_numpy(g["d_act"].index_select(0, rows_t)), o["d_act"], dt,
-                            f"{name} d_act", stored_bf16=True)
+                            f"{name} d_act")
     e["d_x_perm"] = check_grad(to_numpy(g["d_x_perm"].index_select(0, rows_t)), o["d_x_perm"],
-                               dt, f"{name} d_x_perm", stored_bf16=g["d_x_perm"].dtype == torch.bfloat16)
+                               dt, f"{name} d_x_perm")
     e["d_x"] = check_grad(to_numpy(g["d_x"])[tok], o["d_x"], dt, f"{name} d_x")
     pe, pc = pairs[:, 0], pairs[:, 1]
     dwg = to_numpy(g["d_w_gate"])[pe, :, pc]
