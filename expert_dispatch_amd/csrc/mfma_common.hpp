@@ -187,7 +187,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 // silu(z) = z * sigmoid(z) with the hardware exp2 and reciprocal (about 1 ulp
-// each; h is rounded to bf16 right after, 2^-9 relative). For z -> -inf,
+// each; h is rounded to bf16 right after, up to 2^-8 relative). For z -> -inf,
 // 1 + exp(-z) overflows to +inf and the reciprocal gives 0, so silu -> -0.
 __device__ __forceinline__ float silu_fast(float z) {
     return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));

@@ -238,7 +238,7 @@ moe_status moe_permute_recv(const int32_t* recv_counts, int S, int E_loc, int N,
  * stored as bf16 (round to nearest even) between the two products; with
  * MOE_F32 it stays fp32. y is rounded once to y_dt: MOE_BF16 halves the bytes
  * the down product writes and the combine reads, MOE_F32 keeps the fp32 sums.
- * Accuracy of a bf16 y: that one rounding (up to 2^-9 of an element) alone
+ * Accuracy of a bf16 y: that one rounding (up to 2^-8 of an element) alone
  * reaches 2.0-2.6e-2 of the RMS at the largest SwiGLU outputs of the
  * measured workloads, so a bf16-stored y (and a bf16 moe_combine output)
  * misses the 2e-2-of-RMS max-error bar stated for bf16 data with fp32

@@ -10,7 +10,7 @@ same launch configuration as the benchmark.
 
 Outputs the caller asks to store in bf16 (expert outputs y_perm, the layer
 output) carry one more rounding than the fp32 sums the bar is stated for,
-up to 2^-9 of each element; on the heavy-tailed SwiGLU outputs that alone
+up to 2^-8 of each element; on the heavy-tailed SwiGLU outputs that alone
 reaches 2.0-2.6e-2 of the RMS at the largest elements, so they miss the
 strict bar by their own storage rounding. They are held to the bar after
 that rounding is taken off each element (check_rows with an allowance).
@@ -518,7 +518,7 @@ def test_deterministic_bitwise():
 
 def test_bf16_outputs():
     """y_perm and out both stored as bf16 (the narrow-output variant). Each
-    carries its own storage rounding (up to 2^-9 of the element) beyond the
+    carries its own storage rounding (up to 2^-8 of the element) beyond the
     fp32 sums the bar is stated for; with that rounding (and, for out, the
     rounding of the y rows it sums) taken off, they meet 2e-2 of the RMS."""
     inp = _inputs("qwen3_small")
