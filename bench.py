@@ -204,6 +204,23 @@ def traffic_for(stage: str, workload: str):
         return None
 
 
+def input_digests(inp: dict) -> dict:
+    """xxh64 of the bytes of every generated input array (the seeded values
+    both the GPU run and the oracle read), so two runs can show they used the
+    same inputs."""
+    import xxhash
+    out = {}
+    for key in sorted(inp):
+        v = inp[key]
+        parts = [v] if isinstance(v, np.ndarray) else list(v) if isinstance(v, (list, tuple)) else []
+        if parts and all(isinstance(a, np.ndarray) for a in parts):
+            h = xxhash.xxh64()
+            for a in parts:
+                h.update(np.ascontiguousarray(a).view(np.uint8).reshape(-1))
+            out[key] = h.hexdigest()
+    return out
+
+
 def host_info() -> dict:
     """CPU model and thread settings of the host the oracle runs on."""
     model = None
@@ -773,7 +790,8 @@ def main():
                    "kept_rows": kept, "T": cfg.T,
                    "k": cfg.k, "N": cfg.N, "d": d, "f": f, "E": E, "shared": cfg.shared,
                    "rows": rows, "load_max_over_mean": round(float(counts.max() / max(counts.mean(), 1e-9)), 3),
-                   "empty_experts": int((counts == 0).sum())},
+                   "empty_experts": int((counts == 0).sum()),
+                   "input_xxh64": input_digests(inp)},
         **({"partial": {"E_global": cfg.E_global, "e_first": cfg.e_first,
                         "partial_dtype": "bf16" if os_ == 2 else "f32",
                         "tokens_with_local_expert": touched}} if gathered else {}),
