@@ -538,8 +538,8 @@ def main_backward(args):
         "backward_ms": round(sum(stage_us[n] for n in bwd) / 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded Gaussian inputs, weights and output gradient)",
-        "config": {"workload": cfg.name, "T": T, "k": k, "d": d, "f": f, "E": E,
-                   "kept_rows": int(counts.sum())},
+        "config": {"workload": cfg.name, "seed": cfg.seed, "T": T, "k": k, "d": d, "f": f,
+                   "E": E, "kept_rows": int(counts.sum())},
         "roofline": {"kernel": dominant, "bound": dom["bound"], "achieved": round(dom["achieved"], 1),
                      "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4),
                      "traffic": traffic_for(dominant, cfg.name + "/backward")},
@@ -783,7 +783,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if es == 2 else "f32",
         "data": "synthetic (seeded Gaussian inputs and weights of the stated shapes)",
-        "config": {"workload": cfg.name, "description": cfg.description,
+        "config": {"workload": cfg.name, "description": cfg.description, "seed": cfg.seed,
                    "y_perm_dtype": "bf16" if ys == 2 else "f32",
                    "capacity_factor": None if gathered else args.capacity_factor,
                    "router_weights": "softmax over the selected" if renorm else "full softmax",
