@@ -363,7 +363,7 @@ __global__ __launch_bounds__(kT, 1) void nt_mfma_kernel(NtArgs p, const int32_t*
     __shared__ int scratch[kT / kWave + 1];
     const TileList L = build_tile_list(offsets, rows, E, (p.N + kN - 1) / kN, s_sched,
                                        s_sched + kMaxE + 1, s_sched + 2 * kMaxE + 1, scratch);
-    const int total = L.total_big + L.total_small;
+    const int total = L.total_big + L.split + L.total_small;
     const int G = gridDim.x;
     const int base = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
     for (int t = base; t < total; t += G) {

@@ -435,15 +435,20 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void ffn_mfma_kernel(
     __shared__ __attribute__((aligned(1024))) uint16_t smem[kSmemElems];
     __shared__ int s_sched[3 * kMaxE + 1];
     __shared__ int scratch[kMfmaThreads / kWave + 1];
+    // a 128-row tile costs about 7/8 (gate_up) and 3/4 (down) of a 256-row one
+    // (the weight panel it streams is the same): the cost ratio for splitting
+    // the last partial round of 256-row tiles
     const TileList L = build_tile_list(offsets, N, E, NC / BNT, s_sched, s_sched + kMaxE + 1,
-                                       s_sched + 2 * kMaxE + 1, scratch);
-    const int total = L.total_big + L.total_small;
+                                       s_sched + 2 * kMaxE + 1, scratch, GATE_UP ? 7 : 6);
+    const int total = L.total_big + L.split + L.total_small;
     const int G = gridDim.x;
     const int base = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
     for (int t = base; t < total; t += G) {
         const Tile tile = decode_tile(L, t);
-        if (tile.bm == 128)
+        if (tile.bm == 128 && tile.stream)
             ffn_mfma_tile<GATE_UP, Y_BF16, 128, true, SAVE>(A, lda, K, NC, B0, B1, C, act, tile, smem);
+        else if (tile.bm == 128)
+            ffn_mfma_tile<GATE_UP, Y_BF16, 128, false, SAVE>(A, lda, K, NC, B0, B1, C, act, tile, smem);
         else if (tile.stream)
             ffn_mfma_tile<GATE_UP, Y_BF16, 256, true, SAVE>(A, lda, K, NC, B0, B1, C, act, tile, smem);
         else

@@ -77,21 +77,41 @@ __device__ bool schedule_tile(const int32_t* __restrict__ offsets, int N, int E,
 // expert with n rows gets n / 256 tiles of 256 rows; a remainder above 128
 // rows one more 256-row tile, a remainder of at most 128 rows one 128-row tile
 // (a 256-row tile would be more than half padding there). Every row tile
-// spans all n_tiles column tiles. Tile indices [0, big) are the 256-row tiles
-// (expert by expert; inside an expert groups of kGroupM row tiles sweep all
-// column tiles, row tile fastest), [big, big + small) the 128-row tiles.
+// spans all n_tiles column tiles. Tile indices [0, big - split) are 256-row
+// tiles (expert by expert; inside an expert groups of kGroupM row tiles sweep
+// all column tiles, row tile fastest); [big - split, big + split) the last
+// `split` 256-row tiles of that order, each as two 128-row halves (upper half
+// first); then the small 128-row tiles.
 struct TileList {
     const int* off;     // [E+1] clamped offsets
     const int* big;     // [E] exclusive prefix of 256-row tiles x n_tiles
     const int* small;   // [E] exclusive prefix of 128-row tiles x n_tiles
     int E, n_tiles, total_big, total_small;
+    int split;          // 256-row tiles run as two 128-row halves
 };
 
+// Cost, in eighths of a 256-row tile, of the busiest block of a persistent
+// grid of G blocks when the list holds nb 256-row tiles followed by ns
+// 128-row tiles of cost c8 each, dealt cyclically (block position r takes
+// tiles r, r + G, ...): every position gets nb / G and ns / G of them; the
+// first nb % G positions one more 256-row tile, and the ns % G positions
+// from nb % G on (wrapping past G onto the first ones) one more 128-row tile.
+__device__ __forceinline__ int tail_cost(int nb, int ns, int G, int c8) {
+    const int qb = nb / G, rb = nb % G, qs = ns / G, ms = ns % G;
+    int extra = 0;
+    if (rb > 0) extra = 8 + (rb + ms > G ? c8 : 0);
+    if (ms > 0) extra = max(extra, c8);
+    return 8 * qb + c8 * qs + extra;
+}
+
 // All threads of the block must call it. s_off needs E+1 ints, s_big and
-// s_small E ints each.
+// s_small E ints each. half_c8 > 0: the cost of a 128-row tile in eighths of a
+// 256-row one; when the last, partial round of 256-row tiles over the grid
+// (gridDim.x blocks) would end the launch later than running those tiles as
+// 128-row halves, by tail_cost, they are split. 0 keeps every tile whole.
 __device__ TileList build_tile_list(const int32_t* __restrict__ offsets, int N, int E,
                                     int n_tiles, int* s_off, int* s_big, int* s_small,
-                                    int* scratch)
+                                    int* scratch, int half_c8 = 0)
 {
     const int tid = threadIdx.x;
     // offsets NULL: one group of all N rows
@@ -120,6 +140,13 @@ __device__ TileList build_tile_list(const int32_t* __restrict__ offsets, int N, 
     L.n_tiles = n_tiles;
     L.total_big = __builtin_amdgcn_readfirstlane(block_exclusive_scan_lds(s_big, E, scratch));
     L.total_small = __builtin_amdgcn_readfirstlane(block_exclusive_scan_lds(s_small, E, scratch));
+    L.split = 0;
+    const int G = gridDim.x;
+    const int rem = L.total_big % G;
+    if (half_c8 > 0 && rem > 0 &&
+        tail_cost(L.total_big - rem, L.total_small + 2 * rem, G, half_c8) <
+            tail_cost(L.total_big, L.total_small, G, half_c8))
+        L.split = rem;
     return L;
 }
 
@@ -134,9 +161,17 @@ __device__ __forceinline__ int find_owner(const int* pre, int E, int t) {
     return lo;
 }
 
-// Tile t of the list, 0 <= t < total_big + total_small.
+// Tile t of the list, 0 <= t < total_big + split + total_small.
 __device__ Tile decode_tile(const TileList& L, int t) {
     Tile tile;
+    int half = -1;   // 0, 1: upper or lower half of a split 256-row tile
+    if (t >= L.total_big - L.split && t < L.total_big + L.split) {
+        const int u = t - (L.total_big - L.split);
+        half = u & 1;
+        t = L.total_big - L.split + (u >> 1);
+    } else if (t >= L.total_big + L.split) {
+        t -= L.split;   // the small tiles, shifted by the split's extra entries
+    }
     if (t < L.total_big) {
         const int e = find_owner(L.big, L.E, t);
         const int rows_lo = L.off[e];
@@ -153,6 +188,13 @@ __device__ Tile decode_tile(const TileList& L, int t) {
         tile.seg_end = rows_hi;
         tile.bm = 256;
         tile.stream = mt < 2;
+        if (half >= 0) {
+            // both halves read the same weight panel at about the same time
+            // on one XCD (consecutive list entries): keep it cacheable
+            tile.m0 += 128 * half;
+            tile.bm = 128;
+            tile.stream = 0;
+        }
     } else {
         t -= L.total_big;
         const int e = find_owner(L.small, L.E, t);
